@@ -1,0 +1,194 @@
+"""CPU oracle for the W4A4 + INT8-outlier hybrid linear layer.
+
+TEST INFRASTRUCTURE ONLY. The product package never imports this module. Only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it. It shares no code with the HIP path.
+
+The arithmetic lives in ``w4a4_oracle.c`` (plain C, gcc, OpenMP over rows and
+output positions). This wrapper only converts dtypes and shapes:
+
+* fp16 inputs are widened to fp32 with numpy (exact);
+* the fp64 result y* is rounded to fp16 with numpy's float64 -> float16 cast
+  (round to nearest even, pinned in ``tests/test_oracle_pins.py``).
+
+Sources: "QUIK: Towards End-to-End 4-Bit Inference on Generative Large
+Language Models" (abstract) and "Atom: Low-bit Quantization for Efficient and
+Accurate LLM Serving" (research summary page: Summary paragraph 2, Key points
+item 5, Interesting ideas I1 and I3). Readings R1-R8 are listed in the header
+of ``w4a4_oracle.c``.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against facts
+that do not come from the oracle (closed forms, brute force on tiny inputs,
+invariances and a hand-worked fixture in ``tests/golden/``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w4a4_oracle.c")
+_LIB = os.path.join(_HERE, "libw4a4_oracle.so")
+_lib = None
+
+_i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+
+
+def build() -> str:
+    """Compile the C oracle with gcc (no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    c_i32, c_i64 = ctypes.c_int32, ctypes.c_int64
+    lib.w4o_make_perm.argtypes = [c_i32, _i32p, c_i32, _i32p]
+    lib.w4o_make_perm.restype = ctypes.c_int
+    lib.w4o_quantize_block.argtypes = [_f32p, c_i32, c_i32, _i8p, ctypes.POINTER(ctypes.c_float)]
+    lib.w4o_quantize_block.restype = None
+    lib.w4o_num_groups.argtypes = [c_i32, c_i32]
+    lib.w4o_num_groups.restype = c_i32
+    lib.w4o_quantize_rows.argtypes = [_f32p, c_i64, c_i32, c_i64, _i32p, c_i32, c_i32,
+                                      _i8p, _f32p, _i8p, _f32p]
+    lib.w4o_quantize_rows.restype = ctypes.c_int
+    lib.w4o_pack_nibbles.argtypes = [_i8p, c_i64, c_i32, c_i64, _u8p]
+    lib.w4o_pack_nibbles.restype = None
+    lib.w4o_linear_at.argtypes = [_i8p, _f32p, _i8p, _f32p, _i8p, _f32p, _i8p, _f32p,
+                                  c_i32, c_i32, c_i32, _i32p, _i32p, c_i64,
+                                  _i32p, _i32p, _f64p]
+    lib.w4o_linear_at.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_groups(K_n: int, group: int) -> int:
+    return int(_load().w4o_num_groups(K_n, group))
+
+
+def make_perm(K: int, outlier_idx) -> np.ndarray:
+    """Stable outlier permutation (reading R6). Raises ValueError on bad indices."""
+    o = np.ascontiguousarray(np.asarray(outlier_idx, dtype=np.int32).reshape(-1))
+    perm = np.zeros(max(K, 1), dtype=np.int32)
+    if _load().w4o_make_perm(K, o if o.size else np.zeros(1, np.int32), o.size, perm) != 0:
+        raise ValueError("outlier indices out of range or repeated")
+    return perm[:K]
+
+
+def quantize_block(v, qmax: int):
+    """Quantize one block; returns (codes int8, scale float32)."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32).reshape(-1))
+    q = np.zeros(max(v.size, 1), dtype=np.int8)
+    s = ctypes.c_float(0.0)
+    _load().w4o_quantize_block(v if v.size else np.zeros(1, np.float32), v.size, qmax, q,
+                               ctypes.byref(s))
+    return q[: v.size], np.float32(s.value)
+
+
+def quantize_rows(X, perm, n_out: int, group: int):
+    """Reorder + quantize every row of X [rows, K] (fp16 or fp32).
+
+    Returns (q4 int8 [rows, K_n], s4 f32 [rows, G], q8 int8 [rows, n_out],
+    s8 f32 [rows]), codes unpacked one per byte.
+    """
+    X = np.asarray(X)
+    rows, K = X.shape
+    Xf = np.ascontiguousarray(X.astype(np.float32))
+    K_n = K - n_out
+    G = num_groups(K_n, group) if K_n >= 0 else 0
+    q4 = np.zeros((rows, K_n), np.int8)
+    s4 = np.zeros((rows, G), np.float32)
+    q8 = np.zeros((rows, n_out), np.int8)
+    s8 = np.zeros(rows, np.float32)
+    pad = lambda a, dt: a if a.size else np.zeros(1, dt)  # noqa: E731
+    rc = _load().w4o_quantize_rows(pad(Xf, np.float32), rows, K, K,
+                                   pad(np.ascontiguousarray(perm, np.int32), np.int32),
+                                   n_out, group, pad(q4, np.int8), pad(s4, np.float32),
+                                   pad(q8, np.int8), pad(s8, np.float32))
+    if rc != 0:
+        raise ValueError("group must divide K - n_out")
+    return q4, s4, q8, s8
+
+
+def pack_nibbles(q4, pitch: int) -> np.ndarray:
+    """Pack INT4 codes two per byte, low nibble first, zero padded to pitch."""
+    q4 = np.ascontiguousarray(q4, dtype=np.int8)
+    rows, K_n = q4.shape
+    out = np.zeros((rows, pitch), np.uint8)
+    if rows and pitch:
+        _load().w4o_pack_nibbles(q4 if q4.size else np.zeros(1, np.int8), rows, K_n,
+                                 pitch, out)
+    return out
+
+
+def linear_at(qa, qw, group: int, m_idx, n_idx):
+    """Integer GEMM + fp64 dequant at output pairs (m_idx[p], n_idx[p]).
+
+    qa / qw are the 4-tuples returned by quantize_rows for X and W.
+    Returns (acc4 int32 [P, G], acc8 int32 [P], ystar float64 [P]).
+    """
+    qa4, sa4, qa8, sa8 = qa
+    qw4, sw4, qw8, sw8 = qw
+    K_n, n_out = qa4.shape[1], qa8.shape[1]
+    G = num_groups(K_n, group)
+    m_idx = np.ascontiguousarray(m_idx, np.int32)
+    n_idx = np.ascontiguousarray(n_idx, np.int32)
+    P = m_idx.size
+    acc4 = np.zeros((P, G), np.int32)
+    acc8 = np.zeros(P, np.int32)
+    y = np.zeros(P, np.float64)
+    pad = lambda a, dt: np.ascontiguousarray(a, dt) if a.size else np.zeros(1, dt)  # noqa: E731
+    rc = _load().w4o_linear_at(pad(qa4, np.int8), pad(sa4, np.float32), pad(qa8, np.int8),
+                               pad(sa8, np.float32), pad(qw4, np.int8), pad(sw4, np.float32),
+                               pad(qw8, np.int8), pad(sw8, np.float32), K_n, n_out, group,
+                               pad(m_idx, np.int32), pad(n_idx, np.int32), P,
+                               pad(acc4, np.int32), pad(acc8, np.int32), pad(y, np.float64))
+    if rc != 0:
+        raise OverflowError("accumulator outside int32")
+    return acc4, acc8, y
+
+
+def to_fp16(ystar) -> np.ndarray:
+    """fp64 -> fp16, round to nearest even (numpy's direct double->half cast)."""
+    return np.asarray(ystar, np.float64).astype(np.float16)
+
+
+def linear(X, W, outlier_idx, group: int):
+    """Whole layer on small inputs: every output position.
+
+    Returns a dict with perm, the quantized operands, acc4 [G, M, N],
+    acc8 [M, N], ystar [M, N] (fp64) and Y [M, N] (fp16).
+    """
+    X, W = np.asarray(X), np.asarray(W)
+    M, K = X.shape
+    N = W.shape[0]
+    perm = make_perm(K, outlier_idx)
+    n_out = int(np.asarray(outlier_idx).size)
+    qa = quantize_rows(X, perm, n_out, group)
+    qw = quantize_rows(W, perm, n_out, group)
+    mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32),
+                         indexing="ij")
+    acc4, acc8, y = linear_at(qa, qw, group, mm.reshape(-1), nn.reshape(-1))
+    G = acc4.shape[1]
+    return {
+        "perm": perm, "qa": qa, "qw": qw,
+        "acc4": acc4.reshape(M, N, G).transpose(2, 0, 1).copy(),
+        "acc8": acc8.reshape(M, N),
+        "ystar": y.reshape(M, N),
+        "Y": to_fp16(y.reshape(M, N)),
+    }
