@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused W4A4 + INT8-outlier linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
+
+One step is one pass of the layer's run-time path over one batch: the
+activation producer (reorder + INT4/INT8 quantize, ``w4a4_quant_reorder_act``)
+then the mixed-precision GEMM with its fp32 epilogue (``w4a4_outlier_gemm``);
+together they are exactly what ``w4a4_quant_gemm`` launches. Weights are
+quantized and packed once before timing, as the layer does offline.
+
+Inputs are seeded synthetic tensors already resident in HBM. Buffer sets
+(X, packed W, quantized activations, Y) are rotated so that the working set
+of consecutive steps exceeds 512 MB and the 256 MB Infinity Cache cannot
+serve them.
+
+Prints one JSON line. ``value`` is the whole-step throughput in TOPS
+(2 M N K integer ops per step). ``roofline`` describes the dominant kernel,
+the GEMM: its algorithmic ops (or bytes, for memory-bound decode shapes) per
+launch divided by its mean duration, measured with HIP events recorded on
+the launch stream around every launch inside the timed region.
+``cpu_baseline`` times the CPU oracle on the host cores on a bounded row
+sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5033.2      # 256 CU x 2.4 GHz x 8192 dense int8 ops / clk / CU
+PEAK_HBM_GBS = 8000.0        # HBM3E
+ROTATE_BYTES = 512 << 20
+
+from mixed_precision_integer_amd import workloads as wl  # noqa: E402
+
+WORKLOADS = {"tiny": wl.TINY, "qproj": wl.QPROJ_7B, "upproj": wl.UPPROJ_7B,
+             "decode": wl.DECODE_65B, "downproj": wl.DOWNPROJ_65B}
+
+
+def work_counts(w, M):
+    """Algorithmic ops and bytes of one layer call (zero padding not counted)."""
+    N, K, n_out, K_n = w.N, w.K, w.n_out, w.K_n
+    G = (K_n // w.group if w.group else 1) if K_n else 0
+    ops = 2 * M * N * K
+    w_bytes = N * K_n / 2 + N * n_out + 4 * N * G + 4 * N
+    a_bytes = M * K_n / 2 + M * n_out + 4 * M * G + 4 * M
+    gemm_bytes = w_bytes + a_bytes + 2 * M * N
+    producer_bytes = 2 * M * K + a_bytes
+    return ops, gemm_bytes, producer_bytes
+
+
+def traffic_record(workload_name, M):
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if they
+    were taken on the current GEMM source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    src = open(os.path.join(ROOT, "mixed_precision_integer_amd", "csrc", "gemm_kernels.hip"),
+               "rb").read()
+    sha = hashlib.sha256(src).hexdigest()[:16]
+    rec = json.load(open(path)).get(f"{workload_name}:M={M}")
+    if not rec or rec.get("gemm_source_sha256_16") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, X, W, outliers, budget_s):
+    """The CPU oracle on the host: producer + integer GEMM + fp64 dequant for a
+    row sample of X against all N output channels (weights pre-quantized)."""
+    import oracle
+    perm = oracle.make_perm(w.K, outliers)
+    qw = oracle.quantize_rows(W, perm, w.n_out, w.group)
+    nn = np.arange(w.N, dtype=np.int32)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        qa = oracle.quantize_rows(X[:rows], perm, w.n_out, w.group)
+        mm = np.repeat(np.arange(rows, dtype=np.int32), w.N)
+        oracle.linear_at(qa, qw, w.group, mm, np.tile(nn, rows))
+        return time.perf_counter() - t0
+
+    M = X.shape[0]
+    r0 = min(M, 2)
+    t0 = run(r0)
+    rows = int(min(M, max(r0, math.floor(r0 * budget_s / max(t0, 1e-6)))))
+    t = run(rows)
+    return {
+        "value": 2.0 * rows * w.N * w.K / t / 1e12,
+        "unit": "TOPS",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"{rows} of {M} token rows x all {w.N} output channels: producer, integer "
+                   f"GEMM and fp64 dequant (weights quantized beforehand); {t:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qproj", choices=sorted(WORKLOADS))
+    ap.add_argument("--m", type=int, default=None, help="token rows (decode sweep)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the layer shards by rows or columns with no communication, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixed_precision_integer_amd as w4
+
+    w = WORKLOADS[args.workload]
+    M = args.m if args.m is not None else w.M
+    X, W, outliers = wl.draw_workload(w, M if M <= w.M else None)
+    if M > X.shape[0]:
+        raise SystemExit(f"--m {M} exceeds the workload's {w.M} rows")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    perm = torch.from_numpy(w4.make_perm(w.K, outliers)).to(dev)
+    Xd = torch.from_numpy(X).to(dev)
+    wq = w4.pack_int4_weights(torch.from_numpy(W).to(dev), perm, w.n_out, w.group)
+
+    def clone_op(op):
+        return w4.QuantizedOperand(*[None if t is None else t.clone() for t in op[:4]], *op[4:])
+
+    one_set = (Xd.numel() * 2 + M * w.N * 2 + sum(t.numel() * t.element_size()
+                                                   for t in wq[:4] if t is not None) * 2)
+    n_sets = max(2, math.ceil(ROTATE_BYTES / one_set) + 1)
+    plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq)) for _ in range(n_sets)]
+
+    for i in range(args.warmup):
+        p = plans[i % n_sets]
+        p.produce()
+        p.gemm()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        p = plans[i % n_sets]
+        ev[i][0].record()
+        p.produce()
+        ev[i][1].record()
+        p.gemm()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / K
+    prod_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ops, gemm_bytes, prod_bytes = work_counts(w, M)
+    value = ops / (ms_step * 1e-3) / 1e12
+
+    mem_bound = ops / gemm_bytes < PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mem_bound:
+        ach = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS}
+    else:
+        ach = ops / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": ach / PEAK_INT8_TOPS}
+    roof["kernel"] = "gemm_kernel (w4a4_outlier_gemm)"
+    roof["traffic"] = traffic_record(w.name, M)
+
+    # the result is checked against a fused call (same kernels, same bits)
+    yf = torch.empty_like(plans[0].out)
+    w4.quant_gemm(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
+    torch.cuda.synchronize()
+    if not torch.equal(yf, plans[0].out):
+        raise SystemExit("fused call and producer + GEMM disagree")
+
+    out = {
+        "metric": "W4A4+outlier linear TOPS & % INT8-MFMA peak (prefill); GB/s % HBM (decode)",
+        "value": value,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "N": w.N, "K": w.K, "n_out": w.n_out,
+                   "group": w.group, "buffer_sets": n_sets},
+        "roofline": roof,
+        "kernels": {
+            "producer_us": prod_ms * 1e3,
+            "producer_GBps": prod_bytes / (prod_ms * 1e-3) / 1e9,
+            "producer_hbm_frac": prod_bytes / (prod_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "gemm_us": gemm_ms * 1e3,
+            "gemm_TOPS": ops / (gemm_ms * 1e-3) / 1e12,
+            "gemm_GBps": gemm_bytes / (gemm_ms * 1e-3) / 1e9,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, X, W, outliers, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * w4a4.h -- C ABI of the MI355X (gfx950) W4A4 + INT8-outlier linear layer.
+ *
+ * The layer is the hybrid scheme of QUIK ("QUIK: Towards End-to-End 4-Bit
+ * Inference on Generative Large Language Models", abstract) in the form the
+ * Atom summary page gives it ("Atom: Low-bit Quantization for Efficient and
+ * Accurate LLM Serving", Summary paragraph 2; Key points item 5; Interesting
+ * ideas I1-I3):
+ *   - a small set O of outlier input channels is moved to a contiguous tail
+ *     (perm = ascending channels not in O, then ascending channels in O) and
+ *     kept in INT8;
+ *   - every other channel is quantized to INT4, symmetric round-to-nearest
+ *     with an absmax scale per row (group == 0) or per group of `group`
+ *     consecutive reordered channels;
+ *   - activation scales are computed for every input at run time, weights are
+ *     quantized once;
+ *   - Y = sum_t sa4[m,t] sw4[n,t] acc4_t[m,n] + sa8[m] sw8[n] acc8[m,n], with
+ *     exact int32 accumulators and an fp32 epilogue rounded to fp16.
+ *
+ * Quantizer, for every block v of a row (INT4: qmax = 7, INT8: qmax = 127):
+ *   s = fl32(max|v| / qmax);  q = s == 0 ? 0 : clamp(rint(fl32(v / s)),
+ *   -qmax-1, qmax), with correctly rounded fp32 division and ties to even.
+ *
+ * Conventions for every call below
+ *   - All matrices are row-major. X is fp16 [M, ldx] (tokens x channels),
+ *     W is fp16 [N, ldw] (output channels x channels, torch.nn.Linear layout),
+ *     Y is fp16 [M, ldy].
+ *   - K_n = K - n_out; G = w4a4_num_groups(K_n, group).
+ *   - Packed INT4 operand: uint8 [rows, w4a4_pitch4_bytes(K_n)]; byte i of a
+ *     row = (q[2i] & 0xF) | (q[2i+1] & 0xF) << 4 (two's complement nibbles,
+ *     low nibble first); bytes past K_n/2 are zero and are part of the
+ *     format.
+ *   - INT8 tail: int8 [rows, w4a4_pitch8_bytes(n_out)], zero padded.
+ *   - INT4 scales: fp32 [rows, G] row-major; INT8 tail scales: fp32 [rows]
+ *     (0 when n_out == 0).
+ *   - Device pointers are caller-owned device memory; the library allocates
+ *     and frees nothing. Device pointers must be 16-byte aligned (fp16 Y:
+ *     2-byte aligned); ldx and ldw must be multiples of 8 elements.
+ *   - Every device call is asynchronous on `stream` (a hipStream_t; NULL is
+ *     the null stream). Host checks run first; on any error nothing is
+ *     launched and nothing is written. A launch failure returns
+ *     W4A4_ERR_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - M == 0 or N == 0 is a valid empty call and launches nothing.
+ *   - Calls are stateless and thread-safe; calls that share output buffers
+ *     on different streams race.
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w4a4_status {
+    W4A4_OK = 0,
+    W4A4_ERR_INVALID_ARG = 1, /* null pointer, bad size, group not dividing K_n, ld too small,
+                                 repeated / out-of-range outlier index                       */
+    W4A4_ERR_UNSUPPORTED = 2, /* shape outside the kernels' int32 range guard or a group size
+                                 the GPU kernels do not implement                            */
+    W4A4_ERR_ALIGNMENT = 3,   /* misaligned pointer or leading dimension                     */
+    W4A4_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed                  */
+    W4A4_ERR_WORKSPACE = 5    /* workspace smaller than the query function asks for          */
+} w4a4_status;
+
+typedef void *w4a4_stream; /* hipStream_t */
+
+/* Human-readable name of a status code (static storage). */
+const char *w4a4_status_string(int status);
+
+/* Number of INT4 scale groups per row: K_n / group, 1 when group == 0, 0 when
+ * K_n == 0. Returns -1 when group < 0 or group does not divide K_n. */
+int32_t w4a4_num_groups(int32_t K_n, int32_t group);
+
+/* Row pitch in bytes of a packed INT4 operand: round_up(K_n, 128) / 2. */
+int64_t w4a4_pitch4_bytes(int32_t K_n);
+
+/* Row pitch in bytes of an INT8 tail operand: round_up(n_out, 64). */
+int64_t w4a4_pitch8_bytes(int32_t n_out);
+
+/* Host helper: perm[0..K) = ascending channels not in outlier_idx, then the
+ * outlier channels ascending (Atom summary page, Interesting ideas I1: the
+ * outlier channels become one contiguous block at the end). outlier_idx may
+ * be unsorted. Host pointers. INVALID_ARG on a repeated or out-of-range
+ * index, K <= 0, or n_out outside [0, K]. The caller copies perm to the
+ * device for the calls below. */
+w4a4_status w4a4_make_perm(int32_t K, const int32_t *outlier_idx, int32_t n_out,
+                           int32_t *perm);
+
+/* Activation producer (Atom summary page, Summary paragraph 2: scales
+ * computed for each input at run time; reordering fused into one pass).
+ * For every token row m of X: gather by perm, quantize the K_n head to INT4
+ * (scale per row or per group) and the n_out tail to INT8, pack.
+ *   X    device fp16 [M, ldx]          perm device int32 [K] (a permutation)
+ *   Aq4  device uint8 [M, pitch4]      Aq8  device int8 [M, pitch8] (NULL if n_out == 0)
+ *   sa4  device fp32 [M, G]            sa8  device fp32 [M] (written 0 if n_out == 0)
+ * GPU group sizes: 0 or a multiple of 128 dividing K_n (else UNSUPPORTED).
+ * perm is trusted to be a permutation of [0, K); an index outside [0, K) is
+ * undefined behaviour. */
+w4a4_status w4a4_quant_reorder_act(const void *X, int64_t ldx, const int32_t *perm,
+                                   int32_t M, int32_t K, int32_t n_out, int32_t group,
+                                   void *Aq4, void *Aq8, float *sa4, float *sa8,
+                                   w4a4_stream stream);
+
+/* Offline weight preparation (QUIK abstract: outlier weights kept in higher
+ * precision; Atom summary page: INT4 weights, 8-bit outlier channels in the
+ * same reordered layout). The same quantizer applied to the N rows of W, with
+ * the same perm as the activations (outliers are input channels).
+ *   W    device fp16 [N, ldw]   Wq4 device uint8 [N, pitch4]   Wq8 device int8 [N, pitch8]
+ *   sw4  device fp32 [N, G]     sw8 device fp32 [N]
+ * Same argument rules as w4a4_quant_reorder_act. */
+w4a4_status w4a4_pack_int4_weights(const void *W, int64_t ldw, const int32_t *perm,
+                                   int32_t N, int32_t K, int32_t n_out, int32_t group,
+                                   void *Wq4, void *Wq8, float *sw4, float *sw8,
+                                   w4a4_stream stream);
+
+/* Bytes of device workspace w4a4_outlier_gemm needs for this shape (0 means
+ * none; a NULL workspace is then allowed). */
+size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                         int32_t group);
+
+/* Mixed-precision GEMM (Atom summary page, Summary paragraph 2 and
+ * Interesting ideas I3; Key points item 5 for the symmetric epilogue):
+ * INT4 x INT4 over the K_n head plus INT8 x INT8 over the outlier tail, int32
+ * accumulation, fp32 scale epilogue, fp16 output
+ *   Y[m, n] = fp16( sum_t sa4[m,t] sw4[n,t] acc4_t[m,n] + sa8[m] sw8[n] acc8[m,n] ).
+ * Operands in the layouts above (from the two calls above). Y device fp16
+ * [M, ldy], ldy >= N. GPU constraint (UNSUPPORTED otherwise): K_n * 16384 <
+ * 2^31 and n_out * 16384 < 2^31 (int32 range of the widened accumulators). */
+w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4,
+                              const float *sa8, const void *Wq4, const void *Wq8,
+                              const float *sw4, const float *sw8, int32_t M, int32_t N,
+                              int32_t K, int32_t n_out, int32_t group, void *Y,
+                              int64_t ldy, void *workspace, size_t workspace_bytes,
+                              w4a4_stream stream);
+
+/* Test export of the same main loop: instead of Y, writes the exact integer
+ * accumulators acc4 device int32 [G, M, N] (one slice per scale group) and
+ * acc8 device int32 [M, N] (NULL allowed when n_out == 0). Same constraints
+ * as w4a4_outlier_gemm. */
+w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *Wq4,
+                                  const void *Wq8, int32_t M, int32_t N, int32_t K,
+                                  int32_t n_out, int32_t group, int32_t *acc4,
+                                  int32_t *acc8, w4a4_stream stream);
+
+/* Bytes of device workspace w4a4_quant_gemm needs: the quantized activations
+ * (Aq4, Aq8, sa4, sa8 for M rows) plus the GEMM's own workspace. */
+size_t w4a4_quant_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                       int32_t group);
+
+/* The fused layer (Atom summary page, Interesting ideas I2: quantization and
+ * reordering run as part of the layer's own launches): w4a4_quant_reorder_act
+ * on X into the caller's workspace, then w4a4_outlier_gemm with the
+ * pre-packed weights, both on `stream`. */
+w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
+                            const void *Wq8, const float *sw4, const float *sw8, int32_t M,
+                            int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                            int64_t ldy, void *workspace, size_t workspace_bytes,
+                            w4a4_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H */

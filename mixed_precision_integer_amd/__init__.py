@@ -1,0 +1,337 @@
+"""MI355X-native W4A4 + INT8-outlier hybrid linear layer (QUIK / Atom style).
+
+Python binding over the C ABI in ``include/w4a4.h`` (``libw4a4.so``, built
+with ``python -m mixed_precision_integer_amd.build``). This module only
+marshals arguments: every step of the layer runs in the HIP kernels. PyTorch
+provides device memory and the current stream.
+
+Names follow the C ABI: ``quant_reorder_act``, ``pack_int4_weights``,
+``w4a4_outlier_gemm`` (+ ``w4a4_outlier_gemm_i32``, the accumulator export)
+and ``quant_gemm`` map to ``w4a4_quant_reorder_act``,
+``w4a4_pack_int4_weights``, ``w4a4_outlier_gemm`` (+ ``_i32``) and
+``w4a4_quant_gemm``.
+
+There is no fallback: if the library is missing or no GPU is present the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a4.so")
+_lib = None
+
+STATUS = {0: "W4A4_OK", 1: "W4A4_ERR_INVALID_ARG", 2: "W4A4_ERR_UNSUPPORTED",
+          3: "W4A4_ERR_ALIGNMENT", 4: "W4A4_ERR_HIP", 5: "W4A4_ERR_WORKSPACE"}
+
+EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_pitch8_bytes",
+            "w4a4_make_perm", "w4a4_quant_reorder_act", "w4a4_pack_int4_weights",
+            "w4a4_outlier_gemm_workspace_bytes", "w4a4_outlier_gemm", "w4a4_outlier_gemm_i32",
+            "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm")
+
+
+class W4A4Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def lib():
+    """Load libw4a4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mixed_precision_integer_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.w4a4_status_string.argtypes = [ctypes.c_int]
+    L.w4a4_status_string.restype = ctypes.c_char_p
+    L.w4a4_num_groups.argtypes = [i32, i32]
+    L.w4a4_num_groups.restype = i32
+    L.w4a4_pitch4_bytes.argtypes = [i32]
+    L.w4a4_pitch4_bytes.restype = i64
+    L.w4a4_pitch8_bytes.argtypes = [i32]
+    L.w4a4_pitch8_bytes.restype = i64
+    L.w4a4_make_perm.argtypes = [i32, vp, i32, vp]
+    L.w4a4_make_perm.restype = ctypes.c_int
+    for name in ("w4a4_quant_reorder_act", "w4a4_pack_int4_weights"):
+        f = getattr(L, name)
+        f.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        f.restype = ctypes.c_int
+    for name in ("w4a4_outlier_gemm_workspace_bytes", "w4a4_quant_gemm_workspace_bytes"):
+        f = getattr(L, name)
+        f.argtypes = [i32, i32, i32, i32, i32]
+        f.restype = sz
+    L.w4a4_outlier_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                    vp, i64, vp, sz, vp]
+    L.w4a4_outlier_gemm.restype = ctypes.c_int
+    L.w4a4_outlier_gemm_i32.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.w4a4_outlier_gemm_i32.restype = ctypes.c_int
+    L.w4a4_quant_gemm.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64,
+                                  vp, sz, vp]
+    L.w4a4_quant_gemm.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _ok(status: int, call: str):
+    if status != 0:
+        raise W4A4Error(status, call)
+
+
+# ---------------------------------------------------------------------------
+# host helpers
+# ---------------------------------------------------------------------------
+def num_groups(K_n: int, group: int) -> int:
+    return int(lib().w4a4_num_groups(K_n, group))
+
+
+def pitch4_bytes(K_n: int) -> int:
+    return int(lib().w4a4_pitch4_bytes(K_n))
+
+
+def pitch8_bytes(n_out: int) -> int:
+    return int(lib().w4a4_pitch8_bytes(n_out))
+
+
+def make_perm(K: int, outlier_idx) -> np.ndarray:
+    """Host int32 permutation: non-outliers ascending, then outliers ascending."""
+    o = np.ascontiguousarray(np.asarray(outlier_idx, dtype=np.int32).reshape(-1))
+    perm = np.zeros(max(K, 1), np.int32)
+    _ok(lib().w4a4_make_perm(K, o.ctypes.data if o.size else None, o.size, perm.ctypes.data),
+        "w4a4_make_perm")
+    return perm[:K]
+
+
+# ---------------------------------------------------------------------------
+# device calls
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _check(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dim")
+
+
+class QuantizedOperand(NamedTuple):
+    """Quantized rows in the ABI layout (activations or weights)."""
+    q4: object      # uint8 [rows, pitch4]
+    q8: object      # int8 [rows, pitch8] (None when n_out == 0)
+    s4: object      # fp32 [rows, G]
+    s8: object      # fp32 [rows]
+    K: int
+    n_out: int
+    group: int
+
+
+def _quant_args(src, perm, op: QuantizedOperand):
+    rows, K = src.shape
+    return (src.data_ptr(), src.stride(0) if rows else K, perm.data_ptr(), rows, K, op.n_out,
+            op.group, _nz(op.q4), _nz(op.q8), _nz(op.s4), _nz(op.s8), _stream())
+
+
+def _quant_rows(fn, name, src, perm, n_out, group):
+    torch = _torch()
+    _check(src, torch.float16, name, 2)
+    _check(perm, torch.int32, "perm", 1)
+    op = alloc_operand(src.shape[0], src.shape[1], n_out, group, src.device)
+    _ok(fn(*_quant_args(src, perm, op)), name)
+    return op
+
+
+def alloc_operand(rows: int, K: int, n_out: int, group: int, device) -> QuantizedOperand:
+    """Empty device buffers in the ABI layout for `rows` quantized rows."""
+    torch = _torch()
+    K_n = K - n_out
+    G = num_groups(K_n, group)
+    if G < 0:
+        raise ValueError("group must divide K - n_out")
+    return QuantizedOperand(
+        torch.empty((rows, pitch4_bytes(K_n)), dtype=torch.uint8, device=device),
+        torch.empty((rows, pitch8_bytes(n_out)), dtype=torch.int8, device=device) if n_out else None,
+        torch.empty((rows, G), dtype=torch.float32, device=device),
+        torch.empty((rows,), dtype=torch.float32, device=device), K, n_out, group)
+
+
+def quant_reorder_act(X, perm, n_out: int, group: int) -> QuantizedOperand:
+    """Runtime activation producer: reorder + INT4/INT8 quantize every token row."""
+    return _quant_rows(lib().w4a4_quant_reorder_act, "w4a4_quant_reorder_act", X, perm, n_out,
+                       group)
+
+
+def pack_int4_weights(W, perm, n_out: int, group: int) -> QuantizedOperand:
+    """Offline weight preparation with the same quantizer (rows = output channels)."""
+    return _quant_rows(lib().w4a4_pack_int4_weights, "w4a4_pack_int4_weights", W, perm, n_out,
+                       group)
+
+
+def _gemm_ptrs(a: QuantizedOperand, w: QuantizedOperand):
+    if (a.K, a.n_out, a.group) != (w.K, w.n_out, w.group):
+        raise ValueError("activation and weight quantization parameters differ")
+    return a.q4, a.q8, a.s4, a.s8, w.q4, w.q8, w.s4, w.s8
+
+
+def _nz(t):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _gemm_args(a: QuantizedOperand, w: QuantizedOperand, out, ws):
+    M, N = a.s8.shape[0], w.s8.shape[0]
+    return (*[_nz(t) for t in _gemm_ptrs(a, w)], M, N, a.K, a.n_out, a.group, out.data_ptr(),
+            out.stride(0) if M else N, _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+
+
+def outlier_gemm_workspace_bytes(M: int, N: int, K: int, n_out: int, group: int) -> int:
+    return int(lib().w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group))
+
+
+def w4a4_outlier_gemm(a: QuantizedOperand, w: QuantizedOperand, out=None):
+    """Y[M, N] fp16 = INT4 GEMM + INT8 outlier GEMM + fp32 scale epilogue."""
+    torch = _torch()
+    M, N = a.s8.shape[0], w.s8.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.s8.device)
+    _check(out, torch.float16, "out", 2)
+    ws_bytes = outlier_gemm_workspace_bytes(M, N, a.K, a.n_out, a.group)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=out.device) if ws_bytes else None
+    _ok(lib().w4a4_outlier_gemm(*_gemm_args(a, w, out, ws)), "w4a4_outlier_gemm")
+    return out
+
+
+def w4a4_outlier_gemm_i32(a: QuantizedOperand, w: QuantizedOperand):
+    """Accumulator export of the same main loop: (acc4 int32 [G, M, N], acc8 int32 [M, N])."""
+    torch = _torch()
+    M, N = a.s8.shape[0], w.s8.shape[0]
+    G = num_groups(a.K - a.n_out, a.group)
+    dev = a.s8.device
+    acc4 = torch.zeros((G, M, N), dtype=torch.int32, device=dev)
+    acc8 = torch.zeros((M, N), dtype=torch.int32, device=dev)
+    _ok(lib().w4a4_outlier_gemm_i32(_nz(a.q4), _nz(a.q8), _nz(w.q4), _nz(w.q8), M, N, a.K,
+                                    a.n_out, a.group, _nz(acc4), _nz(acc8) if a.n_out else None,
+                                    _stream()), "w4a4_outlier_gemm_i32")
+    return acc4, acc8
+
+
+def quant_gemm_workspace_bytes(M: int, N: int, K: int, n_out: int, group: int) -> int:
+    return int(lib().w4a4_quant_gemm_workspace_bytes(M, N, K, n_out, group))
+
+
+def quant_gemm(X, perm, w: QuantizedOperand, out=None, workspace=None):
+    """The fused layer: activation producer + mixed-precision GEMM on one stream."""
+    torch = _torch()
+    _check(X, torch.float16, "X", 2)
+    _check(perm, torch.int32, "perm", 1)
+    M, K = X.shape
+    N = w.s8.shape[0]
+    if K != w.K:
+        raise ValueError("X and weights disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(out, torch.float16, "out", 2)
+    need = quant_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check(workspace, torch.uint8, "workspace", 1)
+    _ok(lib().w4a4_quant_gemm(X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.q4),
+                              _nz(w.q8), _nz(w.s4), _nz(w.s8), M, N, K, w.n_out, w.group,
+                              out.data_ptr(), out.stride(0) if M else N, workspace.data_ptr(),
+                              workspace.numel(), _stream()), "w4a4_quant_gemm")
+    return out
+
+
+class W4A4Linear:
+    """A linear layer y = x W^T with W held as packed INT4 + INT8 outlier columns."""
+
+    def __init__(self, weight, outlier_idx, group: int = 0):
+        torch = _torch()
+        K = weight.shape[1]
+        self.outlier_idx = np.asarray(outlier_idx, np.int32)
+        self.perm = torch.from_numpy(make_perm(K, self.outlier_idx)).to(weight.device)
+        self.n_out = int(self.outlier_idx.size)
+        self.group = group
+        self.weight = pack_int4_weights(weight, self.perm, self.n_out, group)
+        self._ws = None
+
+    def __call__(self, X, out=None):
+        need = quant_gemm_workspace_bytes(X.shape[0], self.weight.s8.shape[0], self.weight.K,
+                                          self.n_out, self.group)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = _torch().empty(max(need, 1), dtype=_torch().uint8, device=X.device)
+        return quant_gemm(X, self.perm, self.weight, out=out, workspace=self._ws)
+
+
+class LayerPlan:
+    """Arguments of one layer call, marshalled once.
+
+    ``fused()`` is ``w4a4_quant_gemm``; ``produce()`` and ``gemm()`` are its two
+    halves (``w4a4_quant_reorder_act`` into a pre-allocated operand, then
+    ``w4a4_outlier_gemm``), which launch the same kernels. Each call is one
+    ctypes call on the stream that was current when the plan was made.
+    """
+
+    def __init__(self, X, perm, w: QuantizedOperand, out=None):
+        torch = _torch()
+        _check(X, torch.float16, "X", 2)
+        _check(perm, torch.int32, "perm", 1)
+        M, K = X.shape
+        N = w.s8.shape[0]
+        self.out = out if out is not None else torch.empty((M, N), dtype=torch.float16,
+                                                           device=X.device)
+        self.a = alloc_operand(M, K, w.n_out, w.group, X.device)
+        need = quant_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+        gws = outlier_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
+        self.gws = torch.empty(gws, dtype=torch.uint8, device=X.device) if gws else None
+        self._keep = (X, perm, w)
+        L = lib()
+        self._q, self._g, self._f = (L.w4a4_quant_reorder_act, L.w4a4_outlier_gemm,
+                                     L.w4a4_quant_gemm)
+        self._qa = _quant_args(X, perm, self.a)
+        self._ga = _gemm_args(self.a, w, self.out, self.gws)
+        self._fa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.q4), _nz(w.q8),
+                    _nz(w.s4), _nz(w.s8), M, N, K, w.n_out, w.group, self.out.data_ptr(),
+                    self.out.stride(0) if M else N, self.ws.data_ptr(), self.ws.numel(),
+                    _stream())
+
+    def produce(self):
+        st = self._q(*self._qa)
+        if st:
+            raise W4A4Error(st, "w4a4_quant_reorder_act")
+
+    def gemm(self):
+        st = self._g(*self._ga)
+        if st:
+            raise W4A4Error(st, "w4a4_outlier_gemm")
+
+    def fused(self):
+        st = self._f(*self._fa)
+        if st:
+            raise W4A4Error(st, "w4a4_quant_gemm")
+        return self.out

@@ -1,0 +1,294 @@
+// Host side of the C ABI declared in include/w4a4.h: argument checks, then
+// kernel launches on the caller's stream. Nothing here allocates device
+// memory; all buffers belong to the caller.
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/w4a4.h"
+#include "w4a4_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxLds = 160 * 1024;       // LDS per workgroup on gfx950
+constexpr int64_t kAccLimit = int64_t(1) << 31;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape rules shared by every device call.
+w4a4_status check_shape(int32_t rows, int32_t K, int32_t n_out, int32_t group) {
+    if (rows < 0 || K <= 0 || n_out < 0 || n_out > K || group < 0)
+        return W4A4_ERR_INVALID_ARG;
+    const int32_t K_n = K - n_out;
+    if (group > 0 && K_n % group != 0)
+        return W4A4_ERR_INVALID_ARG;
+    if (group % 128 != 0)                       // GPU kernels: 0 or multiples of 128
+        return W4A4_ERR_UNSUPPORTED;
+    // widened INT4 operands carry 16 x 16; |code product| <= 64 (INT4), 16384 (INT8)
+    if ((int64_t)K_n * 64 * 256 >= kAccLimit || (int64_t)n_out * 16384 >= kAccLimit)
+        return W4A4_ERR_UNSUPPORTED;
+    return W4A4_OK;
+}
+
+w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t rows,
+                       int32_t K, int32_t n_out, int32_t group, void *q4, void *q8, float *s4,
+                       float *s8, w4a4_stream stream) {
+    w4a4_status st = check_shape(rows, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    const int32_t K_n = K - n_out;
+    const int32_t G = w4a4_num_groups(K_n, group);
+    if (ld < K)
+        return W4A4_ERR_INVALID_ARG;
+    if (rows == 0)
+        return W4A4_OK;                         // empty call: pointers are not used
+    if (!src || !perm)
+        return W4A4_ERR_INVALID_ARG;
+    if ((K_n > 0 && (!q4 || !s4)) || (n_out > 0 && (!q8 || !s8)))
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(src, 16) || ld % 8 != 0 || !aligned(perm, 16) || (q4 && !aligned(q4, 16)) ||
+        (q8 && !aligned(q8, 16)) || (s4 && !aligned(s4, 4)) || (s8 && !aligned(s8, 4)))
+        return W4A4_ERR_ALIGNMENT;
+    const int64_t lds = round_up(K, 8) * 2 + (group > 0 ? (int64_t)((K_n + 7) / 8 + G) * 4 : 0);
+    if (lds > kMaxLds)
+        return W4A4_ERR_UNSUPPORTED;
+    w4a4::QuantArgs a;
+    a.src = static_cast<const _Float16 *>(src);
+    a.ld = ld;
+    a.perm = perm;
+    a.rows = rows;
+    a.K = K;
+    a.n_out = n_out;
+    a.K_n = K_n;
+    a.group = group;
+    a.G = G;
+    a.q4 = static_cast<uint8_t *>(q4);
+    a.q8 = static_cast<int8_t *>(q8);
+    a.s4 = s4;
+    a.s8 = s8;
+    a.pitch4 = w4a4_pitch4_bytes(K_n);
+    a.pitch8 = n_out > 0 ? w4a4_pitch8_bytes(n_out) : 0;
+    if (w4a4::launch_quant_rows(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+w4a4_status gemm_check(const void *Aq4, const void *Aq8, const void *Wq4, const void *Wq8,
+                       int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
+    if (N < 0)
+        return W4A4_ERR_INVALID_ARG;
+    w4a4_status st = check_shape(M, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    const int32_t K_n = K - n_out;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if ((K_n > 0 && (!Aq4 || !Wq4)) || (n_out > 0 && (!Aq8 || !Wq8)))
+        return W4A4_ERR_INVALID_ARG;
+    if ((Aq4 && !aligned(Aq4, 16)) || (Wq4 && !aligned(Wq4, 16)) || (Aq8 && !aligned(Aq8, 16)) ||
+        (Wq8 && !aligned(Wq8, 16)))
+        return W4A4_ERR_ALIGNMENT;
+    return W4A4_OK;
+}
+
+w4a4::GemmArgs gemm_args(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
+                         const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
+                         int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
+    w4a4::GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    const int32_t K_n = K - n_out;
+    a.a4 = static_cast<const uint8_t *>(Aq4);
+    a.a8 = static_cast<const int8_t *>(Aq8);
+    a.w4 = static_cast<const uint8_t *>(Wq4);
+    a.w8 = static_cast<const int8_t *>(Wq8);
+    a.sa4 = sa4;
+    a.sa8 = sa8;
+    a.sw4 = sw4;
+    a.sw8 = sw8;
+    a.M = M;
+    a.N = N;
+    a.K_n = K_n;
+    a.n_out = n_out;
+    a.group = group;
+    a.G = w4a4_num_groups(K_n, group);
+    a.pitch4 = w4a4_pitch4_bytes(K_n);
+    a.pitch8 = n_out > 0 ? w4a4_pitch8_bytes(n_out) : 0;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a4_status_string(int status) {
+    switch (status) {
+    case W4A4_OK: return "W4A4_OK";
+    case W4A4_ERR_INVALID_ARG: return "W4A4_ERR_INVALID_ARG";
+    case W4A4_ERR_UNSUPPORTED: return "W4A4_ERR_UNSUPPORTED";
+    case W4A4_ERR_ALIGNMENT: return "W4A4_ERR_ALIGNMENT";
+    case W4A4_ERR_HIP: return "W4A4_ERR_HIP";
+    case W4A4_ERR_WORKSPACE: return "W4A4_ERR_WORKSPACE";
+    default: return "W4A4_ERR_UNKNOWN";
+    }
+}
+
+int32_t w4a4_num_groups(int32_t K_n, int32_t group) {
+    if (K_n < 0 || group < 0 || (group > 0 && K_n % group != 0))
+        return -1;
+    if (K_n == 0)
+        return 0;
+    return group > 0 ? K_n / group : 1;
+}
+
+int64_t w4a4_pitch4_bytes(int32_t K_n) { return K_n <= 0 ? 0 : round_up(K_n, 128) / 2; }
+
+int64_t w4a4_pitch8_bytes(int32_t n_out) { return n_out <= 0 ? 0 : round_up(n_out, 64); }
+
+w4a4_status w4a4_make_perm(int32_t K, const int32_t *outlier_idx, int32_t n_out, int32_t *perm) {
+    if (K <= 0 || n_out < 0 || n_out > K || !perm || (n_out > 0 && !outlier_idx))
+        return W4A4_ERR_INVALID_ARG;
+    std::vector<unsigned char> is_out(K, 0);
+    for (int32_t i = 0; i < n_out; ++i) {
+        const int32_t c = outlier_idx[i];
+        if (c < 0 || c >= K || is_out[c])
+            return W4A4_ERR_INVALID_ARG;
+        is_out[c] = 1;
+    }
+    int32_t head = 0, tail = K - n_out;
+    for (int32_t j = 0; j < K; ++j)
+        perm[is_out[j] ? tail++ : head++] = j;
+    return W4A4_OK;
+}
+
+w4a4_status w4a4_quant_reorder_act(const void *X, int64_t ldx, const int32_t *perm, int32_t M,
+                                   int32_t K, int32_t n_out, int32_t group, void *Aq4, void *Aq8,
+                                   float *sa4, float *sa8, w4a4_stream stream) {
+    return quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream);
+}
+
+w4a4_status w4a4_pack_int4_weights(const void *W, int64_t ldw, const int32_t *perm, int32_t N,
+                                   int32_t K, int32_t n_out, int32_t group, void *Wq4, void *Wq8,
+                                   float *sw4, float *sw8, w4a4_stream stream) {
+    return quant_rows(W, ldw, perm, N, K, n_out, group, Wq4, Wq8, sw4, sw8, stream);
+}
+
+size_t w4a4_outlier_gemm_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t) {
+    return 0;
+}
+
+w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
+                              const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
+                              int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group,
+                              void *Y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                              w4a4_stream stream) {
+    w4a4_status st = gemm_check(Aq4, Aq8, Wq4, Wq8, M, N, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    const int32_t K_n = K - n_out;
+    if (ldy < N)
+        return W4A4_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if (!Y || (K_n > 0 && (!sa4 || !sw4)) || (n_out > 0 && (!sa8 || !sw8)))
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(Y, 2) || (sa4 && !aligned(sa4, 4)) || (sw4 && !aligned(sw4, 4)) ||
+        (sa8 && !aligned(sa8, 4)) || (sw8 && !aligned(sw8, 4)))
+        return W4A4_ERR_ALIGNMENT;
+    if (workspace_bytes < w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group))
+        return W4A4_ERR_WORKSPACE;
+    (void)workspace;
+    w4a4::GemmArgs a = gemm_args(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group);
+    a.y = static_cast<_Float16 *>(Y);
+    a.ldy = ldy;
+    if (w4a4::launch_gemm(a, false, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *Wq4,
+                                  const void *Wq8, int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                  int32_t group, int32_t *acc4, int32_t *acc8,
+                                  w4a4_stream stream) {
+    w4a4_status st = gemm_check(Aq4, Aq8, Wq4, Wq8, M, N, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    const int32_t K_n = K - n_out;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if ((K_n > 0 && !acc4) || (n_out > 0 && !acc8))
+        return W4A4_ERR_INVALID_ARG;
+    if ((acc4 && !aligned(acc4, 4)) || (acc8 && !aligned(acc8, 4)))
+        return W4A4_ERR_ALIGNMENT;
+    w4a4::GemmArgs a = gemm_args(Aq4, Aq8, nullptr, nullptr, Wq4, Wq8, nullptr, nullptr, M, N, K,
+                                 n_out, group);
+    a.acc4_out = acc4;
+    a.acc8_out = acc8;
+    if (w4a4::launch_gemm(a, true, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+// Workspace of the fused call: Aq4 | Aq8 | sa4 | sa8, each 256-byte aligned,
+// then the GEMM's own workspace.
+static void quant_gemm_layout(int32_t M, int32_t K, int32_t n_out, int32_t group, size_t off[5]) {
+    const int32_t K_n = K - n_out;
+    const int32_t G = w4a4_num_groups(K_n, group);
+    off[0] = 0;
+    off[1] = off[0] + round_up((int64_t)M * w4a4_pitch4_bytes(K_n), 256);
+    off[2] = off[1] + round_up((int64_t)M * w4a4_pitch8_bytes(n_out), 256);
+    off[3] = off[2] + round_up((int64_t)M * (G > 0 ? G : 0) * 4, 256);
+    off[4] = off[3] + round_up((int64_t)M * 4, 256);
+}
+
+size_t w4a4_quant_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                       int32_t group) {
+    if (M < 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
+        return 0;
+    size_t off[5];
+    quant_gemm_layout(M, K, n_out, group, off);
+    return off[4] + w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group);
+}
+
+w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
+                            const void *Wq8, const float *sw4, const float *sw8, int32_t M,
+                            int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                            int64_t ldy, void *workspace, size_t workspace_bytes,
+                            w4a4_stream stream) {
+    if (N < 0)
+        return W4A4_ERR_INVALID_ARG;
+    w4a4_status st = check_shape(M, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    const int32_t K_n = K - n_out;
+    if (ldx < K || ldy < N)
+        return W4A4_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if (!X || !perm || !Y || (K_n > 0 && (!Wq4 || !sw4)) ||
+        (n_out > 0 && (!Wq8 || !sw8)))
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(perm, 16) || !aligned(Y, 2) ||
+        (Wq4 && !aligned(Wq4, 16)) || (Wq8 && !aligned(Wq8, 16)) || (sw4 && !aligned(sw4, 4)) ||
+        (sw8 && !aligned(sw8, 4)) || !aligned(workspace, 256))
+        return W4A4_ERR_ALIGNMENT;
+    const size_t need = w4a4_quant_gemm_workspace_bytes(M, N, K, n_out, group);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return W4A4_ERR_WORKSPACE;
+    size_t off[5];
+    quant_gemm_layout(M, K, n_out, group, off);
+    char *ws = static_cast<char *>(workspace);
+    void *Aq4 = K_n > 0 ? ws + off[0] : nullptr;
+    void *Aq8 = n_out > 0 ? ws + off[1] : nullptr;
+    float *sa4 = K_n > 0 ? reinterpret_cast<float *>(ws + off[2]) : nullptr;
+    float *sa8 = reinterpret_cast<float *>(ws + off[3]);
+    st = quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream);
+    if (st != W4A4_OK)
+        return st;
+    return w4a4_outlier_gemm(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy,
+                             ws + off[4], workspace_bytes - off[4], stream);
+}
+
+}  // extern "C"

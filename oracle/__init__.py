@@ -58,6 +58,8 @@ def _load():
         build()
     lib = ctypes.CDLL(_LIB)
     c_i32, c_i64 = ctypes.c_int32, ctypes.c_int64
+    lib.w4o_max_threads.argtypes = []
+    lib.w4o_max_threads.restype = ctypes.c_int
     lib.w4o_make_perm.argtypes = [c_i32, _i32p, c_i32, _i32p]
     lib.w4o_make_perm.restype = ctypes.c_int
     lib.w4o_quantize_block.argtypes = [_f32p, c_i32, c_i32, _i8p, ctypes.POINTER(ctypes.c_float)]
@@ -75,6 +77,11 @@ def _load():
     lib.w4o_linear_at.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().w4o_max_threads())
 
 
 def num_groups(K_n: int, group: int) -> int:

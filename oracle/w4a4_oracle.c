@@ -38,9 +38,13 @@
  * excess precision), so every fp32 division is correctly rounded.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the OpenMP loops below use (reported by the benchmark). */
+int w4o_max_threads(void) { return omp_get_max_threads(); }
 
 /* Outlier permutation: perm = ascending(j not in O) ++ ascending(j in O).
  * [ATOM] Interesting ideas I1; reading R6.

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Bars (from the layer's definition; the oracle is pinned separately):
+* codes, padding bytes and fp32 scales of the producer: bit-exact;
+* int32 accumulators of the GEMM (exported from the production main loop):
+  bit-exact;
+* fp16 output: max |Y - Y_oracle| <= 1e-2 * max |Y_oracle| (the GPU sums the
+  scaled groups in fp32 in its own order; the oracle sums in fp64).
+
+Mid-size cases compare every output and span several 128 x 128 tiles with
+ragged M, N and K edges. The five named workloads run at full size and are
+compared on every producer byte and on sampled GEMM outputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import mixed_precision_integer_amd as w4
+from mixed_precision_integer_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 1e-2
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    sys.stderr.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def pitch4(K_n):
+    return ((K_n + 127) // 128) * 128 // 2
+
+
+def pitch8(n_out):
+    return ((n_out + 63) // 64) * 64
+
+
+def as_u32(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def oracle_quant(oracle, A, perm, n_out, group):
+    q4, s4, q8, s8 = oracle.quantize_rows(A, perm, n_out, group)
+    p4 = oracle.pack_nibbles(q4, pitch4(q4.shape[1]))
+    p8 = np.zeros((A.shape[0], pitch8(n_out)), np.int8)
+    p8[:, :n_out] = q8
+    return (q4, s4, q8, s8), p4, p8
+
+
+def check_producer(oracle, gpu_op, A, perm, n_out, group):
+    ref, p4, p8 = oracle_quant(oracle, A, perm, n_out, group)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_op.q4.cpu().numpy(), p4), "INT4 codes / padding"
+    if n_out:
+        assert np.array_equal(gpu_op.q8.cpu().numpy(), p8), "INT8 codes / padding"
+    assert np.array_equal(as_u32(gpu_op.s4.cpu().numpy()), as_u32(ref[1])), "INT4 scales"
+    s8 = ref[3] if n_out else np.zeros(A.shape[0], np.float32)
+    assert np.array_equal(as_u32(gpu_op.s8.cpu().numpy()), as_u32(s8)), "INT8 scales"
+    return ref
+
+
+def run_layer(X, W, outliers, group):
+    K = X.shape[1]
+    perm = torch.from_numpy(w4.make_perm(K, outliers)).to(DEV)
+    Xd = torch.from_numpy(X).to(DEV)
+    Wd = torch.from_numpy(W).to(DEV)
+    n_out = len(outliers)
+    a = w4.quant_reorder_act(Xd, perm, n_out, group)
+    w = w4.pack_int4_weights(Wd, perm, n_out, group)
+    return perm, Xd, a, w
+
+
+def check_y(y_gpu, y_ref_fp16):
+    ref = y_ref_fp16.astype(np.float64)
+    got = y_gpu.astype(np.float64)
+    amax = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    assert np.all(np.isfinite(got))
+    assert err <= TOL * amax, f"max err {err} vs bound {TOL * amax}"
+    return err / max(amax, 1e-30), int((y_gpu != y_ref_fp16).sum())
+
+
+def full_compare(oracle, X, W, outliers, group):
+    """Every output position: producer, accumulators, Y and the fused call."""
+    M, K = X.shape
+    N = W.shape[0]
+    n_out = len(outliers)
+    perm, Xd, a, w = run_layer(X, W, outliers, group)
+    perm_h = perm.cpu().numpy()
+    qa = check_producer(oracle, a, X, perm_h, n_out, group)
+    qw = check_producer(oracle, w, W, perm_h, n_out, group)
+    mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")
+    acc4, acc8, ystar = oracle.linear_at(qa, qw, group, mm.reshape(-1), nn.reshape(-1))
+    G = acc4.shape[1]
+    g4, g8 = w4.w4a4_outlier_gemm_i32(a, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(g4.cpu().numpy(), acc4.reshape(M, N, G).transpose(2, 0, 1)), "acc4"
+    if n_out:
+        assert np.array_equal(g8.cpu().numpy(), acc8.reshape(M, N)), "acc8"
+    y = w4.w4a4_outlier_gemm(a, w)
+    rel, ndiff = check_y(y.cpu().numpy(), oracle.to_fp16(ystar).reshape(M, N))
+    yf = w4.quant_gemm(Xd, perm, w)
+    torch.cuda.synchronize()
+    assert torch.equal(yf, y), "fused call differs from producer + GEMM"
+    return rel, ndiff
+
+
+MID = [
+    # M, N, K, n_out, group
+    (16, 256, 256, 16, 0),          # the tiny workload's shape, other seed
+    (200, 300, 1024, 32, 0),        # ragged M and N, K_n = 992 not a tile multiple
+    (130, 257, 1152, 128, 128),     # group 128, G = 8, ragged N
+    (300, 130, 2176, 128, 256),     # group 256 spans two K-tiles
+    (37, 200, 640, 100, 0),         # tail of 100 padded to 128
+    (1, 128, 512, 0, 0),            # one token, no outliers
+    (64, 64, 256, 256, 0),          # every channel an outlier: plain W8A8
+    (70, 90, 384, 0, 128),          # group mode without outliers
+    (512, 512, 4096, 128, 128),     # several full tiles in both directions
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out,group", MID)
+def test_mid_size_parity(oracle, M, N, K, n_out, group):
+    X, W, o = wl.draw(M, N, K, n_out, seed=M * 7 + K, outlier_factor=40.0)
+    full_compare(oracle, X, W, o, group)
+
+
+def test_laplace_inputs(oracle):
+    X, W, o = wl.draw(96, 160, 896, 64, seed=9, x_dist="laplace", outlier_factor=50.0)
+    full_compare(oracle, X, W, o, 0)
+
+
+def test_tiny_workload(oracle):
+    X, W, o = wl.draw_workload(wl.TINY)
+    full_compare(oracle, X, W, o, wl.TINY.group)
+
+
+def test_special_values(oracle):
+    """Zero rows, fp16 extremes and subnormals through the whole layer."""
+    M, N, K, n_out = 40, 70, 512, 32
+    X, W, o = wl.draw(M, N, K, n_out, seed=77)
+    X[3] = 0                                      # all-zero token: s = 0, codes 0
+    X[5, :8] = np.float16(65504)                   # fp16 max on a few channels (the
+    X[6, 8:16] = -np.float16(65504)                # output itself stays finite)
+    X[7, :] = np.float16(6e-8)                     # subnormal fp16
+    X[8, ::2] = np.float16(-6e-8)
+    W[2] = 0
+    W[4, :] = np.float16(1e-7)
+    full_compare(oracle, X, W, o, 0)
+
+
+# ---------------------------------------------------------------------------
+# the GEMM on hand-made operands: extreme codes (-8, -128) and int32 range
+# ---------------------------------------------------------------------------
+def upload_codes(oracle, q4, s4, q8, s8):
+    rows = q4.shape[0]
+    p4 = oracle.pack_nibbles(q4, pitch4(q4.shape[1]))
+    p8 = np.zeros((rows, pitch8(q8.shape[1])), np.int8)
+    p8[:, :q8.shape[1]] = q8
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)  # noqa: E731
+    return w4.QuantizedOperand(t(p4), t(p8) if q8.shape[1] else None, t(s4), t(s8),
+                               q4.shape[1] + q8.shape[1], q8.shape[1], 0)
+
+
+@pytest.mark.parametrize("mode", ["random_full_range", "all_min"])
+def test_gemm_extreme_codes(oracle, mode):
+    rng = np.random.default_rng(123)
+    M, N, K_n, n_out = 96, 160, 21760, 256          # the largest K_n of the workloads
+    if mode == "all_min":
+        qa4 = np.full((M, K_n), -8, np.int8); qw4 = np.full((N, K_n), -8, np.int8)
+        qa8 = np.full((M, n_out), -128, np.int8); qw8 = np.full((N, n_out), -128, np.int8)
+    else:
+        qa4 = rng.integers(-8, 8, (M, K_n), dtype=np.int8); qw4 = rng.integers(-8, 8, (N, K_n), dtype=np.int8)
+        qa8 = rng.integers(-128, 128, (M, n_out), dtype=np.int8)
+        qw8 = rng.integers(-128, 128, (N, n_out), dtype=np.int8)
+    sa4 = rng.uniform(0.5, 2, (M, 1)).astype(np.float32); sw4 = rng.uniform(1e-3, 2e-3, (N, 1)).astype(np.float32)
+    sa8 = rng.uniform(0.5, 2, M).astype(np.float32); sw8 = rng.uniform(1e-4, 2e-4, N).astype(np.float32)
+    a = upload_codes(oracle, qa4, sa4, qa8, sa8)
+    w = upload_codes(oracle, qw4, sw4, qw8, sw8)
+    mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")
+    acc4, acc8, ystar = oracle.linear_at((qa4, sa4, qa8, sa8), (qw4, sw4, qw8, sw8), 0,
+                                         mm.reshape(-1), nn.reshape(-1))
+    g4, g8 = w4.w4a4_outlier_gemm_i32(a, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(g4.cpu().numpy()[0], acc4[:, 0].reshape(M, N))
+    assert np.array_equal(g8.cpu().numpy(), acc8.reshape(M, N))
+    y = w4.w4a4_outlier_gemm(a, w)
+    check_y(y.cpu().numpy(), oracle.to_fp16(ystar).reshape(M, N))
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: every producer byte, sampled GEMM outputs
+# ---------------------------------------------------------------------------
+def sample_pairs(M, N, P, seed):
+    rng = np.random.default_rng(seed)
+    m = rng.integers(0, M, P).astype(np.int32)
+    n = rng.integers(0, N, P).astype(np.int32)
+    corners = np.array([[0, 0], [M - 1, N - 1], [0, N - 1], [M - 1, 0]], np.int32)
+    return np.concatenate([m, corners[:, 0]]), np.concatenate([n, corners[:, 1]])
+
+
+def full_size_check(oracle, X, W, o, group, P=4096):
+    M, K = X.shape
+    N = W.shape[0]
+    n_out = len(o)
+    perm, Xd, a, w = run_layer(X, W, o, group)
+    perm_h = perm.cpu().numpy()
+    qa = check_producer(oracle, a, X, perm_h, n_out, group)
+    qw = check_producer(oracle, w, W, perm_h, n_out, group)
+    mi, ni = sample_pairs(M, N, P, seed=M + N)
+    acc4, acc8, ystar = oracle.linear_at(qa, qw, group, mi, ni)
+    g4, g8 = w4.w4a4_outlier_gemm_i32(a, w)
+    mt, nt = torch.from_numpy(mi).long().to(DEV), torch.from_numpy(ni).long().to(DEV)
+    got4 = g4[:, mt, nt].cpu().numpy().T
+    got8 = g8[mt, nt].cpu().numpy()
+    del g4, g8
+    assert np.array_equal(got4, acc4), "acc4 (sampled)"
+    assert np.array_equal(got8, acc8), "acc8 (sampled)"
+    y = w4.quant_gemm(Xd, perm, w)
+    y_s = y[mt, nt].cpu().numpy()
+    ref = oracle.to_fp16(ystar)
+    # the tolerance scale is max |Y_oracle| over the sampled outputs
+    rel, _ = check_y(y_s, ref)
+    y2 = w4.w4a4_outlier_gemm(a, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    return rel
+
+
+@pytest.mark.parametrize("work", [wl.QPROJ_7B, wl.UPPROJ_7B, wl.DOWNPROJ_65B],
+                         ids=lambda w: w.name)
+def test_full_size_workload(oracle, work):
+    X, W, o = wl.draw_workload(work)
+    full_size_check(oracle, X, W, o, work.group)
+
+
+def test_decode_sweep(oracle):
+    X, W, o = wl.draw_workload(wl.DECODE_65B)
+    for M in wl.DECODE_M:
+        sys.stderr.write(f"[gpu case] decode M={M}\n")
+        sys.stderr.flush()
+        full_size_check(oracle, np.ascontiguousarray(X[:M]), W, o, wl.DECODE_65B.group, P=2048)
+
+
+def test_repeatable(oracle):
+    X, W, o = wl.draw(300, 260, 1280, 64, seed=5)
+    perm, Xd, a, w = run_layer(X, W, o, 128 if (1280 - 64) % 128 == 0 else 0)
+    y1 = w4.quant_gemm(Xd, perm, w)
+    y2 = w4.quant_gemm(Xd, perm, w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y3 = w4.quant_gemm(Xd, perm, w)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+
+
+def test_empty_batch():
+    X = torch.zeros((0, 256), dtype=torch.float16, device=DEV)
+    W = torch.randn((64, 256), device=DEV).half()
+    perm = torch.from_numpy(w4.make_perm(256, [1, 2])).to(DEV)
+    w = w4.pack_int4_weights(W, perm, 2, 0)
+    y = w4.quant_gemm(X, perm, w)
+    assert y.shape == (0, 64)
