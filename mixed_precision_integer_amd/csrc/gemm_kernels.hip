@@ -8,274 +8,342 @@
 // loop) and the QUIK abstract (hybrid 4-bit layer with higher-precision
 // outliers).
 //
-// CDNA4 design notes
+// CDNA4 design
 // * CDNA4 has no INT4 matrix instruction, so packed nibbles are widened
 //   exactly to int8 in registers: for a packed dword p,
 //     hi = p & 0xF0F0F0F0         -> four int8 lanes holding 16 * q_odd
 //     lo = (p << 4) & 0xF0F0F0F0  -> four int8 lanes holding 16 * q_even
 //   (the sign comes for free from the two's complement nibble). Both
 //   operands carry the factor 16, so the int32 accumulator holds 256 * acc,
-//   which is exact while K_n * 64 * 256 < 2^31; the epilogue folds 2^-8 into
-//   the fp32 scale and the accumulator export shifts right by 8.
-// * The nibble order inside an MFMA operand does not have to follow the
-//   channel order: a dot product is invariant under any permutation of K
-//   applied to both operands, and A and B are unpacked identically, so the
-//   widened lo/hi dwords are fed to v_mfma_i32_32x32x32_i8 as they come.
+//   exact while K_n * 64 * 256 < 2^31; the epilogue folds 2^-8 into the fp32
+//   scale and the accumulator export shifts right by 8.
+// * The nibble order inside an MFMA operand need not follow the channel
+//   order: a dot product is invariant under one permutation of K applied to
+//   both operands, and A and B are unpacked identically, so the widened
+//   dwords go to v_mfma_i32_32x32x32_i8 as they come.
 // * A K-tile is 64 bytes of every row: 128 INT4 channels or 64 INT8 tail
-//   channels. Tail tiles run first on a separate set of int32 accumulators
-//   (different scales), then the INT4 tiles. At the end of each scale group
-//   the int32 accumulators are converted and added into fp32 accumulators.
-// * LDS rows are 80 bytes (64 + 16 padding): a lane reads 16 bytes of its
-//   row per 64 K-values, and the 16-byte row skew keeps the eight lanes of a
-//   ds_read_b128 phase on distinct bank groups.
-// * Double-buffered LDS: tile t+1 is fetched into registers while tile t is
-//   multiplied; one barrier per tile.
+//   channels. The tail tiles run first as one scale group, then the INT4
+//   tiles (a group per `group` channels, or one group for per-row scales).
+//   The first MFMA of a group reads a zero C operand, so no accumulator is
+//   ever cleared; at the end of a group the int32 sums are converted and
+//   added into fp32 accumulators.
+// * Tiles reach LDS through direct global->LDS DMA (global_load_lds_dwordx4):
+//   no VGPR staging and no ds_write. A 4-stage LDS ring with prefetch
+//   distance 2 needs one barrier per tile: the stage written at tile t was
+//   last read at tile t-2, which every wave has finished once it has passed
+//   the barrier of tile t-1. Every wave waits for its own DMA with an explicit
+//   vmcnt before that barrier.
+// * LDS rows are 64 bytes = four 16-byte chunks; chunk c of row r is stored
+//   at slot c ^ ((r >> 1) & 3), so the eight rows that one ds_read_b128
+//   phase touches hit eight different 16-byte bank groups.
+// * The fp32 scales of a tile's group ride along with every tile (DMA
+//   dwords), so each tile costs the same number of DMA instructions and the
+//   vmcnt bookkeeping is a constant.
+// * Workgroups are mapped so that each XCD (own L2) works on a contiguous
+//   range of tiles, walked in bands of 8 tile rows.
 #include "w4a4_internal.h"
 
 namespace w4a4 {
-namespace {
+namespace gemm_impl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 64;   // bytes of each row per K-tile
-constexpr int kLdsPitch = 80;    // LDS bytes per row (64 data + 16 skew)
+constexpr int kStages = 4;
+constexpr int kPrefetch = kStages - 2;
 
 __device__ __forceinline__ uint32_t nib_hi(uint32_t p) { return p & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t nib_lo(uint32_t p) { return (p << 4) & 0xF0F0F0F0u; }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EXPORT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-    static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
-    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-    constexpr int CA = BM * 4 / kThreads;       // 16-byte chunks per lane, A tile
-    constexpr int CB = BN * 4 / kThreads;
-    static_assert(CA >= 1 && CB >= 1 && BM <= kThreads && BN <= kThreads, "loader");
-    constexpr int A_BYTES = BM * kLdsPitch, B_BYTES = BN * kLdsPitch;
-    constexpr int STAGE = A_BYTES + B_BYTES + (BM + BN) * 4;
+// s_waitcnt immediate with only vmcnt constrained (gfx9 encoding).
+constexpr int vmcnt_only(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-    __shared__ __align__(16) unsigned char lds[2 * STAGE];
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// byte offset of 16-byte chunk c of row r inside a tile
+__device__ __forceinline__ int swz(int r, int c) { return (r << 6) | (((c ^ (r >> 1)) & 3) << 4); }
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int DA = BM * 4 / kThreads, DB = BN * 4 / kThreads;
+    static constexpr int DS = (BM + BN + kThreads - 1) / kThreads;  // scale DMAs per lane
+    static constexpr int A_BYTES = BM * kTileBytes, B_BYTES = BN * kTileBytes;
+    static constexpr int S_BYTES = DS * kThreads * 4;
+    static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+    static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert(DA >= 1 && DB >= 1 && BM * 4 % kThreads == 0 && BN * 4 % kThreads == 0, "loader");
+};
+
+// MFMAs of one K-tile held in LDS stage `st`. FRESH: the tile opens a scale
+// group (its first MFMAs take C = 0). TAIL: an INT8 tail tile (no widening).
+template <class C, bool FRESH, bool TAIL>
+__device__ __forceinline__ void mma_tile(v16i (&acc)[C::FM][C::FN], const unsigned char *st, int wm,
+                                         int wn, int li, int lh) {
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const unsigned char *sA = st, *sB = st + C::A_BYTES;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int c = 2 * s + lh;
+        uint4 pa[C::FM], pb[C::FN];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+            pa[fm] = *reinterpret_cast<const uint4 *>(sA + swz(wm * C::WTM + fm * 32 + li, c));
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+            pb[fn] = *reinterpret_cast<const uint4 *>(sB + swz(wn * C::WTN + fn * 32 + li, c));
+        const bool z = FRESH && s == 0;
+        if constexpr (TAIL) {
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn) {
+                    const v4i x = {(int)pa[fm].x, (int)pa[fm].y, (int)pa[fm].z, (int)pa[fm].w};
+                    const v4i w = {(int)pb[fn].x, (int)pb[fn].y, (int)pb[fn].z, (int)pb[fn].w};
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x, w, z ? zero : acc[fm][fn], 0, 0, 0);
+                }
+        } else {
+            v4i wb0[C::FN], wb1[C::FN];
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                wb0[fn] = v4i{(int)nib_lo(pb[fn].x), (int)nib_hi(pb[fn].x), (int)nib_lo(pb[fn].y),
+                              (int)nib_hi(pb[fn].y)};
+                wb1[fn] = v4i{(int)nib_lo(pb[fn].z), (int)nib_hi(pb[fn].z), (int)nib_lo(pb[fn].w),
+                              (int)nib_hi(pb[fn].w)};
+            }
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm) {
+                const v4i xa0 = {(int)nib_lo(pa[fm].x), (int)nib_hi(pa[fm].x), (int)nib_lo(pa[fm].y),
+                                 (int)nib_hi(pa[fm].y)};
+                const v4i xa1 = {(int)nib_lo(pa[fm].z), (int)nib_hi(pa[fm].z), (int)nib_lo(pa[fm].w),
+                                 (int)nib_hi(pa[fm].w)};
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn) {
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa0, wb0[fn], z ? zero : acc[fm][fn], 0, 0, 0);
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1, wb1[fn], acc[fm][fn], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// End of a scale group: y += float(acc) * (sa[m] * sw[n]) (the INT4 sums also
+// * 2^-8), with the group's scales read from the LDS stage of its last tile:
+// floats [0, BM) are the row scales, [BM, BM + BN) the column scales.
+template <class C, bool TAIL>
+__device__ __forceinline__ void dequant_group(const v16i (&acc)[C::FM][C::FN],
+                                              float (&yacc)[C::FM][C::FN][16],
+                                              const unsigned char *st, int wm, int wn, int li,
+                                              int lh) {
+    const float *sS = reinterpret_cast<const float *>(st + C::A_BYTES + C::B_BYTES);
+    constexpr float unit = TAIL ? 1.0f : (1.0f / 256.0f);
+    float cs[C::FN];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+        cs[fn] = sS[C::BM + wn * C::WTN + fn * 32 + li] * unit;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+        float rs[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(sS + wm * C::WTM + fm * 32 + q * 8 + lh * 4);
+            rs[q * 4 + 0] = v.x;
+            rs[q * 4 + 1] = v.y;
+            rs[q * 4 + 2] = v.z;
+            rs[q * 4 + 3] = v.w;
+        }
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                yacc[fm][fn][r] += (float)acc[fm][fn][r] * (rs[r] * cs[fn]);
+    }
+}
+
+// Accumulator export (test path): write the exact integer sums of a group.
+template <class C, bool TAIL>
+__device__ __forceinline__ void export_group(const v16i (&acc)[C::FM][C::FN], const GemmArgs &a,
+                                             int gidx, int row0, int col0, int wm, int wn, int li,
+                                             int lh) {
+    int32_t *dst = TAIL ? a.acc8_out : a.acc4_out + (int64_t)gidx * a.M * a.N;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+            const int n = col0 + wn * C::WTN + fn * 32 + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
+                const int v = acc[fm][fn][r];
+                if (m < a.M && n < a.N)
+                    dst[(int64_t)m * a.N + n] = TAIL ? v : (v >> 8);
+            }
+        }
+}
+
+template <class C, bool EXPORT>
+__device__ __forceinline__ void gemm_body(const GemmArgs &a) {
+    constexpr int BM = C::BM, BN = C::BN, FM = C::FM, FN = C::FN;
+    constexpr int STAGE = C::A_BYTES + C::B_BYTES + (EXPORT ? 0 : C::S_BYTES);
+    constexpr int D = C::DA + C::DB + (EXPORT ? 0 : C::DS);   // DMA instructions per tile per lane
+
+    __shared__ __align__(16) unsigned char lds[kStages * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int li = lane & 31, lh = lane >> 5;
 
-    const int tiles_n = (a.N + BN - 1) / BN;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    // ---- tile of this workgroup ----------------------------------------------
+    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int tiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (tiles % 8 == 0)                       // consecutive workgroups alternate XCDs
+        tile = (tile % 8) * (tiles / 8) + tile / 8;
+    constexpr int BAND = 8;
+    const int band = tile / (BAND * tiles_n);
+    const int first_m = band * BAND;
+    const int band_m = min(tiles_m - first_m, BAND);
+    const int in_band = tile - band * BAND * tiles_n;
+    const int tm = first_m + in_band % band_m, tn = in_band / band_m;
     const int row0 = tm * BM, col0 = tn * BN;
 
     const int T8 = (int)(a.pitch8 / kTileBytes);
     const int T4 = (int)(a.pitch4 / kTileBytes);
     const int T = T8 + T4;
-    const int tiles_per_group = a.group > 0 ? a.group / 128 : T4;
+    // INT4 tiles per scale group (per-row scales: all of them); G groups. With
+    // no INT4 channels (every channel an outlier) there are no INT4 groups.
+    const int tiles_per_group = a.group > 0 ? a.group / 128 : max(T4, 1);
+    const int G = T4 / tiles_per_group;
 
-    // ---- tile loader state -------------------------------------------------
-    uint4 ra[CA], rb[CB];
-    float rsa = 0.0f, rsb = 0.0f;
+    // ---- DMA sources of this lane ----------------------------------------------
+    // slot q = j * 256 + tid of a tile holds row q / 4, chunk (q % 4) ^ ((row >> 1) & 3)
+    int a_off[C::DA], b_off[C::DB];   // row * 0 + chunk * 16 (row index kept separately)
+    int a_row[C::DA], b_row[C::DB];
+#pragma unroll
+    for (int j = 0; j < C::DA; ++j) {
+        const int q = j * kThreads + tid, r = q >> 2;
+        a_row[j] = min(row0 + r, a.M - 1);
+        a_off[j] = (((q & 3) ^ (r >> 1)) & 3) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < C::DB; ++j) {
+        const int q = j * kThreads + tid, r = q >> 2;
+        b_row[j] = min(col0 + r, a.N - 1);
+        b_off[j] = (((q & 3) ^ (r >> 1)) & 3) * 16;
+    }
+    // scale slots: rows of A first, then columns of B
+    bool s_is_a[C::DS];
+    int s_idx[C::DS];
+#pragma unroll
+    for (int j = 0; j < C::DS; ++j) {
+        const int e = min(j * kThreads + tid, BM + BN - 1);
+        s_is_a[j] = e < BM;
+        s_idx[j] = e < BM ? min(row0 + e, a.M - 1) : min(col0 + e - BM, a.N - 1);
+    }
 
-    auto group_end = [&](int tt, int &gidx) -> bool {
-        if (tt < T8) {
-            gidx = -1;
-            return tt == T8 - 1;
-        }
-        const int t4 = tt - T8;
-        gidx = (t4 + 1) / tiles_per_group - 1;
-        return (t4 + 1) % tiles_per_group == 0;
-    };
-
-    auto load_tile = [&](int tt) {
+    auto issue = [&](int tt) {
+        unsigned char *st = lds + (tt % kStages) * STAGE;
         const bool tail = tt < T8;
         const uint8_t *abase = tail ? reinterpret_cast<const uint8_t *>(a.a8) : a.a4;
         const uint8_t *bbase = tail ? reinterpret_cast<const uint8_t *>(a.w8) : a.w4;
         const int64_t pitch = tail ? a.pitch8 : a.pitch4;
         const int64_t koff = (int64_t)(tail ? tt : tt - T8) * kTileBytes;
 #pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            const int c = tid + i * kThreads;
-            const int r = min(row0 + c / 4, a.M - 1);
-            ra[i] = *reinterpret_cast<const uint4 *>(abase + (int64_t)r * pitch + koff + (c % 4) * 16);
-        }
+        for (int j = 0; j < C::DA; ++j)
+            __builtin_amdgcn_global_load_lds(abase + a_row[j] * pitch + koff + a_off[j],
+                                             (lds_void *)(st + j * 4096 + wave * 1024), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int c = tid + i * kThreads;
-            const int r = min(col0 + c / 4, a.N - 1);
-            rb[i] = *reinterpret_cast<const uint4 *>(bbase + (int64_t)r * pitch + koff + (c % 4) * 16);
-        }
-        int gidx;
-        if (!EXPORT && group_end(tt, gidx)) {
-            const float *sa = tail ? a.sa8 : a.sa4;
-            const float *sb = tail ? a.sw8 : a.sw4;
-            const int stride = tail ? 1 : a.G;
-            const int g = tail ? 0 : gidx;
-            if (tid < BM)
-                rsa = sa[(int64_t)min(row0 + tid, a.M - 1) * stride + g];
-            if (tid < BN)
-                rsb = sb[(int64_t)min(col0 + tid, a.N - 1) * stride + g];
+        for (int j = 0; j < C::DB; ++j)
+            __builtin_amdgcn_global_load_lds(bbase + b_row[j] * pitch + koff + b_off[j],
+                                             (lds_void *)(st + C::A_BYTES + j * 4096 + wave * 1024), 16, 0, 0);
+        if constexpr (!EXPORT) {
+            const int g = tail ? 0 : (tt - T8) / tiles_per_group;
+#pragma unroll
+            for (int j = 0; j < C::DS; ++j) {
+                const float *src = tail ? (s_is_a[j] ? a.sa8 : a.sw8) + s_idx[j]
+                                        : (s_is_a[j] ? a.sa4 : a.sw4) + (int64_t)s_idx[j] * a.G + g;
+                __builtin_amdgcn_global_load_lds(
+                    src, (lds_void *)(st + C::A_BYTES + C::B_BYTES + j * 1024 + wave * 256), 4, 0, 0);
+            }
         }
     };
 
-    auto store_tile = [&](int tt, int stage) {
-        unsigned char *sA = lds + stage * STAGE;
-        unsigned char *sB = sA + A_BYTES;
-        float *sS = reinterpret_cast<float *>(sB + B_BYTES);
-#pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            const int c = tid + i * kThreads;
-            *reinterpret_cast<uint4 *>(sA + (c / 4) * kLdsPitch + (c % 4) * 16) = ra[i];
+    // Wait for tile tt (after issuing tile tt + kPrefetch) and make it visible
+    // to the whole workgroup.
+    auto begin_tile = [&](int tt) -> const unsigned char * {
+        compiler_fence();
+        if (tt + kPrefetch < T) {
+            issue(tt + kPrefetch);
+            if constexpr (EXPORT)
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // accumulator stores share vmcnt
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(kPrefetch * D));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
         }
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int c = tid + i * kThreads;
-            *reinterpret_cast<uint4 *>(sB + (c / 4) * kLdsPitch + (c % 4) * 16) = rb[i];
-        }
-        int gidx;
-        if (!EXPORT && group_end(tt, gidx)) {
-            if (tid < BM)
-                sS[tid] = rsa;
-            if (tid < BN)
-                sS[BM + tid] = rsb;
-        }
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        return lds + (tt % kStages) * STAGE;
     };
 
-    // ---- accumulators ------------------------------------------------------
     v16i acc[FM][FN];
-    float yacc[EXPORT ? 1 : FM][EXPORT ? 1 : FN][16];
+    float yacc[FM][FN][16];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            acc[fm][fn] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-            if constexpr (!EXPORT) {
+        for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    yacc[fm][fn][r] = 0.0f;
-            }
-        }
+            for (int r = 0; r < 16; ++r)
+                yacc[fm][fn][r] = 0.0f;
 
-    // ---- main loop -----------------------------------------------------------
-    if (T > 0) {
-        load_tile(0);
-        store_tile(0, 0);
+    // ---- main loop: the tail group, then the INT4 groups ------------------------------
+#pragma unroll
+    for (int p = 0; p < kPrefetch; ++p)
+        if (p < T)
+            issue(p);
+
+    int tt = 0;
+    if (T8 > 0) {
+        const unsigned char *st = begin_tile(tt++);
+        mma_tile<C, true, true>(acc, st, wm, wn, li, lh);
+        while (tt < T8) {
+            st = begin_tile(tt++);
+            mma_tile<C, false, true>(acc, st, wm, wn, li, lh);
+        }
+        if constexpr (EXPORT)
+            export_group<C, true>(acc, a, 0, row0, col0, wm, wn, li, lh);
+        else
+            dequant_group<C, true>(acc, yacc, st, wm, wn, li, lh);
     }
-    __syncthreads();
-
-    for (int tt = 0; tt < T; ++tt) {
-        const int stage = tt & 1;
-        if (tt + 1 < T)
-            load_tile(tt + 1);
-
-        const unsigned char *sA = lds + stage * STAGE + (wm * WTM + li) * kLdsPitch + lh * 16;
-        const unsigned char *sB = lds + stage * STAGE + A_BYTES + (wn * WTN + li) * kLdsPitch + lh * 16;
-        const bool tail = tt < T8;
-
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            uint4 pa[FM], pb[FN];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-                pa[fm] = *reinterpret_cast<const uint4 *>(sA + fm * 32 * kLdsPitch + s * 32);
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                pb[fn] = *reinterpret_cast<const uint4 *>(sB + fn * 32 * kLdsPitch + s * 32);
-            if (tail) {
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn) {
-                        const v4i x = {(int)pa[fm].x, (int)pa[fm].y, (int)pa[fm].z, (int)pa[fm].w};
-                        const v4i w = {(int)pb[fn].x, (int)pb[fn].y, (int)pb[fn].z, (int)pb[fn].w};
-                        acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x, w, acc[fm][fn], 0, 0, 0);
-                    }
-            } else {
-                v4i xa0[FM], xa1[FM], wb0[FN], wb1[FN];
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    xa0[fm] = v4i{(int)nib_lo(pa[fm].x), (int)nib_hi(pa[fm].x),
-                                  (int)nib_lo(pa[fm].y), (int)nib_hi(pa[fm].y)};
-                    xa1[fm] = v4i{(int)nib_lo(pa[fm].z), (int)nib_hi(pa[fm].z),
-                                  (int)nib_lo(pa[fm].w), (int)nib_hi(pa[fm].w)};
-                }
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    wb0[fn] = v4i{(int)nib_lo(pb[fn].x), (int)nib_hi(pb[fn].x),
-                                  (int)nib_lo(pb[fn].y), (int)nib_hi(pb[fn].y)};
-                    wb1[fn] = v4i{(int)nib_lo(pb[fn].z), (int)nib_hi(pb[fn].z),
-                                  (int)nib_lo(pb[fn].w), (int)nib_hi(pb[fn].w)};
-                }
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn) {
-                        acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa0[fm], wb0[fn], acc[fm][fn], 0, 0, 0);
-                        acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1[fm], wb1[fn], acc[fm][fn], 0, 0, 0);
-                    }
-            }
+    for (int g = 0; g < G; ++g) {
+        const unsigned char *st = begin_tile(tt++);
+        mma_tile<C, true, false>(acc, st, wm, wn, li, lh);
+        for (int k = 1; k < tiles_per_group; ++k) {
+            st = begin_tile(tt++);
+            mma_tile<C, false, false>(acc, st, wm, wn, li, lh);
         }
-
-        int gidx;
-        if (group_end(tt, gidx)) {
-            if constexpr (EXPORT) {
-                int32_t *dst = tail ? a.acc8_out : a.acc4_out + (int64_t)gidx * a.M * a.N;
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn) {
-                        const int n = col0 + wn * WTN + fn * 32 + li;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int m = row0 + wm * WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
-                            const int v = acc[fm][fn][r];
-                            if (m < a.M && n < a.N)
-                                dst[(int64_t)m * a.N + n] = tail ? v : (v >> 8);
-                            acc[fm][fn][r] = 0;
-                        }
-                    }
-            } else {
-                const float *sS = reinterpret_cast<const float *>(lds + stage * STAGE + A_BYTES + B_BYTES);
-                const float unit = tail ? 1.0f : (1.0f / 256.0f);
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    float rs[16];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 v = *reinterpret_cast<const float4 *>(sS + wm * WTM + fm * 32 + q * 8 + lh * 4);
-                        rs[q * 4 + 0] = v.x;
-                        rs[q * 4 + 1] = v.y;
-                        rs[q * 4 + 2] = v.z;
-                        rs[q * 4 + 3] = v.w;
-                    }
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn) {
-                        const float cs = sS[BM + wn * WTN + fn * 32 + li] * unit;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            yacc[fm][fn][r] += (float)acc[fm][fn][r] * (rs[r] * cs);
-                            acc[fm][fn][r] = 0;
-                        }
-                    }
-                }
-            }
-        }
-
-        if (tt + 1 < T)
-            store_tile(tt + 1, stage ^ 1);
-        __syncthreads();
+        if constexpr (EXPORT)
+            export_group<C, false>(acc, a, g, row0, col0, wm, wn, li, lh);
+        else
+            dequant_group<C, false>(acc, yacc, st, wm, wn, li, lh);
     }
 
-    // ---- epilogue: fp16 store -----------------------------------------------
+    // ---- epilogue: fp16 store -------------------------------------------------------
     if constexpr (!EXPORT) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int n = col0 + wn * WTN + fn * 32 + li;
+                const int n = col0 + wn * C::WTN + fn * 32 + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int m = row0 + wm * WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
+                    const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
                     if (m < a.M && n < a.N)
                         a.y[(int64_t)m * a.ldy + n] = (_Float16)yacc[fm][fn][r];
                 }
@@ -283,24 +351,39 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EXPORT>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+    gemm_body<Cfg<BM, BN, WAVES_M, WAVES_N>, EXPORT>(a);
+}
+
+template <class C>
 hipError_t launch_cfg(const GemmArgs &a, bool export_acc, hipStream_t stream) {
-    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
     if (export_acc)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true>), dim3(tiles), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, true>), dim3(tiles),
+                           dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false>), dim3(tiles), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, false>), dim3(tiles),
+                           dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-}  // namespace
+using CfgLarge = Cfg<256, 128, 2, 2>;   // waves of 128 x 64
+using CfgMid = Cfg<128, 128, 2, 2>;     // waves of 64 x 64
+using CfgSmall = Cfg<64, 128, 1, 4>;    // waves of 64 x 32
+
+}  // namespace gemm_impl
+
+using namespace gemm_impl;
 
 hipError_t launch_gemm(const GemmArgs &a, bool export_acc, hipStream_t stream) {
     if (a.M == 0 || a.N == 0)
         return hipSuccess;
+    if (a.M > 256)
+        return launch_cfg<CfgLarge>(a, export_acc, stream);
     if (a.M > 64)
-        return launch_cfg<128, 128, 2, 2>(a, export_acc, stream);
-    return launch_cfg<64, 128, 2, 2>(a, export_acc, stream);
+        return launch_cfg<CfgMid>(a, export_acc, stream);
+    return launch_cfg<CfgSmall>(a, export_acc, stream);
 }
 
 }  // namespace w4a4

@@ -123,6 +123,8 @@ MID = [
     (64, 64, 256, 256, 0),          # every channel an outlier: plain W8A8
     (70, 90, 384, 0, 128),          # group mode without outliers
     (512, 512, 4096, 128, 128),     # several full tiles in both directions
+    (600, 300, 2304, 256, 0),       # large-tile path with ragged M and N
+    (520, 260, 1664, 128, 128),     # large-tile path, group mode, ragged
 ]
 
 
