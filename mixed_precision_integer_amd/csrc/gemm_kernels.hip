@@ -34,8 +34,10 @@
 //   the barrier of tile t-1. Every wave waits for its own DMA with an explicit
 //   vmcnt before that barrier.
 // * LDS rows are 64 bytes = four 16-byte chunks; chunk c of row r is stored
-//   at slot c ^ ((r >> 1) & 3), so the eight rows that one ds_read_b128
-//   phase touches hit eight different 16-byte bank groups.
+//   at slot (c ^ (r >> 1) ^ (r >> 2)) & 3. Any 8 consecutive rows then land on
+//   8 distinct 16-byte slots modulo 128 bytes and any 16 on 16 distinct slots
+//   modulo 256 bytes, so a ds_read_b128 of 32 rows is conflict-free whether
+//   the banks serve 8 or 16 lanes per pass.
 // * The fp32 scales of a tile's group ride along with every tile (DMA
 //   dwords), so each tile costs the same number of DMA instructions and the
 //   vmcnt bookkeeping is a constant.
@@ -64,7 +66,7 @@ constexpr int vmcnt_only(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // byte offset of 16-byte chunk c of row r inside a tile
-__device__ __forceinline__ int swz(int r, int c) { return (r << 6) | (((c ^ (r >> 1)) & 3) << 4); }
+__device__ __forceinline__ int swz(int r, int c) { return (r << 6) | (((c ^ (r >> 1) ^ (r >> 2)) & 3) << 4); }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct Cfg {
@@ -116,18 +118,24 @@ __device__ __forceinline__ void mma_tile(v16i (&acc)[C::FM][C::FN], const unsign
                 wb1[fn] = v4i{(int)nib_lo(pb[fn].z), (int)nib_hi(pb[fn].z), (int)nib_lo(pb[fn].w),
                               (int)nib_hi(pb[fn].w)};
             }
+            // first halves of every block, then second halves: consecutive MFMAs
+            // never chain on one accumulator
+            v4i xa1[C::FM];
 #pragma unroll
             for (int fm = 0; fm < C::FM; ++fm) {
                 const v4i xa0 = {(int)nib_lo(pa[fm].x), (int)nib_hi(pa[fm].x), (int)nib_lo(pa[fm].y),
                                  (int)nib_hi(pa[fm].y)};
-                const v4i xa1 = {(int)nib_lo(pa[fm].z), (int)nib_hi(pa[fm].z), (int)nib_lo(pa[fm].w),
-                                 (int)nib_hi(pa[fm].w)};
+                xa1[fm] = v4i{(int)nib_lo(pa[fm].z), (int)nib_hi(pa[fm].z), (int)nib_lo(pa[fm].w),
+                              (int)nib_hi(pa[fm].w)};
 #pragma unroll
-                for (int fn = 0; fn < C::FN; ++fn) {
+                for (int fn = 0; fn < C::FN; ++fn)
                     acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa0, wb0[fn], z ? zero : acc[fm][fn], 0, 0, 0);
-                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1, wb1[fn], acc[fm][fn], 0, 0, 0);
-                }
             }
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa1[fm], wb1[fn], acc[fm][fn], 0, 0, 0);
         }
     }
 }
@@ -222,54 +230,72 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     const int G = T4 / tiles_per_group;
 
     // ---- DMA sources of this lane ----------------------------------------------
-    // slot q = j * 256 + tid of a tile holds row q / 4, chunk (q % 4) ^ ((row >> 1) & 3)
-    int a_off[C::DA], b_off[C::DB];   // row * 0 + chunk * 16 (row index kept separately)
-    int a_row[C::DA], b_row[C::DB];
+    // Slot q = j * 256 + tid of a tile holds row r = q / 4, chunk (q % 4) ^ f(r).
+    // Per-lane byte offsets are fixed for the whole K loop; only the uniform
+    // base (operand pointer + 64 * tile) moves.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t a4o[C::DA], a8o[C::DA], b4o[C::DB], b8o[C::DB];
 #pragma unroll
     for (int j = 0; j < C::DA; ++j) {
         const int q = j * kThreads + tid, r = q >> 2;
-        a_row[j] = min(row0 + r, a.M - 1);
-        a_off[j] = (((q & 3) ^ (r >> 1)) & 3) * 16;
+        const uint32_t row = min(row0 + r, a.M - 1);
+        const uint32_t off = (((q & 3) ^ (r >> 1) ^ (r >> 2)) & 3) * 16;
+        a4o[j] = row * (uint32_t)a.pitch4 + off;
+        a8o[j] = row * (uint32_t)a.pitch8 + off;
     }
 #pragma unroll
     for (int j = 0; j < C::DB; ++j) {
         const int q = j * kThreads + tid, r = q >> 2;
-        b_row[j] = min(col0 + r, a.N - 1);
-        b_off[j] = (((q & 3) ^ (r >> 1)) & 3) * 16;
+        const uint32_t row = min(col0 + r, a.N - 1);
+        const uint32_t off = (((q & 3) ^ (r >> 1) ^ (r >> 2)) & 3) * 16;
+        b4o[j] = row * (uint32_t)a.pitch4 + off;
+        b8o[j] = row * (uint32_t)a.pitch8 + off;
     }
     // scale slots: rows of A first, then columns of B
     bool s_is_a[C::DS];
-    int s_idx[C::DS];
+    uint32_t s_row[C::DS];
 #pragma unroll
     for (int j = 0; j < C::DS; ++j) {
         const int e = min(j * kThreads + tid, BM + BN - 1);
         s_is_a[j] = e < BM;
-        s_idx[j] = e < BM ? min(row0 + e, a.M - 1) : min(col0 + e - BM, a.N - 1);
+        s_row[j] = e < BM ? min(row0 + e, a.M - 1) : min(col0 + e - BM, a.N - 1);
     }
 
     auto issue = [&](int tt) {
         unsigned char *st = lds + (tt % kStages) * STAGE;
-        const bool tail = tt < T8;
-        const uint8_t *abase = tail ? reinterpret_cast<const uint8_t *>(a.a8) : a.a4;
-        const uint8_t *bbase = tail ? reinterpret_cast<const uint8_t *>(a.w8) : a.w4;
-        const int64_t pitch = tail ? a.pitch8 : a.pitch4;
-        const int64_t koff = (int64_t)(tail ? tt : tt - T8) * kTileBytes;
+        unsigned char *sa = st + wave_u * 1024, *sb = st + C::A_BYTES + wave_u * 1024;
+        unsigned char *ss = st + C::A_BYTES + C::B_BYTES + wave_u * 256;
+        if (tt < T8) {
+            const uint8_t *A = reinterpret_cast<const uint8_t *>(a.a8) + tt * kTileBytes;
+            const uint8_t *B = reinterpret_cast<const uint8_t *>(a.w8) + tt * kTileBytes;
 #pragma unroll
-        for (int j = 0; j < C::DA; ++j)
-            __builtin_amdgcn_global_load_lds(abase + a_row[j] * pitch + koff + a_off[j],
-                                             (lds_void *)(st + j * 4096 + wave * 1024), 16, 0, 0);
+            for (int j = 0; j < C::DA; ++j)
+                __builtin_amdgcn_global_load_lds(A + a8o[j], (lds_void *)(sa + j * 4096), 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < C::DB; ++j)
-            __builtin_amdgcn_global_load_lds(bbase + b_row[j] * pitch + koff + b_off[j],
-                                             (lds_void *)(st + C::A_BYTES + j * 4096 + wave * 1024), 16, 0, 0);
-        if constexpr (!EXPORT) {
-            const int g = tail ? 0 : (tt - T8) / tiles_per_group;
+            for (int j = 0; j < C::DB; ++j)
+                __builtin_amdgcn_global_load_lds(B + b8o[j], (lds_void *)(sb + j * 4096), 16, 0, 0);
+            if constexpr (!EXPORT) {
 #pragma unroll
-            for (int j = 0; j < C::DS; ++j) {
-                const float *src = tail ? (s_is_a[j] ? a.sa8 : a.sw8) + s_idx[j]
-                                        : (s_is_a[j] ? a.sa4 : a.sw4) + (int64_t)s_idx[j] * a.G + g;
-                __builtin_amdgcn_global_load_lds(
-                    src, (lds_void *)(st + C::A_BYTES + C::B_BYTES + j * 1024 + wave * 256), 4, 0, 0);
+                for (int j = 0; j < C::DS; ++j)
+                    __builtin_amdgcn_global_load_lds((s_is_a[j] ? a.sa8 : a.sw8) + s_row[j],
+                                                     (lds_void *)(ss + j * 1024), 4, 0, 0);
+            }
+        } else {
+            const int t4 = tt - T8;
+            const uint8_t *A = a.a4 + t4 * kTileBytes;
+            const uint8_t *B = a.w4 + t4 * kTileBytes;
+#pragma unroll
+            for (int j = 0; j < C::DA; ++j)
+                __builtin_amdgcn_global_load_lds(A + a4o[j], (lds_void *)(sa + j * 4096), 16, 0, 0);
+#pragma unroll
+            for (int j = 0; j < C::DB; ++j)
+                __builtin_amdgcn_global_load_lds(B + b4o[j], (lds_void *)(sb + j * 4096), 16, 0, 0);
+            if constexpr (!EXPORT) {
+                const int g = t4 / tiles_per_group;
+#pragma unroll
+                for (int j = 0; j < C::DS; ++j)
+                    __builtin_amdgcn_global_load_lds((s_is_a[j] ? a.sa4 : a.sw4) + s_row[j] * (uint32_t)a.G + g,
+                                                     (lds_void *)(ss + j * 1024), 4, 0, 0);
             }
         }
     };
@@ -379,8 +405,6 @@ using namespace gemm_impl;
 hipError_t launch_gemm(const GemmArgs &a, bool export_acc, hipStream_t stream) {
     if (a.M == 0 || a.N == 0)
         return hipSuccess;
-    if (a.M > 256)
-        return launch_cfg<CfgLarge>(a, export_acc, stream);
     if (a.M > 64)
         return launch_cfg<CfgMid>(a, export_acc, stream);
     return launch_cfg<CfgSmall>(a, export_acc, stream);
