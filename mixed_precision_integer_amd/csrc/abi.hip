@@ -11,7 +11,6 @@
 
 namespace {
 
-constexpr int64_t kMaxLds = 160 * 1024;       // LDS per workgroup on gfx950
 constexpr int64_t kAccLimit = int64_t(1) << 31;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -52,9 +51,6 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
     if (!aligned(src, 16) || ld % 8 != 0 || !aligned(perm, 16) || (q4 && !aligned(q4, 16)) ||
         (q8 && !aligned(q8, 16)) || (s4 && !aligned(s4, 4)) || (s8 && !aligned(s8, 4)))
         return W4A4_ERR_ALIGNMENT;
-    const int64_t lds = round_up(K, 8) * 2 + (group > 0 ? (int64_t)((K_n + 7) / 8 + G) * 4 : 0);
-    if (lds > kMaxLds)
-        return W4A4_ERR_UNSUPPORTED;
     w4a4::QuantArgs a;
     a.src = static_cast<const _Float16 *>(src);
     a.ld = ld;
@@ -71,6 +67,9 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
     a.s8 = s8;
     a.pitch4 = w4a4_pitch4_bytes(K_n);
     a.pitch8 = n_out > 0 ? w4a4_pitch8_bytes(n_out) : 0;
+    // the permutation and two row buffers live in LDS
+    if (K > w4a4::quant_rows_max_k())
+        return W4A4_ERR_UNSUPPORTED;
     if (w4a4::launch_quant_rows(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return W4A4_ERR_HIP;
     return W4A4_OK;

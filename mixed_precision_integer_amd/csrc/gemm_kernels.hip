@@ -27,8 +27,9 @@
 //   The first MFMA of a group reads a zero C operand, so no accumulator is
 //   ever cleared; at the end of a group the int32 sums are converted and
 //   added into fp32 accumulators.
-// * Tiles reach LDS through direct global->LDS DMA (global_load_lds_dwordx4):
-//   no VGPR staging and no ds_write. A 4-stage LDS ring with prefetch
+// * Tiles reach LDS through direct global->LDS DMA (global_load_lds_dwordx4,
+//   issued as inline asm with a uniform base and 32-bit lane offsets): no VGPR
+//   staging and no ds_write. A 4-stage LDS ring with prefetch
 //   distance 2 needs one barrier per tile: the stage written at tile t was
 //   last read at tile t-2, which every wave has finished once it has passed
 //   the barrier of tile t-1. Every wave waits for its own DMA with an explicit
@@ -50,7 +51,6 @@ namespace gemm_impl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 64;   // bytes of each row per K-tile
@@ -262,23 +262,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     }
 
     auto issue = [&](int tt) {
-        unsigned char *st = lds + (tt % kStages) * STAGE;
-        unsigned char *sa = st + wave_u * 1024, *sb = st + C::A_BYTES + wave_u * 1024;
-        unsigned char *ss = st + C::A_BYTES + C::B_BYTES + wave_u * 256;
+        const uint32_t st = lds_addr(lds) + (tt % kStages) * STAGE;
+        const uint32_t sa = st + wave_u * 1024, sb = st + C::A_BYTES + wave_u * 1024;
+        const uint32_t ss = st + C::A_BYTES + C::B_BYTES + wave_u * 256;
         if (tt < T8) {
             const uint8_t *A = reinterpret_cast<const uint8_t *>(a.a8) + tt * kTileBytes;
             const uint8_t *B = reinterpret_cast<const uint8_t *>(a.w8) + tt * kTileBytes;
 #pragma unroll
             for (int j = 0; j < C::DA; ++j)
-                __builtin_amdgcn_global_load_lds(A + a8o[j], (lds_void *)(sa + j * 4096), 16, 0, 0);
+                dma16(A, a8o[j], sa + j * 4096);
 #pragma unroll
             for (int j = 0; j < C::DB; ++j)
-                __builtin_amdgcn_global_load_lds(B + b8o[j], (lds_void *)(sb + j * 4096), 16, 0, 0);
+                dma16(B, b8o[j], sb + j * 4096);
             if constexpr (!EXPORT) {
 #pragma unroll
                 for (int j = 0; j < C::DS; ++j)
-                    __builtin_amdgcn_global_load_lds((s_is_a[j] ? a.sa8 : a.sw8) + s_row[j],
-                                                     (lds_void *)(ss + j * 1024), 4, 0, 0);
+                    dma4((s_is_a[j] ? a.sa8 : a.sw8) + s_row[j], ss + j * 1024);
             }
         } else {
             const int t4 = tt - T8;
@@ -286,16 +285,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
             const uint8_t *B = a.w4 + t4 * kTileBytes;
 #pragma unroll
             for (int j = 0; j < C::DA; ++j)
-                __builtin_amdgcn_global_load_lds(A + a4o[j], (lds_void *)(sa + j * 4096), 16, 0, 0);
+                dma16(A, a4o[j], sa + j * 4096);
 #pragma unroll
             for (int j = 0; j < C::DB; ++j)
-                __builtin_amdgcn_global_load_lds(B + b4o[j], (lds_void *)(sb + j * 4096), 16, 0, 0);
+                dma16(B, b4o[j], sb + j * 4096);
             if constexpr (!EXPORT) {
                 const int g = t4 / tiles_per_group;
 #pragma unroll
                 for (int j = 0; j < C::DS; ++j)
-                    __builtin_amdgcn_global_load_lds((s_is_a[j] ? a.sa4 : a.sw4) + s_row[j] * (uint32_t)a.G + g,
-                                                     (lds_void *)(ss + j * 1024), 4, 0, 0);
+                    dma4((s_is_a[j] ? a.sa4 : a.sw4) + s_row[j] * (uint32_t)a.G + g, ss + j * 1024);
             }
         }
     };

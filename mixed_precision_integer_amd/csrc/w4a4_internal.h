@@ -7,6 +7,30 @@
 
 namespace w4a4 {
 
+// Direct global->LDS DMA (gfx950 global_load_lds): lane i's bytes land at
+// M0 + i * size. Issued through inline asm so that the compiler does not put
+// a wait for every outstanding DMA in front of each later LDS read; the
+// kernels order DMA and LDS reads themselves with explicit vmcnt waits and
+// workgroup barriers. The instructions return nothing to VGPRs.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// 16 bytes per lane from base + voff. base and lds are wave-uniform; they are
+// moved to SGPRs explicitly (readfirstlane of a uniform value is exact).
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(sl)
+                 : "memory", "m0");
+}
+// 4 bytes per lane from a per-lane address
+__device__ __forceinline__ void dma4(const void *p, uint32_t lds) {
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(p), "s"(sl) : "memory", "m0");
+}
+
 // Arguments of the row quantizer: one launch quantizes `rows` rows of a
 // [rows, ld] fp16 matrix (activations or weights).
 struct QuantArgs {
@@ -22,6 +46,7 @@ struct QuantArgs {
 };
 
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream);
+int quant_rows_max_k();   // longest row (channels) the quantizer takes
 
 // Arguments of the mixed-precision GEMM.
 struct GemmArgs {
