@@ -109,6 +109,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qproj", choices=sorted(WORKLOADS))
     ap.add_argument("--m", type=int, default=None, help="token rows (decode sweep)")
+    ap.add_argument("--custom", default=None,
+                    help="M,N,K,n_out,group: a synthetic shape instead of a named workload")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -123,6 +125,10 @@ def main():
     import mixed_precision_integer_amd as w4
 
     w = WORKLOADS[args.workload]
+    if args.custom:
+        cm, cn, ck, co, cg = (int(v) for v in args.custom.split(","))
+        w = wl.Workload(f"custom_m{cm}_n{cn}_k{ck}_o{co}_g{cg}", cm, cn, ck, co, cg, 7, "normal",
+                        30.0, 0.02)
     M = args.m if args.m is not None else w.M
     X, W, outliers = wl.draw_workload(w, M if M <= w.M else None)
     if M > X.shape[0]:

@@ -4,7 +4,8 @@
 
 hipcc cross-compiles without a GPU. Packed-FP32 instructions are disabled
 for the device code (-packed-fp32-ops); hipcc's host pass warns that it does
-not know that target feature, which is harmless.
+not know that target feature, which is harmless. MFMA accumulators are kept
+in architectural VGPRs (-amdgpu-mfma-vgpr-form).
 """
 from __future__ import annotations
 
@@ -31,6 +32,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in ordinary VGPRs: the fp32 epilogue reads them
+           # with plain VALU ops instead of v_accvgpr_read copies
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"),
            *srcs, "-o", tmp]
     if verbose:

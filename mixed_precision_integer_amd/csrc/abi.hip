@@ -6,7 +6,7 @@
 
 #include <vector>
 
-#include "../../include/w4a4.h"
+#include "w4a4.h"
 #include "w4a4_internal.h"
 
 namespace {

@@ -286,10 +286,7 @@ hipError_t launch(const QuantArgs &a, hipStream_t stream) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED>,
                                                      THREADS, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
-    // about four rows per workgroup amortise its permutation load and keep a
-    // row in flight behind the one being quantized
-    const long want = std::max<long>(cus, (a.rows + 3) / 4);
-    const int grid = (int)std::min<long>(std::min<long>(a.rows, want), (long)cus * per_cu);
+    const int grid = (int)std::min<long>(a.rows, (long)cus * per_cu);
     hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED>), dim3(grid), dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
