@@ -102,6 +102,27 @@ def cpu_baseline(w, X, W, outliers, budget_s):
     }
 
 
+def copy_probe(torch, nbytes, steps, warmup):
+    """A plain copy of known size: it reads and writes exactly `nbytes` of HBM
+    per launch, so the hardware counters it produces give the scale from
+    FETCH_SIZE / WRITE_SIZE to bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    dst = [torch.empty_like(src) for _ in range(2)]
+    for i in range(warmup):
+        dst[i % 2].copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        dst[i % 2].copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / max(steps, 1)
+    print(json.dumps({"copy_probe_bytes": nbytes, "us_per_copy": us,
+                      "GBps": 2 * nbytes / us / 1e3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +134,9 @@ def main():
                     help="M,N,K,n_out,group: a synthetic shape instead of a named workload")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the layer, time a plain device-to-device copy of this many "
+                         "MiB (reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -123,6 +147,10 @@ def main():
 
     import torch
     import mixed_precision_integer_amd as w4
+
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib << 20, args.steps, args.warmup)
+        return
 
     w = WORKLOADS[args.workload]
     if args.custom:
