@@ -118,7 +118,11 @@ w4a4_status w4a4_pack_int4_weights(const void *W, int64_t ldw, const int32_t *pe
                                    w4a4_stream stream);
 
 /* Bytes of device workspace w4a4_outlier_gemm needs for this shape (0 means
- * none; a NULL workspace is then allowed). */
+ * none; a NULL workspace is then allowed). Shapes with few output tiles for
+ * the chip (decode batches) split K across workgroups; the workspace then
+ * holds one arrival counter per output tile (a fixed 2048-byte block at its
+ * start, the same place for every shape) and fp32 partial sums
+ * [splits, M, N]. A pure function of the shape. */
 size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
                                          int32_t group);
 
@@ -129,7 +133,14 @@ size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_
  *   Y[m, n] = fp16( sum_t sa4[m,t] sw4[n,t] acc4_t[m,n] + sa8[m] sw8[n] acc8[m,n] ).
  * Operands in the layouts above (from the two calls above). Y device fp16
  * [M, ldy], ldy >= N. GPU constraint (UNSUPPORTED otherwise): K_n * 16384 <
- * 2^31 and n_out * 16384 < 2^31 (int32 range of the widened accumulators). */
+ * 2^31 and n_out * 16384 < 2^31 (int32 range of the widened accumulators).
+ * workspace: device memory of at least w4a4_outlier_gemm_workspace_bytes
+ * bytes, 256-byte aligned (ALIGNMENT otherwise; WORKSPACE if too small). It
+ * must be all zero before the first call that uses it (allocate it zeroed
+ * once); every call leaves its counters at zero again when it completes, so
+ * it can be reused by later calls of any shape. Calls that share a workspace
+ * must not run concurrently. With split K the partial sums are added in a
+ * fixed order, so results are bit-identical from call to call. */
 w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4,
                               const float *sa8, const void *Wq4, const void *Wq8,
                               const float *sw4, const float *sw8, int32_t M, int32_t N,
@@ -147,7 +158,8 @@ w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *
                                   int32_t *acc8, w4a4_stream stream);
 
 /* Bytes of device workspace w4a4_quant_gemm needs: the quantized activations
- * (Aq4, Aq8, sa4, sa8 for M rows) plus the GEMM's own workspace. */
+ * (Aq4, Aq8, sa4, sa8 for M rows) plus the GEMM's own workspace, under the
+ * same zero-on-first-use rule as w4a4_outlier_gemm's workspace. */
 size_t w4a4_quant_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
                                        int32_t group);
 

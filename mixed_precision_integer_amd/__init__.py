@@ -220,7 +220,7 @@ def w4a4_outlier_gemm(a: QuantizedOperand, w: QuantizedOperand, out=None):
         out = torch.empty((M, N), dtype=torch.float16, device=a.s8.device)
     _check(out, torch.float16, "out", 2)
     ws_bytes = outlier_gemm_workspace_bytes(M, N, a.K, a.n_out, a.group)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=out.device) if ws_bytes else None
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=out.device) if ws_bytes else None
     _ok(lib().w4a4_outlier_gemm(*_gemm_args(a, w, out, ws)), "w4a4_outlier_gemm")
     return out
 
@@ -257,7 +257,7 @@ def quant_gemm(X, perm, w: QuantizedOperand, out=None, workspace=None):
     _check(out, torch.float16, "out", 2)
     need = quant_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=X.device)
     _check(workspace, torch.uint8, "workspace", 1)
     _ok(lib().w4a4_quant_gemm(X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.q4),
                               _nz(w.q8), _nz(w.s4), _nz(w.s8), M, N, K, w.n_out, w.group,
@@ -283,7 +283,7 @@ class W4A4Linear:
         need = quant_gemm_workspace_bytes(X.shape[0], self.weight.s8.shape[0], self.weight.K,
                                           self.n_out, self.group)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = _torch().empty(max(need, 1), dtype=_torch().uint8, device=X.device)
+            self._ws = _torch().zeros(max(need, 1), dtype=_torch().uint8, device=X.device)
         return quant_gemm(X, self.perm, self.weight, out=out, workspace=self._ws)
 
 
@@ -306,9 +306,9 @@ class LayerPlan:
                                                            device=X.device)
         self.a = alloc_operand(M, K, w.n_out, w.group, X.device)
         need = quant_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
-        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+        self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=X.device)
         gws = outlier_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
-        self.gws = torch.empty(gws, dtype=torch.uint8, device=X.device) if gws else None
+        self.gws = torch.zeros(gws, dtype=torch.uint8, device=X.device) if gws else None
         self._keep = (X, perm, w)
         L = lib()
         self._q, self._g, self._f = (L.w4a4_quant_reorder_act, L.w4a4_outlier_gemm,

@@ -174,8 +174,11 @@ w4a4_status w4a4_pack_int4_weights(const void *W, int64_t ldw, const int32_t *pe
     return quant_rows(W, ldw, perm, N, K, n_out, group, Wq4, Wq8, sw4, sw8, stream);
 }
 
-size_t w4a4_outlier_gemm_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t) {
-    return 0;
+size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                         int32_t group) {
+    if (M <= 0 || N <= 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
+        return 0;
+    return w4a4::plan_gemm(M, N, K - n_out, n_out, group, false).workspace_bytes;
 }
 
 w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
@@ -196,13 +199,15 @@ w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4
     if (!aligned(Y, 2) || (sa4 && !aligned(sa4, 4)) || (sw4 && !aligned(sw4, 4)) ||
         (sa8 && !aligned(sa8, 4)) || (sw8 && !aligned(sw8, 4)))
         return W4A4_ERR_ALIGNMENT;
-    if (workspace_bytes < w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group))
+    const size_t need = w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group);
+    if (workspace_bytes < need || (need > 0 && !workspace))
         return W4A4_ERR_WORKSPACE;
-    (void)workspace;
+    if (need > 0 && !aligned(workspace, 256))
+        return W4A4_ERR_ALIGNMENT;
     w4a4::GemmArgs a = gemm_args(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group);
     a.y = static_cast<_Float16 *>(Y);
     a.ldy = ldy;
-    if (w4a4::launch_gemm(a, false, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (w4a4::launch_gemm(a, false, workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
         return W4A4_ERR_HIP;
     return W4A4_OK;
 }
@@ -225,7 +230,7 @@ w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *
                                  n_out, group);
     a.acc4_out = acc4;
     a.acc8_out = acc8;
-    if (w4a4::launch_gemm(a, true, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (w4a4::launch_gemm(a, true, nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
         return W4A4_ERR_HIP;
     return W4A4_OK;
 }

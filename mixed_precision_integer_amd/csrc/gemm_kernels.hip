@@ -44,6 +44,9 @@
 //   vmcnt bookkeeping is a constant.
 // * Workgroups are mapped so that each XCD (own L2) works on a contiguous
 //   range of tiles, walked in bands of 8 tile rows.
+#include <algorithm>
+
+#include "w4a4.h"
 #include "w4a4_internal.h"
 
 namespace w4a4 {
@@ -54,8 +57,6 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 64;   // bytes of each row per K-tile
-constexpr int kStages = 4;
-constexpr int kPrefetch = kStages - 2;
 
 __device__ __forceinline__ uint32_t nib_hi(uint32_t p) { return p & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t nib_lo(uint32_t p) { return (p << 4) & 0xF0F0F0F0u; }
@@ -68,9 +69,11 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // byte offset of 16-byte chunk c of row r inside a tile
 __device__ __forceinline__ int swz(int r, int c) { return (r << 6) | (((c ^ (r >> 1) ^ (r >> 2)) & 3) << 4); }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    // LDS ring depth; tiles in flight ahead of the one being multiplied
+    static constexpr int STAGES = STAGES_, PREFETCH = STAGES_ - 2;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int DA = BM * 4 / kThreads, DB = BN * 4 / kThreads;
@@ -80,7 +83,23 @@ struct Cfg {
     static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
     static_assert(DA >= 1 && DB >= 1 && BM * 4 % kThreads == 0 && BN * 4 % kThreads == 0, "loader");
+    static_assert(PREFETCH >= 1 && PREFETCH <= 6, "ring depth");
 };
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 6 * per_tile]: the count must be
+// an immediate, so the few values a ring can leave outstanding are spelled out.
+template <int PER_TILE>
+__device__ __forceinline__ void wait_tiles(int tiles_outstanding) {
+    switch (tiles_outstanding) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_only(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_only(1 * PER_TILE)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * PER_TILE)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_only(3 * PER_TILE)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_only(4 * PER_TILE)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_only(5 * PER_TILE)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_only(6 * PER_TILE)); break;
+    }
+}
 
 // MFMAs of one K-tile held in LDS stage `st`. FRESH: the tile opens a scale
 // group (its first MFMAs take C = 0). TAIL: an INT8 tail tile (no widening).
@@ -194,24 +213,28 @@ __device__ __forceinline__ void export_group(const v16i (&acc)[C::FM][C::FN], co
         }
 }
 
-template <class C, bool EXPORT>
+template <class C, bool EXPORT, bool SPLIT>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     constexpr int BM = C::BM, BN = C::BN, FM = C::FM, FN = C::FN;
+    constexpr int STAGES = C::STAGES, PREFETCH = C::PREFETCH;
     constexpr int STAGE = C::A_BYTES + C::B_BYTES + (EXPORT ? 0 : C::S_BYTES);
     constexpr int D = C::DA + C::DB + (EXPORT ? 0 : C::DS);   // DMA instructions per tile per lane
 
-    __shared__ __align__(16) unsigned char lds[kStages * STAGE];
+    __shared__ __align__(16) unsigned char lds[STAGES * STAGE];
+    __shared__ int last_split;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int li = lane & 31, lh = lane >> 5;
 
-    // ---- tile of this workgroup ----------------------------------------------
+    // ---- output tile and K split of this workgroup ------------------------------
+    const int S = SPLIT ? a.splits : 1;
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    int tile = blockIdx.x;
-    if (tiles % 8 == 0)                       // consecutive workgroups alternate XCDs
+    const int ks = blockIdx.x % S;
+    int tile = blockIdx.x / S;
+    if (S == 1 && tiles % 8 == 0)             // consecutive workgroups alternate XCDs
         tile = (tile % 8) * (tiles / 8) + tile / 8;
     constexpr int BAND = 8;
     const int band = tile / (BAND * tiles_n);
@@ -224,10 +247,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     const int T8 = (int)(a.pitch8 / kTileBytes);
     const int T4 = (int)(a.pitch4 / kTileBytes);
     const int T = T8 + T4;
-    // INT4 tiles per scale group (per-row scales: all of them); G groups. With
-    // no INT4 channels (every channel an outlier) there are no INT4 groups.
+    // INT4 tiles per scale group (per-row scales: all of them). With no INT4
+    // channels (every channel an outlier) there are no INT4 groups.
     const int tiles_per_group = a.group > 0 ? a.group / 128 : max(T4, 1);
-    const int G = T4 / tiles_per_group;
+    // K-tiles [t_begin, t_end) of this split; split boundaries may cut a scale
+    // group, whose two parts are then dequantized with the same scales.
+    const int t_begin = (int)((int64_t)ks * T / S), t_end = (int)((int64_t)(ks + 1) * T / S);
 
     // ---- DMA sources of this lane ----------------------------------------------
     // Slot q = j * 256 + tid of a tile holds row r = q / 4, chunk (q % 4) ^ f(r).
@@ -262,7 +287,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     }
 
     auto issue = [&](int tt) {
-        const uint32_t st = lds_addr(lds) + (tt % kStages) * STAGE;
+        const uint32_t st = lds_addr(lds) + (tt % STAGES) * STAGE;
         const uint32_t sa = st + wave_u * 1024, sb = st + C::A_BYTES + wave_u * 1024;
         const uint32_t ss = st + C::A_BYTES + C::B_BYTES + wave_u * 256;
         if (tt < T8) {
@@ -298,22 +323,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         }
     };
 
-    // Wait for tile tt (after issuing tile tt + kPrefetch) and make it visible
-    // to the whole workgroup.
+    // Wait for tile tt (after issuing tile tt + PREFETCH if it is in this
+    // split) and make it visible to the whole workgroup. Tiles after tt that
+    // are already in flight stay in flight.
     auto begin_tile = [&](int tt) -> const unsigned char * {
         compiler_fence();
-        if (tt + kPrefetch < T) {
-            issue(tt + kPrefetch);
+        if (tt + PREFETCH < t_end) {
+            issue(tt + PREFETCH);
             if constexpr (EXPORT)
                 __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // accumulator stores share vmcnt
             else
-                __builtin_amdgcn_s_waitcnt(vmcnt_only(kPrefetch * D));
-        } else {
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(PREFETCH * D));
+        } else if constexpr (EXPORT) {
             __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        } else {
+            wait_tiles<D>(t_end - 1 - tt);
         }
         __builtin_amdgcn_s_barrier();
         compiler_fence();
-        return lds + (tt % kStages) * STAGE;
+        return lds + (tt % STAGES) * STAGE;
     };
 
     v16i acc[FM][FN];
@@ -328,15 +356,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 
     // ---- main loop: the tail group, then the INT4 groups ------------------------------
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p)
-        if (p < T)
-            issue(p);
+    for (int p = 0; p < PREFETCH; ++p)
+        if (t_begin + p < t_end)
+            issue(t_begin + p);
 
-    int tt = 0;
-    if (T8 > 0) {
+    int tt = t_begin;
+    if (tt < T8) {
+        const int run_end = min(T8, t_end);
         const unsigned char *st = begin_tile(tt++);
         mma_tile<C, true, true>(acc, st, wm, wn, li, lh);
-        while (tt < T8) {
+        while (tt < run_end) {
             st = begin_tile(tt++);
             mma_tile<C, false, true>(acc, st, wm, wn, li, lh);
         }
@@ -345,10 +374,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         else
             dequant_group<C, true>(acc, yacc, st, wm, wn, li, lh);
     }
-    for (int g = 0; g < G; ++g) {
+    while (tt < t_end) {
+        const int g = (tt - T8) / tiles_per_group;
+        const int run_end = min(T8 + (g + 1) * tiles_per_group, t_end);
         const unsigned char *st = begin_tile(tt++);
         mma_tile<C, true, false>(acc, st, wm, wn, li, lh);
-        for (int k = 1; k < tiles_per_group; ++k) {
+        while (tt < run_end) {
             st = begin_tile(tt++);
             mma_tile<C, false, false>(acc, st, wm, wn, li, lh);
         }
@@ -358,54 +389,195 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
             dequant_group<C, false>(acc, yacc, st, wm, wn, li, lh);
     }
 
-    // ---- epilogue: fp16 store -------------------------------------------------------
     if constexpr (!EXPORT) {
+        if constexpr (!SPLIT) {
+            // ---- epilogue: fp16 store --------------------------------------------------
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+            for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int n = col0 + wn * C::WTN + fn * 32 + li;
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int n = col0 + wn * C::WTN + fn * 32 + li;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
-                    if (m < a.M && n < a.N)
-                        a.y[(int64_t)m * a.ldy + n] = (_Float16)yacc[fm][fn][r];
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
+                        if (m < a.M && n < a.N)
+                            a.y[(int64_t)m * a.ldy + n] = (_Float16)yacc[fm][fn][r];
+                    }
                 }
+        } else {
+            // ---- split-K epilogue ------------------------------------------------------
+            // Every split stores its fp32 partial tile; the last split of the tile
+            // to arrive (device-wide counter) adds the S partials in split order,
+            // so the result does not depend on which one that is, writes fp16 and
+            // returns the counter to zero for the next call.
+            // The partials and the counter are touched only by agent-scope
+            // relaxed atomics, which are coherent across the XCDs' L2s without
+            // a whole-cache write-back or invalidate; the partial stores are
+            // complete (vmcnt 0) before the counter is incremented, and the
+            // reads are issued only after the increment has returned.
+            float *part = a.part + (int64_t)ks * a.M * a.N;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int n = col0 + wn * C::WTN + fn * 32 + li;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
+                        if (m < a.M && n < a.N)
+                            __hip_atomic_store(part + (int64_t)m * a.N + n, yacc[fm][fn][r],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            compiler_fence();
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            compiler_fence();
+            __syncthreads();
+            if (tid == 0) {
+                const uint32_t prev = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                const int is_last = prev == (uint32_t)(S - 1);
+                if (is_last)
+                    __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last_split = is_last;
             }
+            __syncthreads();
+            if (last_split) {
+                // Partials of up to kSB splits for all of this lane's elements are
+                // loaded as one batch (every load in bounds: rows past M and
+                // splits past S are clamped and their values discarded), so the
+                // batch costs one memory latency.
+                constexpr int kSB = 4;
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const int n = col0 + wn * C::WTN + fn * 32 + li;
+                        const int ncl = min(n, a.N - 1);
+                        float sum[16];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            sum[r] = 0.0f;
+                        for (int s0 = 0; s0 < S; s0 += kSB) {
+                            float v[kSB][16];
+#pragma unroll
+                            for (int j = 0; j < kSB; ++j) {
+                                const float *src = a.part + (int64_t)min(s0 + j, S - 1) * a.M * a.N;
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
+                                    v[j][r] = __hip_atomic_load(src + (int64_t)min(m, a.M - 1) * a.N + ncl,
+                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                }
+                            }
+#pragma unroll
+                            for (int j = 0; j < kSB; ++j)
+                                if (s0 + j < S)
+#pragma unroll
+                                    for (int r = 0; r < 16; ++r)
+                                        sum[r] += v[j][r];
+                        }
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
+                            if (m < a.M && n < a.N)
+                                a.y[(int64_t)m * a.ldy + n] = (_Float16)sum[r];
+                        }
+                    }
+            }
+        }
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EXPORT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool EXPORT, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-    gemm_body<Cfg<BM, BN, WAVES_M, WAVES_N>, EXPORT>(a);
+    gemm_body<Cfg<BM, BN, WAVES_M, WAVES_N, STAGES>, EXPORT, SPLIT>(a);
 }
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs &a, bool export_acc, hipStream_t stream) {
     const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
+    const dim3 grid(tiles * a.splits);
     if (export_acc)
-        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, true>), dim3(tiles),
+        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, true, false>), grid,
+                           dim3(kThreads), 0, stream, a);
+    else if (a.splits > 1)
+        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, false, true>), grid,
                            dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, false>), dim3(tiles),
+        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, false, false>), grid,
                            dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-using CfgLarge = Cfg<256, 128, 2, 2>;   // waves of 128 x 64
-using CfgMid = Cfg<128, 128, 2, 2>;     // waves of 64 x 64
-using CfgSmall = Cfg<64, 128, 1, 4>;    // waves of 64 x 32
+using CfgMid = Cfg<128, 128, 2, 2, 4>;     // waves of 64 x 64, two workgroups per CU
+using CfgSmall = Cfg<64, 64, 2, 2, 4>;     // waves of 32 x 32, four workgroups per CU
 
 }  // namespace gemm_impl
 
 using namespace gemm_impl;
 
-hipError_t launch_gemm(const GemmArgs &a, bool export_acc, hipStream_t stream) {
-    if (a.M == 0 || a.N == 0)
+namespace {
+
+constexpr int kDeviceCUs = 256;            // MI355X; the split choice is tuned for it
+constexpr int kMaxSplitTiles = kDeviceCUs * 2;   // a shape splits K only below this
+constexpr size_t kSplitCounterBytes = (kMaxSplitTiles * sizeof(uint32_t) + 255) / 256 * 256;
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+// Tile shape and K split for a shape. Pure function of the shape, so the
+// workspace query and the launch always agree.
+GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc) {
+    (void)group;
+    GemmPlan p{};
+    const bool small = M <= 64;
+    const int bm = small ? CfgSmall::BM : CfgMid::BM, bn = small ? CfgSmall::BN : CfgMid::BN;
+    const int per_cu = small ? 4 : 2;                          // resident workgroups per CU (LDS)
+    p.cfg = small ? 0 : 1;
+    p.tiles = ceil_div(M, bm) * ceil_div(N, bn);
+    const int T = (int)(w4a4_pitch4_bytes(K_n) / 64 + w4a4_pitch8_bytes(n_out) / 64);
+    int S = 1;
+    const int slots = kDeviceCUs * per_cu;
+    if (!export_acc && p.tiles > 0 && p.tiles * 2 <= slots && p.tiles <= kMaxSplitTiles) {
+        // about half the resident slots: measured on the 8192 x 8192 decode
+        // shapes, more splits cost more in partial-sum traffic and arrival
+        // latency than they gain in memory parallelism. At least two K-tiles
+        // per split, and the fp32 partial traffic (S * M * N * 8 bytes) at most
+        // the packed weights' size (N * K_n / 2).
+        S = ceil_div(slots / 2, p.tiles);
+        S = std::min(S, std::max(1, T / 2));
+        S = std::min(S, std::max(1, (int)(K_n / 8 / std::max(M, 1))));
+        S = std::min(S, 32);
+        S = std::max(S, 1);
+    }
+    p.splits = S;
+    if (S > 1) {
+        // The counters sit at a fixed place, first in the workspace, sized for
+        // the most tiles that are ever split: partial sums of one shape then
+        // never land on the counters of another, and a zeroed workspace stays
+        // valid for calls of any shape.
+        p.part_offset = kSplitCounterBytes;
+        p.part_bytes = (size_t)S * M * N * sizeof(float);
+        p.workspace_bytes = p.part_offset + p.part_bytes;
+    }
+    return p;
+}
+
+hipError_t launch_gemm(const GemmArgs &a_in, bool export_acc, void *workspace, hipStream_t stream) {
+    if (a_in.M == 0 || a_in.N == 0)
         return hipSuccess;
-    if (a.M > 64)
-        return launch_cfg<CfgMid>(a, export_acc, stream);
-    return launch_cfg<CfgSmall>(a, export_acc, stream);
+    GemmArgs a = a_in;
+    const GemmPlan p = plan_gemm(a.M, a.N, a.K_n, a.n_out, a.group, export_acc);
+    a.splits = p.splits;
+    if (p.splits > 1) {
+        a.ctr = static_cast<uint32_t *>(workspace);
+        a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.part_offset);
+    }
+    if (p.cfg == 0)
+        return launch_cfg<CfgSmall>(a, export_acc, stream);
+    return launch_cfg<CfgMid>(a, export_acc, stream);
 }
 
 }  // namespace w4a4

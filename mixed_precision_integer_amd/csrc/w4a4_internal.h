@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace w4a4 {
@@ -60,8 +61,25 @@ struct GemmArgs {
     int32_t *acc8_out;    // [M, N] or nullptr
     int32_t M, N, K_n, n_out, group, G;
     int64_t pitch4, pitch8, ldy;
+    int32_t splits;       // K splits (1: no split); set by launch_gemm
+    float *part;          // [splits, M, N] fp32 partial sums (splits > 1)
+    uint32_t *ctr;        // [output tiles] arrival counters, zero between calls
 };
 
-hipError_t launch_gemm(const GemmArgs &a, bool export_acc, hipStream_t stream);
+// Launch shape of the GEMM for one problem: a pure function of the shape.
+struct GemmPlan {
+    int cfg;                  // tile configuration
+    int tiles;                // output tiles
+    int splits;               // K splits per output tile
+    size_t part_offset;       // byte offset of the fp32 partial sums (counters first)
+    size_t part_bytes;        // fp32 partial sums
+    size_t workspace_bytes;   // 0 when splits == 1
+};
+
+GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc);
+
+// `workspace` holds plan_gemm(...).workspace_bytes bytes; its counter part
+// must be zero on entry and is zero again when the kernel completes.
+hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipStream_t stream);
 
 }  // namespace w4a4

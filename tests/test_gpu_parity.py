@@ -134,6 +134,43 @@ def test_mid_size_parity(oracle, M, N, K, n_out, group):
     full_compare(oracle, X, W, o, group)
 
 
+# Shapes with few output tiles and long K: the GEMM splits K across workgroups
+# (fp32 partials in the workspace, added in split order by the last split).
+SPLIT_K = [
+    # M, N, K, n_out, group
+    (4, 384, 4224, 128, 128),       # group mode, 3 output tiles
+    (3, 1000, 4096, 64, 0),         # per-row scales, ragged N, split inside the one group
+    (100, 256, 8192, 128, 128),     # 128 x 128 tiles, ragged M
+    (1, 640, 2176, 128, 256),       # one token, group of two K-tiles cut by splits
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out,group", SPLIT_K)
+def test_split_k_parity(oracle, M, N, K, n_out, group):
+    assert w4.outlier_gemm_workspace_bytes(M, N, K, n_out, group) > 0, "shape does not split K"
+    X, W, o = wl.draw(M, N, K, n_out, seed=M * 11 + K, outlier_factor=30.0)
+    full_compare(oracle, X, W, o, group)
+
+
+def test_split_k_workspace_reuse(oracle):
+    """One workspace for shapes with different tile and split counts, in turn:
+    every call must leave the tile counters at zero for the next one."""
+    shapes = [(4, 384, 4224, 128, 128), (3, 1000, 4096, 64, 0), (4, 384, 4224, 128, 128)]
+    need = max(w4.outlier_gemm_workspace_bytes(*s) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i, (M, N, K, n_out, group) in enumerate(shapes):
+        X, W, o = wl.draw(M, N, K, n_out, seed=50 + i)
+        perm, Xd, a, w = run_layer(X, W, o, group)
+        fresh = w4.w4a4_outlier_gemm(a, w)
+        y = torch.empty_like(fresh)
+        for _ in range(3):
+            y.fill_(float("nan"))          # a split that never reduces would leave NaN
+            st = w4.lib().w4a4_outlier_gemm(*w4._gemm_args(a, w, y, ws))
+            assert st == 0
+            torch.cuda.synchronize()
+            assert torch.equal(y, fresh), f"shape {i}: reused workspace gives a different Y"
+
+
 def test_laplace_inputs(oracle):
     X, W, o = wl.draw(96, 160, 896, 64, seed=9, x_dist="laplace", outlier_factor=50.0)
     full_compare(oracle, X, W, o, 0)
