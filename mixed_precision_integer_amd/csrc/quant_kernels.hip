@@ -9,12 +9,21 @@
 // quantizing pass).
 //
 // Design (HBM-bound: every input byte is read once, every code written once)
-// * Persistent workgroups loop over rows. The permutation is read once per
-//   workgroup into LDS as uint16; rows stream in by direct global->LDS DMA
-//   (16 bytes per lane), double buffered: the next row's DMA is in flight
-//   while the current row is quantized. LDS is sized statically per
-//   row-length bucket (K <= 4096, 8192, 16384, 24576); long rows use more
-//   lanes per workgroup so that each CU still runs 4 or more waves per SIMD.
+// * Persistent workgroups loop over rows. Rows stream in by direct
+//   global->LDS DMA (16 bytes per lane), double buffered: the first two rows
+//   are requested at once, then each next row's DMA is in flight while the
+//   current row is quantized. LDS holds only the two row buffers and small
+//   reduction tables, sized statically per row-length bucket (K <= 4096,
+//   8192, 16384, 24576); long rows use more lanes per workgroup. Up to 512
+//   lanes the kernel is held to 64 VGPRs so that every workgroup the
+//   occupancy query counts is resident from the start.
+// * The channels a lane handles are the same in every row, so the
+//   permutation entries it needs are loaded once per workgroup into
+//   registers (uint16 pairs); the per-row gather is then one LDS read per
+//   channel with no dependent index load.
+// * Two barriers per row: one after the row has landed, one after the
+//   absmax reductions; every lane then derives the scale and reciprocal it
+//   needs itself (identical arithmetic in every lane, so identical values).
 // * A lane owns "units" of 8 reordered head channels (one packed dword of
 //   output); consecutive lanes own consecutive units, so stores coalesce. A
 //   unit's 8 fp16 values are gathered once and stay in registers as four
@@ -34,6 +43,7 @@
 //   to the definition. Offset codes q + 8 are packed with v_cvt_pk_u8_f32 and
 //   turned into two's complement nibbles with one xor per dword.
 #include <algorithm>
+#include <atomic>
 
 #include "w4a4_internal.h"
 
@@ -41,6 +51,8 @@ namespace w4a4 {
 namespace quant_impl {
 
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxDevices = 64;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -82,32 +94,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Static LDS for rows of up to KMAX channels: the permutation as uint16, two
-// row buffers (whole DMA rounds) and the group tables.
+// Static LDS for rows of up to KMAX channels: two row buffers (whole DMA
+// rounds), the group maxima of two consecutive rows and the wave maxima.
 template <int KMAX, int THREADS>
 struct RowLds {
     static constexpr int ROUND = THREADS * 16;   // bytes one DMA instruction moves per workgroup
     static constexpr int XB = (KMAX * 2 + ROUND - 1) / ROUND * ROUND;
     static constexpr int GMAX = KMAX / 128;
-    uint16_t perm[KMAX];
     unsigned char x[2][XB];
-    float gs[GMAX], gr[GMAX];
     unsigned gmax[2][GMAX];
+    float red_h[2][THREADS / 64], red_t[2][THREADS / 64];
 };
 
-template <int KMAX, int THREADS, bool GROUPED>
-__global__ __launch_bounds__(THREADS) void quant_rows_kernel(QuantArgs a) {
+// WIDE_TAIL: the outlier tail may need more than one 4-channel word per lane.
+// Up to 512 lanes a workgroup is register-limited: 64 VGPRs (eight waves per
+// SIMD) keep every workgroup the occupancy query counts resident at once.
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL ? 8 : 4)))
+void quant_rows_kernel(QuantArgs a) {
     using L = RowLds<KMAX, THREADS>;
-    constexpr int GMAX = L::GMAX, NW = THREADS / 64;
-    constexpr int UMAX = (KMAX / 8 + THREADS - 1) / THREADS;   // head units per lane
+    constexpr int NW = THREADS / 64;
+    constexpr int UMAX = (KMAX / 8 + THREADS - 1) / THREADS;    // head units (8 channels) per lane
+    constexpr int TW = WIDE_TAIL ? (KMAX / 4 + THREADS - 1) / THREADS : 1;   // tail words per lane
     __shared__ __align__(16) L sm;
-    __shared__ float red_h[NW], red_t[NW], row_sr[4];
 
     const int K = a.K, K_n = a.K_n, n_out = a.n_out, G = a.G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
-    uint16_t *perm16 = sm.perm;
-    unsigned *gmax = &sm.gmax[0][0];
 
     const int nfull = K / 8;                       // whole 16-byte chunks of a row
     const int rounds = (nfull + THREADS - 1) / THREADS;
@@ -126,16 +139,70 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(QuantArgs a) {
     int row = blockIdx.x;
     if (row < a.rows)
         issue_row(row, 0);
-    // permutation -> LDS (uint16), once per workgroup, while the first row streams in
-    for (int j = tid; j < K; j += THREADS)
-        perm16[j] = (uint16_t)a.perm[j];
+    if (row + (int)gridDim.x < a.rows)         // the second row streams in at once as well
+        issue_row(row + gridDim.x, 1);
+
+    // The channels a lane reads are the same in every row, so their source
+    // positions (the permutation) are loaded once into registers as uint16
+    // pairs: head unit u = i * THREADS + tid holds reordered channels 8u..8u+7,
+    // tail word w = i * THREADS + tid holds K_n + 4w .. K_n + 4w + 3. All loads
+    // are issued (indices clamped into the array) before any is waited for.
+    uint32_t pv[UMAX][4], pt[TW][2];
+    {
+        // 16-byte loads (a head unit's 8 entries are two of them; a tail word
+        // is one when K_n % 4 == 0), index clamped into the array; entries
+        // past the last whole int4 are fixed up with scalar loads after.
+        const int K4 = K / 4;
+        const int4 *perm4 = reinterpret_cast<const int4 *>(a.perm);
+        int4 e[UMAX][2], f[TW];
+        if (K4 > 0) {
+#pragma unroll
+            for (int i = 0; i < UMAX; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    e[i][h] = perm4[min(2 * (i * THREADS + tid) + h, K4 - 1)];
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+                f[i] = perm4[min(K_n / 4 + i * THREADS + tid, K4 - 1)];
+        } else {                                   // K < 4: every entry comes from fix() below
+#pragma unroll
+            for (int i = 0; i < UMAX; ++i)
+                e[i][0] = e[i][1] = int4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+                f[i] = int4{0, 0, 0, 0};
+        }
+        const bool tail4 = (K_n & 3) == 0;
+        auto fix = [&](int v, int j) { return (j >= 4 * K4 && j < K) ? a.perm[j] : v; };
+        auto pack = [](int lo, int hi) { return (uint32_t)(lo & 0xFFFF) | ((uint32_t)hi << 16); };
+#pragma unroll
+        for (int i = 0; i < UMAX; ++i) {
+            const int j0 = (i * THREADS + tid) * 8;
+            pv[i][0] = pack(fix(e[i][0].x, j0), fix(e[i][0].y, j0 + 1));
+            pv[i][1] = pack(fix(e[i][0].z, j0 + 2), fix(e[i][0].w, j0 + 3));
+            pv[i][2] = pack(fix(e[i][1].x, j0 + 4), fix(e[i][1].y, j0 + 5));
+            pv[i][3] = pack(fix(e[i][1].z, j0 + 6), fix(e[i][1].w, j0 + 7));
+        }
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int j0 = K_n + (i * THREADS + tid) * 4;
+            if (tail4) {
+                pt[i][0] = pack(fix(f[i].x, j0), fix(f[i].y, j0 + 1));
+                pt[i][1] = pack(fix(f[i].z, j0 + 2), fix(f[i].w, j0 + 3));
+            } else {
+                pt[i][0] = pack(j0 < K ? a.perm[j0] : 0, j0 + 1 < K ? a.perm[j0 + 1] : 0);
+                pt[i][1] = pack(j0 + 2 < K ? a.perm[j0 + 2] : 0, j0 + 3 < K ? a.perm[j0 + 3] : 0);
+            }
+        }
+    }
     if (GROUPED)
-        for (int t = tid; t < 2 * GMAX; t += THREADS)
-            gmax[t] = 0u;
+        for (int t = tid; t < 2 * L::GMAX; t += THREADS)
+            (&sm.gmax[0][0])[t] = 0u;
+
     for (int it = 0; row < a.rows; ++it, row += gridDim.x) {
         const int buf = it & 1;
         const uint16_t *xs = reinterpret_cast<const uint16_t *>(sm.x[buf]);
-        unsigned *gm = gmax + buf * GMAX;
+        unsigned *gm = sm.gmax[buf];
         // (1) this row has landed in LDS and the previous row is finished
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(kWaitAll);
@@ -147,28 +214,29 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(QuantArgs a) {
                 reinterpret_cast<_Float16 *>(sm.x[buf])[nfull * 8 + tid] = src[nfull * 8 + tid];
             lds_barrier();
         }
-        if (row + (int)gridDim.x < a.rows)
+        if (it > 0 && row + (int)gridDim.x < a.rows)   // buffer buf ^ 1 held the previous row
             issue_row(row + gridDim.x, buf ^ 1);
+        if (GROUPED)                               // the next row accumulates in the other table
+            for (int t = tid; t < G; t += THREADS)
+                sm.gmax[buf ^ 1][t] = 0u;
 
-        // (2) gather the head units into registers; absmax in packed fp16
-        uint32_t v[UMAX][4];
+        // (2) gather head units and tail words into registers; absmax (packed fp16)
+        uint32_t v[UMAX][4], tv[TW][2];
         float hmax = 0.0f, tmax = 0.0f;
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
             const int u = i * THREADS + tid;
             const int j0 = u * 8;
             if (u < U && j0 + 8 <= K_n) {
-                const uint4 p = *reinterpret_cast<const uint4 *>(perm16 + j0);
-                const uint32_t w[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    v[i][k] = (uint32_t)xs[w[k] & 0xFFFF] | ((uint32_t)xs[w[k] >> 16] << 16);
+                    v[i][k] = (uint32_t)xs[pv[i][k] & 0xFFFF] | ((uint32_t)xs[pv[i][k] >> 16] << 16);
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int j = j0 + 2 * k;
-                    const uint32_t lo = (u < U && j < K_n) ? xs[perm16[j]] : 0u;
-                    const uint32_t hi = (u < U && j + 1 < K_n) ? xs[perm16[j + 1]] : 0u;
+                    const uint32_t lo = (u < U && j < K_n) ? xs[pv[i][k] & 0xFFFF] : 0u;
+                    const uint32_t hi = (u < U && j + 1 < K_n) ? xs[pv[i][k] >> 16] : 0u;
                     v[i][k] = lo | (hi << 16);
                 }
             }
@@ -187,44 +255,43 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(QuantArgs a) {
                 hmax = fmaxf(hmax, m);
             }
         }
-        for (int j = K_n + tid; j < K; j += THREADS)
-            tmax = fmaxf(tmax, fabsf((float)__builtin_bit_cast(_Float16, xs[perm16[j]])));
-        hmax = wave_max(hmax);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int w = i * THREADS + tid;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int j = K_n + 4 * w + 2 * k;
+                const uint32_t lo = j < K ? xs[pt[i][k] & 0xFFFF] : 0u;
+                const uint32_t hi = j + 1 < K ? xs[pt[i][k] >> 16] : 0u;
+                tv[i][k] = lo | (hi << 16);
+                const half2 h = __builtin_bit_cast(half2, tv[i][k] & 0x7FFF7FFFu);
+                tmax = fmaxf(tmax, fmaxf((float)h.x, (float)h.y));
+            }
+        }
+        if (!GROUPED)
+            hmax = wave_max(hmax);
         tmax = wave_max(tmax);
         if (lane == 0) {
-            red_h[wave] = hmax;
-            red_t[wave] = tmax;
+            sm.red_h[buf][wave] = hmax;
+            sm.red_t[buf][wave] = tmax;
         }
         lds_barrier();
 
-        // (3) scales and reciprocals
-        if (GROUPED) {
-            for (int t = tid; t < G; t += THREADS) {
-                const float s = __uint_as_float(gm[t]) / 7.0f;
-                sm.gs[t] = s;
-                sm.gr[t] = recip_or_zero(s);
-                a.s4[(int64_t)row * G + t] = s;
-                gmax[(buf ^ 1) * GMAX + t] = 0u;   // the next row accumulates there
-            }
-        }
-        if (tid == 0) {
-            float ra = 0.0f, ta = 0.0f;
+        // (3) scales: every lane derives the ones it needs (identical values)
+        float ra = 0.0f, ta = 0.0f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                ra = fmaxf(ra, red_h[w]);
-                ta = fmaxf(ta, red_t[w]);
-            }
-            const float s = ra / 7.0f, s8 = ta / 127.0f;
-            row_sr[0] = s;
-            row_sr[1] = recip_or_zero(s);
-            row_sr[2] = s8;
-            row_sr[3] = recip_or_zero(s8);
+        for (int w = 0; w < NW; ++w) {
+            ra = fmaxf(ra, sm.red_h[buf][w]);
+            ta = fmaxf(ta, sm.red_t[buf][w]);
+        }
+        const float s_row = ra / 7.0f, r_row = recip_or_zero(s_row);
+        const float s8 = ta / 127.0f, r8 = recip_or_zero(s8);
+        if (tid == 0) {
             if (!GROUPED && G > 0)
-                a.s4[row] = s;
+                a.s4[row] = s_row;
             if (a.s8)
                 a.s8[row] = n_out > 0 ? s8 : 0.0f;
         }
-        lds_barrier();
 
         // (4) INT4 head: codes + 8 as bytes, even channels in one dword and odd
         //     ones in another, then one nibble interleave and an xor with 8
@@ -233,20 +300,19 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(QuantArgs a) {
         for (int i = 0; i < UMAX; ++i) {
             const int u = i * THREADS + tid;
             if (u < U) {
-                float s, r;
+                float sc = s_row, rc = r_row;
                 if (GROUPED) {
                     const int t = (u * 8) / a.group;
-                    s = sm.gs[t];
-                    r = sm.gr[t];
-                } else {
-                    s = row_sr[0];
-                    r = row_sr[1];
+                    sc = __uint_as_float(gm[t]) / 7.0f;
+                    rc = recip_or_zero(sc);
+                    if ((u * 8) % a.group == 0)    // the group's first unit stores its scale
+                        a.s4[(int64_t)row * G + t] = sc;
                 }
                 uint32_t ev = 0, od = 0;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float c0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), s, r)) + 8.0f;
-                    const float c1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), s, r)) + 8.0f;
+                    const float c0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), sc, rc)) + 8.0f;
+                    const float c1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), sc, rc)) + 8.0f;
                     ev = __builtin_amdgcn_cvt_pk_u8_f32(c0, k, ev);
                     od = __builtin_amdgcn_cvt_pk_u8_f32(c1, k, od);
                 }
@@ -256,39 +322,69 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(QuantArgs a) {
         for (int u = U + tid; u < W4; u += THREADS)   // zero padding of the row pitch
             q4row[u] = 0u;
 
-        // (5) INT8 tail: 4 codes -> one dword
+        // (5) INT8 tail: 4 codes -> one dword (zero past the last outlier)
         if (a.q8) {
             uint32_t *q8row = reinterpret_cast<uint32_t *>(a.q8 + (int64_t)row * a.pitch8);
-            const float s8 = row_sr[2], r8 = row_sr[3];
-            for (int w = tid; w < W8; w += THREADS) {
-                uint32_t word = 0;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int j = K_n + w * 4 + k;
-                    if (j < K) {
-                        const float x = (float)__builtin_bit_cast(_Float16, xs[perm16[j]]);
-                        const int q = (int)__builtin_rintf(exact_quotient(x, s8, r8));
-                        word |= (uint32_t)(q & 0xFF) << (8 * k);
+            for (int i = 0; i < TW; ++i) {
+                const int w = i * THREADS + tid;
+                if (w < W8) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int j = K_n + 4 * w + k;
+                        if (j < K) {
+                            const uint32_t h = (k & 1) ? (tv[i][k >> 1] >> 16) : (tv[i][k >> 1] & 0xFFFF);
+                            const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+                            const int q = (int)__builtin_rintf(exact_quotient(x, s8, r8));
+                            word |= (uint32_t)(q & 0xFF) << (8 * k);
+                        }
                     }
+                    q8row[w] = word;
                 }
-                q8row[w] = word;
             }
         }
     }
 }
 
-template <int KMAX, int THREADS, bool GROUPED>
-hipError_t launch(const QuantArgs &a, hipStream_t stream) {
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+// Resident workgroups of one instantiation on the current device, queried on
+// first use (a launch then costs no runtime queries).
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL>
+long resident_slots() {
+    static std::atomic<long> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        dev = -1;
+    if (dev >= 0) {
+        const long c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 256, per_cu = 1;
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL>,
                                                      THREADS, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
-    const int grid = (int)std::min<long>(a.rows, (long)cus * per_cu);
-    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED>), dim3(grid), dim3(THREADS), 0, stream, a);
+    const long slots = (long)cus * per_cu;
+    if (dev >= 0)
+        cached[dev].store(slots, std::memory_order_relaxed);
+    return slots;
+}
+
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL>
+hipError_t launch_tail(const QuantArgs &a, hipStream_t stream) {
+    const int grid = (int)std::min<long>(a.rows, resident_slots<KMAX, THREADS, GROUPED, WIDE_TAIL>());
+    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL>), dim3(grid), dim3(THREADS), 0,
+                       stream, a);
     return hipGetLastError();
+}
+
+template <int KMAX, int THREADS, bool GROUPED>
+hipError_t launch(const QuantArgs &a, hipStream_t stream) {
+    if (a.pitch8 / 4 > THREADS)                   // more than one tail word per lane
+        return launch_tail<KMAX, THREADS, GROUPED, true>(a, stream);
+    return launch_tail<KMAX, THREADS, GROUPED, false>(a, stream);
 }
 
 // Row-length buckets: (longest row, lanes per workgroup).
