@@ -2,10 +2,14 @@
 
     python -m mixed_precision_integer_amd.build
 
-hipcc cross-compiles without a GPU. Packed-FP32 instructions are disabled
-for the device code (-packed-fp32-ops); hipcc's host pass warns that it does
-not know that target feature, which is harmless. MFMA accumulators are kept
-in architectural VGPRs (-amdgpu-mfma-vgpr-form).
+hipcc cross-compiles without a GPU. Each source is compiled to an object with
+its own flags, then the objects are linked into one shared library.
+Packed-FP32 instructions are disabled for all device code (-packed-fp32-ops);
+hipcc's host pass warns that it does not know that target feature, which is
+harmless. The 64 x 64 and 128 x 128 GEMM keeps MFMA accumulators in
+architectural VGPRs (-amdgpu-mfma-vgpr-form), since its fp32 epilogue reads
+them every scale group; the 256 x 256 GEMM holds 256 accumulator registers per
+lane, which only fit as AGPRs, and is built without that option.
 """
 from __future__ import annotations
 
@@ -14,10 +18,18 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libw4a4.so")
+
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wno-unused-command-line-argument"]
+# per-source extra flags (default: accumulators in architectural VGPRs)
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"gemm_big.hip": []}
 
 
 def hipcc() -> str:
@@ -27,22 +39,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # MFMA accumulators in ordinary VGPRs: the fp32 epilogue reads them
-           # with plain VALU ops instead of v_accvgpr_read copies
-           "-mllvm", "-amdgpu-mfma-vgpr-form",
-           "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"),
-           *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed")
+
+
+def build(verbose: bool = False) -> str:
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    tmp = LIB + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="w4a4_build_") as objdir:
+        objs = []
+        for src in srcs:
+            name = os.path.basename(src)
+            obj = os.path.join(objdir, name + ".o")
+            _run([hipcc(), *COMMON, *EXTRA.get(name, VGPR_FORM), *inc, "-c", src, "-o", obj], verbose)
+            objs.append(obj)
+        _run([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

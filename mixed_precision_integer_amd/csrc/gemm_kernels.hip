@@ -47,27 +47,10 @@
 #include <algorithm>
 
 #include "w4a4.h"
-#include "w4a4_internal.h"
+#include "gemm_common.h"
 
 namespace w4a4 {
 namespace gemm_impl {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int kThreads = 256;
-constexpr int kTileBytes = 64;   // bytes of each row per K-tile
-
-__device__ __forceinline__ uint32_t nib_hi(uint32_t p) { return p & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t nib_lo(uint32_t p) { return (p << 4) & 0xF0F0F0F0u; }
-
-// s_waitcnt immediate with only vmcnt constrained (gfx9 encoding).
-constexpr int vmcnt_only(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// byte offset of 16-byte chunk c of row r inside a tile
-__device__ __forceinline__ int swz(int r, int c) { return (r << 6) | (((c ^ (r >> 1) ^ (r >> 2)) & 3) << 4); }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct Cfg {
@@ -85,21 +68,6 @@ struct Cfg {
     static_assert(DA >= 1 && DB >= 1 && BM * 4 % kThreads == 0 && BN * 4 % kThreads == 0, "loader");
     static_assert(PREFETCH >= 1 && PREFETCH <= 6, "ring depth");
 };
-
-// s_waitcnt vmcnt(n) for a run-time n in [0, 6 * per_tile]: the count must be
-// an immediate, so the few values a ring can leave outstanding are spelled out.
-template <int PER_TILE>
-__device__ __forceinline__ void wait_tiles(int tiles_outstanding) {
-    switch (tiles_outstanding) {
-    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_only(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_only(1 * PER_TILE)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * PER_TILE)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_only(3 * PER_TILE)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_only(4 * PER_TILE)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_only(5 * PER_TILE)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_only(6 * PER_TILE)); break;
-    }
-}
 
 // MFMAs of one K-tile held in LDS stage `st`. FRESH: the tile opens a scale
 // group (its first MFMAs take C = 0). TAIL: an INT8 tail tile (no widening).
@@ -231,17 +199,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     // ---- output tile and K split of this workgroup ------------------------------
     const int S = SPLIT ? a.splits : 1;
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-    const int tiles = tiles_m * tiles_n;
     const int ks = blockIdx.x % S;
-    int tile = blockIdx.x / S;
-    if (S == 1 && tiles % 8 == 0)             // consecutive workgroups alternate XCDs
-        tile = (tile % 8) * (tiles / 8) + tile / 8;
-    constexpr int BAND = 8;
-    const int band = tile / (BAND * tiles_n);
-    const int first_m = band * BAND;
-    const int band_m = min(tiles_m - first_m, BAND);
-    const int in_band = tile - band * BAND * tiles_n;
-    const int tm = first_m + in_band % band_m, tn = in_band / band_m;
+    const int tile = blockIdx.x / S;
+    int tm, tn;
+    tile_coords(tile, tiles_m, tiles_n, S == 1, tm, tn);
     const int row0 = tm * BM, col0 = tn * BN;
 
     const int T8 = (int)(a.pitch8 / kTileBytes);
@@ -264,7 +225,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     for (int j = 0; j < C::DA; ++j) {
         const int q = j * kThreads + tid, r = q >> 2;
         const uint32_t row = min(row0 + r, a.M - 1);
-        const uint32_t off = (((q & 3) ^ (r >> 1) ^ (r >> 2)) & 3) * 16;
+        const uint32_t off = dma_chunk_offset(q);
         a4o[j] = row * (uint32_t)a.pitch4 + off;
         a8o[j] = row * (uint32_t)a.pitch8 + off;
     }
@@ -272,7 +233,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     for (int j = 0; j < C::DB; ++j) {
         const int q = j * kThreads + tid, r = q >> 2;
         const uint32_t row = min(col0 + r, a.N - 1);
-        const uint32_t off = (((q & 3) ^ (r >> 1) ^ (r >> 2)) & 3) * 16;
+        const uint32_t off = dma_chunk_offset(q);
         b4o[j] = row * (uint32_t)a.pitch4 + off;
         b8o[j] = row * (uint32_t)a.pitch8 + off;
     }
@@ -530,8 +491,13 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // Tile shape and K split for a shape. Pure function of the shape, so the
 // workspace query and the launch always agree.
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc) {
-    (void)group;
     GemmPlan p{};
+    if (gemm_big_fits(M, N, K_n, n_out, w4a4_num_groups(K_n, group))) {
+        p.cfg = 2;
+        p.tiles = ((M + 255) / 256) * ((N + 255) / 256);
+        p.splits = 1;
+        return p;
+    }
     const bool small = M <= 64;
     const int bm = small ? CfgSmall::BM : CfgMid::BM, bn = small ? CfgSmall::BN : CfgMid::BN;
     const int per_cu = small ? 4 : 2;                          // resident workgroups per CU (LDS)
@@ -575,6 +541,8 @@ hipError_t launch_gemm(const GemmArgs &a_in, bool export_acc, void *workspace, h
         a.ctr = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.part_offset);
     }
+    if (p.cfg == 2)
+        return launch_gemm_big(a, export_acc, stream);
     if (p.cfg == 0)
         return launch_cfg<CfgSmall>(a, export_acc, stream);
     return launch_cfg<CfgMid>(a, export_acc, stream);

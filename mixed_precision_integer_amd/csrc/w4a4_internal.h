@@ -68,7 +68,7 @@ struct GemmArgs {
 
 // Launch shape of the GEMM for one problem: a pure function of the shape.
 struct GemmPlan {
-    int cfg;                  // tile configuration
+    int cfg;                  // tile configuration: 0 64 x 64, 1 128 x 128, 2 256 x 256
     int tiles;                // output tiles
     int splits;               // K splits per output tile
     size_t part_offset;       // byte offset of the fp32 partial sums (counters first)
@@ -81,5 +81,9 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
 // `workspace` holds plan_gemm(...).workspace_bytes bytes; its counter part
 // must be zero on entry and is zero again when the kernel completes.
 hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipStream_t stream);
+
+// 256 x 256 tile kernel for one scale group per row (gemm_big.hip).
+bool gemm_big_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t G);
+hipError_t launch_gemm_big(const GemmArgs &a, bool export_acc, hipStream_t stream);
 
 }  // namespace w4a4

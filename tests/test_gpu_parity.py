@@ -280,6 +280,23 @@ def test_full_size_workload(oracle, work):
     full_size_check(oracle, X, W, o, work.group)
 
 
+# Per-row-scale shapes with at least 256 tiles of 256 x 256 take the
+# large-tile kernel (accumulators in AGPRs, outlier tail folded in per block).
+BIG_TILE = [
+    # M, N, K, n_out, group
+    (4096, 4096, 1152, 128, 0),     # 256 tiles exactly, two tail tiles
+    (4000, 4100, 1304, 100, 0),     # ragged M, N and K_n (1204 -> 640-byte rows)
+    (4096, 4096, 1024, 0, 0),       # no outlier tail
+    (4096, 4352, 2048, 256, 1792),  # one group spanning the head, four tail tiles
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out,group", BIG_TILE)
+def test_big_tile_parity(oracle, M, N, K, n_out, group):
+    X, W, o = wl.draw(M, N, K, n_out, seed=M + N + K, outlier_factor=40.0)
+    full_size_check(oracle, X, W, o, group, P=6144)
+
+
 def test_decode_sweep(oracle):
     X, W, o = wl.draw_workload(wl.DECODE_65B)
     for M in wl.DECODE_M:
