@@ -19,6 +19,8 @@ __device__ __forceinline__ uint32_t nib_lo(uint32_t p) { return (p << 4) & 0xF0F
 
 // s_waitcnt immediate with only vmcnt constrained (gfx9 encoding).
 constexpr int vmcnt_only(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt immediate with only lgkmcnt constrained.
+constexpr int lgkmcnt_only(int n) { return 0xF | (0x3 << 14) | (0x7 << 4) | ((n & 0xF) << 8); }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
