@@ -42,6 +42,12 @@ constexpr int DA = BM * 4 / kThreads, DB = BN * 4 / kThreads;
 constexpr int D = DA + DB;                               // DMA instructions per tile per lane
 constexpr int MAX_TAIL_TILES = STAGES;
 constexpr int SCALE_BYTES = 4 * BM * 4;                // sa4, sa8, sw4, sw8 of the tile (BM == BN)
+// Per-wave fp16 staging of the interior epilogue: 32 rows x 64 columns, rows
+// padded by 16 bytes so the eight-byte writes of a column of lanes spread
+// over the banks.
+constexpr int STG_PITCH = 64 * 2 + 16;
+constexpr int STG_BYTES = 32 * STG_PITCH;
+constexpr int LDS_BYTES = STAGES * STAGE + SCALE_BYTES + 4 * STG_BYTES;
 
 // Raw packed fragments of one sub-step (64 channels) of a K-tile: lane
 // (li, lh) reads 16 bytes of row li of each 32-row block, chunk 2 s + lh.
@@ -129,102 +135,77 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
-// Epilogue, block by block: the INT8 tail product of the block (its tiles
-// are in the ring), then y = fp16(acc4 * (sa4 * sw4 / 256) + acc8 * (sa8 * sw8)).
-// Column-block outer: the weight side of the tail and the column scales are
-// read once per column block and kept in registers over the row blocks.
-// Lane (li, lh) of block (fm, fn) owns row m = base + li and the columns
-// n0 + 8 q + {0..3}, q = 0..3, with n0 = column base + 4 lh. INTERIOR: the
-// whole tile is inside Y and Y rows are 8-byte aligned, so every lane stores
-// its four columns as one 8-byte store with no guard.
-template <bool EXPORT, bool INTERIOR>
-__device__ __forceinline__ void epilogue(const GemmArgs &a, const v16i (&acc)[FM][FN], const unsigned char *lds,
+// Epilogue of edge tiles and of the accumulator export, block by block
+// (column block outer, so the weight side of the tail is read once per
+// column): the INT4 sums of the block are copied out (and converted to the
+// fp32 partial acc4 * (sa4 * sw4 / 256), or exported), the INT8 tail product
+// is accumulated in place on top of them, always over MAX_TAIL_TILES tiles
+// with the weight operand zeroed past the tail, and recovered as the
+// difference; y = fp16(partial + acc8 * (sa8 * sw8)). Stores are guarded
+// element by element at the ragged edges.
+template <bool EXPORT>
+__device__ __forceinline__ void epilogue(const GemmArgs &a, v16i (&acc)[FM][FN], const unsigned char *lds,
                                          const float *sS, int T4, int T8, int row0, int col0, int wm, int wn,
                                          int li, int lh) {
-    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const bool vec_store = ((reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2)) & 7) == 0;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         const int nl = wn * WTN + fn * 32 + lh * 4;        // tile-local first column of the lane
-        uint4 pb8[MAX_TAIL_TILES][2];
+        v4i pb8[MAX_TAIL_TILES][2];
 #pragma unroll
         for (int j = 0; j < MAX_TAIL_TILES; ++j)
-            if (j < T8)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    pb8[j][s] = *reinterpret_cast<const uint4 *>(lds + ((T4 + j) % STAGES) * STAGE + A_BYTES +
-                                                                 swz(wn * WTN + fn * 32 + li, 2 * s + lh));
-        float4 cs4[4], cs8[4];
-        if constexpr (!EXPORT) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                cs4[q] = *reinterpret_cast<const float4 *>(sS + 2 * BM + nl + q * 8);
-                cs8[q] = T8 > 0 ? *reinterpret_cast<const float4 *>(sS + 3 * BM + nl + q * 8)
-                                : float4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int s = 0; s < 2; ++s) {
+                const uint4 p = *reinterpret_cast<const uint4 *>(lds + ((T4 + j) % STAGES) * STAGE + A_BYTES +
+                                                                swz(wn * WTN + fn * 32 + li, 2 * s + lh));
+                pb8[j][s] = j < T8 ? v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w} : v4i{0, 0, 0, 0};
             }
-        }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int ml = wm * WTM + fm * 32 + li;           // tile-local row of the lane
+            const int ml = wm * WTM + fm * 32 + li;
             const int m = row0 + ml;
-            // The INT4 block is consumed first (converted, or exported), so its
-            // 16 accumulator registers are free for the tail product: the 256
-            // accumulators of the wave fill the whole accumulator file.
-            float y[16];
+            int a4[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                a4[r] = acc[fm][fn][r];
+#pragma unroll
+            for (int j = 0; j < MAX_TAIL_TILES; ++j)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint4 p = *reinterpret_cast<const uint4 *>(lds + ((T4 + j) % STAGES) * STAGE + swz(ml, 2 * s + lh));
+                    const v4i x = {(int)p.x, (int)p.y, (int)p.z, (int)p.w};
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(pb8[j][s], x, acc[fm][fn], 0, 0, 0);
+                }
             if constexpr (EXPORT) {
                 if (m < a.M) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int n = col0 + nl + (r / 4) * 8 + (r % 4);
-                        if (n < a.N)
-                            a.acc4_out[(int64_t)m * a.N + n] = acc[fm][fn][r] >> 8;
+                        if (n < a.N) {
+                            const int64_t e = (int64_t)m * a.N + n;
+                            a.acc4_out[e] = a4[r] >> 8;
+                            if (a.acc8_out)
+                                a.acc8_out[e] = acc[fm][fn][r] - a4[r];
+                        }
                     }
                 }
             } else {
                 const float rs4 = sS[ml] * (1.0f / 256.0f);
+                const float rs8 = T8 > 0 ? sS[BM + ml] : 0.0f;   // tail scales are not loaded when T8 == 0
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float c4[4] = {cs4[q].x, cs4[q].y, cs4[q].z, cs4[q].w};
+                    const float4 c4 = *reinterpret_cast<const float4 *>(sS + 2 * BM + nl + q * 8);
+                    const float4 c8v = *reinterpret_cast<const float4 *>(sS + 3 * BM + nl + q * 8);
+                    const float4 c8 = T8 > 0 ? c8v : float4{0.0f, 0.0f, 0.0f, 0.0f};
+                    const float cs4[4] = {c4.x, c4.y, c4.z, c4.w}, cs8[4] = {c8.x, c8.y, c8.z, c8.w};
+                    float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        y[q * 4 + e] = (float)acc[fm][fn][q * 4 + e] * (rs4 * c4[e]);
-                }
-            }
-            v16i acc8 = zero;
-#pragma unroll
-            for (int j = 0; j < MAX_TAIL_TILES; ++j)
-                if (j < T8)
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const uint4 pa = *reinterpret_cast<const uint4 *>(
-                            lds + ((T4 + j) % STAGES) * STAGE + swz(ml, 2 * s + lh));
-                        const v4i x = {(int)pa.x, (int)pa.y, (int)pa.z, (int)pa.w};
-                        const v4i w = {(int)pb8[j][s].x, (int)pb8[j][s].y, (int)pb8[j][s].z, (int)pb8[j][s].w};
-                        acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(w, x, acc8, 0, 0, 0);
-                    }
-            if constexpr (EXPORT) {
-                if (m < a.M && a.acc8_out) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int n = col0 + nl + (r / 4) * 8 + (r % 4);
-                        if (n < a.N)
-                            a.acc8_out[(int64_t)m * a.N + n] = acc8[r];
-                    }
-                }
-            } else {
-                const float rs8 = T8 > 0 ? sS[BM + ml] : 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float c8[4] = {cs8[q].x, cs8[q].y, cs8[q].z, cs8[q].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        y[q * 4 + e] += (float)acc8[q * 4 + e] * (rs8 * c8[e]);
+                        v[e] = (float)a4[q * 4 + e] * (rs4 * cs4[e]) +
+                               (float)(acc[fm][fn][q * 4 + e] - a4[q * 4 + e]) * (rs8 * cs8[e]);
                     const int n = col0 + nl + q * 8;
                     _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
-                    const float *v = y + q * 4;
-                    if (INTERIOR) {
-                        *reinterpret_cast<uint2 *>(dst) = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
-                    } else if (m < a.M) {
+                    if (m < a.M) {
                         if (vec_store && n + 3 < a.N) {
                             *reinterpret_cast<uint2 *>(dst) = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
                         } else {
@@ -235,6 +216,89 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const v16i (&acc)[FM
                         }
                     }
                 }
+            }
+        }
+    }
+}
+
+// Epilogue of a tile that lies inside Y (rows 16-byte aligned), by halves of
+// 64 columns, row block by row block. For each half of a row block, its two
+// column blocks are finished (fp32 partial from the INT4 sums, the INT8 tail
+// product, accumulated in place on top of the INT4 sums and recovered as
+// the difference, y = fp16(acc4 * (sa4 * sw4 / 256) + acc8 * (sa8 * sw8))) and
+// written to the wave's LDS staging area in the transposed accumulator
+// layout; the 32 x 64 result is then read back row-major and stored with
+// 16-byte stores, eight full 128-byte lines per store instruction. The
+// staging area belongs to one wave, whose LDS operations complete in order,
+// so it needs no barrier.
+__device__ __forceinline__ void epilogue_interior(const GemmArgs &a, v16i (&acc)[FM][FN], unsigned char *lds,
+                                                  const float *sS, int T4, int T8, int row0, int col0, int wm,
+                                                  int wn, int li, int lh, int wave, int lane) {
+    unsigned char *stg = lds + STAGES * STAGE + SCALE_BYTES + wave * STG_BYTES;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        // weight side of the tail for the two column blocks of this half; zero past the tail
+        v4i pb8[2][MAX_TAIL_TILES][2];
+#pragma unroll
+        for (int f2 = 0; f2 < 2; ++f2)
+#pragma unroll
+            for (int j = 0; j < MAX_TAIL_TILES; ++j)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint4 p = *reinterpret_cast<const uint4 *>(lds + ((T4 + j) % STAGES) * STAGE + A_BYTES +
+                                                                    swz(wn * WTN + (2 * h + f2) * 32 + li, 2 * s + lh));
+                    pb8[f2][j][s] = j < T8 ? v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w} : v4i{0, 0, 0, 0};
+                }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int ml = wm * WTM + fm * 32 + li;           // tile-local row of the lane
+            const float rs4 = sS[ml] * (1.0f / 256.0f);
+            const float rs8 = T8 > 0 ? sS[BM + ml] : 0.0f;    // tail scales are not loaded when T8 == 0
+            v4i pa8[MAX_TAIL_TILES][2];
+#pragma unroll
+            for (int j = 0; j < MAX_TAIL_TILES; ++j)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint4 p = *reinterpret_cast<const uint4 *>(lds + ((T4 + j) % STAGES) * STAGE + swz(ml, 2 * s + lh));
+                    pa8[j][s] = v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w};
+                }
+#pragma unroll
+            for (int f2 = 0; f2 < 2; ++f2) {
+                const int fn = 2 * h + f2;
+                const int nl = wn * WTN + fn * 32 + lh * 4;   // tile-local first column of the lane
+                // INT4 sums copied out (exact ints), then the tail product is
+                // accumulated in place on top of them: acc8 = sum - acc4
+                int a4[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    a4[r] = acc[fm][fn][r];
+#pragma unroll
+                for (int j = 0; j < MAX_TAIL_TILES; ++j)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(pb8[f2][j][s], pa8[j][s], acc[fm][fn], 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 c4 = *reinterpret_cast<const float4 *>(sS + 2 * BM + nl + q * 8);
+                    const float4 c8v = *reinterpret_cast<const float4 *>(sS + 3 * BM + nl + q * 8);
+                    const float4 c8 = T8 > 0 ? c8v : float4{0.0f, 0.0f, 0.0f, 0.0f};
+                    const float cs4[4] = {c4.x, c4.y, c4.z, c4.w}, cs8[4] = {c8.x, c8.y, c8.z, c8.w};
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = (float)a4[q * 4 + e] * (rs4 * cs4[e]) +
+                               (float)(acc[fm][fn][q * 4 + e] - a4[q * 4 + e]) * (rs8 * cs8[e]);
+                    *reinterpret_cast<uint2 *>(stg + li * STG_PITCH + (f2 * 32 + q * 8 + lh * 4) * 2) =
+                        uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
+                }
+            }
+            // 32 x 64 staged: lane reads 16 bytes of row 8 i + lane / 8
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = i * 8 + (lane >> 3), c = lane & 7;
+                const uint4 v = *reinterpret_cast<const uint4 *>(stg + r * STG_PITCH + c * 16);
+                _Float16 *dst = a.y + (int64_t)(row0 + wm * WTM + fm * 32 + r) * a.ldy + col0 + wn * WTN + h * 64 + c * 8;
+                *reinterpret_cast<uint4 *>(dst) = v;
             }
         }
     }
@@ -391,16 +455,19 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs &a, unsigned char *
     __builtin_amdgcn_s_barrier();
     compiler_fence();
 
-    epilogue<EXPORT, INTERIOR>(a, acc, lds, sS, T4, T8, row0, col0, wm, wn, li, lh);
+    if constexpr (INTERIOR && !EXPORT)
+        epilogue_interior(a, acc, lds, sS, T4, T8, row0, col0, wm, wn, li, lh, wave, lane);
+    else
+        epilogue<EXPORT>(a, acc, lds, sS, T4, T8, row0, col0, wm, wn, li, lh);
 }
 
 // INTERIOR: every tile lies inside Y (M and N multiples of the tile) and Y
-// rows are 8-byte aligned, so the epilogue stores with no guard. It is a
+// rows are 16-byte aligned, so the epilogue stores with no guard. It is a
 // separate kernel rather than a branch per tile: with both epilogues in one
 // body the accumulator file overflows into scratch.
 template <bool EXPORT, bool INTERIOR>
 __global__ __launch_bounds__(kThreads) void gemm_big_kernel(GemmArgs a) {
-    __shared__ __align__(16) unsigned char lds[STAGES * STAGE + SCALE_BYTES];
+    __shared__ __align__(16) unsigned char lds[LDS_BYTES];
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, true, tm, tn);
@@ -413,13 +480,15 @@ using namespace gemm_big_impl;
 
 bool gemm_big_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t G) {
     const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    return G == 1 && K_n > 0 && w4a4_pitch8_bytes(n_out) / kTileBytes <= MAX_TAIL_TILES && tiles >= 256;
+    // the tail is accumulated on top of the INT4 sums (16384 * (K_n + n_out) must fit int32)
+    return G == 1 && K_n > 0 && w4a4_pitch8_bytes(n_out) / kTileBytes <= MAX_TAIL_TILES && tiles >= 256 &&
+           (int64_t)(K_n + n_out) * 16384 < (int64_t)1 << 31;
 }
 
 hipError_t launch_gemm_big(const GemmArgs &a, bool export_acc, hipStream_t stream) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    const bool interior = a.M % BM == 0 && a.N % BN == 0 && a.ldy % 4 == 0 &&
-                          reinterpret_cast<uintptr_t>(a.y) % 8 == 0;
+    const bool interior = a.M % BM == 0 && a.N % BN == 0 && a.ldy % 8 == 0 &&
+                          reinterpret_cast<uintptr_t>(a.y) % 16 == 0;
     if (export_acc)
         hipLaunchKernelGGL((gemm_big_kernel<true, false>), dim3(tiles), dim3(kThreads), 0, stream, a);
     else if (interior)
