@@ -519,6 +519,11 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
         S = std::max(S, 1);
     }
     p.splits = S;
+    if (S == 1 && !export_acc && gemm_group_fits(M, N, K_n, n_out, group)) {
+        p.cfg = 3;
+        p.tiles = ceil_div(M, 128) * ceil_div(N, 128);
+        return p;
+    }
     if (S > 1) {
         // The counters sit at a fixed place, first in the workspace, sized for
         // the most tiles that are ever split: partial sums of one shape then
@@ -543,6 +548,8 @@ hipError_t launch_gemm(const GemmArgs &a_in, bool export_acc, void *workspace, h
     }
     if (p.cfg == 2)
         return launch_gemm_big(a, export_acc, stream);
+    if (p.cfg == 3)
+        return launch_gemm_group(a, stream);
     if (p.cfg == 0)
         return launch_cfg<CfgSmall>(a, export_acc, stream);
     return launch_cfg<CfgMid>(a, export_acc, stream);

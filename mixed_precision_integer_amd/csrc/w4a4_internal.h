@@ -26,6 +26,19 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t 
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(sl)
                  : "memory", "m0");
 }
+// 4 bytes per lane from base + voff (base wave-uniform).
+__device__ __forceinline__ void dma4s(const void *base, uint32_t voff, uint32_t lds) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sb), "s"(sl)
+                 : "memory", "m0");
+}
+// The compiler waits for outstanding vector memory operations before it
+// rewrites a register that one of these asm statements read, so the offset
+// and address operands passed to them should stay in registers that are not
+// recomputed inside a pipelined loop.
 // 4 bytes per lane from a per-lane address
 __device__ __forceinline__ void dma4(const void *p, uint32_t lds) {
     const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
@@ -68,7 +81,8 @@ struct GemmArgs {
 
 // Launch shape of the GEMM for one problem: a pure function of the shape.
 struct GemmPlan {
-    int cfg;                  // tile configuration: 0 64 x 64, 1 128 x 128, 2 256 x 256
+    int cfg;                  // tile configuration: 0 64 x 64, 1 128 x 128, 2 256 x 256,
+                              // 3 128 x 128 for 128-channel scale groups
     int tiles;                // output tiles
     int splits;               // K splits per output tile
     size_t part_offset;       // byte offset of the fp32 partial sums (counters first)
@@ -81,6 +95,10 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
 // `workspace` holds plan_gemm(...).workspace_bytes bytes; its counter part
 // must be zero on entry and is zero again when the kernel completes.
 hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipStream_t stream);
+
+// 128 x 128 tile kernel for 128-channel scale groups (gemm_group.hip).
+bool gemm_group_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
+hipError_t launch_gemm_group(const GemmArgs &a, hipStream_t stream);
 
 // 256 x 256 tile kernel for one scale group per row (gemm_big.hip).
 bool gemm_big_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t G);

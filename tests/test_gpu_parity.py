@@ -297,6 +297,26 @@ def test_big_tile_parity(oracle, M, N, K, n_out, group):
     full_size_check(oracle, X, W, o, group, P=6144)
 
 
+# Shapes with 128-channel scale groups and more than 256 output tiles of
+# 128 x 128 take the group-tile kernel (scale products on the matrix core,
+# fp32 fold per group, the outlier tail as the first group).
+GROUP_TILE = [
+    # M, N, K, n_out, group
+    (2048, 2100, 1280, 128, 128),   # ragged N, two tail tiles
+    (2050, 2048, 1152, 0, 128),     # ragged M, no outlier tail
+    (2176, 2112, 1344, 64, 128),    # one tail tile
+    (2100, 2060, 1384, 104, 128),   # ragged M and N, tail of 104 padded to 128
+    (2048, 2048, 4352, 256, 128),   # 32 groups, four tail tiles
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out,group", GROUP_TILE)
+def test_group_tile_parity(oracle, M, N, K, n_out, group):
+    assert w4.outlier_gemm_workspace_bytes(M, N, K, n_out, group) == 0, "shape splits K"
+    X, W, o = wl.draw(M, N, K, n_out, seed=M + 3 * N + K, outlier_factor=30.0)
+    full_size_check(oracle, X, W, o, group, P=6144)
+
+
 def test_decode_sweep(oracle):
     X, W, o = wl.draw_workload(wl.DECODE_65B)
     for M in wl.DECODE_M:
