@@ -1,0 +1,237 @@
+// GEMM for decode batches (M <= 32 tokens): the weights are streamed once
+// from HBM.
+//
+// Method: Atom summary page (Summary paragraph 2: INT4 main part with group
+// quantization plus an 8-bit outlier part over reordered channels; Key points
+// item 5: symmetric scales factor out of the integer sums) and the QUIK
+// abstract (one-token decode is memory-bound).
+//
+// CDNA4 design (HBM-bound: every weight byte is read once)
+// * A workgroup owns 32 output columns and all M <= 32 token rows: one
+//   32 x 32 block of v_mfma_i32_32x32x32_i8 with the weight fragment as the
+//   first operand (lane (li, lh) holds token row li and the columns
+//   8 (r / 4) + 4 lh + r % 4). Token rows past M repeat row M - 1; their
+//   results are dropped.
+// * Its eight waves split the INT4 K-tiles (64 bytes of every row, 128
+//   channels) into contiguous ranges. Each wave moves pairs of tiles (128
+//   bytes of each of the 32 weight rows and 32 token rows) into a two-slot
+//   LDS ring of its own by direct global->LDS DMA, eight lanes per row, so
+//   each DMA instruction covers eight whole cache lines; it reads them back
+//   in MFMA layout (16-byte chunks XOR-swizzled by row, conflict-free).
+// * Each INT4 tile is folded at once: y += float(acc) * (sa * sw / 256) with
+//   the scale products from one v_mfma_f32_32x32x2_f32 (an outer product of
+//   the column and the row scales in the accumulator layout); this holds for
+//   any group size that is a multiple of 128 (a tile lies inside one group).
+//   A wave's scales are loaded before its first DMA. The INT8 tail is read
+//   directly, accumulated over its tiles and folded once.
+// * The eight partial blocks are added through LDS in wave order (the same
+//   order in every call), then written as fp16.
+#include <algorithm>
+
+#include "w4a4.h"
+#include "gemm_common.h"
+
+namespace w4a4 {
+namespace gemm_decode_impl {
+
+using namespace gemm_impl;
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int WAVES = 8, THREADS = WAVES * 64;
+constexpr int BN = 32;                    // output columns per workgroup
+constexpr int MAXM = 32;                  // token rows
+constexpr int MAXT = 16;                  // INT4 tiles per wave (K_n <= 16384)
+constexpr int PAIR = 128;                 // bytes of a row in a pair of tiles
+constexpr int SLOT = 2 * 32 * PAIR;       // 32 weight rows, then 32 token rows
+constexpr int WAVE_LDS = 2 * SLOT;        // two slots per wave
+constexpr int RED_BYTES = WAVES * 16 * 64 * 4;
+static_assert(WAVES * WAVE_LDS >= RED_BYTES, "the reduction reuses the ring");
+
+__device__ __forceinline__ v4i as_v4i(uint4 p) { return v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w}; }
+
+// 16-byte chunk c of row r of a pair slot sits at chunk position c ^ (r & 7)
+__device__ __forceinline__ int pair_off(int r, int c) { return r * PAIR + ((c ^ (r & 7)) << 4); }
+
+__global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
+    __shared__ __align__(16) unsigned char lds[WAVES * WAVE_LDS];
+
+    const int tid = threadIdx.x;
+    // the wave index is uniform, so the tile schedule is scalar code
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lh = lane >> 5;
+
+    const int n0 = blockIdx.x * BN;
+    const int T4 = (int)(a.pitch4 / kTileBytes), T8 = (int)(a.pitch8 / kTileBytes);
+    const int tiles_per_group = a.group > 0 ? a.group / 128 : max(T4, 1);
+    const int per = (T4 + WAVES - 1) / WAVES;                 // <= MAXT (checked at launch)
+    const int tb = min(wave * per, T4), te = min(tb + per, T4);
+    const int nt = te - tb, np = (nt + 1) / 2;                // tiles and pairs of this wave
+
+    // ---- scales of this wave's tiles, before any DMA (the DMA is tracked by
+    // hand; nothing else may be outstanding when its waits run)
+    const int64_t nrow = min(n0 + li, a.N - 1), mrow = min(li, a.M - 1);
+    float sw[MAXT], sa[MAXT];
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k) {
+        const int g = min(tb + k, T4 - 1) / tiles_per_group;
+        sw[k] = a.sw4[nrow * a.G + g] * (1.0f / 256.0f);
+        sa[k] = a.sa4[mrow * a.G + g];
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+
+    // ---- DMA of a pair of tiles: instruction i covers rows 8 i .. 8 i + 7, lane
+    // q row 8 i + q / 8 and stored chunk q % 8 (logical chunk (q % 8) ^ (row & 7));
+    // chunks 4..7 are the second tile, or the first again past the last tile
+    uint32_t ow[4], ox[4], owd[4], oxd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        const int64_t wr = min(n0 + r, a.N - 1), xr = min(r, a.M - 1);
+        ow[i] = (uint32_t)(wr * a.pitch4) + 16 * c;
+        ox[i] = (uint32_t)(xr * a.pitch4) + 16 * c;
+        owd[i] = (uint32_t)(wr * a.pitch4) + 16 * (c & 3);
+        oxd[i] = (uint32_t)(xr * a.pitch4) + 16 * (c & 3);
+    }
+    unsigned char *wl = lds + wave * WAVE_LDS;
+    auto issue = [&](int j) {                                 // pair j into slot j % 2
+        const int t0 = tb + 2 * j;
+        const bool dup = t0 + 1 >= te;                        // odd last pair: no second tile
+        const uint32_t st = lds_addr(wl + (j & 1) * SLOT);
+        const uint8_t *W = a.w4 + t0 * kTileBytes, *X = a.a4 + t0 * kTileBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16(W, dup ? owd[i] : ow[i], st + i * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16(X, dup ? oxd[i] : ox[i], st + 32 * PAIR + i * 1024);
+    };
+
+    v16f y = {};
+    const v16f zf = {};
+    const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    // tile h of the pair in slot `sl`, k-th tile of the wave
+    auto tile = [&](const unsigned char *sl, int h, int k) {
+        v16i acc;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int c = 4 * h + 2 * s + lh;
+            const uint4 pw = *reinterpret_cast<const uint4 *>(sl + pair_off(li, c));
+            const uint4 px = *reinterpret_cast<const uint4 *>(sl + 32 * PAIR + pair_off(li, c));
+            const v4i w0 = {(int)nib_lo(pw.x), (int)nib_hi(pw.x), (int)nib_lo(pw.y), (int)nib_hi(pw.y)};
+            const v4i w1 = {(int)nib_lo(pw.z), (int)nib_hi(pw.z), (int)nib_lo(pw.w), (int)nib_hi(pw.w)};
+            const v4i x0 = {(int)nib_lo(px.x), (int)nib_hi(px.x), (int)nib_lo(px.y), (int)nib_hi(px.y)};
+            const v4i x1 = {(int)nib_lo(px.z), (int)nib_hi(px.z), (int)nib_lo(px.w), (int)nib_hi(px.w)};
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0, x0, s == 0 ? zi : acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1, x1, acc, 0, 0, 0);
+        }
+        // scale products S[n][m] = sw[n] * sa[m] / 256 (the k = 1 lanes give zero)
+        const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw[k], lh ? 0.0f : sa[k], zf, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            y[e] = __builtin_fmaf((float)acc[e], S[e], y[e]);
+    };
+
+    // ---- INT4 tiles: two pairs in flight; the loop is unrolled (the scales of
+    // tile k sit in registers sw[k], sa[k])
+    if (np > 0)
+        issue(0);
+    if (np > 1)
+        issue(1);
+#pragma unroll
+    for (int j = 0; j < MAXT / 2; ++j) {
+        if (j < np) {
+            compiler_fence();
+            if (j + 1 < np)
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(8));    // pair j + 1 may stay in flight
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            compiler_fence();
+            const unsigned char *sl = wl + (j & 1) * SLOT;
+            tile(sl, 0, 2 * j);
+            if (2 * j + 1 < nt)
+                tile(sl, 1, 2 * j + 1);
+            compiler_fence();
+            __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));       // this slot's reads are back
+            compiler_fence();
+            if (j + 2 < np)
+                issue(j + 2);
+        }
+    }
+
+    // ---- INT8 tail: wave w takes tail tiles w, w + 8, ... (folded once) ------------------
+    if (T8 > wave) {
+        const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
+        const uint8_t *x8row = reinterpret_cast<const uint8_t *>(a.a8) + mrow * a.pitch8 + 16 * lh;
+        v16i acc8 = zi;
+        for (int t = wave; t < T8; t += WAVES) {
+            const uint4 w0 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes);
+            const uint4 w1 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes + 32);
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(x8row + t * kTileBytes);
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(x8row + t * kTileBytes + 32);
+            acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w0), as_v4i(x0), acc8, 0, 0, 0);
+            acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w1), as_v4i(x1), acc8, 0, 0, 0);
+        }
+        const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : a.sw8[nrow], lh ? 0.0f : a.sa8[mrow], zf,
+                                                             0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            y[e] = __builtin_fmaf((float)acc8[e], S[e], y[e]);
+    }
+
+    // ---- the eight partial blocks, added in wave order (in the ring's LDS, once
+    // every wave is done with its ring) ------------------------------------------------
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);              // [wave][register][lane]
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        red[(wave * 16 + e) * 64 + lane] = y[e];
+    __syncthreads();
+    // thread tid: lane tid % 64, registers 2 (tid / 64) and 2 (tid / 64) + 1
+    // (two consecutive columns of one token row)
+    {
+        const int l = tid & 63, e0 = 2 * (tid >> 6);
+        float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            v0 += red[(w * 16 + e0) * 64 + l];
+            v1 += red[(w * 16 + e0 + 1) * 64 + l];
+        }
+        const int m = l & 31;
+        const int n = n0 + 8 * (e0 / 4) + 4 * (l >> 5) + (e0 % 4);
+        if (m < a.M) {
+            _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
+            const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+            if (n + 1 < a.N && ((reinterpret_cast<uintptr_t>(dst) & 3) == 0)) {
+                *reinterpret_cast<uint32_t *>(dst) =
+                    (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            } else {
+                if (n < a.N)
+                    dst[0] = h0;
+                if (n + 1 < a.N)
+                    dst[1] = h1;
+            }
+        }
+    }
+}
+
+}  // namespace gemm_decode_impl
+
+using namespace gemm_decode_impl;
+
+bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
+    (void)N;
+    (void)n_out;
+    const int T4 = (K_n + 127) / 128;
+    return M >= 1 && M <= MAXM && K_n >= 128 && (group == 0 || group % 128 == 0) &&
+           (T4 + WAVES - 1) / WAVES <= MAXT;
+}
+
+hipError_t launch_gemm_decode(const GemmArgs &a, hipStream_t stream) {
+    const int blocks = (a.N + BN - 1) / BN;
+    hipLaunchKernelGGL(gemm_decode_kernel, dim3(blocks), dim3(THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace w4a4

@@ -492,6 +492,12 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // workspace query and the launch always agree.
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc) {
     GemmPlan p{};
+    if (!export_acc && gemm_decode_fits(M, N, K_n, n_out, group)) {
+        p.cfg = 4;
+        p.tiles = ceil_div(N, 32);
+        p.splits = 1;
+        return p;
+    }
     if (gemm_big_fits(M, N, K_n, n_out, w4a4_num_groups(K_n, group))) {
         p.cfg = 2;
         p.tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -550,6 +556,8 @@ hipError_t launch_gemm(const GemmArgs &a_in, bool export_acc, void *workspace, h
         return launch_gemm_big(a, export_acc, stream);
     if (p.cfg == 3)
         return launch_gemm_group(a, stream);
+    if (p.cfg == 4)
+        return launch_gemm_decode(a, stream);
     if (p.cfg == 0)
         return launch_cfg<CfgSmall>(a, export_acc, stream);
     return launch_cfg<CfgMid>(a, export_acc, stream);
