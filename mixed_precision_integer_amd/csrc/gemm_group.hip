@@ -15,17 +15,9 @@
 //   y += float(acc) * (sa[m, t] * sw[n, t] / 256).
 // * The per-element scale products come from the matrix core: one
 //   v_mfma_f32_32x32x1_2b_f32 forms the outer products of two (row scales,
-//   column scales) vector pairs as two 32 x 32 blocks, fp32 products in the
-//   accumulator layout of the i8 MFMAs. Two of them cover a wave's four blocks.
-// * No int -> float conversion: each INT4 group's MFMA chain starts from the
-//   bit pattern of fp32 1/(2 pi) (an inline constant, c0) instead of zero.
-//   Every group sum lies in [-7 * 8 * 128, 8 * 8 * 128] x 256 = [-1835008,
-//   2^21], well inside c0's binade [1/8, 1/4) (mantissa offset 2291075), so the
-//   biased int32 read as fp32 is exactly c0 + acc * 2^-26. Two more outer-product
-//   MFMAs subtract c0 * S from the running fp32 result (C operand = result), and
-//   the fold is one FMA per element: y = F * S + (y - c0 * S). The subtraction
-//   rounds at the magnitude of c0 * S, a few hundred times a group's own term:
-//   about 17 significant bits survive, against 11 in the fp16 output.
+//   column scales) vector pairs as two 32 x 32 blocks, exact fp32 products in
+//   the accumulator layout of the i8 MFMAs. Two of them cover a wave's four
+//   blocks, so the dequantization costs a conversion and an FMA per element.
 // * The weight fragment is the i8 MFMA's first operand: lane (li, lh) of
 //   block (fm, fn) holds output row li and the columns 8 (r / 4) + 4 lh + r % 4,
 //   so the fp16 result leaves as 8-byte stores of four consecutive columns.
@@ -45,10 +37,7 @@ namespace gemm_group_impl {
 
 using namespace gemm_impl;
 
-typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
-
-constexpr int kBiasBits = 0x3E22F983;               // fp32 1/(2 pi): an inline constant of the ISA
 
 constexpr int BM = 128, BN = 128, WT = 64, F = 2;    // tile, wave tile, 32 x 32 blocks per wave side
 constexpr int STAGES = 4, PREFETCH = 3;                // ring tiles in flight ahead of the one in use
@@ -59,47 +48,24 @@ constexpr int D = DA + DB + 1;                         // DMA instructions per t
 static_assert(DA == 2 && DB == 2, "two 16-byte DMA rounds per operand");
 static_assert(BM + BN == kThreads, "one scale per lane per tile");
 
-// The four i8 MFMAs of one 32-channel k-step over the wave's 2 x 2 blocks;
-// an INT4 group's first k-step starts from the bias c0 (see the header). The
-// bias block is rebuilt from an opaque scalar at every use: hoisted out of
-// the K loop it would hold 16 VGPRs for the whole loop.
+// The four i8 MFMAs of one 32-channel k-step over the wave's 2 x 2 blocks.
 __device__ __forceinline__ void mma_k(v16i (&acc)[F][F], const v4i (&x)[F], const v4i (&w)[F], bool fresh) {
-    int b = kBiasBits;
-    if (fresh)
-        asm volatile("" : "+s"(b));
-    const v16i bias = {b, b, b, b, b, b, b, b, b, b, b, b, b, b, b, b};
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int fm = 0; fm < F; ++fm)
 #pragma unroll
         for (int fn = 0; fn < F; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[fn], x[fm], fresh ? bias : acc[fm][fn], 0, 0, 0);
+            acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[fn], x[fm], fresh ? zero : acc[fm][fn], 0, 0, 0);
 }
 
-// The fp32 results live as two 2-block MFMA accumulators: Y[0] holds blocks
-// (0, 0) | (1, 1) and Y[1] blocks (0, 1) | (1, 0), i.e. block (fm, fn) is
-// registers 16 fm .. 16 fm + 15 of Y[fm ^ fn].
-//
-// Y[C] = float(acc) * S for the INT8 tail group (plain int32 sums, first group).
+// y += float(acc) * S for two of the wave's blocks: S holds the scale
+// products of block (0, c) in registers 0-15 and of block (1, 1 - c) in 16-31.
 template <int C>
-__device__ __forceinline__ void fold_plain(v32f (&Y)[2], const v16i (&acc)[F][F], const v32f &S) {
+__device__ __forceinline__ void fold_half(float (&y)[F][F][16], const v16i (&acc)[F][F], const v32f &S) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        Y[C][r] = (float)acc[0][C][r] * S[r];
-        Y[C][16 + r] = (float)acc[1][1 - C][r] * S[16 + r];
-    }
-}
-
-// Y[C] = F * S + D for a biased INT4 group, D = Y[C] - c0 * S already formed
-// on the matrix core.
-// (The whole accumulator vector is reinterpreted: clang lowers a bit_cast of
-// one ext-vector element as a read of element 0.)
-template <int C>
-__device__ __forceinline__ void fold_biased(v32f (&Y)[2], const v16i (&acc)[F][F], const v32f &S) {
-    const v16f f0 = __builtin_bit_cast(v16f, acc[0][C]), f1 = __builtin_bit_cast(v16f, acc[1][1 - C]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        Y[C][r] = __builtin_fmaf(f0[r], S[r], Y[C][r]);
-        Y[C][16 + r] = __builtin_fmaf(f1[r], S[16 + r], Y[C][16 + r]);
+        y[0][C][r] = __builtin_fmaf((float)acc[0][C][r], S[r], y[0][C][r]);
+        y[1][1 - C][r] = __builtin_fmaf((float)acc[1][1 - C][r], S[16 + r], y[1][1 - C][r]);
     }
 }
 
@@ -172,7 +138,14 @@ void gemm_group_kernel(GemmArgs a) {
         }
     };
 
-    v32f Y[2] = {};
+    float y[F][F][16];
+#pragma unroll
+    for (int fm = 0; fm < F; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                y[fm][fn][r] = 0.0f;
     v16i acc[F][F];
 
     // The same for ring tiles that are never tail tiles (the INT4 loop).
@@ -222,16 +195,17 @@ void gemm_group_kernel(GemmArgs a) {
         compiler_fence();
         read_tile(tt + 1);
     };
-    // The scale products rs x (ca | cb) on the matrix core: blocks (0,0) |
-    // (1,1) from the column scales ca, then (0,1) | (1,0) from cb (one
-    // 32-register product live at a time).
-    auto fold_tail = [&](float r_scale, float c_a, float c_b) {
+    // y += float(acc) * (rs * unit) x (ca | cb): the scale products on the
+    // matrix core, blocks (0,0) | (1,1) from the column scales ca, then
+    // (0,1) | (1,0) from cb (one 32-register product live at a time)
+    auto fold_group = [&](float r_scale, float c_a, float c_b) {
         const v32f z = {};
         const v32f S1 = __builtin_amdgcn_mfma_f32_32x32x1f32(c_a, r_scale, z, 0, 0, 0);
-        fold_plain<0>(Y, acc, S1);
+        fold_half<0>(y, acc, S1);
         const v32f S2 = __builtin_amdgcn_mfma_f32_32x32x1f32(c_b, r_scale, z, 0, 0, 0);
-        fold_plain<1>(Y, acc, S2);
+        fold_half<1>(y, acc, S2);
     };
+
 #pragma unroll
     for (int p = 0; p <= PREFETCH; ++p)
         issue(p);
@@ -267,20 +241,8 @@ void gemm_group_kernel(GemmArgs a) {
         const float r0 = rs, a0 = ca, b0 = cb;
         next_tile(tt, false);
         if (tt == T8 - 1)
-            fold_tail(r0, a0, b0);
+            fold_group(r0, a0, b0);
     }
-
-    // r_scale = rs * 2^18: acc / 256 = (F - c0) * 2^18
-    auto fold_group = [&](float r_scale, float c_a, float c_b) {
-        const float nr = -__builtin_bit_cast(float, kBiasBits) * r_scale;
-        const v32f z = {};
-        const v32f S1 = __builtin_amdgcn_mfma_f32_32x32x1f32(c_a, r_scale, z, 0, 0, 0);
-        Y[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(c_a, nr, Y[0], 0, 0, 0);
-        fold_biased<0>(Y, acc, S1);
-        const v32f S2 = __builtin_amdgcn_mfma_f32_32x32x1f32(c_b, r_scale, z, 0, 0, 0);
-        Y[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(c_b, nr, Y[1], 0, 0, 0);
-        fold_biased<1>(Y, acc, S2);
-    };
 
     // ---- INT4 tiles, one 128-channel group each ------------------------------------
     // The MFMAs of tile t run from registers; then the next tile's barrier,
@@ -303,7 +265,7 @@ void gemm_group_kernel(GemmArgs a) {
             mma_k(acc, x[0], w[0], s == 0);
             mma_k(acc, x[1], w[1], false);
         }
-        const float r0 = rs * 262144.0f, a0 = ca, b0 = cb;
+        const float r0 = rs * (1.0f / 256.0f), a0 = ca, b0 = cb;
         next_tile(tt, true);
         fold_group(r0, a0, b0);
     }
@@ -327,8 +289,7 @@ void gemm_group_kernel(GemmArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = col0 + ewn * WT + fn * 32 + q * 8 + elh * 4;
-                const float v[4] = {Y[fm ^ fn][fm * 16 + q * 4], Y[fm ^ fn][fm * 16 + q * 4 + 1],
-                                    Y[fm ^ fn][fm * 16 + q * 4 + 2], Y[fm ^ fn][fm * 16 + q * 4 + 3]};
+                const float *v = &y[fm][fn][q * 4];
                 _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
                 if (vec && n + 3 < a.N) {
                     const _Float16 h0 = (_Float16)v[0], h1 = (_Float16)v[1], h2 = (_Float16)v[2], h3 = (_Float16)v[3];
