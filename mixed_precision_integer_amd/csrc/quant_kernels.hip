@@ -347,6 +347,181 @@ void quant_rows_kernel(QuantArgs a) {
     }
 }
 
+// Group scales (group of 128, 256, 512 or 64 * 8 * UPL channels, dividing a
+// chunk): waves are independent
+// workers, with no LDS and no barrier. The reordered head of a row is cut
+// into chunks of 64 * UPL units (8 channels, one packed dword each); worker
+// wave w quantizes chunk w % (NC + 1) (chunk NC: the outlier tail and the
+// row's pitch padding) of row w / (NC + 1). It loads its permutation entries,
+// then gathers the fp16 sources straight from global memory (a near-identity
+// permutation reads whole cache lines, served from L1 after the first of the
+// eight loads). An aligned
+// segment of group / 8 lanes (one unit index i) is one group, so the group
+// absmax is a few xor-shuffles. Codes and scales: the same arithmetic as the
+// row kernel above (exact quotient, rint, offset nibbles).
+template <int UPL, int TW>
+__global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
+    const int lane = threadIdx.x & 63;
+    const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+    const int c = gw % (NC + 1), row = gw / (NC + 1);
+    if (row >= a.rows)
+        return;
+    const int K = a.K, K_n = a.K_n, G = a.G;
+    const int U = (K_n + 7) / 8;
+    const int W4 = (int)(a.pitch4 / 4), W8 = (int)(a.pitch8 / 4);
+    const int seg = a.group / 8;                   // units per group: 16, 32, 64 or 64 UPL
+    // entries are clamped into [0, K) once here, so that even a malformed
+    // permutation (undefined behaviour by contract) reads inside the row
+    auto pack = [K](int lo, int hi) {
+        lo = min(max(lo, 0), K - 1);
+        hi = min(max(hi, 0), K - 1);
+        return (uint32_t)lo | ((uint32_t)hi << 16);
+    };
+
+    if (c < NC) {
+        // ---- head chunk: units u = c * 64 UPL + 64 i + lane
+        uint32_t pv[UPL][4];
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) {
+            const int u = c * 64 * UPL + 64 * i + lane, j0 = 8 * u;
+            if (j0 + 8 <= K_n) {
+                const int4 e0 = *reinterpret_cast<const int4 *>(a.perm + j0);
+                const int4 e1 = *reinterpret_cast<const int4 *>(a.perm + j0 + 4);
+                pv[i][0] = pack(e0.x, e0.y);
+                pv[i][1] = pack(e0.z, e0.w);
+                pv[i][2] = pack(e1.x, e1.y);
+                pv[i][3] = pack(e1.z, e1.w);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    pv[i][k] = pack(j0 + 2 * k < K_n ? a.perm[j0 + 2 * k] : 0,
+                                    j0 + 2 * k + 1 < K_n ? a.perm[j0 + 2 * k + 1] : 0);
+            }
+        }
+        uint32_t v[UPL][4];
+        {
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src + (int64_t)row * a.ld);
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) {
+                const int j0 = 8 * (c * 64 * UPL + 64 * i + lane);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t lo = j0 + 2 * k < K_n ? src[pv[i][k] & 0xFFFF] : 0u;
+                    const uint32_t hi = j0 + 2 * k + 1 < K_n ? src[pv[i][k] >> 16] : 0u;
+                    v[i][k] = lo | (hi << 16);
+                }
+            }
+        }
+        {
+            uint32_t *q4row = reinterpret_cast<uint32_t *>(a.q4 + (int64_t)row * a.pitch4);
+            // group absmax: over seg lanes of one unit index, and over all
+            // of the chunk's units when a group is the whole chunk
+            float gm[UPL];
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) {
+                half2 m2 = {(_Float16)0, (_Float16)0};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2, v[i][k] & 0x7FFF7FFFu));
+                float m = fmaxf((float)m2.x, (float)m2.y);
+                for (int off = 1; off < seg && off < 64; off <<= 1)
+                    m = fmaxf(m, __shfl_xor(m, off, 64));
+                gm[i] = m;
+            }
+            if (seg > 64) {
+                float m = gm[0];
+#pragma unroll
+                for (int i = 1; i < UPL; ++i)
+                    m = fmaxf(m, gm[i]);
+#pragma unroll
+                for (int i = 0; i < UPL; ++i)
+                    gm[i] = m;
+            }
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) {
+                const int u = c * 64 * UPL + 64 * i + lane;
+                const float sc = gm[i] / 7.0f, rc = recip_or_zero(sc);
+                if (u < U) {
+                    if ((u & (seg - 1)) == 0)             // the group's first unit stores its scale
+                        a.s4[(int64_t)row * G + (8 * u) / a.group] = sc;
+                    uint32_t ev = 0, od = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float c0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), sc, rc)) + 8.0f;
+                        const float c1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), sc, rc)) + 8.0f;
+                        ev = __builtin_amdgcn_cvt_pk_u8_f32(c0, k, ev);
+                        od = __builtin_amdgcn_cvt_pk_u8_f32(c1, k, od);
+                    }
+                    q4row[u] = (ev | (od << 4)) ^ 0x88888888u;
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- the outlier tail (per-row INT8 scale) and the pitch padding of q4
+    uint32_t pt[TW][2];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const int j0 = K_n + 4 * (64 * i + lane);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            pt[i][k] = pack(j0 + 2 * k < K ? a.perm[j0 + 2 * k] : 0, j0 + 2 * k + 1 < K ? a.perm[j0 + 2 * k + 1] : 0);
+    }
+    uint32_t tv[TW][2];
+    {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src + (int64_t)row * a.ld);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int j0 = K_n + 4 * (64 * i + lane);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t lo = j0 + 2 * k < K ? src[pt[i][k] & 0xFFFF] : 0u;
+                const uint32_t hi = j0 + 2 * k + 1 < K ? src[pt[i][k] >> 16] : 0u;
+                tv[i][k] = lo | (hi << 16);
+            }
+        }
+    }
+    {
+        float tmax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const half2 h = __builtin_bit_cast(half2, tv[i][k] & 0x7FFF7FFFu);
+                tmax = fmaxf(tmax, fmaxf((float)h.x, (float)h.y));
+            }
+        tmax = wave_max(tmax);
+        const float s8 = tmax / 127.0f, r8 = recip_or_zero(s8);
+        if (lane == 0 && a.s8)
+            a.s8[row] = a.n_out > 0 ? s8 : 0.0f;
+        if (a.q8) {
+            uint32_t *q8row = reinterpret_cast<uint32_t *>(a.q8 + (int64_t)row * a.pitch8);
+#pragma unroll
+            for (int i = 0; i < TW; ++i) {
+                const int w = 64 * i + lane;
+                if (w < W8) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int j = K_n + 4 * w + k;
+                        if (j < K) {
+                            const uint32_t h = (k & 1) ? (tv[i][k >> 1] >> 16) : (tv[i][k >> 1] & 0xFFFF);
+                            const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+                            const int q = (int)__builtin_rintf(exact_quotient(x, s8, r8));
+                            word |= (uint32_t)(q & 0xFF) << (8 * k);
+                        }
+                    }
+                    q8row[w] = word;
+                }
+            }
+        }
+        uint32_t *q4row = reinterpret_cast<uint32_t *>(a.q4 + (int64_t)row * a.pitch4);
+        for (int u = U + lane; u < W4; u += 64)      // zero padding of the row pitch
+            q4row[u] = 0u;
+    }
+}
+
 // Resident workgroups of one instantiation on the current device, queried on
 // first use (a launch then costs no runtime queries).
 template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL>
@@ -397,6 +572,23 @@ hipError_t launch_grouping(const QuantArgs &a, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+// The group kernel serves short batches (decode): one worker wave per
+// (row, chunk), so a row's chunks are quantized side by side. Longer batches
+// keep the row kernel, which measured faster there (its row DMA keeps more
+// bytes in flight per instruction than eight 2-byte gathers).
+constexpr int kGroupUPL = 2;
+constexpr int kGroupMaxRows = 64;
+
+template <int TW>
+hipError_t launch_group(const QuantArgs &a, hipStream_t stream) {
+    const int U = (a.K_n + 7) / 8;
+    const int NC = (U + 64 * kGroupUPL - 1) / (64 * kGroupUPL);
+    const long waves = (long)(NC + 1) * a.rows;
+    const int grid = (int)((waves + 3) / 4);
+    hipLaunchKernelGGL((quant_group_kernel<kGroupUPL, TW>), dim3(grid), dim3(256), 0, stream, a, NC);
+    return hipGetLastError();
+}
+
 }  // namespace quant_impl
 
 int quant_rows_max_k() { return 24576; }
@@ -404,6 +596,13 @@ int quant_rows_max_k() { return 24576; }
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream) {
     if (a.rows == 0)
         return hipSuccess;
+    if (a.rows <= quant_impl::kGroupMaxRows &&
+        (a.group == 128 || a.group == 256 || a.group == 512 || a.group == 64 * 8 * quant_impl::kGroupUPL)) {
+        const int tw = (int)((a.pitch8 / 4 + 63) / 64);
+        if (tw <= 1) return quant_impl::launch_group<1>(a, stream);
+        if (tw <= 2) return quant_impl::launch_group<2>(a, stream);
+        if (tw <= 4) return quant_impl::launch_group<4>(a, stream);
+    }
     return a.group > 0 ? quant_impl::launch_grouping<true>(a, stream)
                        : quant_impl::launch_grouping<false>(a, stream);
 }

@@ -301,6 +301,37 @@ def test_full_size_workload(oracle, work):
     full_size_check(oracle, X, W, o, work.group)
 
 
+# The activation producer on its own (codes, scales and padding bit-exact
+# against the oracle). Batches of up to 64 rows with group sizes of 128 to
+# 1024 channels take the wave-worker kernel (head chunks of 1024 channels, one
+# wave for the outlier tail); longer batches, other group sizes, per-row
+# scales and tails over 1024 channels take the row kernel.
+PRODUCER = [
+    # rows, K, n_out, group
+    (1, 8192, 128, 128),        # one decode row over eight head chunks
+    (5, 2176, 128, 256),        # 256-channel groups: 32-lane segments
+    (37, 4608, 512, 512),       # 512-channel groups: whole-wave segments
+    (9, 3072, 1024, 1024),      # group = the whole chunk; 1024 outliers (four tail words per lane)
+    (64, 1152, 128, 128),       # the longest batch of the wave-worker kernel
+    (65, 1152, 128, 128),       # one row more: row kernel
+    (11, 1408, 256, 384),       # 384-channel groups: row kernel
+    (6, 3200, 1100, 0),         # per-row scales: row kernel
+    (3, 2112, 1088, 128),       # tail of 1088 channels: row kernel
+    (7, 1024, 0, 128),          # no outliers
+    (2, 256, 256, 128),         # no INT4 head at all
+]
+
+
+@pytest.mark.parametrize("rows,K,n_out,group", PRODUCER)
+def test_producer_parity(oracle, rows, K, n_out, group):
+    sys.stderr.write(f"[gpu case] producer rows={rows} K={K} n_out={n_out} group={group}\n")
+    sys.stderr.flush()
+    X, _, o = wl.draw(rows, 1, K, n_out, seed=rows + K + n_out, outlier_factor=30.0)
+    perm = torch.from_numpy(w4.make_perm(K, o)).to(DEV)
+    a = w4.quant_reorder_act(torch.from_numpy(X).to(DEV), perm, n_out, group)
+    check_producer(oracle, a, X, perm.cpu().numpy(), n_out, group)
+
+
 # Per-row-scale shapes with at least 256 tiles of 256 x 256 take the
 # large-tile kernel (accumulators in AGPRs, outlier tail folded in per block).
 BIG_TILE = [
