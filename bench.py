@@ -25,7 +25,6 @@ between the two kernels of a timed step).
 sample of the same workload.
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -60,16 +59,15 @@ def work_counts(w, M):
 
 
 def traffic_record(workload_name, M):
-    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if they
-    were taken on the current GEMM source; else None."""
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs
+    (profiles/gemm_traffic.json), if they were taken on the current GEMM
+    sources; else None."""
+    from mixed_precision_integer_amd import profile_summary as ps
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
-    src = open(os.path.join(ROOT, "mixed_precision_integer_amd", "csrc", "gemm_kernels.hip"),
-               "rb").read()
-    sha = hashlib.sha256(src).hexdigest()[:16]
-    rec = json.load(open(path)).get(f"{workload_name}:M={M}")
-    if not rec or rec.get("gemm_source_sha256_16") != sha:
+    rec = json.load(open(path)).get(ps.traffic_key(workload_name, M))
+    if not rec or rec.get("gemm_sources_sha256_16") != ps.gemm_source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -225,7 +223,7 @@ def main():
         ach = ops / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "frac": ach / PEAK_INT8_TOPS}
-    roof["kernel"] = "gemm_kernel (w4a4_outlier_gemm)"
+    roof["kernel"] = w4.outlier_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group)
     roof["traffic"] = traffic_record(w.name, M)
 
     # the result is checked against a fused call (same kernels, same bits)

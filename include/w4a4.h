@@ -126,6 +126,13 @@ w4a4_status w4a4_pack_int4_weights(const void *W, int64_t ldw, const int32_t *pe
 size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
                                          int32_t group);
 
+/* Name of the GPU kernel w4a4_outlier_gemm launches for this shape (as in a
+ * kernel trace), for profiling and benchmarks: a static string owned by the
+ * library, or NULL for a shape the call would reject. A pure function of the
+ * shape, like the workspace size. */
+const char *w4a4_outlier_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                          int32_t group);
+
 /* Mixed-precision GEMM (Atom summary page, Summary paragraph 2 and
  * Interesting ideas I3; Key points item 5 for the symmetric epilogue):
  * INT4 x INT4 over the K_n head plus INT8 x INT8 over the outlier tail, int32

@@ -31,7 +31,8 @@ STATUS = {0: "W4A4_OK", 1: "W4A4_ERR_INVALID_ARG", 2: "W4A4_ERR_UNSUPPORTED",
 
 EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_pitch8_bytes",
             "w4a4_make_perm", "w4a4_quant_reorder_act", "w4a4_pack_int4_weights",
-            "w4a4_outlier_gemm_workspace_bytes", "w4a4_outlier_gemm", "w4a4_outlier_gemm_i32",
+            "w4a4_outlier_gemm_workspace_bytes", "w4a4_outlier_gemm_kernel_name", "w4a4_outlier_gemm",
+            "w4a4_outlier_gemm_i32",
             "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm")
 
 
@@ -69,6 +70,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [i32, i32, i32, i32, i32]
         f.restype = sz
+    L.w4a4_outlier_gemm_kernel_name.argtypes = [i32, i32, i32, i32, i32]
+    L.w4a4_outlier_gemm_kernel_name.restype = ctypes.c_char_p
     L.w4a4_outlier_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     vp, i64, vp, sz, vp]
     L.w4a4_outlier_gemm.restype = ctypes.c_int
@@ -210,6 +213,12 @@ def _gemm_args(a: QuantizedOperand, w: QuantizedOperand, out, ws):
 
 def outlier_gemm_workspace_bytes(M: int, N: int, K: int, n_out: int, group: int) -> int:
     return int(lib().w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group))
+
+
+def outlier_gemm_kernel_name(M: int, N: int, K: int, n_out: int, group: int):
+    """Kernel the GEMM launches for this shape (as named in a kernel trace), or None."""
+    r = lib().w4a4_outlier_gemm_kernel_name(M, N, K, n_out, group)
+    return None if r is None else r.decode()
 
 
 def w4a4_outlier_gemm(a: QuantizedOperand, w: QuantizedOperand, out=None):

@@ -181,6 +181,12 @@ size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_
     return w4a4::plan_gemm(M, N, K - n_out, n_out, group, false).workspace_bytes;
 }
 
+const char *w4a4_outlier_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
+    if (M <= 0 || N <= 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
+        return nullptr;
+    return w4a4::gemm_kernel_name(w4a4::plan_gemm(M, N, K - n_out, n_out, group, false));
+}
+
 w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
                               const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
                               int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group,

@@ -490,6 +490,17 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Tile shape and K split for a shape. Pure function of the shape, so the
 // workspace query and the launch always agree.
+const char *gemm_kernel_name(const GemmPlan &p) {
+    switch (p.cfg) {
+    case 0: return p.splits > 1 ? "gemm_kernel<64, 64> (split K)" : "gemm_kernel<64, 64>";
+    case 1: return p.splits > 1 ? "gemm_kernel<128, 128> (split K)" : "gemm_kernel<128, 128>";
+    case 2: return "gemm_big_kernel";
+    case 3: return "gemm_group_kernel";
+    case 4: return "gemm_decode_kernel";
+    default: return "unknown";
+    }
+}
+
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc) {
     GemmPlan p{};
     if (!export_acc && gemm_decode_fits(M, N, K_n, n_out, group)) {

@@ -93,6 +93,9 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc);
 
+// Kernel of a plan, as named in a kernel trace (static string).
+const char *gemm_kernel_name(const GemmPlan &p);
+
 // `workspace` holds plan_gemm(...).workspace_bytes bytes; its counter part
 // must be zero on entry and is zero again when the kernel completes.
 hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipStream_t stream);

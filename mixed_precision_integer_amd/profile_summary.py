@@ -1,0 +1,168 @@
+"""Summaries of rocprofv3 runs of bench.py for the profiles/ folder.
+
+    python -m mixed_precision_integer_amd.profile_summary DIR WORKLOAD TITLE OUT.md [--m M]
+
+DIR holds the output of five rocprofv3 runs of bench.py (the commands are
+written into the summary):
+
+    DIR/trace   --kernel-trace --stats over the workload
+    DIR/fetch   --pmc FETCH_SIZE over the workload
+    DIR/write   --pmc WRITE_SIZE over the workload
+    DIR/cfetch  --pmc FETCH_SIZE over a plain 512 MiB device copy
+    DIR/cwrite  --pmc WRITE_SIZE over the same copy
+
+The copy reads and writes exactly 512 MiB, so it gives the scale from the
+counters to bytes. The summary is written to profiles/OUT.md, and the GEMM's
+HBM bytes per launch are recorded in profiles/gemm_traffic.json under the
+workload, with a digest of the GEMM sources: bench.py reports the record as
+roofline traffic only while the sources are unchanged.
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+GEMM_SOURCES = ("gemm_kernels.hip", "gemm_big.hip", "gemm_group.hip", "gemm_decode.hip",
+                "gemm_common.h", "w4a4_internal.h")
+COPY_KIB = 512 * 1024
+
+
+def gemm_source_digest() -> str:
+    """First 16 hex digits of the SHA-256 of the GEMM sources, in a fixed order."""
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(HERE, "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_key(workload: str, M: int) -> str:
+    return f"{workload}:M={M}"
+
+
+def _csv(folder: str, suffix: str):
+    files = glob.glob(os.path.join(folder, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {folder}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _pmc(folder: str, counter: str):
+    """Mean counter value per dispatch, by kernel name."""
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    for r in _csv(folder, "counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            tot[r["Kernel_Name"]] += float(r["Counter_Value"])
+            disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+    return {k: (tot[k] / len(disp[k]), len(disp[k])) for k in tot}
+
+
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "")
+
+
+def _bench_line(log: str):
+    with open(log) as f:
+        lines = [l for l in f if l.startswith("{")]
+    return json.loads(lines[-1])
+
+
+def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "") -> str:
+    stats = _csv(os.path.join(d, "trace"), "kernel_stats.csv")
+    fetch = _pmc(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = _pmc(os.path.join(d, "write"), "WRITE_SIZE")
+    cf = _pmc(os.path.join(d, "cfetch"), "FETCH_SIZE")
+    cw = _pmc(os.path.join(d, "cwrite"), "WRITE_SIZE")
+    ck = next(k for k in cf if "copyBuffer" in k)
+    f_scale, w_scale = COPY_KIB / cf[ck][0], COPY_KIB / cw[ck][0]
+    bj = _bench_line(os.path.join(d, "trace.log"))
+    c = bj["config"]
+    gemm_name = bj["roofline"]["kernel"]
+    run = f"python3 bench.py --workload {workload}{m_arg}"
+    L = [f"# {title}\n",
+         "Workload: `%s` (M=%d, N=%d, K=%d, n_out=%d, group=%d), seeded synthetic inputs resident in "
+         "HBM, buffer sets rotated over more than 512 MB. GEMM kernel for this shape: `%s`.\n"
+         % (c["workload"], c["M"], c["N"], c["K"], c["n_out"], c["group"], gemm_name),
+         "## Kernel trace (rocprofv3 --kernel-trace --stats)\n",
+         "```\ncd /tmp && export TMPDIR=/tmp && cd <repo>\n"
+         f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
+         f"{run} --steps 20 --warmup 5 --no-cpu-baseline\n```\n",
+         "| kernel | calls | average µs | min µs | max µs | share of GPU time |",
+         "|---|---|---|---|---|---|"]
+    for r in stats:
+        if "w4a4" in r["Name"]:
+            L.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    L.append("\nThe other kernels in the trace (torch set-up copies and fills, the result check) "
+             "are not part of a step.\n")
+    k = bj["kernels"]
+    roof = bj["roofline"]
+    L.append("bench.py line printed in the same run (HIP events on the launch stream around each GEMM "
+             "launch of the timed region): producer %.2f µs, GEMM %.2f µs, step %.2f µs, value %.1f %s; "
+             "roofline: %.1f of %.0f %s (%.1f%%, %s-bound).\n"
+             % (k["producer_us"], k["gemm_us"], bj["ms_per_step"] * 1e3, bj["value"], bj["unit"],
+                roof["achieved"], roof["peak"], roof["unit"], 100 * roof["frac"], roof["bound"]))
+    L.append("## HBM traffic (rocprofv3 --pmc, one counter per run)\n")
+    cmds = [("FETCH_SIZE", "fetch", f"{run} --steps 5 --warmup 2 --no-cpu-baseline"),
+            ("WRITE_SIZE", "write", f"{run} --steps 5 --warmup 2 --no-cpu-baseline"),
+            ("FETCH_SIZE", "cfetch", "python3 bench.py --copy-probe-mib 512 --steps 5 --warmup 2"),
+            ("WRITE_SIZE", "cwrite", "python3 bench.py --copy-probe-mib 512 --steps 5 --warmup 2")]
+    L.append("```\n" + "\n".join(
+        f"timeout -s KILL 120 rocprofv3 --pmc {cn} --output-format csv -d {d}/{o} -o p -- {cmd}"
+        for cn, o, cmd in cmds) + "\n```\n")
+    L.append(f"Calibration: the plain 512 MiB device copy (`{_short(ck)}`, {cf[ck][1]} dispatches) reads "
+             f"{cf[ck][0]:.0f} KiB (FETCH_SIZE) and writes {cw[ck][0]:.0f} KiB (WRITE_SIZE) per dispatch "
+             f"for {COPY_KIB} KiB moved each way, so bytes = FETCH_SIZE x {f_scale:.3f} KiB and "
+             f"WRITE_SIZE x {w_scale:.3f} KiB.\n")
+    L.append("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | "
+             "total MB per launch |")
+    L.append("|---|---|---|---|---|---|---|")
+    traffic = {}
+    for kn, (fk, n) in fetch.items():
+        if "w4a4" not in kn:
+            continue
+        wk = write.get(kn, (0.0, 0))[0]
+        rb, wb = fk * f_scale * 1024, wk * w_scale * 1024
+        traffic[_short(kn)] = rb + wb
+        L.append(f"| `{_short(kn)}` | {n} | {fk:.0f} | {wk:.0f} | {rb / 1e6:.2f} | {wb / 1e6:.2f} | "
+                 f"{(rb + wb) / 1e6:.2f} |")
+    text = "\n".join(L) + "\n"
+    with open(os.path.join(ROOT, "profiles", out), "w") as f:
+        f.write(text)
+    base = gemm_name.split("<")[0].split(" ")[0]
+    gk = [kk for kk in traffic if kk.split("::")[-1].split("<")[0] == base]
+    if gk:
+        p = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+        rec = json.load(open(p)) if os.path.exists(p) else {}
+        rec[traffic_key(c["workload"], c["M"])] = {
+            "gemm_sources_sha256_16": gemm_source_digest(), "kernel": gk[0],
+            "hbm_bytes_per_launch": traffic[gk[0]], "fetch_scale_kib": f_scale,
+            "write_scale_kib": w_scale, "profile": out}
+        with open(p, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return text
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("dir")
+    ap.add_argument("workload")
+    ap.add_argument("title")
+    ap.add_argument("out")
+    ap.add_argument("--m", default=None, help="the --m argument the runs were made with")
+    a = ap.parse_args()
+    print(summarize(os.path.relpath(a.dir, ROOT) if os.path.isabs(a.dir) else a.dir, a.workload, a.title,
+                    a.out, f" --m {a.m}" if a.m else ""))
+
+
+if __name__ == "__main__":
+    main()

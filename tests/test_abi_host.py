@@ -159,3 +159,15 @@ def test_device_calls_fail_loudly_without_gpu():
     perm = torch.arange(256, dtype=torch.int32)
     with pytest.raises(ValueError):
         w4.quant_reorder_act(X, perm, 16, 0)
+
+
+@pytest.mark.parametrize("shape,name", [
+    ((1, 8192, 8192, 128, 128), "gemm_decode_kernel"),         # decode batch: weights streamed once
+    ((2048, 4096, 4096, 128, 128), "gemm_group_kernel"),       # 128-channel groups
+    ((2048, 11008, 4096, 256, 0), "gemm_big_kernel"),          # per-row scales, >= 256 large tiles
+    ((48, 384, 4224, 128, 128), "gemm_kernel<64, 64> (split K)"),
+    ((0, 1, 1, 0, 0), None),                                   # rejected shapes
+    ((4, 4, 130, 0, 128), None),
+])
+def test_gemm_kernel_name(shape, name):
+    assert w4.outlier_gemm_kernel_name(*shape) == name
