@@ -1,4 +1,4 @@
-// GEMM for decode batches (M <= 32 tokens): the weights are streamed once
+// GEMM for decode batches (M <= 128 tokens): the weights are streamed once
 // from HBM.
 //
 // Method: Atom summary page (Summary paragraph 2: INT4 main part with group
@@ -27,6 +27,7 @@
 // * The eight partial blocks are added through LDS in wave order (the same
 //   order in every call), then written as fp16.
 #include <algorithm>
+#include <type_traits>
 
 #include "w4a4.h"
 #include "gemm_common.h"
@@ -37,6 +38,7 @@ namespace gemm_decode_impl {
 using namespace gemm_impl;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int WAVES = 8, THREADS = WAVES * 64;
 constexpr int BN = 32;                    // output columns per workgroup
@@ -216,21 +218,277 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
     }
 }
 
+// Decode batches of 32 < M <= 32 MB token rows: the same column stripes and K
+// ranges, with MB row blocks per wave. Every wave streams single K-tiles of
+// its 32 weight rows and 32 MB token rows into a two-slot LDS ring of its own
+// by direct DMA (a tile's 64-byte row segments, chunks swizzled as in the
+// other GEMM kernels); every row segment crosses from L2 once. Row blocks go
+// in pairs, side by side (one MFMA per block per k-step), and the scale
+// products of a pair come from one v_mfma_f32_32x32x1_2b_f32 (block b in
+// lanes 0-31, b + 1 in 32-63). All scales sit in registers, loaded before the
+// first DMA, which bounds a wave's range to MAXT_ROWS tiles. The partial
+// blocks are added through LDS in wave order, one row block at a time.
+constexpr int MAXT_ROWS = 8;                              // K_n <= 8192
+
+template <int MB>
+struct RowsRing {
+    static constexpr int ROWS = 32 + 32 * MB;             // weight rows, then token rows
+    static constexpr int DMA = ROWS / 16;                 // DMA instructions per tile
+    static constexpr int SLOT = ROWS * kTileBytes;
+    static constexpr int WAVE = 2 * SLOT;
+    static constexpr int BYTES = WAVES * WAVE > WAVES * 16 * 64 * 4 ? WAVES * WAVE : WAVES * 16 * 64 * 4;
+};
+
+template <int MB>
+__global__ __launch_bounds__(THREADS) void gemm_decode_rows_kernel(GemmArgs a) {
+    using R = RowsRing<MB>;
+    __shared__ __align__(16) unsigned char lds[R::BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lh = lane >> 5;
+
+    const int n0 = blockIdx.x * BN;
+    const int T4 = (int)(a.pitch4 / kTileBytes), T8 = (int)(a.pitch8 / kTileBytes);
+    const int tiles_per_group = a.group > 0 ? a.group / 128 : max(T4, 1);
+    const int per = (T4 + WAVES - 1) / WAVES;             // <= MAXT_ROWS (checked at launch)
+    const int tb = min(wave * per, T4), te = min(tb + per, T4);
+    const int nt = te - tb;
+
+    // ---- scales of this wave's tiles, before any DMA (the DMA waits count DMA only)
+    const int64_t nrow = min(n0 + li, a.N - 1);
+    int64_t mrow[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+        mrow[b] = min(32 * b + li, a.M - 1);
+    float sw[MAXT_ROWS], sa[MAXT_ROWS][MB];
+#pragma unroll
+    for (int k = 0; k < MAXT_ROWS; ++k) {
+        const int g = min(tb + k, T4 - 1) / tiles_per_group;
+        sw[k] = a.sw4[nrow * a.G + g] * (1.0f / 256.0f);
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+            sa[k][b] = a.sa4[mrow[b] * a.G + g];
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+
+    // ---- DMA of one tile: instruction i covers ring rows 16 i .. 16 i + 15, lane
+    // q row 16 i + q / 4 and stored chunk q % 4 (see dma_chunk_offset)
+    uint32_t voff[R::DMA];
+#pragma unroll
+    for (int i = 0; i < R::DMA; ++i) {
+        const int r = 16 * i + (lane >> 2);
+        const int64_t src = r < 32 ? min(n0 + r, a.N - 1) : min(r - 32, a.M - 1);
+        voff[i] = (uint32_t)(src * a.pitch4) + dma_chunk_offset(r * 4 + (lane & 3));
+    }
+    unsigned char *wl = lds + wave * R::WAVE;
+    // ring rows [16 I0, 16 I1) of tile tb + k into slot k % 2
+    auto issue_rows = [&](int k, auto i0, auto i1) {
+        const int t = tb + k;
+        const uint32_t st = lds_addr(wl + (k & 1) * R::SLOT);
+        const uint8_t *W = a.w4 + t * kTileBytes, *X = a.a4 + t * kTileBytes;
+#pragma unroll
+        for (int i = decltype(i0)::value; i < decltype(i1)::value; ++i)
+            dma16(i < 2 ? W : X, voff[i], st + i * 1024);
+    };
+    auto issue = [&](int k) { issue_rows(k, std::integral_constant<int, 0>{}, std::integral_constant<int, R::DMA>{}); };
+
+    v16f y[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+        y[b] = v16f{};
+    const v16f zf = {};
+    const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    // Tile k from slot k % 2, a pair of row blocks at a time: the rows of the
+    // weights and of a pair are read into registers, then those ring rows take
+    // their part of tile k + 2 at once, while this tile's MFMAs run.
+    auto tile = [&](int k) {
+        const unsigned char *sl = wl + (k & 1) * R::SLOT;
+        v4i w[2][2];
+#pragma unroll
+        for (int b0 = 0; b0 < MB; b0 += 2) {
+            constexpr int kPair = 2;
+            const int nb = b0 + 1 < MB ? kPair : 1;
+            uint4 pw[2], px[kPair][2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (b0 == 0)
+                    pw[s] = *reinterpret_cast<const uint4 *>(sl + swz(li, 2 * s + lh));
+#pragma unroll
+                for (int i = 0; i < kPair; ++i)
+                    if (i < nb)
+                        px[i][s] = *reinterpret_cast<const uint4 *>(sl + swz(32 + 32 * (b0 + i) + li, 2 * s + lh));
+            }
+            compiler_fence();
+            __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));       // these ring rows are free again
+            compiler_fence();
+            if (k + 2 < nt) {
+                // weights (ring rows 0..31) with the first pair; a pair's token rows
+                // are ring rows 32 + 32 b0 .. 32 + 32 (b0 + nb) - 1
+                if (b0 == 0)
+                    issue_rows(k + 2, std::integral_constant<int, 0>{},
+                               std::integral_constant<int, (MB >= 2 ? 6 : 4)>{});
+                else if (b0 == 2)
+                    issue_rows(k + 2, std::integral_constant<int, 6>{}, std::integral_constant<int, R::DMA>{});
+            }
+            if (b0 == 0)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    w[s][0] = v4i{(int)nib_lo(pw[s].x), (int)nib_hi(pw[s].x), (int)nib_lo(pw[s].y), (int)nib_hi(pw[s].y)};
+                    w[s][1] = v4i{(int)nib_lo(pw[s].z), (int)nib_hi(pw[s].z), (int)nib_lo(pw[s].w), (int)nib_hi(pw[s].w)};
+                }
+            v4i x[kPair][2][2];
+#pragma unroll
+            for (int i = 0; i < kPair; ++i)
+                if (i < nb)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const uint4 q = px[i][s];
+                        x[i][s][0] = v4i{(int)nib_lo(q.x), (int)nib_hi(q.x), (int)nib_lo(q.y), (int)nib_hi(q.y)};
+                        x[i][s][1] = v4i{(int)nib_lo(q.z), (int)nib_hi(q.z), (int)nib_lo(q.w), (int)nib_hi(q.w)};
+                    }
+            v16i acc[kPair];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < kPair; ++i)
+                    if (i < nb)
+                        acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[q >> 1][q & 1], x[i][q >> 1][q & 1],
+                                                                       q == 0 ? zi : acc[i], 0, 0, 0);
+            // scale products one block at a time (16 registers live)
+#pragma unroll
+            for (int i = 0; i < kPair; ++i)
+                if (i < nb) {
+                    const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw[k], lh ? 0.0f : sa[k][b0 + i],
+                                                                         zf, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        y[b0 + i][e] = __builtin_fmaf((float)acc[i][e], S[e], y[b0 + i][e]);
+                }
+        }
+    };
+
+    // ---- INT4 tiles: two in flight, the loop unrolled (scales in registers)
+    if (nt > 0)
+        issue(0);
+    if (nt > 1)
+        issue(1);
+#pragma unroll
+    for (int k = 0; k < MAXT_ROWS; ++k) {
+        if (k < nt) {
+            compiler_fence();
+            if (k + 1 < nt)
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(R::DMA));      // tile k + 1 may stay in flight
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            compiler_fence();
+            tile(k);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+
+    // ---- INT8 tail: wave w takes tail tiles w, w + 8, ...; row blocks in pairs,
+    // each tile's loads for a pair issued before its MFMAs
+    if (T8 > wave) {
+        const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
+        const float sw8 = a.sw8[nrow];
+#pragma unroll
+        for (int b0 = 0; b0 < MB; b0 += 2) {
+            const int nb = b0 + 1 < MB ? 2 : 1;
+            v16i acc8[2] = {zi, zi};
+            for (int t = wave; t < T8; t += WAVES) {
+                const uint4 w0 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes);
+                const uint4 w1 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes + 32);
+                uint4 x0[2], x1[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    if (i < nb) {
+                        const uint8_t *x8 = reinterpret_cast<const uint8_t *>(a.a8) + mrow[b0 + i] * a.pitch8 +
+                                            16 * lh + t * kTileBytes;
+                        x0[i] = *reinterpret_cast<const uint4 *>(x8);
+                        x1[i] = *reinterpret_cast<const uint4 *>(x8 + 32);
+                    }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    if (i < nb) {
+                        acc8[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w0), as_v4i(x0[i]), acc8[i], 0, 0, 0);
+                        acc8[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w1), as_v4i(x1[i]), acc8[i], 0, 0, 0);
+                    }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                if (i < nb) {
+                    const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw8, lh ? 0.0f : a.sa8[mrow[b0 + i]],
+                                                                         zf, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        y[b0 + i][e] = __builtin_fmaf((float)acc8[i][e], S[e], y[b0 + i][e]);
+                }
+        }
+    }
+
+    // ---- partial blocks added in wave order, one row block at a time
+    float *red = reinterpret_cast<float *>(lds);              // [wave][register][lane]
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            red[(wave * 16 + e) * 64 + lane] = y[b][e];
+        __syncthreads();
+        const int l = tid & 63, e0 = 2 * (tid >> 6);
+        float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            v0 += red[(w * 16 + e0) * 64 + l];
+            v1 += red[(w * 16 + e0 + 1) * 64 + l];
+        }
+        const int m = 32 * b + (l & 31);
+        const int n = n0 + 8 * (e0 / 4) + 4 * (l >> 5) + (e0 % 4);
+        if (m < a.M) {
+            _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
+            const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+            if (n + 1 < a.N && ((reinterpret_cast<uintptr_t>(dst) & 3) == 0)) {
+                *reinterpret_cast<uint32_t *>(dst) =
+                    (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            } else {
+                if (n < a.N)
+                    dst[0] = h0;
+                if (n + 1 < a.N)
+                    dst[1] = h1;
+            }
+        }
+    }
+}
+
 }  // namespace gemm_decode_impl
 
 using namespace gemm_decode_impl;
 
 bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
-    (void)N;
     (void)n_out;
     const int T4 = (K_n + 127) / 128;
-    return M >= 1 && M <= MAXM && K_n >= 128 && (group == 0 || group % 128 == 0) &&
-           (T4 + WAVES - 1) / WAVES <= MAXT;
+    const int per = (T4 + WAVES - 1) / WAVES;
+    // DMA offsets are 32-bit: every packed operand row must start below 4 GiB
+    const int64_t pitch4 = (int64_t)T4 * kTileBytes;
+    if ((int64_t)N * pitch4 >= (int64_t(1) << 32) || (int64_t)M * pitch4 >= (int64_t(1) << 32))
+        return false;
+    return M >= 1 && K_n >= 128 && (group == 0 || group % 128 == 0) &&
+           ((M <= MAXM && per <= MAXT) || (M <= 4 * MAXM && per <= MAXT_ROWS));
 }
 
 hipError_t launch_gemm_decode(const GemmArgs &a, hipStream_t stream) {
     const int blocks = (a.N + BN - 1) / BN;
-    hipLaunchKernelGGL(gemm_decode_kernel, dim3(blocks), dim3(THREADS), 0, stream, a);
+    const int mb = (a.M + MAXM - 1) / MAXM;
+    if (mb <= 1)
+        hipLaunchKernelGGL(gemm_decode_kernel, dim3(blocks), dim3(THREADS), 0, stream, a);
+    else if (mb == 2)
+        hipLaunchKernelGGL(gemm_decode_rows_kernel<2>, dim3(blocks), dim3(THREADS), 0, stream, a);
+    else if (mb == 3)
+        hipLaunchKernelGGL(gemm_decode_rows_kernel<3>, dim3(blocks), dim3(THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL(gemm_decode_rows_kernel<4>, dim3(blocks), dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

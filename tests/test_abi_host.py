@@ -165,7 +165,8 @@ def test_device_calls_fail_loudly_without_gpu():
     ((1, 8192, 8192, 128, 128), "gemm_decode_kernel"),         # decode batch: weights streamed once
     ((2048, 4096, 4096, 128, 128), "gemm_group_kernel"),       # 128-channel groups
     ((2048, 11008, 4096, 256, 0), "gemm_big_kernel"),          # per-row scales, >= 256 large tiles
-    ((48, 384, 4224, 128, 128), "gemm_kernel<64, 64> (split K)"),
+    ((48, 384, 4224, 128, 128), "gemm_decode_kernel"),         # decode batch of two row blocks
+    ((48, 384, 17536, 128, 128), "gemm_kernel<64, 64> (split K)"),   # K_n past the decode kernel's range
     ((0, 1, 1, 0, 0), None),                                   # rejected shapes
     ((4, 4, 130, 0, 128), None),
 ])

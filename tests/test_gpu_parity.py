@@ -137,11 +137,11 @@ def test_mid_size_parity(oracle, M, N, K, n_out, group):
 # Shapes with few output tiles and long K: the GEMM splits K across workgroups
 # (fp32 partials in the workspace, added in split order by the last split).
 SPLIT_K = [
-    # M, N, K, n_out, group
-    (48, 384, 4224, 128, 128),      # group mode, 64 x 64 tiles, 6 output tiles
-    (40, 1000, 4096, 64, 0),        # per-row scales, ragged N, split inside the one group
-    (100, 256, 8192, 128, 128),     # 128 x 128 tiles, ragged M
-    (33, 640, 2176, 128, 256),      # group of two K-tiles cut by splits
+    # M, N, K, n_out, group (M <= 128 takes the decode kernel unless K_n > 16384)
+    (48, 384, 17536, 128, 128),     # group mode, 64 x 64 tiles, K_n past the decode kernel's range
+    (40, 1000, 16832, 64, 0),       # per-row scales, ragged N, split inside the one group
+    (160, 384, 4224, 128, 128),     # 128 x 128 tiles, ragged M
+    (150, 640, 4224, 128, 256),     # group of two K-tiles cut by splits
 ]
 
 
@@ -155,7 +155,7 @@ def test_split_k_parity(oracle, M, N, K, n_out, group):
 def test_split_k_workspace_reuse(oracle):
     """One workspace for shapes with different tile and split counts, in turn:
     every call must leave the tile counters at zero for the next one."""
-    shapes = [(48, 384, 4224, 128, 128), (40, 1000, 4096, 64, 0), (48, 384, 4224, 128, 128)]
+    shapes = [(48, 384, 17536, 128, 128), (40, 1000, 16832, 64, 0), (48, 384, 17536, 128, 128)]
     need = max(w4.outlier_gemm_workspace_bytes(*s) for s in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     for i, (M, N, K, n_out, group) in enumerate(shapes):
@@ -171,7 +171,7 @@ def test_split_k_workspace_reuse(oracle):
             assert torch.equal(y, fresh), f"shape {i}: reused workspace gives a different Y"
 
 
-# Decode batches (M <= 32): the weights stream once through the decode
+# Decode batches (M <= 128): the weights stream once through the decode
 # kernel (eight waves per 32 output columns take the K-tiles in turn, the
 # partial blocks are added in wave order).
 DECODE = [
@@ -182,12 +182,20 @@ DECODE = [
     (32, 2048, 2176, 128, 128),     # a full 32-row block
     (17, 300, 1536, 0, 0),          # no outlier tail, ragged N
     (9, 96, 8320, 128, 128),        # one workgroup short of columns, 64 groups
+    # 32 < M <= 128: two to four row blocks per wave, token fragments from L2
+    (48, 384, 4224, 128, 128),      # two blocks, the second ragged
+    (64, 1000, 4096, 64, 0),        # two full blocks, per-row scales, ragged N
+    (65, 300, 1536, 0, 0),          # three blocks (one row in the third), no tail
+    (96, 96, 8320, 128, 128),       # three full blocks, 64 groups
+    (100, 640, 2176, 128, 256),     # four blocks, group of two K-tiles
+    (128, 2048, 2176, 128, 128),    # four full blocks
 ]
 
 
 @pytest.mark.parametrize("M,N,K,n_out,group", DECODE)
 def test_decode_parity(oracle, M, N, K, n_out, group):
     assert w4.outlier_gemm_workspace_bytes(M, N, K, n_out, group) == 0
+    assert w4.outlier_gemm_kernel_name(M, N, K, n_out, group) == "gemm_decode_kernel"
     X, W, o = wl.draw(M, N, K, n_out, seed=M * 13 + K, outlier_factor=30.0)
     full_compare(oracle, X, W, o, group)
 
