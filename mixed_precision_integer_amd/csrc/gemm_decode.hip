@@ -22,8 +22,9 @@
 //   the scale products from one v_mfma_f32_32x32x2_f32 (an outer product of
 //   the column and the row scales in the accumulator layout); this holds for
 //   any group size that is a multiple of 128 (a tile lies inside one group).
-//   A wave's scales are loaded before its first DMA. The INT8 tail is read
-//   directly, accumulated over its tiles and folded once.
+//   A wave's scales and first INT8 tail tile are requested just before its
+//   first DMA. The INT8 tail is read directly, accumulated over its tiles and
+//   folded once.
 // * The eight partial blocks are added through LDS in wave order (the same
 //   order in every call), then written as fp16.
 #include <algorithm>
@@ -70,8 +71,10 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
     const int tb = min(wave * per, T4), te = min(tb + per, T4);
     const int nt = te - tb, np = (nt + 1) / 2;                // tiles and pairs of this wave
 
-    // ---- scales of this wave's tiles, before any DMA (the DMA is tracked by
-    // hand; nothing else may be outstanding when its waits run)
+    // ---- scales of this wave's tiles and its first INT8 tail tile, requested
+    // before any DMA. The DMA waits are counted by hand; loads complete in
+    // order, so the first wait on a DMA also covers these older loads, and they
+    // travel together with the first pairs.
     const int64_t nrow = min(n0 + li, a.N - 1), mrow = min(li, a.M - 1);
     float sw[MAXT], sa[MAXT];
 #pragma unroll
@@ -80,7 +83,15 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
         sw[k] = a.sw4[nrow * a.G + g] * (1.0f / 256.0f);
         sa[k] = a.sa4[mrow * a.G + g];
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
+    const uint8_t *x8row = reinterpret_cast<const uint8_t *>(a.a8) + mrow * a.pitch8 + 16 * lh;
+    uint4 tw[2] = {}, tx[2] = {};
+    if (T8 > wave) {
+        tw[0] = *reinterpret_cast<const uint4 *>(w8row + wave * kTileBytes);
+        tw[1] = *reinterpret_cast<const uint4 *>(w8row + wave * kTileBytes + 32);
+        tx[0] = *reinterpret_cast<const uint4 *>(x8row + wave * kTileBytes);
+        tx[1] = *reinterpret_cast<const uint4 *>(x8row + wave * kTileBytes + 32);
+    }
 
     // ---- DMA of a pair of tiles: instruction i covers rows 8 i .. 8 i + 7, lane
     // q row 8 i + q / 8 and stored chunk q % 8 (logical chunk (q % 8) ^ (row & 7));
@@ -162,12 +173,12 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
         }
     }
 
-    // ---- INT8 tail: wave w takes tail tiles w, w + 8, ... (folded once) ------------------
+    // ---- INT8 tail: wave w takes tail tiles w, w + 8, ... (the first one is
+    // already in registers; folded once) -------------------------------------------------
     if (T8 > wave) {
-        const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
-        const uint8_t *x8row = reinterpret_cast<const uint8_t *>(a.a8) + mrow * a.pitch8 + 16 * lh;
-        v16i acc8 = zi;
-        for (int t = wave; t < T8; t += WAVES) {
+        v16i acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(tw[0]), as_v4i(tx[0]), zi, 0, 0, 0);
+        acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(tw[1]), as_v4i(tx[1]), acc8, 0, 0, 0);
+        for (int t = wave + WAVES; t < T8; t += WAVES) {
             const uint4 w0 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes);
             const uint4 w1 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes + 32);
             const uint4 x0 = *reinterpret_cast<const uint4 *>(x8row + t * kTileBytes);
@@ -270,7 +281,21 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_rows_kernel(GemmArgs a) {
         for (int b = 0; b < MB; ++b)
             sa[k][b] = a.sa4[mrow[b] * a.G + g];
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    // INT8 tail items (tile t, row block b), i = t MB + b, go to wave i % 8;
+    // this wave's first item is requested here, with the scales (loads
+    // complete in order: the first DMA wait covers them)
+    const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
+    auto x8ptr = [&](int i) {
+        return reinterpret_cast<const uint8_t *>(a.a8) + min(32 * (i % MB) + li, a.M - 1) * (int64_t)a.pitch8 +
+               16 * lh + (i / MB) * kTileBytes;
+    };
+    uint4 tw[2] = {}, tx[2] = {};
+    if (T8 * MB > wave) {
+        tw[0] = *reinterpret_cast<const uint4 *>(w8row + (wave / MB) * kTileBytes);
+        tw[1] = *reinterpret_cast<const uint4 *>(w8row + (wave / MB) * kTileBytes + 32);
+        tx[0] = *reinterpret_cast<const uint4 *>(x8ptr(wave));
+        tx[1] = *reinterpret_cast<const uint4 *>(x8ptr(wave) + 32);
+    }
 
     // ---- DMA of one tile: instruction i covers ring rows 16 i .. 16 i + 15, lane
     // q row 16 i + q / 4 and stored chunk q % 4 (see dma_chunk_offset)
@@ -388,43 +413,28 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_rows_kernel(GemmArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 
-    // ---- INT8 tail: wave w takes tail tiles w, w + 8, ...; row blocks in pairs,
-    // each tile's loads for a pair issued before its MFMAs
-    if (T8 > wave) {
-        const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
+    // ---- INT8 tail items of this wave (the first one already in registers)
+    if (T8 * MB > wave) {
         const float sw8 = a.sw8[nrow];
-#pragma unroll
-        for (int b0 = 0; b0 < MB; b0 += 2) {
-            const int nb = b0 + 1 < MB ? 2 : 1;
-            v16i acc8[2] = {zi, zi};
-            for (int t = wave; t < T8; t += WAVES) {
-                const uint4 w0 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes);
-                const uint4 w1 = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes + 32);
-                uint4 x0[2], x1[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    if (i < nb) {
-                        const uint8_t *x8 = reinterpret_cast<const uint8_t *>(a.a8) + mrow[b0 + i] * a.pitch8 +
-                                            16 * lh + t * kTileBytes;
-                        x0[i] = *reinterpret_cast<const uint4 *>(x8);
-                        x1[i] = *reinterpret_cast<const uint4 *>(x8 + 32);
-                    }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    if (i < nb) {
-                        acc8[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w0), as_v4i(x0[i]), acc8[i], 0, 0, 0);
-                        acc8[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w1), as_v4i(x1[i]), acc8[i], 0, 0, 0);
-                    }
+        for (int i = wave; i < T8 * MB; i += WAVES) {
+            const int t = i / MB, b = i % MB;
+            if (i != wave) {
+                tw[0] = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes);
+                tw[1] = *reinterpret_cast<const uint4 *>(w8row + t * kTileBytes + 32);
+                tx[0] = *reinterpret_cast<const uint4 *>(x8ptr(i));
+                tx[1] = *reinterpret_cast<const uint4 *>(x8ptr(i) + 32);
             }
+            v16i acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(tw[0]), as_v4i(tx[0]), zi, 0, 0, 0);
+            acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(tw[1]), as_v4i(tx[1]), acc8, 0, 0, 0);
+            const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw8, lh ? 0.0f : a.sa8[min(32 * b + li, a.M - 1)],
+                                                                 zf, 0, 0, 0);
+            // the block index is uniform: select y[b] without indexing a register array
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                if (i < nb) {
-                    const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw8, lh ? 0.0f : a.sa8[mrow[b0 + i]],
-                                                                         zf, 0, 0, 0);
+            for (int bb = 0; bb < MB; ++bb)
+                if (bb == b)
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
-                        y[b0 + i][e] = __builtin_fmaf((float)acc8[i][e], S[e], y[b0 + i][e]);
-                }
+                        y[bb][e] = __builtin_fmaf((float)acc8[e], S[e], y[bb][e]);
         }
     }
 
