@@ -109,6 +109,7 @@ def gemm(**kw):
     (dict(q4=FAKE + 8), ALIGN), (dict(s4=FAKE + 2), ALIGN),
     (dict(K=140000, ld=140000, n_out=0), UNSUPPORTED),  # int32 guard of the accumulators
     (dict(K=90000, ld=90000, n_out=0), UNSUPPORTED),    # row larger than LDS
+    (dict(K=24584, ld=24584, n_out=0), UNSUPPORTED),    # one step past the longest row (24576)
 ])
 def test_quant_rejects(kw, code):
     assert quant(**kw) == code

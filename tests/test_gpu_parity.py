@@ -340,6 +340,18 @@ def test_producer_parity(oracle, rows, K, n_out, group):
     check_producer(oracle, a, X, perm.cpu().numpy(), n_out, group)
 
 
+# The longest row the producer takes (24576 channels, the 1024-lane bucket)
+# through the producer alone and through the whole layer (a short batch: K
+# past the decode kernels' range, so split K).
+@pytest.mark.parametrize("n_out,group", [(256, 0), (256, 128), (0, 128)])
+def test_longest_row(oracle, n_out, group):
+    K = 24576
+    sys.stderr.write(f"[gpu case] longest row K={K} n_out={n_out} group={group}\n")
+    sys.stderr.flush()
+    X, W, o = wl.draw(3, 200, K, n_out, seed=K + n_out + group, outlier_factor=30.0)
+    full_compare(oracle, X, W, o, group)
+
+
 # Per-row-scale shapes with at least 256 tiles of 256 x 256 take the
 # large-tile kernel (accumulators in AGPRs, outlier tail folded in per block).
 BIG_TILE = [
