@@ -6,7 +6,8 @@
 // item 5: symmetric scales factor out of the integer sums) and the QUIK
 // abstract (one-token decode is memory-bound).
 //
-// CDNA4 design (HBM-bound: every weight byte is read once)
+// CDNA4 design (HBM-bound: every weight byte is read once). For M <= 32
+// (gemm_decode_kernel; the row-block kernel further down takes 32 < M <= 128):
 // * A workgroup owns 32 output columns and all M <= 32 token rows: one
 //   32 x 32 block of v_mfma_i32_32x32x32_i8 with the weight fragment as the
 //   first operand (lane (li, lh) holds token row li and the columns

@@ -83,7 +83,7 @@ struct GemmArgs {
 struct GemmPlan {
     int cfg;                  // tile configuration: 0 64 x 64, 1 128 x 128, 2 256 x 256,
                               // 3 128 x 128 for 128-channel scale groups,
-                              // 4 decode (M <= 32, weights streamed once)
+                              // 4 decode (M <= 128, weights streamed once)
     int tiles;                // output tiles
     int splits;               // K splits per output tile
     size_t part_offset;       // byte offset of the fp32 partial sums (counters first)
@@ -100,7 +100,7 @@ const char *gemm_kernel_name(const GemmPlan &p);
 // must be zero on entry and is zero again when the kernel completes.
 hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipStream_t stream);
 
-// Decode kernel for M <= 32 token rows (gemm_decode.hip).
+// Decode kernels for M <= 128 token rows (gemm_decode.hip).
 bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
 hipError_t launch_gemm_decode(const GemmArgs &a, hipStream_t stream);
 

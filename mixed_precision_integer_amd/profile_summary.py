@@ -32,12 +32,39 @@ GEMM_SOURCES = ("gemm_kernels.hip", "gemm_big.hip", "gemm_group.hip", "gemm_deco
 COPY_KIB = 512 * 1024
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed, so that an
+    edit of a comment alone leaves the digest (and the counter records) valid.
+    String and character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def gemm_source_digest() -> str:
-    """First 16 hex digits of the SHA-256 of the GEMM sources, in a fixed order."""
+    """First 16 hex digits of the SHA-256 of the GEMM sources (code only, in a
+    fixed order)."""
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        with open(os.path.join(HERE, "csrc", name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(HERE, "csrc", name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
