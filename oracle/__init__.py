@@ -69,6 +69,8 @@ def _load():
     lib.w4o_quantize_rows.argtypes = [_f32p, c_i64, c_i32, c_i64, _i32p, c_i32, c_i32,
                                       _i8p, _f32p, _i8p, _f32p]
     lib.w4o_quantize_rows.restype = ctypes.c_int
+    lib.w4o_rms_rstd_rows.argtypes = [_f32p, c_i64, c_i32, c_i64, ctypes.c_float, _f32p]
+    lib.w4o_rms_rstd_rows.restype = ctypes.c_int
     lib.w4o_pack_nibbles.argtypes = [_i8p, c_i64, c_i32, c_i64, _u8p]
     lib.w4o_pack_nibbles.restype = None
     lib.w4o_linear_at.argtypes = [_i8p, _f32p, _i8p, _f32p, _i8p, _f32p, _i8p, _f32p,
@@ -130,6 +132,43 @@ def quantize_rows(X, perm, n_out: int, group: int):
     if rc != 0:
         raise ValueError("group must divide K - n_out")
     return q4, s4, q8, s8
+
+
+def rms_rstd(X, eps: float) -> np.ndarray:
+    """RMSNorm factor of every row of X [rows, K] (fp16): float32 [rows].
+
+    Readings N1-N3 in ``w4a4_oracle.c``: exact sum of squares, then
+    fl32(1 / sqrt(fl64(fl64(S) / K) + eps)) in binary64; 0 for a zero row at
+    eps = 0.
+    """
+    X = np.asarray(X)
+    if X.dtype != np.float16:
+        raise TypeError("rms_rstd takes fp16 rows")
+    rows, K = X.shape
+    Xf = np.ascontiguousarray(X.astype(np.float32))
+    out = np.zeros(max(rows, 1), np.float32)
+    if rows and _load().w4o_rms_rstd_rows(Xf, rows, K, K, float(eps), out) != 0:
+        raise ValueError("K must be in [1, 32768] and eps finite and >= 0")
+    return out[:rows]
+
+
+def rmsnorm(X, gamma, eps: float) -> np.ndarray:
+    """RMSNorm of fp16 rows as an fp16 model computes it: the row is scaled in
+    fp32 by rstd and rounded to fp16, then multiplied by the fp16 weight gamma
+    (the product of two fp16 values is exact in fp32, so one rounding to fp16).
+    Both roundings are to nearest even (numpy's float32 -> float16 cast)."""
+    X = np.asarray(X)
+    g = np.asarray(gamma)
+    if g.dtype != np.float16 or g.shape != (X.shape[1],):
+        raise TypeError("gamma must be fp16 [K]")
+    r = rms_rstd(X, eps)
+    h = (X.astype(np.float32) * r[:, None]).astype(np.float16)
+    return (h.astype(np.float32) * g.astype(np.float32)).astype(np.float16)
+
+
+def rmsnorm_quantize_rows(X, gamma, eps: float, perm, n_out: int, group: int):
+    """The fused producer's result: quantize_rows of rmsnorm(X, gamma, eps)."""
+    return quantize_rows(rmsnorm(X, gamma, eps), perm, n_out, group)
 
 
 def pack_nibbles(q4, pitch: int) -> np.ndarray:

@@ -32,6 +32,7 @@
  *   R7 the tail has one scale per row (token for X, output channel for W).
  *   R8 dequantized output y* is evaluated in fp64 and rounded to fp16 by the
  *      caller (fp64 -> fp16 round to nearest even).
+ *   N1-N3 (RMSNorm in front of the quantizer): at w4o_rms_rstd_rows.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  * All floating point here is IEEE binary32 / binary64 on x86-64 SSE (no x87
@@ -102,6 +103,40 @@ void w4o_quantize_block(const float *v, int32_t len, int32_t qmax,
             r = (float)(-qmax - 1);
         q[j] = (int8_t)r;
     }
+}
+
+/* RMSNorm factor of each row of a [rows, K] matrix of fp16 values (given
+ * widened to fp32, row pitch ld floats), for the norm that precedes the
+ * quantizer when the two are fused. [ATOM] Summary paragraph 2 (quantization
+ * fused into the operators around the GEMM) and Interesting ideas I2; the
+ * norm itself (mean square, eps, reciprocal square root) is the standard
+ * RMSNorm of the Llama models the pages evaluate.
+ * Readings (the pages give no arithmetic for the norm):
+ *   N1 the sum of squares is exact: every x^2 * 2^48 is an integer below
+ *      2^80 for fp16 x, so the sum of up to 2^15 of them is an integer below
+ *      2^95, held in 128 bits;
+ *   N2 rstd = fl32(1 / sqrt(fl64(fl64(S) / K) + eps)), each step one correctly
+ *      rounded IEEE binary64 operation (S rounded to binary64 once);
+ *   N3 a row whose mean square plus eps is zero (all zeros, eps = 0) has
+ *      rstd = 0, so it normalizes to zeros.
+ * Returns 0, or -1 for K <= 0 or K > 2^15 or eps negative or not finite. */
+int w4o_rms_rstd_rows(const float *X, int64_t rows, int32_t K, int64_t ld, float eps,
+                      float *rstd)
+{
+    if (K <= 0 || K > 32768 || !(eps >= 0.0f) || !isfinite(eps))
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        unsigned __int128 S = 0;
+        for (int32_t j = 0; j < K; ++j) {
+            double x = (double)X[r * ld + j];
+            S += (unsigned __int128)(x * x * 0x1p48);
+        }
+        double d = (double)S * 0x1p-48;
+        double v = d / (double)K + (double)eps;
+        rstd[r] = v == 0.0 ? 0.0f : (float)(1.0 / sqrt(v));
+    }
+    return 0;
 }
 
 /* Number of INT4 scale groups per row: G = K_n / group, or 1 for one scale per
