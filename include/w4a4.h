@@ -105,6 +105,26 @@ w4a4_status w4a4_quant_reorder_act(const void *X, int64_t ldx, const int32_t *pe
                                    void *Aq4, void *Aq8, float *sa4, float *sa8,
                                    w4a4_stream stream);
 
+/* Producer fused with the RMSNorm that precedes the layer (Atom summary page,
+ * Summary paragraph 2 and Interesting ideas I2: quantization fused into the
+ * operators around the GEMM; the norm is the standard RMSNorm of the Llama
+ * models the pages evaluate). Each token row is normalized in registers and
+ * quantized as by w4a4_quant_reorder_act; the normalized row never goes to
+ * memory. The normalized value of channel c is
+ *   y_c = fp16( gamma[c] * fp16( fp32(x_c) * rstd ) )      (both roundings to nearest even)
+ *   rstd = fp32( 1 / sqrt( fp64(S) / K + eps ) )            (binary64 operations)
+ * with S = sum_c x_c^2 computed exactly (every x_c^2 is a multiple of 2^-48);
+ * rstd = 0 when the mean square plus eps is 0 (a zero row with eps = 0).
+ *   gamma device fp16 [K], original channel order (2-byte aligned)
+ *   eps   >= 0 and finite (else INVALID_ARG)
+ *   rstd  device fp32 [M] (may be NULL): the norm factor of each row
+ * Other arguments and layouts as w4a4_quant_reorder_act. The normalized row
+ * must be finite (|gamma[c]| * sqrt(K) below the fp16 range is enough). */
+w4a4_status w4a4_rmsnorm_quant_reorder_act(const void *X, int64_t ldx, const void *gamma, float eps,
+                                           const int32_t *perm, int32_t M, int32_t K, int32_t n_out,
+                                           int32_t group, void *Aq4, void *Aq8, float *sa4,
+                                           float *sa8, float *rstd, w4a4_stream stream);
+
 /* Offline weight preparation (QUIK abstract: outlier weights kept in higher
  * precision; Atom summary page: INT4 weights, 8-bit outlier channels in the
  * same reordered layout). The same quantizer applied to the N rows of W, with
@@ -179,6 +199,16 @@ w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, con
                             int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
                             int64_t ldy, void *workspace, size_t workspace_bytes,
                             w4a4_stream stream);
+
+/* The fused layer behind an RMSNorm: w4a4_rmsnorm_quant_reorder_act on X
+ * into the caller's workspace (the same size as w4a4_quant_gemm's), then
+ * w4a4_outlier_gemm, both on `stream`. gamma and eps as in
+ * w4a4_rmsnorm_quant_reorder_act. */
+w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamma, float eps,
+                                    const int32_t *perm, const void *Wq4, const void *Wq8,
+                                    const float *sw4, const float *sw8, int32_t M, int32_t N,
+                                    int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
+                                    void *workspace, size_t workspace_bytes, w4a4_stream stream);
 
 #ifdef __cplusplus
 }

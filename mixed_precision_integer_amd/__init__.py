@@ -9,7 +9,9 @@ Names follow the C ABI: ``quant_reorder_act``, ``pack_int4_weights``,
 ``w4a4_outlier_gemm`` (+ ``w4a4_outlier_gemm_i32``, the accumulator export)
 and ``quant_gemm`` map to ``w4a4_quant_reorder_act``,
 ``w4a4_pack_int4_weights``, ``w4a4_outlier_gemm`` (+ ``_i32``) and
-``w4a4_quant_gemm``.
+``w4a4_quant_gemm``; ``rmsnorm_quant_reorder_act`` and ``rmsnorm_quant_gemm``
+(the producer fused with the preceding RMSNorm) map to
+``w4a4_rmsnorm_quant_reorder_act`` and ``w4a4_rmsnorm_quant_gemm``.
 
 There is no fallback: if the library is missing or no GPU is present the
 calls raise.
@@ -33,7 +35,8 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_make_perm", "w4a4_quant_reorder_act", "w4a4_pack_int4_weights",
             "w4a4_outlier_gemm_workspace_bytes", "w4a4_outlier_gemm_kernel_name", "w4a4_outlier_gemm",
             "w4a4_outlier_gemm_i32",
-            "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm")
+            "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm",
+            "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm")
 
 
 class W4A4Error(RuntimeError):
@@ -80,6 +83,13 @@ def lib():
     L.w4a4_quant_gemm.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64,
                                   vp, sz, vp]
     L.w4a4_quant_gemm.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    L.w4a4_rmsnorm_quant_reorder_act.argtypes = [vp, i64, vp, f32, vp, i32, i32, i32, i32, vp, vp,
+                                                 vp, vp, vp, vp]
+    L.w4a4_rmsnorm_quant_reorder_act.restype = ctypes.c_int
+    L.w4a4_rmsnorm_quant_gemm.argtypes = [vp, i64, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                          i32, vp, i64, vp, sz, vp]
+    L.w4a4_rmsnorm_quant_gemm.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -189,6 +199,34 @@ def quant_reorder_act(X, perm, n_out: int, group: int) -> QuantizedOperand:
                        group)
 
 
+def _norm_args(X, gamma, eps):
+    torch = _torch()
+    _check(gamma, torch.float16, "gamma", 1)
+    if gamma.shape[0] != X.shape[1] or (gamma.numel() and gamma.stride(0) != 1):
+        raise ValueError("gamma must be a contiguous [K] vector")
+    return gamma.data_ptr(), float(eps)
+
+
+def rmsnorm_quant_reorder_act(X, gamma, eps: float, perm, n_out: int, group: int,
+                              want_rstd: bool = False):
+    """Producer fused with the preceding RMSNorm: normalize every token row
+    (weight gamma [K] fp16, original channel order), then reorder and quantize
+    it as quant_reorder_act does. Returns the operand, or (operand, rstd fp32
+    [M]) with want_rstd."""
+    torch = _torch()
+    _check(X, torch.float16, "X", 2)
+    _check(perm, torch.int32, "perm", 1)
+    g, e = _norm_args(X, gamma, eps)
+    M, K = X.shape
+    op = alloc_operand(M, K, n_out, group, X.device)
+    rstd = torch.empty((M,), dtype=torch.float32, device=X.device) if want_rstd else None
+    _ok(lib().w4a4_rmsnorm_quant_reorder_act(X.data_ptr(), X.stride(0) if M else K, g, e,
+                                             perm.data_ptr(), M, K, n_out, group, _nz(op.q4),
+                                             _nz(op.q8), _nz(op.s4), _nz(op.s8), _nz(rstd),
+                                             _stream()), "w4a4_rmsnorm_quant_reorder_act")
+    return (op, rstd) if want_rstd else op
+
+
 def pack_int4_weights(W, perm, n_out: int, group: int) -> QuantizedOperand:
     """Offline weight preparation with the same quantizer (rows = output channels)."""
     return _quant_rows(lib().w4a4_pack_int4_weights, "w4a4_pack_int4_weights", W, perm, n_out,
@@ -275,6 +313,31 @@ def quant_gemm(X, perm, w: QuantizedOperand, out=None, workspace=None):
     return out
 
 
+def rmsnorm_quant_gemm(X, gamma, eps: float, perm, w: QuantizedOperand, out=None, workspace=None):
+    """The fused layer behind an RMSNorm: norm + producer, then the GEMM."""
+    torch = _torch()
+    _check(X, torch.float16, "X", 2)
+    _check(perm, torch.int32, "perm", 1)
+    g, e = _norm_args(X, gamma, eps)
+    M, K = X.shape
+    N = w.s8.shape[0]
+    if K != w.K:
+        raise ValueError("X and weights disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(out, torch.float16, "out", 2)
+    need = quant_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check(workspace, torch.uint8, "workspace", 1)
+    _ok(lib().w4a4_rmsnorm_quant_gemm(X.data_ptr(), X.stride(0) if M else K, g, e, perm.data_ptr(),
+                                      _nz(w.q4), _nz(w.q8), _nz(w.s4), _nz(w.s8), M, N, K,
+                                      w.n_out, w.group, out.data_ptr(),
+                                      out.stride(0) if M else N, workspace.data_ptr(),
+                                      workspace.numel(), _stream()), "w4a4_rmsnorm_quant_gemm")
+    return out
+
+
 class W4A4Linear:
     """A linear layer y = x W^T with W held as packed INT4 + INT8 outlier columns."""
 
@@ -301,11 +364,13 @@ class LayerPlan:
 
     ``fused()`` is ``w4a4_quant_gemm``; ``produce()`` and ``gemm()`` are its two
     halves (``w4a4_quant_reorder_act`` into a pre-allocated operand, then
-    ``w4a4_outlier_gemm``), which launch the same kernels. Each call is one
-    ctypes call on the stream that was current when the plan was made.
+    ``w4a4_outlier_gemm``), which launch the same kernels. With ``norm=(gamma,
+    eps)`` the producer is the RMSNorm-fused one (``w4a4_rmsnorm_quant_*``).
+    Each call is one ctypes call on the stream that was current when the plan
+    was made.
     """
 
-    def __init__(self, X, perm, w: QuantizedOperand, out=None):
+    def __init__(self, X, perm, w: QuantizedOperand, out=None, norm=None):
         torch = _torch()
         _check(X, torch.float16, "X", 2)
         _check(perm, torch.int32, "perm", 1)
@@ -318,21 +383,30 @@ class LayerPlan:
         self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=X.device)
         gws = outlier_gemm_workspace_bytes(M, N, K, w.n_out, w.group)
         self.gws = torch.zeros(gws, dtype=torch.uint8, device=X.device) if gws else None
-        self._keep = (X, perm, w)
+        self._keep = (X, perm, w, norm)
         L = lib()
-        self._q, self._g, self._f = (L.w4a4_quant_reorder_act, L.w4a4_outlier_gemm,
-                                     L.w4a4_quant_gemm)
-        self._qa = _quant_args(X, perm, self.a)
+        self._g = L.w4a4_outlier_gemm
         self._ga = _gemm_args(self.a, w, self.out, self.gws)
-        self._fa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.q4), _nz(w.q8),
-                    _nz(w.s4), _nz(w.s8), M, N, K, w.n_out, w.group, self.out.data_ptr(),
-                    self.out.stride(0) if M else N, self.ws.data_ptr(), self.ws.numel(),
-                    _stream())
+        qa = _quant_args(X, perm, self.a)
+        fa = (perm.data_ptr(), _nz(w.q4), _nz(w.q8), _nz(w.s4), _nz(w.s8), M, N, K, w.n_out,
+              w.group, self.out.data_ptr(), self.out.stride(0) if M else N, self.ws.data_ptr(),
+              self.ws.numel(), _stream())
+        xa = (X.data_ptr(), X.stride(0) if M else K)
+        if norm is None:
+            self._qname, self._fname = "w4a4_quant_reorder_act", "w4a4_quant_gemm"
+            self._q, self._f = L.w4a4_quant_reorder_act, L.w4a4_quant_gemm
+            self._qa, self._fa = qa, (*xa, *fa)
+        else:
+            g, e = _norm_args(X, *norm)
+            self._qname, self._fname = "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm"
+            self._q, self._f = L.w4a4_rmsnorm_quant_reorder_act, L.w4a4_rmsnorm_quant_gemm
+            self._qa = (*xa, g, e, *qa[2:11], None, qa[11])
+            self._fa = (*xa, g, e, *fa)
 
     def produce(self):
         st = self._q(*self._qa)
         if st:
-            raise W4A4Error(st, "w4a4_quant_reorder_act")
+            raise W4A4Error(st, self._qname)
 
     def gemm(self):
         st = self._g(*self._ga)
@@ -342,5 +416,5 @@ class LayerPlan:
     def fused(self):
         st = self._f(*self._fa)
         if st:
-            raise W4A4Error(st, "w4a4_quant_gemm")
+            raise W4A4Error(st, self._fname)
         return self.out

@@ -32,9 +32,16 @@ w4a4_status check_shape(int32_t rows, int32_t K, int32_t n_out, int32_t group) {
     return W4A4_OK;
 }
 
+// Optional RMSNorm in front of the quantizer (gamma == nullptr: none).
+struct NormArgs {
+    const void *gamma;
+    float eps;
+    float *rstd;
+};
+
 w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t rows,
                        int32_t K, int32_t n_out, int32_t group, void *q4, void *q8, float *s4,
-                       float *s8, w4a4_stream stream) {
+                       float *s8, w4a4_stream stream, const NormArgs &norm = NormArgs{nullptr, 0.0f, nullptr}) {
     w4a4_status st = check_shape(rows, K, n_out, group);
     if (st != W4A4_OK)
         return st;
@@ -50,6 +57,8 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
         return W4A4_ERR_INVALID_ARG;
     if (!aligned(src, 16) || ld % 8 != 0 || !aligned(perm, 16) || (q4 && !aligned(q4, 16)) ||
         (q8 && !aligned(q8, 16)) || (s4 && !aligned(s4, 4)) || (s8 && !aligned(s8, 4)))
+        return W4A4_ERR_ALIGNMENT;
+    if (norm.gamma && (!aligned(norm.gamma, 2) || (norm.rstd && !aligned(norm.rstd, 4))))
         return W4A4_ERR_ALIGNMENT;
     w4a4::QuantArgs a;
     a.src = static_cast<const _Float16 *>(src);
@@ -67,11 +76,23 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
     a.s8 = s8;
     a.pitch4 = w4a4_pitch4_bytes(K_n);
     a.pitch8 = n_out > 0 ? w4a4_pitch8_bytes(n_out) : 0;
+    a.gamma = static_cast<const _Float16 *>(norm.gamma);
+    a.eps = norm.eps;
+    a.rstd = norm.gamma ? norm.rstd : nullptr;
     // the permutation and two row buffers live in LDS
     if (K > w4a4::quant_rows_max_k())
         return W4A4_ERR_UNSUPPORTED;
     if (w4a4::launch_quant_rows(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+// Arguments of the norm that are checked before anything else.
+w4a4_status norm_check(int32_t rows, const void *gamma, float eps) {
+    if (!(eps >= 0.0f) || eps > 3.4028235e38f)    // negative, NaN or infinite
+        return W4A4_ERR_INVALID_ARG;
+    if (rows > 0 && !gamma)
+        return W4A4_ERR_INVALID_ARG;
     return W4A4_OK;
 }
 
@@ -168,6 +189,17 @@ w4a4_status w4a4_quant_reorder_act(const void *X, int64_t ldx, const int32_t *pe
     return quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream);
 }
 
+w4a4_status w4a4_rmsnorm_quant_reorder_act(const void *X, int64_t ldx, const void *gamma, float eps,
+                                           const int32_t *perm, int32_t M, int32_t K, int32_t n_out,
+                                           int32_t group, void *Aq4, void *Aq8, float *sa4, float *sa8,
+                                           float *rstd, w4a4_stream stream) {
+    w4a4_status st = norm_check(M, gamma, eps);
+    if (st != W4A4_OK)
+        return st;
+    return quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream,
+                      NormArgs{gamma, eps, rstd});
+}
+
 w4a4_status w4a4_pack_int4_weights(const void *W, int64_t ldw, const int32_t *perm, int32_t N,
                                    int32_t K, int32_t n_out, int32_t group, void *Wq4, void *Wq8,
                                    float *sw4, float *sw8, w4a4_stream stream) {
@@ -262,11 +294,13 @@ size_t w4a4_quant_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t 
     return off[4] + w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group);
 }
 
-w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
-                            const void *Wq8, const float *sw4, const float *sw8, int32_t M,
-                            int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
-                            int64_t ldy, void *workspace, size_t workspace_bytes,
-                            w4a4_stream stream) {
+}  // extern "C"
+
+static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
+                              const void *Wq8, const float *sw4, const float *sw8, int32_t M,
+                              int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                              int64_t ldy, void *workspace, size_t workspace_bytes,
+                              w4a4_stream stream, const NormArgs &norm) {
     if (N < 0)
         return W4A4_ERR_INVALID_ARG;
     w4a4_status st = check_shape(M, K, n_out, group);
@@ -294,11 +328,34 @@ w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, con
     void *Aq8 = n_out > 0 ? ws + off[1] : nullptr;
     float *sa4 = K_n > 0 ? reinterpret_cast<float *>(ws + off[2]) : nullptr;
     float *sa8 = reinterpret_cast<float *>(ws + off[3]);
-    st = quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream);
+    st = quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream, norm);
     if (st != W4A4_OK)
         return st;
     return w4a4_outlier_gemm(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy,
                              ws + off[4], workspace_bytes - off[4], stream);
+}
+
+extern "C" {
+
+w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
+                            const void *Wq8, const float *sw4, const float *sw8, int32_t M,
+                            int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                            int64_t ldy, void *workspace, size_t workspace_bytes,
+                            w4a4_stream stream) {
+    return quant_gemm(X, ldx, perm, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, workspace,
+                      workspace_bytes, stream, NormArgs{nullptr, 0.0f, nullptr});
+}
+
+w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamma, float eps,
+                                    const int32_t *perm, const void *Wq4, const void *Wq8,
+                                    const float *sw4, const float *sw8, int32_t M, int32_t N,
+                                    int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
+                                    void *workspace, size_t workspace_bytes, w4a4_stream stream) {
+    w4a4_status st = norm_check(M, gamma, eps);
+    if (st != W4A4_OK)
+        return st;
+    return quant_gemm(X, ldx, perm, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, workspace,
+                      workspace_bytes, stream, NormArgs{gamma, eps, nullptr});
 }
 
 }  // extern "C"

@@ -76,10 +76,42 @@ __device__ __forceinline__ float exact_quotient(float x, float s, float r) {
     return __builtin_fmaf(e, r, q0);
 }
 
-__device__ __forceinline__ float recip_or_zero(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
-
 __device__ __forceinline__ _Float16 lo_half(uint32_t p) { return __builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFF)); }
 __device__ __forceinline__ _Float16 hi_half(uint32_t p) { return __builtin_bit_cast(_Float16, (uint16_t)(p >> 16)); }
+
+__device__ __forceinline__ float recip_or_zero(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
+
+// x^2 * 2^48 of an fp16 value, exactly, as an integer below 2^80: with
+// x = Mx * 2^(sh - 24) (Mx the significand with its hidden bit, sh = 0 for
+// subnormals), x^2 * 2^48 = Mx^2 * 2^(2 sh).
+__device__ __forceinline__ unsigned __int128 square_q48(uint32_t h) {
+    const uint32_t e = (h >> 10) & 31, m = h & 1023;
+    const uint32_t mx = e ? (m | 1024u) : m, sh = e ? e - 1 : 0;
+    return (unsigned __int128)(mx * mx) << (2 * sh);
+}
+
+__device__ __forceinline__ unsigned __int128 wave_sum_u128(unsigned __int128 s) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w[k] = (uint32_t)__shfl_xor((int)(uint32_t)(s >> (32 * k)), off, 64);
+        s += (unsigned __int128)w[0] | ((unsigned __int128)w[1] << 32) | ((unsigned __int128)w[2] << 64) |
+             ((unsigned __int128)w[3] << 96);
+    }
+    return s;
+}
+
+// RMSNorm of two packed fp16 values: fl16(gamma * fl16(fl32(x * rstd))). The
+// product of two fp16 values is exact in fp32, so the packed fp16 multiply
+// rounds it once, like the fp16 model does.
+__device__ __forceinline__ uint32_t norm_pair(uint32_t xv, uint32_t g, float rstd) {
+#pragma clang fp contract(off)
+    const float p0 = (float)lo_half(xv) * rstd, p1 = (float)hi_half(xv) * rstd;
+    const half2 h = {(_Float16)p0, (_Float16)p1};
+    return __builtin_bit_cast(uint32_t, h * __builtin_bit_cast(half2, g));
+}
 
 // s_waitcnt immediates (gfx9 encoding): all counters zero, or LDS only.
 constexpr int kWaitAll = 0;
@@ -104,13 +136,25 @@ struct RowLds {
     unsigned char x[2][XB];
     unsigned gmax[2][GMAX];
     float red_h[2][THREADS / 64], red_t[2][THREADS / 64];
+    uint32_t red_q[2][THREADS / 64][4];   // sums of squares per wave (RMSNorm)
 };
 
 // WIDE_TAIL: the outlier tail may need more than one 4-channel word per lane.
 // Up to 512 lanes a workgroup is register-limited: 64 VGPRs (eight waves per
 // SIMD) keep every workgroup the occupancy query counts resident at once.
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL ? 8 : 4)))
+//
+// NORM: the row is RMS-normalized first (the norm that precedes the layer,
+// fused so that its fp16 output never goes to memory). The lane's gathered
+// values cover every channel once, so the sum of squares comes from them:
+// exact, as a 128-bit integer of x^2 * 2^48 terms (below 2^95 for K <= 2^15),
+// reduced over the wave by shuffles and over the workgroup through LDS (a
+// third barrier per row). Every lane then derives
+// rstd = fl32(1 / sqrt(fl64(fl64(S) / K) + eps)) with correctly rounded binary64
+// operations, normalizes its values in registers and only then takes the
+// absmax. The norm weights of the lane's channels are gathered once per
+// workgroup, like the permutation.
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL && !NORM ? 8 : 4)))
 void quant_rows_kernel(QuantArgs a) {
     using L = RowLds<KMAX, THREADS>;
     constexpr int NW = THREADS / 64;
@@ -195,6 +239,25 @@ void quant_rows_kernel(QuantArgs a) {
             }
         }
     }
+    // norm weights of the lane's channels (indices clamped into the row)
+    uint32_t gv[NORM ? UMAX : 1][4], gt[NORM ? TW : 1][2];
+    if constexpr (NORM) {
+        const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.gamma);
+        const uint32_t last = (uint32_t)K - 1;
+        auto g2 = [&](uint32_t p) {
+            return (uint32_t)gp[min(p & 0xFFFF, last)] | ((uint32_t)gp[min(p >> 16, last)] << 16);
+        };
+#pragma unroll
+        for (int i = 0; i < UMAX; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                gv[i][k] = g2(pv[i][k]);
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                gt[i][k] = g2(pt[i][k]);
+    }
     if (GROUPED)
         for (int t = tid; t < 2 * L::GMAX; t += THREADS)
             (&sm.gmax[0][0])[t] = 0u;
@@ -223,6 +286,31 @@ void quant_rows_kernel(QuantArgs a) {
         // (2) gather head units and tail words into registers; absmax (packed fp16)
         uint32_t v[UMAX][4], tv[TW][2];
         float hmax = 0.0f, tmax = 0.0f;
+        auto head_absmax = [&](int i) {
+            const int u = i * THREADS + tid;
+            const int j0 = u * 8;
+            half2 m2 = {(_Float16)0, (_Float16)0};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2, v[i][k] & 0x7FFF7FFFu));
+            float m = fmaxf((float)m2.x, (float)m2.y);
+            if (GROUPED) {
+                if (i * THREADS < U) {             // uniform: every lane of the wave takes part
+                    m = seg16_max(m);
+                    if ((lane & 15) == 0 && u < U)
+                        atomicMax(&gm[j0 / a.group], __float_as_uint(m));
+                }
+            } else {
+                hmax = fmaxf(hmax, m);
+            }
+        };
+        auto tail_absmax = [&](int i) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const half2 h = __builtin_bit_cast(half2, tv[i][k] & 0x7FFF7FFFu);
+                tmax = fmaxf(tmax, fmaxf((float)h.x, (float)h.y));
+            }
+        };
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
             const int u = i * THREADS + tid;
@@ -240,20 +328,8 @@ void quant_rows_kernel(QuantArgs a) {
                     v[i][k] = lo | (hi << 16);
                 }
             }
-            half2 m2 = {(_Float16)0, (_Float16)0};
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(half2, v[i][k] & 0x7FFF7FFFu));
-            float m = fmaxf((float)m2.x, (float)m2.y);
-            if (GROUPED) {
-                if (i * THREADS < U) {             // uniform: every lane of the wave takes part
-                    m = seg16_max(m);
-                    if ((lane & 15) == 0 && u < U)
-                        atomicMax(&gm[j0 / a.group], __float_as_uint(m));
-                }
-            } else {
-                hmax = fmaxf(hmax, m);
-            }
+            if (!NORM)
+                head_absmax(i);
         }
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
@@ -264,8 +340,52 @@ void quant_rows_kernel(QuantArgs a) {
                 const uint32_t lo = j < K ? xs[pt[i][k] & 0xFFFF] : 0u;
                 const uint32_t hi = j + 1 < K ? xs[pt[i][k] >> 16] : 0u;
                 tv[i][k] = lo | (hi << 16);
-                const half2 h = __builtin_bit_cast(half2, tv[i][k] & 0x7FFF7FFFu);
-                tmax = fmaxf(tmax, fmaxf((float)h.x, (float)h.y));
+            }
+            if (!NORM)
+                tail_absmax(i);
+        }
+        if constexpr (NORM) {
+            // (2n) exact sum of squares (zeros past the row's end add nothing),
+            // rstd, then the normalized values and their absmax
+            unsigned __int128 ss = 0;
+#pragma unroll
+            for (int i = 0; i < UMAX; ++i)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    ss += square_q48(v[i][k] & 0xFFFF) + square_q48(v[i][k] >> 16);
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    ss += square_q48(tv[i][k] & 0xFFFF) + square_q48(tv[i][k] >> 16);
+            ss = wave_sum_u128(ss);
+            if (lane == 0)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    sm.red_q[buf][wave][k] = (uint32_t)(ss >> (32 * k));
+            lds_barrier();
+            unsigned __int128 S = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                S += (unsigned __int128)sm.red_q[buf][w][0] | ((unsigned __int128)sm.red_q[buf][w][1] << 32) |
+                     ((unsigned __int128)sm.red_q[buf][w][2] << 64) | ((unsigned __int128)sm.red_q[buf][w][3] << 96);
+            const double var = (double)S * 0x1p-48 / (double)K + (double)a.eps;
+            const float rstd = var == 0.0 ? 0.0f : (float)(1.0 / __builtin_sqrt(var));
+            if (tid == 0 && a.rstd)
+                a.rstd[row] = rstd;
+#pragma unroll
+            for (int i = 0; i < UMAX; ++i) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    v[i][k] = norm_pair(v[i][k], gv[i][k], rstd);
+                head_absmax(i);
+            }
+#pragma unroll
+            for (int i = 0; i < TW; ++i) {
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    tv[i][k] = norm_pair(tv[i][k], gt[i][k], rstd);
+                tail_absmax(i);
             }
         }
         if (!GROUPED)
@@ -524,7 +644,7 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
 
 // Resident workgroups of one instantiation on the current device, queried on
 // first use (a launch then costs no runtime queries).
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL>
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM>
 long resident_slots() {
     static std::atomic<long> cached[kMaxDevices];
     int dev = 0;
@@ -538,7 +658,7 @@ long resident_slots() {
     int cus = 256, per_cu = 1;
     if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM>,
                                                      THREADS, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
     const long slots = (long)cus * per_cu;
@@ -547,28 +667,28 @@ long resident_slots() {
     return slots;
 }
 
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL>
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM>
 hipError_t launch_tail(const QuantArgs &a, hipStream_t stream) {
-    const int grid = (int)std::min<long>(a.rows, resident_slots<KMAX, THREADS, GROUPED, WIDE_TAIL>());
-    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL>), dim3(grid), dim3(THREADS), 0,
-                       stream, a);
+    const int grid = (int)std::min<long>(a.rows, resident_slots<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM>());
+    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM>), dim3(grid), dim3(THREADS),
+                       0, stream, a);
     return hipGetLastError();
 }
 
-template <int KMAX, int THREADS, bool GROUPED>
+template <int KMAX, int THREADS, bool GROUPED, bool NORM>
 hipError_t launch(const QuantArgs &a, hipStream_t stream) {
     if (a.pitch8 / 4 > THREADS)                   // more than one tail word per lane
-        return launch_tail<KMAX, THREADS, GROUPED, true>(a, stream);
-    return launch_tail<KMAX, THREADS, GROUPED, false>(a, stream);
+        return launch_tail<KMAX, THREADS, GROUPED, true, NORM>(a, stream);
+    return launch_tail<KMAX, THREADS, GROUPED, false, NORM>(a, stream);
 }
 
 // Row-length buckets: (longest row, lanes per workgroup).
-template <bool GROUPED>
+template <bool GROUPED, bool NORM>
 hipError_t launch_grouping(const QuantArgs &a, hipStream_t stream) {
-    if (a.K <= 4096) return launch<4096, 256, GROUPED>(a, stream);
-    if (a.K <= 8192) return launch<8192, 512, GROUPED>(a, stream);
-    if (a.K <= 16384) return launch<16384, 1024, GROUPED>(a, stream);
-    if (a.K <= 24576) return launch<24576, 1024, GROUPED>(a, stream);
+    if (a.K <= 4096) return launch<4096, 256, GROUPED, NORM>(a, stream);
+    if (a.K <= 8192) return launch<8192, 512, GROUPED, NORM>(a, stream);
+    if (a.K <= 16384) return launch<16384, 1024, GROUPED, NORM>(a, stream);
+    if (a.K <= 24576) return launch<24576, 1024, GROUPED, NORM>(a, stream);
     return hipErrorInvalidValue;
 }
 
@@ -596,6 +716,9 @@ int quant_rows_max_k() { return 24576; }
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream) {
     if (a.rows == 0)
         return hipSuccess;
+    if (a.gamma)                                  // the norm needs whole rows: row kernel
+        return a.group > 0 ? quant_impl::launch_grouping<true, true>(a, stream)
+                           : quant_impl::launch_grouping<false, true>(a, stream);
     if (a.rows <= quant_impl::kGroupMaxRows &&
         (a.group == 128 || a.group == 256 || a.group == 512 || a.group == 64 * 8 * quant_impl::kGroupUPL)) {
         const int tw = (int)((a.pitch8 / 4 + 63) / 64);
@@ -603,8 +726,8 @@ hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream) {
         if (tw <= 2) return quant_impl::launch_group<2>(a, stream);
         if (tw <= 4) return quant_impl::launch_group<4>(a, stream);
     }
-    return a.group > 0 ? quant_impl::launch_grouping<true>(a, stream)
-                       : quant_impl::launch_grouping<false>(a, stream);
+    return a.group > 0 ? quant_impl::launch_grouping<true, false>(a, stream)
+                       : quant_impl::launch_grouping<false, false>(a, stream);
 }
 
 }  // namespace w4a4

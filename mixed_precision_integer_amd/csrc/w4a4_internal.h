@@ -57,6 +57,10 @@ struct QuantArgs {
     float *s4;            // [rows, G]
     float *s8;            // [rows] or nullptr
     int64_t pitch4, pitch8;
+    // RMSNorm in front of the quantizer (nullptr gamma: none)
+    const _Float16 *gamma;  // [K] norm weight, original channel order
+    float eps;
+    float *rstd;          // [rows] norm factor per row, or nullptr
 };
 
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream);

@@ -12,6 +12,9 @@ Recipe (numpy PCG64 ``default_rng(seed)``), in this draw order:
   2. X [M, K] in float32 from the config's distribution, outlier columns
      multiplied by the config's factor, then cast to fp16 (round to nearest);
   3. W [N, K] in float32 ~ N(0, w_std), cast to fp16.
+For the producer fused with the preceding RMSNorm, X is the norm's input and
+the norm weight gamma [K] ~ 1 + N(0, 0.1) in fp16 comes from a generator of
+its own (``draw_norm_weight``).
 """
 from __future__ import annotations
 
@@ -75,6 +78,13 @@ def draw(M: int, N: int, K: int, n_out: int, seed: int, x_dist: str = "normal",
     X = X.astype(np.float16)
     W = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(w_std)).astype(np.float16)
     return X, W, outliers
+
+
+def draw_norm_weight(K: int, seed: int, std: float = 0.1):
+    """RMSNorm weight gamma fp16 [K] ~ 1 + N(0, std), from its own generator
+    (seed sequence [seed, 1]) so that the draws above are unchanged."""
+    rng = np.random.default_rng([seed, 1])
+    return (1.0 + std * rng.standard_normal(K, dtype=np.float32)).astype(np.float16)
 
 
 def draw_workload(w: Workload, M: int | None = None):

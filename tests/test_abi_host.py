@@ -115,6 +115,39 @@ def test_quant_rejects(kw, code):
     assert quant(**kw) == code
 
 
+def norm_quant(**kw):
+    args = dict(X=FAKE, ld=256, gamma=FAKE, eps=1e-6, perm=FAKE, rows=4, K=256, n_out=16, group=0,
+                q4=FAKE, q8=FAKE, s4=FAKE, s8=FAKE, rstd=None)
+    args.update(kw)
+    return w4.lib().w4a4_rmsnorm_quant_reorder_act(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gamma=None), INVALID), (dict(eps=-1e-6), INVALID), (dict(eps=float("nan")), INVALID),
+    (dict(eps=float("inf")), INVALID), (dict(gamma=FAKE + 1), ALIGN), (dict(rstd=FAKE + 2), ALIGN),
+    (dict(K=0), INVALID), (dict(ld=100), INVALID), (dict(q4=None), INVALID),
+    (dict(X=FAKE + 2), ALIGN), (dict(K=24584, ld=24584, n_out=0), UNSUPPORTED),
+])
+def test_norm_quant_rejects(kw, code):
+    assert norm_quant(**kw) == code
+
+
+def test_norm_quant_empty_is_ok():
+    assert norm_quant(rows=0, X=None, gamma=None, perm=None, q4=None, q8=None, s4=None,
+                      s8=None) == OK
+
+
+def test_norm_quant_gemm_rejects():
+    L = w4.lib()
+    need = w4.quant_gemm_workspace_bytes(16, 256, 256, 16, 0)
+    head = [FAKE, 256]
+    tail = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, 256, 256, 16, 0, FAKE, 256]
+    assert L.w4a4_rmsnorm_quant_gemm(*head, None, 1e-6, *tail, FAKE, need, None) == INVALID
+    assert L.w4a4_rmsnorm_quant_gemm(*head, FAKE, -1.0, *tail, FAKE, need, None) == INVALID
+    assert L.w4a4_rmsnorm_quant_gemm(*head, FAKE, 1e-6, *tail, FAKE, need - 1, None) == WS
+    assert L.w4a4_rmsnorm_quant_gemm(*head, FAKE, 1e-6, *tail, FAKE + 16, need, None) == ALIGN
+
+
 def test_quant_empty_is_ok():
     assert quant(rows=0, X=None, perm=None, q4=None, q8=None, s4=None, s8=None) == OK
 
