@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the fused W4A4 + INT8-outlier linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M] [--norm]
 
 One step is one pass of the layer's run-time path over one batch: the
 activation producer (reorder + INT4/INT8 quantize, ``w4a4_quant_reorder_act``)
 then the mixed-precision GEMM with its fp32 epilogue (``w4a4_outlier_gemm``);
 together they are exactly what ``w4a4_quant_gemm`` launches. Weights are
-quantized and packed once before timing, as the layer does offline.
+quantized and packed once before timing, as the layer does offline. With
+``--norm`` the producer is the one fused with the preceding RMSNorm
+(``w4a4_rmsnorm_quant_reorder_act``, gamma ~ 1 + N(0, 0.1), eps = 1e-6), and
+the step is what ``w4a4_rmsnorm_quant_gemm`` launches.
 
 Inputs are seeded synthetic tensors already resident in HBM. Buffer sets
 (X, packed W, quantized activations, Y) are rotated so that the working set
@@ -46,15 +49,16 @@ WORKLOADS = {"tiny": wl.TINY, "qproj": wl.QPROJ_7B, "upproj": wl.UPPROJ_7B,
              "decode": wl.DECODE_65B, "downproj": wl.DOWNPROJ_65B}
 
 
-def work_counts(w, M):
-    """Algorithmic ops and bytes of one layer call (zero padding not counted)."""
+def work_counts(w, M, norm=False):
+    """Algorithmic ops and bytes of one layer call (zero padding not counted);
+    the norm-fused producer also reads the K fp16 norm weights."""
     N, K, n_out, K_n = w.N, w.K, w.n_out, w.K_n
     G = (K_n // w.group if w.group else 1) if K_n else 0
     ops = 2 * M * N * K
     w_bytes = N * K_n / 2 + N * n_out + 4 * N * G + 4 * N
     a_bytes = M * K_n / 2 + M * n_out + 4 * M * G + 4 * M
     gemm_bytes = w_bytes + a_bytes + 2 * M * N
-    producer_bytes = 2 * M * K + a_bytes
+    producer_bytes = 2 * M * K + a_bytes + (2 * K if norm else 0)
     return ops, gemm_bytes, producer_bytes
 
 
@@ -72,9 +76,10 @@ def traffic_record(workload_name, M):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, X, W, outliers, budget_s):
-    """The CPU oracle on the host: producer + integer GEMM + fp64 dequant for a
-    row sample of X against all N output channels (weights pre-quantized)."""
+def cpu_baseline(w, X, W, outliers, budget_s, gamma=None, eps=0.0):
+    """The CPU oracle on the host: producer (after the RMSNorm when gamma is
+    given) + integer GEMM + fp64 dequant for a row sample of X against all N
+    output channels (weights pre-quantized)."""
     import oracle
     perm = oracle.make_perm(w.K, outliers)
     qw = oracle.quantize_rows(W, perm, w.n_out, w.group)
@@ -82,7 +87,10 @@ def cpu_baseline(w, X, W, outliers, budget_s):
 
     def run(rows):
         t0 = time.perf_counter()
-        qa = oracle.quantize_rows(X[:rows], perm, w.n_out, w.group)
+        if gamma is None:
+            qa = oracle.quantize_rows(X[:rows], perm, w.n_out, w.group)
+        else:
+            qa = oracle.rmsnorm_quantize_rows(X[:rows], gamma, eps, perm, w.n_out, w.group)
         mm = np.repeat(np.arange(rows, dtype=np.int32), w.N)
         oracle.linear_at(qa, qw, w.group, mm, np.tile(nn, rows))
         return time.perf_counter() - t0
@@ -97,7 +105,8 @@ def cpu_baseline(w, X, W, outliers, budget_s):
         "unit": "TOPS",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": (f"{rows} of {M} token rows x all {w.N} output channels: producer, integer "
+        "sample": (f"{rows} of {M} token rows x all {w.N} output channels: "
+                   f"{'RMSNorm + ' if gamma is not None else ''}producer, integer "
                    f"GEMM and fp64 dequant (weights quantized beforehand); {t:.1f} s"),
     }
 
@@ -134,6 +143,8 @@ def main():
                     help="M,N,K,n_out,group: a synthetic shape instead of a named workload")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--norm", action="store_true",
+                    help="producer fused with the preceding RMSNorm (eps 1e-6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, time a plain device-to-device copy of this many "
                          "MiB (reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -174,7 +185,10 @@ def main():
     one_set = (Xd.numel() * 2 + M * w.N * 2 + sum(t.numel() * t.element_size()
                                                    for t in wq[:4] if t is not None) * 2)
     n_sets = max(2, math.ceil(ROTATE_BYTES / one_set) + 1)
-    plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq)) for _ in range(n_sets)]
+    norm = None
+    if args.norm:
+        norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
+    plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq), norm=norm) for _ in range(n_sets)]
 
     for i in range(args.warmup):
         p = plans[i % n_sets]
@@ -211,7 +225,7 @@ def main():
         p.gemm()
     torch.cuda.synchronize()
     prod_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
-    ops, gemm_bytes, prod_bytes = work_counts(w, M)
+    ops, gemm_bytes, prod_bytes = work_counts(w, M, args.norm)
     value = ops / (ms_step * 1e-3) / 1e12
 
     mem_bound = ops / gemm_bytes < PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -228,7 +242,10 @@ def main():
 
     # the result is checked against a fused call (same kernels, same bits)
     yf = torch.empty_like(plans[0].out)
-    w4.quant_gemm(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
+    if norm is None:
+        w4.quant_gemm(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
+    else:
+        w4.rmsnorm_quant_gemm(plans[0]._keep[0], norm[0], norm[1], perm, plans[0]._keep[2], out=yf)
     torch.cuda.synchronize()
     if not torch.equal(yf, plans[0].out):
         raise SystemExit("fused call and producer + GEMM disagree")
@@ -247,7 +264,8 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": w.N, "K": w.K, "n_out": w.n_out,
-                   "group": w.group, "buffer_sets": n_sets},
+                   "group": w.group, "buffer_sets": n_sets,
+                   "producer": "rmsnorm_fused" if args.norm else "plain"},
         "roofline": roof,
         "kernels": {
             "producer_us": prod_ms * 1e3,
@@ -259,7 +277,8 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, X, W, outliers, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, X, W, outliers, args.cpu_budget,
+                                           *((norm[0].cpu().numpy(), norm[1]) if norm else ()))
     print(json.dumps(out), flush=True)
 
 
