@@ -171,6 +171,32 @@ def rmsnorm_quantize_rows(X, gamma, eps: float, perm, n_out: int, group: int):
     return quantize_rows(rmsnorm(X, gamma, eps), perm, n_out, group)
 
 
+def channel_absmax(Xcal) -> np.ndarray:
+    """Per-channel max |x| over the rows of a calibration batch Xcal [R, K]
+    (fp16): fp16 [K], exact (0 for R == 0)."""
+    X = np.asarray(Xcal)
+    if X.dtype != np.float16 or X.ndim != 2:
+        raise TypeError("channel_absmax takes an fp16 [R, K] batch")
+    if X.shape[0] == 0:
+        return np.zeros(X.shape[1], np.float16)
+    return np.abs(X).max(axis=0)
+
+
+def select_outliers(Xcal, n_out: int) -> np.ndarray:
+    """Offline outlier-channel selection (reading S1): the n_out channels with
+    the largest calibration absmax, ties to the lower channel index, returned
+    in ascending channel order (int32 [n_out]). The pages keep a small set of
+    outlier channels in 8 bits (Atom summary page, Summary paragraph 2) but
+    give no rule for choosing them; the absmax is the statistic the quantizer
+    itself scales by."""
+    a = channel_absmax(Xcal).astype(np.float32)
+    K = a.size
+    if not 0 <= n_out <= K:
+        raise ValueError("n_out must be in [0, K]")
+    order = np.lexsort((np.arange(K), -a))      # by score descending, then index ascending
+    return np.sort(order[:n_out]).astype(np.int32)
+
+
 def pack_nibbles(q4, pitch: int) -> np.ndarray:
     """Pack INT4 codes two per byte, low nibble first, zero padded to pitch."""
     q4 = np.ascontiguousarray(q4, dtype=np.int8)
