@@ -210,6 +210,35 @@ w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamm
                                     int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
                                     void *workspace, size_t workspace_bytes, w4a4_stream stream);
 
+/* Bytes of device workspace w4a4_select_outliers needs (0 for arguments it
+ * would reject). A pure function of rows and K. */
+size_t w4a4_select_outliers_workspace_bytes(int32_t rows, int32_t K);
+
+/* Offline outlier-channel selection, the step before w4a4_make_perm (the
+ * Atom summary page keeps a small set of outlier channels in 8 bits after
+ * reordering them to a contiguous tail, Summary paragraph 2 and Interesting
+ * ideas I1; neither page gives the rule that chooses them). Score of channel
+ * c = max over the rows r of |Xcal[r, c]| (exact); the n_out channels with
+ * the highest scores are selected, a tie going to the lower channel index.
+ *   Xcal        device fp16 [rows, ldx], a calibration batch; rows may be 0
+ *               (every score 0: channels 0 .. n_out-1)
+ *   outlier_idx device int32 [n_out]: the selected channels, ascending
+ *               (NULL allowed when n_out == 0)
+ *   perm        device int32 [K]: the unselected channels ascending, then the
+ *               selected ones ascending (what w4a4_make_perm returns for
+ *               outlier_idx)
+ *   chan_absmax device fp16 [K] (may be NULL): the scores
+ *   workspace   device, >= w4a4_select_outliers_workspace_bytes(rows, K),
+ *               256-byte aligned; no contents are required on entry
+ * Xcal must be finite. INVALID_ARG for n_out outside [0, K], ldx < K, or a
+ * NULL required pointer; ALIGNMENT unless Xcal is 16-byte aligned with
+ * ldx % 8 == 0; UNSUPPORTED for K > 32768; WORKSPACE for a short workspace.
+ * Three launches on `stream`. */
+w4a4_status w4a4_select_outliers(const void *Xcal, int64_t ldx, int32_t rows, int32_t K,
+                                 int32_t n_out, int32_t *outlier_idx, int32_t *perm,
+                                 void *chan_absmax, void *workspace, size_t workspace_bytes,
+                                 w4a4_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

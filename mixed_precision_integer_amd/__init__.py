@@ -36,7 +36,8 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_outlier_gemm_workspace_bytes", "w4a4_outlier_gemm_kernel_name", "w4a4_outlier_gemm",
             "w4a4_outlier_gemm_i32",
             "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm",
-            "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm")
+            "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm",
+            "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers")
 
 
 class W4A4Error(RuntimeError):
@@ -90,6 +91,10 @@ def lib():
     L.w4a4_rmsnorm_quant_gemm.argtypes = [vp, i64, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                           i32, vp, i64, vp, sz, vp]
     L.w4a4_rmsnorm_quant_gemm.restype = ctypes.c_int
+    L.w4a4_select_outliers_workspace_bytes.argtypes = [i32, i32]
+    L.w4a4_select_outliers_workspace_bytes.restype = sz
+    L.w4a4_select_outliers.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.w4a4_select_outliers.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -336,6 +341,33 @@ def rmsnorm_quant_gemm(X, gamma, eps: float, perm, w: QuantizedOperand, out=None
                                       out.stride(0) if M else N, workspace.data_ptr(),
                                       workspace.numel(), _stream()), "w4a4_rmsnorm_quant_gemm")
     return out
+
+
+def select_outliers_workspace_bytes(rows: int, K: int) -> int:
+    return int(lib().w4a4_select_outliers_workspace_bytes(rows, K))
+
+
+def select_outliers(Xcal, n_out: int, workspace=None, want_absmax: bool = False):
+    """Offline outlier-channel selection on the GPU: the n_out channels of the
+    calibration batch Xcal [rows, K] (fp16) with the largest absmax, ties to
+    the lower index. Returns (outlier_idx int32 [n_out] ascending, perm int32
+    [K]), plus the fp16 scores [K] with want_absmax."""
+    torch = _torch()
+    _check(Xcal, torch.float16, "Xcal", 2)
+    rows, K = Xcal.shape
+    dev = Xcal.device
+    need = select_outliers_workspace_bytes(rows, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(workspace, torch.uint8, "workspace", 1)
+    idx = torch.empty((n_out,), dtype=torch.int32, device=dev)
+    perm = torch.empty((K,), dtype=torch.int32, device=dev)
+    amax = torch.empty((K,), dtype=torch.float16, device=dev) if want_absmax else None
+    _ok(lib().w4a4_select_outliers(Xcal.data_ptr() if rows else None, Xcal.stride(0) if rows else K,
+                                   rows, K, n_out, _nz(idx), perm.data_ptr(), _ptr(amax),
+                                   workspace.data_ptr(), workspace.numel(), _stream()),
+        "w4a4_select_outliers")
+    return (idx, perm, amax) if want_absmax else (idx, perm)
 
 
 class W4A4Linear:

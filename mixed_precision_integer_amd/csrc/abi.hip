@@ -346,6 +346,45 @@ w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, con
                       workspace_bytes, stream, NormArgs{nullptr, 0.0f, nullptr});
 }
 
+size_t w4a4_select_outliers_workspace_bytes(int32_t rows, int32_t K) {
+    if (rows < 0 || K <= 0 || K > w4a4::select_max_k())
+        return 0;
+    return w4a4::plan_select(rows, K).workspace_bytes;
+}
+
+w4a4_status w4a4_select_outliers(const void *Xcal, int64_t ldx, int32_t rows, int32_t K,
+                                 int32_t n_out, int32_t *outlier_idx, int32_t *perm,
+                                 void *chan_absmax, void *workspace, size_t workspace_bytes,
+                                 w4a4_stream stream) {
+    if (rows < 0 || K <= 0 || n_out < 0 || n_out > K || ldx < K)
+        return W4A4_ERR_INVALID_ARG;
+    if (K > w4a4::select_max_k())
+        return W4A4_ERR_UNSUPPORTED;
+    if (!perm || (n_out > 0 && !outlier_idx) || (rows > 0 && !Xcal))
+        return W4A4_ERR_INVALID_ARG;
+    if ((rows > 0 && (!aligned(Xcal, 16) || ldx % 8 != 0)) || !aligned(perm, 4) ||
+        (outlier_idx && !aligned(outlier_idx, 4)) || (chan_absmax && !aligned(chan_absmax, 2)))
+        return W4A4_ERR_ALIGNMENT;
+    const size_t need = w4a4_select_outliers_workspace_bytes(rows, K);
+    if (workspace_bytes < need || !workspace)
+        return W4A4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return W4A4_ERR_ALIGNMENT;
+    w4a4::SelectArgs a;
+    a.X = Xcal;
+    a.ld = ldx;
+    a.rows = rows;
+    a.K = K;
+    a.n_out = n_out;
+    a.outlier_idx = n_out > 0 ? outlier_idx : nullptr;
+    a.perm = perm;
+    a.absmax = chan_absmax;
+    a.workspace = workspace;
+    if (w4a4::launch_select(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
 w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamma, float eps,
                                     const int32_t *perm, const void *Wq4, const void *Wq8,
                                     const float *sw4, const float *sw8, int32_t M, int32_t N,

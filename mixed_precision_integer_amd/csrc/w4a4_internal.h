@@ -116,4 +116,25 @@ hipError_t launch_gemm_group(const GemmArgs &a, hipStream_t stream);
 bool gemm_big_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t G);
 hipError_t launch_gemm_big(const GemmArgs &a, bool export_acc, hipStream_t stream);
 
+// Offline outlier-channel selection (select_kernels.hip).
+struct SelectArgs {
+    const void *X;        // [rows, ld] fp16 calibration batch
+    int64_t ld;
+    int32_t rows, K, n_out;
+    int32_t *outlier_idx; // [n_out] or nullptr
+    int32_t *perm;        // [K]
+    void *absmax;         // [K] fp16 or nullptr
+    void *workspace;      // plan_select(rows, K).workspace_bytes, 256-byte aligned
+};
+
+struct SelectPlan {
+    int stripes, chunks, rows_per_chunk;
+    int64_t kp;                   // channels rounded up to 8
+    size_t keys_offset, workspace_bytes;
+};
+
+SelectPlan plan_select(int32_t rows, int32_t K);
+int select_max_k();
+hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
+
 }  // namespace w4a4

@@ -148,6 +148,33 @@ def test_norm_quant_gemm_rejects():
     assert L.w4a4_rmsnorm_quant_gemm(*head, FAKE, 1e-6, *tail, FAKE + 16, need, None) == ALIGN
 
 
+def select(**kw):
+    args = dict(X=FAKE, ld=256, rows=64, K=256, n_out=16, idx=FAKE, perm=FAKE, amax=None, ws=FAKE,
+                ws_bytes=1 << 20)
+    args.update(kw)
+    return w4.lib().w4a4_select_outliers(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), INVALID), (dict(rows=-1), INVALID), (dict(n_out=-1), INVALID), (dict(n_out=257), INVALID),
+    (dict(ld=200), INVALID), (dict(perm=None), INVALID), (dict(idx=None), INVALID), (dict(X=None), INVALID),
+    (dict(K=40000, ld=40000), UNSUPPORTED), (dict(X=FAKE + 2), ALIGN), (dict(ld=260), ALIGN),
+    (dict(perm=FAKE + 2), ALIGN), (dict(amax=FAKE + 1), ALIGN), (dict(ws_bytes=16), WS), (dict(ws=None), WS),
+    (dict(ws=FAKE + 64), ALIGN),
+])
+def test_select_rejects(kw, code):
+    assert select(**kw) == code
+
+
+def test_select_workspace_query():
+    assert w4.select_outliers_workspace_bytes(-1, 64) == 0
+    assert w4.select_outliers_workspace_bytes(10, 0) == 0
+    assert w4.select_outliers_workspace_bytes(10, 40000) == 0
+    assert w4.select_outliers_workspace_bytes(0, 64) >= 64 * 2          # the keys alone
+    big = w4.select_outliers_workspace_bytes(32768, 4096)
+    assert 4096 * 2 < big < 64 << 20
+
+
 def test_quant_empty_is_ok():
     assert quant(rows=0, X=None, perm=None, q4=None, q8=None, s4=None, s8=None) == OK
 
