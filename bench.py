@@ -111,6 +111,64 @@ def cpu_baseline(w, X, W, outliers, budget_s, gamma=None, eps=0.0):
     }
 
 
+SELECT_WORKLOADS = {
+    # name: (calibration rows, K, n_out): 16 x 2048 tokens of a 4096-channel
+    # input, and 4 x 2048 tokens of the 65B down_proj's 22016 channels
+    "qproj": (32768, 4096, 128),
+    "downproj": (8192, 22016, 256),
+}
+
+
+def select_bench(torch, w4, args):
+    """Offline outlier-channel selection (w4a4_select_outliers): HBM-bound
+    column absmax over a synthetic calibration batch plus the one-workgroup
+    select. Prints its own JSON line."""
+    rows, K, n_out = SELECT_WORKLOADS[args.select_outliers]
+    X, _, _ = wl.draw(rows, 1, K, n_out, seed=rows + K, outlier_factor=30.0)
+    dev = torch.device("cuda:0")
+    n_sets = max(2, math.ceil(ROTATE_BYTES / (rows * K * 2)))
+    Xs = [torch.from_numpy(X).to(dev) for _ in range(n_sets)]
+    ws = torch.empty(max(w4.select_outliers_workspace_bytes(rows, K), 256), dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        w4.select_outliers(Xs[i % n_sets], n_out, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, e in enumerate(ev):
+        e[0].record()
+        w4.select_outliers(Xs[i % n_sets], n_out, workspace=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    nbytes = 2.0 * rows * K
+    ach = nbytes / (call_ms * 1e-3) / 1e9
+    idx, _ = w4.select_outliers(Xs[0], n_out, workspace=ws)
+    out = {
+        "metric": "outlier-channel selection GB/s (calibration absmax + top-n select) & % HBM",
+        "value": ach, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u16", "data": "synthetic",
+        "config": {"workload": f"select_outliers_{args.select_outliers}_rows{rows}_k{K}_n{n_out}",
+                   "rows": rows, "K": K, "n_out": n_out, "buffer_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "colmax_kernel + fold_kernel + select_kernel (one call)"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        r = max(64, min(rows, int(rows * 0.25)))
+        t = time.perf_counter()
+        want = oracle.select_outliers(X[:r], n_out)
+        dt = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": 2.0 * r * K / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{r} of {rows} calibration rows (numpy absmax + lexsort), {dt:.2f} s"}
+        del want
+    print(json.dumps(out), flush=True)
+    return idx
+
+
 def copy_probe(torch, nbytes, steps, warmup):
     """A plain copy of known size: it reads and writes exactly `nbytes` of HBM
     per launch, so the hardware counters it produces give the scale from
@@ -143,6 +201,8 @@ def main():
                     help="M,N,K,n_out,group: a synthetic shape instead of a named workload")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select-outliers", default=None, choices=sorted(SELECT_WORKLOADS),
+                    help="instead of the layer, time the offline outlier-channel selection")
     ap.add_argument("--norm", action="store_true",
                     help="producer fused with the preceding RMSNorm (eps 1e-6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -161,6 +221,9 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib << 20, args.steps, args.warmup)
+        return
+    if args.select_outliers:
+        select_bench(torch, w4, args)
         return
 
     w = WORKLOADS[args.workload]

@@ -34,7 +34,7 @@ namespace select_impl {
 constexpr int kStripe = 512;          // columns per workgroup
 constexpr int kWaves = 4;             // waves per column-absmax workgroup
 constexpr int kRowsInFlight = 4;      // rows each lane loads before it reduces
-constexpr int kTargetGroups = 2048;   // column-absmax workgroups to aim for
+constexpr int kTargetGroups = 2048;   // column-absmax workgroups: 8 resident per CU
 constexpr int kMinRowsPerChunk = 16;
 constexpr int kMaxK = 32768;          // keys held in LDS by the select launch
 constexpr int kSelThreads = 1024;
@@ -96,20 +96,40 @@ __global__ __launch_bounds__(kWaves * 64) void colmax_kernel(const uint16_t *X, 
     }
 }
 
-// keys[c] = max over chunks of partial[chunk][c], 8 channels per lane; the
-// optional fp16 absmax output gets the same values (the sign bit is clear).
-__global__ __launch_bounds__(256) void fold_kernel(const uint16_t *partial, int chunks, int64_t kp, int K,
-                                                   uint16_t *keys, uint16_t *absmax_out) {
-    const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
-    if (c0 >= kp)
-        return;
+// keys[c] = max over chunks of partial[chunk][c]. A workgroup takes 16
+// groups of 8 channels; the 16 lanes of a group split the chunks between
+// them (several loads in flight each) and meet in LDS. The optional fp16
+// absmax output gets the same values (the sign bit is clear).
+constexpr int kFoldGroups = 16, kFoldSlices = 16;
+
+__global__ __launch_bounds__(kFoldGroups * kFoldSlices) void fold_kernel(const uint16_t *partial, int chunks,
+                                                                         int64_t kp, int K, uint16_t *keys,
+                                                                         uint16_t *absmax_out) {
+    __shared__ uint4 red[kFoldSlices][kFoldGroups];
+    const int g = threadIdx.x % kFoldGroups, sl = threadIdx.x / kFoldGroups;
+    const int c0 = (blockIdx.x * kFoldGroups + g) * 8;
     uint32_t m[4] = {0u, 0u, 0u, 0u};
-    for (int ch = 0; ch < chunks; ++ch) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(partial + (int64_t)ch * kp + c0);
-        m[0] = max_u16x2(m[0], v.x);
-        m[1] = max_u16x2(m[1], v.y);
-        m[2] = max_u16x2(m[2], v.z);
-        m[3] = max_u16x2(m[3], v.w);
+    if (c0 < kp) {
+#pragma unroll 4
+        for (int ch = sl; ch < chunks; ch += kFoldSlices) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(partial + (int64_t)ch * kp + c0);
+            m[0] = max_u16x2(m[0], v.x);
+            m[1] = max_u16x2(m[1], v.y);
+            m[2] = max_u16x2(m[2], v.z);
+            m[3] = max_u16x2(m[3], v.w);
+        }
+    }
+    red[sl][g] = uint4{m[0], m[1], m[2], m[3]};
+    __syncthreads();
+    if (sl != 0 || c0 >= kp)
+        return;
+#pragma unroll
+    for (int t = 1; t < kFoldSlices; ++t) {
+        const uint4 o = red[t][g];
+        m[0] = max_u16x2(m[0], o.x);
+        m[1] = max_u16x2(m[1], o.y);
+        m[2] = max_u16x2(m[2], o.z);
+        m[3] = max_u16x2(m[3], o.w);
     }
     *reinterpret_cast<uint4 *>(keys + c0) = uint4{m[0], m[1], m[2], m[3]};
     if (absmax_out)
@@ -173,17 +193,80 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wtot) {
     return before + incl - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const uint16_t *keys_g, int K, int n_out,
+// Histogram copies: lane l adds into copy l % 4, so that lanes of one wave
+// hitting the same bin are spread over four LDS banks (stride 260 words).
+constexpr int kHistCopies = 4, kHistStride = 260;
+constexpr int kKeysPerLane = kMaxK / kSelThreads;   // 32
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const uint16_t *keys_g, int64_t kp, int K, int n_out,
                                                              int32_t *out_idx, int32_t *perm) {
-    __shared__ uint16_t key[kMaxK];
+    __shared__ __align__(16) uint16_t key[kMaxK];
+    __shared__ uint32_t hcopy[kHistCopies * kHistStride];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t wtot[kSelThreads / 64];
     __shared__ int sh_bin;
     __shared__ uint32_t sh_above;
     const int tid = threadIdx.x;
-    for (int c = tid; c < K; c += kSelThreads)
-        key[c] = keys_g[c];
+    {
+        // 8 keys per 16-byte load (the keys past K up to kp are zero); all of
+        // a lane's loads are issued before the first is stored
+        constexpr int kLoads = kMaxK / 8 / kSelThreads;
+        const int n8 = (int)(kp / 8);
+        uint4 v[kLoads];
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int q = i * kSelThreads + tid;
+            if (q < n8)
+                v[i] = reinterpret_cast<const uint4 *>(keys_g)[q];
+        }
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int q = i * kSelThreads + tid;
+            if (q < n8)
+                reinterpret_cast<uint4 *>(key)[q] = v[i];
+        }
+    }
     __syncthreads();
+
+    // lane t owns channels [t P, t P + P), P a multiple of 8 (16-byte LDS
+    // reads); its keys stay in registers, two per dword
+    const int P = ((K + kSelThreads - 1) / kSelThreads + 7) / 8 * 8;
+    const int b0 = min(tid * P, K), b1 = min(b0 + P, K);
+    uint32_t kr[kKeysPerLane / 2];
+#pragma unroll
+    for (int q = 0; q < kKeysPerLane / 8; ++q) {
+        const uint4 v = q * 8 < P && b0 + q * 8 < K ? reinterpret_cast<const uint4 *>(key + b0)[q]
+                                                    : uint4{0u, 0u, 0u, 0u};
+        kr[4 * q] = v.x;
+        kr[4 * q + 1] = v.y;
+        kr[4 * q + 2] = v.z;
+        kr[4 * q + 3] = v.w;
+    }
+    auto key_at = [&](int i) { return (int)((kr[i >> 1] >> (16 * (i & 1))) & 0xFFFF); };
+    uint32_t *my_hist = hcopy + (tid & (kHistCopies - 1)) * kHistStride;
+    auto build_hist = [&](int level, int hb) {
+        for (int t = tid; t < kHistCopies * kHistStride; t += kSelThreads)
+            hcopy[t] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kKeysPerLane; ++i)
+            if (i < b1 - b0) {
+                const int k = key_at(i);
+                if (level == 0)
+                    atomicAdd(&my_hist[k >> 8], 1u);   // keys <= 0x7FFF: 128 high bins
+                else if ((k >> 8) == hb)
+                    atomicAdd(&my_hist[k & 255], 1u);
+            }
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t h = 0;
+#pragma unroll
+            for (int c = 0; c < kHistCopies; ++c)
+                h += hcopy[c * kHistStride + tid];
+            hist[tid] = h;
+        }
+        __syncthreads();
+    };
 
     // threshold T and the number of keys equal to T that are taken
     int T;
@@ -195,25 +278,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint16_t *key
         T = -1;                                // below every key: everything selected
         take_eq = 0;
     } else {
-        if (tid < 256)
-            hist[tid] = 0u;
-        __syncthreads();
-        for (int c = tid; c < K; c += kSelThreads)
-            atomicAdd(&hist[key[c] >> 8], 1u);  // keys <= 0x7FFF: 128 high bins
-        __syncthreads();
+        build_hist(0, 0);
         if (tid < 64)
             find_crossing<2>(hist, (uint32_t)n_out, &sh_bin, &sh_above);
         __syncthreads();
         const int hb = sh_bin;
         const uint32_t above_hi = sh_above;
         __syncthreads();
-        if (tid < 256)
-            hist[tid] = 0u;
-        __syncthreads();
-        for (int c = tid; c < K; c += kSelThreads)
-            if ((key[c] >> 8) == hb)
-                atomicAdd(&hist[key[c] & 255], 1u);
-        __syncthreads();
+        build_hist(1, hb);
         if (tid < 64)
             find_crossing<4>(hist, (uint32_t)n_out - above_hi, &sh_bin, &sh_above);
         __syncthreads();
@@ -221,23 +293,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint16_t *key
         take_eq = (uint32_t)n_out - above_hi - sh_above;
     }
 
-    // channels in index order: lane t owns [t P, t P + P)
-    const int P = (K + kSelThreads - 1) / kSelThreads;
-    const int b0 = min(tid * P, K), b1 = min(b0 + P, K);
+    // channels in index order
+    const int nk = b1 - b0;
     uint32_t eq = 0;
-    for (int c = b0; c < b1; ++c)
-        eq += (int)key[c] == T;
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i)
+        eq += i < nk && key_at(i) == T;
     uint32_t eq_seen = block_exclusive_scan(eq, wtot);
     uint32_t nsel = 0;
-    for (int c = b0; c < b1; ++c) {
-        const int k = key[c];
-        nsel += k > T || (k == T && eq_seen++ < take_eq);
-    }
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i)
+        if (i < nk) {
+            const int k = key_at(i);
+            nsel += k > T || (k == T && eq_seen++ < take_eq);
+        }
     uint32_t pos = block_exclusive_scan(nsel, wtot);   // selected channels before b0
     eq_seen -= eq;                                     // replay the same decisions
     const int head = K - n_out;
-    for (int c = b0; c < b1; ++c) {
-        const int k = key[c];
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i) {
+        if (i >= nk)
+            break;
+        const int c = b0 + i, k = key_at(i);
         if (k > T || (k == T && eq_seen++ < take_eq)) {
             if (out_idx)
                 out_idx[pos] = c;
@@ -260,7 +337,7 @@ SelectPlan plan_select(int32_t rows, int32_t K) {
         p.chunks = 0;
         p.rows_per_chunk = 0;
     } else {
-        const long want = std::max<long>(1, (kTargetGroups + p.stripes - 1) / p.stripes);
+        const long want = std::max<long>(1, kTargetGroups / p.stripes);   // one wave of workgroups
         const long most = std::max<long>(1, (rows + kMinRowsPerChunk - 1) / kMinRowsPerChunk);
         const long chunks = std::min(want, most);
         p.rows_per_chunk = (int)((rows + chunks - 1) / chunks);
@@ -282,11 +359,11 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t stream) {
     if (p.chunks > 0)
         hipLaunchKernelGGL(colmax_kernel, dim3(p.stripes, p.chunks), dim3(kWaves * 64), 0, stream,
                            static_cast<const uint16_t *>(a.X), a.ld, a.rows, a.K, p.rows_per_chunk, p.kp, partial);
-    const int fold_groups = (int)((p.kp / 8 + 255) / 256);
-    hipLaunchKernelGGL(fold_kernel, dim3(fold_groups), dim3(256), 0, stream, partial, p.chunks, p.kp, a.K, keys,
-                       static_cast<uint16_t *>(a.absmax));
-    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), 0, stream, keys, a.K, a.n_out, a.outlier_idx,
-                       a.perm);
+    const int fold_groups = (int)((p.kp / 8 + kFoldGroups - 1) / kFoldGroups);
+    hipLaunchKernelGGL(fold_kernel, dim3(fold_groups), dim3(kFoldGroups * kFoldSlices), 0, stream, partial, p.chunks,
+                       p.kp, a.K, keys, static_cast<uint16_t *>(a.absmax));
+    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), 0, stream, keys, p.kp, a.K, a.n_out,
+                       a.outlier_idx, a.perm);
     return hipGetLastError();
 }
 
