@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 runs of bench.py for the profiles/ folder.
 
     python -m mixed_precision_integer_amd.profile_summary DIR WORKLOAD TITLE OUT.md [--m M]
+    python -m mixed_precision_integer_amd.profile_summary DIR - TITLE OUT.md --args "BENCH ARGS"
 
 DIR holds the output of five rocprofv3 runs of bench.py (the commands are
 written into the summary):
@@ -16,6 +17,11 @@ counters to bytes. The summary is written to profiles/OUT.md, and the GEMM's
 HBM bytes per launch are recorded in profiles/gemm_traffic.json under the
 workload, with a digest of the GEMM sources: bench.py reports the record as
 roofline traffic only while the sources are unchanged.
+
+With ``--args`` (the workload given as ``-``) the runs were made with
+``python3 bench.py ARGS`` and the summary covers every kernel of the library
+in them (the fused RMSNorm producer, the outlier selection), with no GEMM
+traffic record.
 """
 import argparse
 import collections
@@ -179,6 +185,73 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "") -> s
     return text
 
 
+def summarize_kernels(d: str, bench_args: str, title: str, out: str) -> str:
+    """Kernel trace and HBM traffic of every library kernel in a bench.py run
+    made with `bench_args` (no GEMM traffic record)."""
+    stats = _csv(os.path.join(d, "trace"), "kernel_stats.csv")
+    fetch = _pmc(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = _pmc(os.path.join(d, "write"), "WRITE_SIZE")
+    cf = _pmc(os.path.join(d, "cfetch"), "FETCH_SIZE")
+    cw = _pmc(os.path.join(d, "cwrite"), "WRITE_SIZE")
+    ck = next(k for k in cf if "copyBuffer" in k)
+    f_scale, w_scale = COPY_KIB / cf[ck][0], COPY_KIB / cw[ck][0]
+    bj = _bench_line(os.path.join(d, "trace.log"))
+    run = f"python3 bench.py {bench_args}"
+    L = [f"# {title}\n",
+         f"bench.py configuration: `{json.dumps(bj['config'])}`; seeded synthetic inputs resident in HBM, "
+         "buffer sets rotated over more than 512 MB.\n",
+         "## Kernel trace (rocprofv3 --kernel-trace --stats)\n",
+         "```\ncd /tmp && export TMPDIR=/tmp && cd <repo>\n"
+         f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
+         f"{run} --steps 20 --warmup 5 --no-cpu-baseline\n```\n",
+         "| kernel | calls | average µs | min µs | max µs | share of GPU time |",
+         "|---|---|---|---|---|---|"]
+    avg = {}
+    for r in stats:
+        if "w4a4" in r["Name"]:
+            avg[_short(r["Name"])] = float(r["AverageNs"]) / 1e3
+            L.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    L.append("\nThe other kernels in the trace (torch set-up copies and fills) are not part of a step.\n")
+    roof = bj["roofline"]
+    line = (f"bench.py line printed in the same run: value {bj['value']:.1f} {bj['unit']}, "
+            f"{bj['ms_per_step'] * 1e3:.2f} µs per step; roofline {roof['achieved']:.1f} of "
+            f"{roof['peak']:.0f} {roof['unit']} ({100 * roof['frac']:.1f}%, {roof['bound']}-bound, "
+            f"{roof['kernel']})")
+    if "kernels" in bj:
+        k = bj["kernels"]
+        line += (f"; producer {k['producer_us']:.2f} µs ({k['producer_GBps']:.0f} GB/s), "
+                 f"GEMM {k['gemm_us']:.2f} µs")
+    L.append(line + ".\n")
+    L.append("## HBM traffic (rocprofv3 --pmc, one counter per run)\n")
+    cmds = [("FETCH_SIZE", "fetch", f"{run} --steps 5 --warmup 2 --no-cpu-baseline"),
+            ("WRITE_SIZE", "write", f"{run} --steps 5 --warmup 2 --no-cpu-baseline"),
+            ("FETCH_SIZE", "cfetch", "python3 bench.py --copy-probe-mib 512 --steps 5 --warmup 2"),
+            ("WRITE_SIZE", "cwrite", "python3 bench.py --copy-probe-mib 512 --steps 5 --warmup 2")]
+    L.append("```\n" + "\n".join(
+        f"timeout -s KILL 120 rocprofv3 --pmc {cn} --output-format csv -d {d}/{o} -o p -- {cmd}"
+        for cn, o, cmd in cmds) + "\n```\n")
+    L.append(f"Calibration: the plain 512 MiB device copy (`{_short(ck)}`) reads {cf[ck][0]:.0f} KiB "
+             f"(FETCH_SIZE) and writes {cw[ck][0]:.0f} KiB (WRITE_SIZE) per dispatch for {COPY_KIB} KiB "
+             f"moved each way: bytes = FETCH_SIZE x {f_scale:.3f} KiB and WRITE_SIZE x {w_scale:.3f} KiB.\n")
+    L.append("| kernel | dispatches | HBM read MB | HBM write MB | total MB per launch | GB/s at the trace's "
+             "average duration |")
+    L.append("|---|---|---|---|---|---|")
+    for kn, (fk, n) in fetch.items():
+        if "w4a4" not in kn:
+            continue
+        wk = write.get(kn, (0.0, 0))[0]
+        rb, wb = fk * f_scale * 1024, wk * w_scale * 1024
+        t = avg.get(_short(kn))
+        rate = f"{(rb + wb) / (t * 1e-6) / 1e9:.0f}" if t else "-"
+        L.append(f"| `{_short(kn)}` | {n} | {rb / 1e6:.2f} | {wb / 1e6:.2f} | {(rb + wb) / 1e6:.2f} | {rate} |")
+    text = "\n".join(L) + "\n"
+    with open(os.path.join(ROOT, "profiles", out), "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("dir")
@@ -186,7 +259,12 @@ def main():
     ap.add_argument("title")
     ap.add_argument("out")
     ap.add_argument("--m", default=None, help="the --m argument the runs were made with")
+    ap.add_argument("--args", default=None, help="bench.py arguments of a kernel-summary run")
     a = ap.parse_args()
+    if a.args is not None:
+        print(summarize_kernels(os.path.relpath(a.dir, ROOT) if os.path.isabs(a.dir) else a.dir, a.args,
+                                a.title, a.out))
+        return
     print(summarize(os.path.relpath(a.dir, ROOT) if os.path.isabs(a.dir) else a.dir, a.workload, a.title,
                     a.out, f" --m {a.m}" if a.m else ""))
 
