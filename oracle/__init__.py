@@ -77,6 +77,9 @@ def _load():
                                   c_i32, c_i32, c_i32, _i32p, _i32p, c_i64,
                                   _i32p, _i32p, _f64p]
     lib.w4o_linear_at.restype = ctypes.c_int
+    lib.w4o_w4a8_linear_at.argtypes = [_i8p, _f32p, _i8p, _f32p, c_i32, c_i32, _i32p, _i32p, c_i64,
+                                       _i32p, _f64p]
+    lib.w4o_w4a8_linear_at.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -264,3 +267,49 @@ def linear(X, W, outlier_idx, group: int):
         "ystar": y.reshape(M, N),
         "Y": to_fp16(y.reshape(M, N)),
     }
+
+
+def w4a8_quantize(X, W, group: int):
+    """W4A8 operands (QQQ abstract): per-token INT8 activations over all K
+    channels and INT4 weights with one scale per output channel (group 0) or
+    per `group` channels, both by the same symmetric quantizer (readings
+    R1-R5), in the original channel order. Returns ((q8, s8), (q4, s4))."""
+    X, W = np.asarray(X), np.asarray(W)
+    K = X.shape[1]
+    ident = np.arange(K, dtype=np.int32)
+    _, _, qa8, sa8 = quantize_rows(X, ident, K, 0)
+    qw4, sw4, _, _ = quantize_rows(W, ident, 0, group)
+    return (qa8, sa8), (qw4, sw4)
+
+
+def w4a8_linear_at(qa, qw, group: int, m_idx, n_idx):
+    """W4A8 integer GEMM + fp64 dequant at output pairs (m_idx[p], n_idx[p]):
+    acc int32 [P, G] and y* = sa8[m] * sum_t sw4[n, t] * acc[p, t] (fp64 [P])."""
+    qa8, sa8 = qa
+    qw4, sw4 = qw
+    K = qa8.shape[1]
+    G = num_groups(K, group)
+    m_idx = np.ascontiguousarray(m_idx, np.int32)
+    n_idx = np.ascontiguousarray(n_idx, np.int32)
+    P = m_idx.size
+    acc = np.zeros((P, G), np.int32)
+    y = np.zeros(P, np.float64)
+    pad = lambda a, dt: np.ascontiguousarray(a, dt) if a.size else np.zeros(1, dt)  # noqa: E731
+    rc = _load().w4o_w4a8_linear_at(pad(qa8, np.int8), pad(sa8, np.float32), pad(qw4, np.int8),
+                                    pad(sw4, np.float32), K, group, pad(m_idx, np.int32),
+                                    pad(n_idx, np.int32), P, pad(acc, np.int32), pad(y, np.float64))
+    if rc != 0:
+        raise OverflowError("accumulator outside int32")
+    return acc, y
+
+
+def w4a8_linear(X, W, group: int):
+    """Whole W4A8 layer on small inputs: acc [G, M, N], ystar [M, N], Y fp16."""
+    X, W = np.asarray(X), np.asarray(W)
+    M, N = X.shape[0], W.shape[0]
+    qa, qw = w4a8_quantize(X, W, group)
+    mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")
+    acc, y = w4a8_linear_at(qa, qw, group, mm.reshape(-1), nn.reshape(-1))
+    G = acc.shape[1]
+    return {"qa": qa, "qw": qw, "acc": acc.reshape(M, N, G).transpose(2, 0, 1).copy(),
+            "ystar": y.reshape(M, N), "Y": to_fp16(y.reshape(M, N))}

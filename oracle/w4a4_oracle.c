@@ -239,3 +239,36 @@ int w4o_linear_at(const int8_t *qa4, const float *sa4, const int8_t *qa8,
     }
     return bad ? -1 : 0;
 }
+
+/* W4A8 layer (QQQ abstract: 4-bit weights, 8-bit activations, per-channel
+ * and per-group GEMMs) at selected output positions (m[p], n[p]):
+ *   acc[p, t] = sum_{j in block t} qa8[m, j] * qw4[n, j]       (int64, exact)
+ *   y[p] = sa8[m] * sum_t sw4[n, t] * acc[p, t]                 (fp64)
+ * qa8 [M, K] INT8 codes with one scale per token (sa8 [M]); qw4 [N, K] INT4
+ * codes with G = K / group scale groups per output channel (one when group
+ * is 0). Returns 0, or -1 if an accumulator leaves the int32 range. */
+int w4o_w4a8_linear_at(const int8_t *qa8, const float *sa8, const int8_t *qw4,
+                       const float *sw4, int32_t K, int32_t group,
+                       const int32_t *m_idx, const int32_t *n_idx, int64_t npairs,
+                       int32_t *acc, double *y)
+{
+    int32_t G = w4o_num_groups(K, group);
+    int32_t gl = group > 0 ? group : K;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 64) reduction(| : bad)
+    for (int64_t p = 0; p < npairs; ++p) {
+        int64_t m = m_idx[p], n = n_idx[p];
+        double yp = 0.0;
+        for (int32_t t = 0; t < G; ++t) {
+            int64_t s = 0;
+            for (int32_t j = t * gl; j < (t + 1) * gl; ++j)
+                s += (int64_t)qa8[m * K + j] * (int64_t)qw4[n * K + j];
+            if (s > INT32_MAX || s < INT32_MIN)
+                bad = 1;
+            acc[p * G + t] = (int32_t)s;
+            yp += (double)sw4[n * G + t] * (double)s;
+        }
+        y[p] = (double)sa8[m] * yp;
+    }
+    return bad ? -1 : 0;
+}
