@@ -99,7 +99,7 @@ w4a4_status w4a4_make_perm(int32_t K, const int32_t *outlier_idx, int32_t n_out,
  *   sa4  device fp32 [M, G]            sa8  device fp32 [M] (written 0 if n_out == 0)
  * GPU group sizes: 0 or a multiple of 128 dividing K_n (else UNSUPPORTED).
  * perm is trusted to be a permutation of [0, K); an index outside [0, K) is
- * undefined behaviour. */
+ * undefined behaviour. A NULL perm is the identity order (no reordering). */
 w4a4_status w4a4_quant_reorder_act(const void *X, int64_t ldx, const int32_t *perm,
                                    int32_t M, int32_t K, int32_t n_out, int32_t group,
                                    void *Aq4, void *Aq8, float *sa4, float *sa8,
@@ -209,6 +209,29 @@ w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamm
                                     const float *sw4, const float *sw8, int32_t M, int32_t N,
                                     int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
                                     void *workspace, size_t workspace_bytes, w4a4_stream stream);
+
+/* W4A8 GEMM (QQQ abstract: 4-bit weights with 8-bit activations, a
+ * per-channel and a per-group GEMM), without outlier channels:
+ *   Y[m, n] = fp16( sa8[m] * sum_t sw4[n, t] * acc_t[m, n] ),
+ *   acc_t[m, n] = sum over the channels j of group t of qa8[m, j] * qw4[n, j].
+ * Operands, all in the original channel order (a NULL perm):
+ *   Aq8 device int8 [M, K], sa8 device fp32 [M]: w4a4_quant_reorder_act(X, ldx,
+ *       NULL, M, K, n_out = K, group = 0, NULL, Aq8, NULL, sa8) (per-token INT8)
+ *   Wq4 device uint8 [N, K / 2], sw4 device fp32 [N, G]: w4a4_pack_int4_weights(W,
+ *       ldw, NULL, N, K, n_out = 0, group, Wq4, NULL, sw4, NULL)
+ * G = K / group, or 1 for group 0 (one scale per output channel). Y device
+ * fp16 [M, ldy], ldy >= N. UNSUPPORTED unless K is a multiple of 128, group
+ * is 0 or a multiple of 128, and K * 16384 < 2^31. INVALID_ARG for a group
+ * not dividing K or a NULL pointer; ALIGNMENT unless Aq8 and Wq4 are 16-byte
+ * aligned. */
+w4a4_status w4a4_w4a8_gemm(const void *Aq8, const float *sa8, const void *Wq4, const float *sw4,
+                           int32_t M, int32_t N, int32_t K, int32_t group, void *Y, int64_t ldy,
+                           w4a4_stream stream);
+
+/* Accumulator export of the same main loop (test path): acc device int32
+ * [G, M, N], the exact integer sums of every scale group. */
+w4a4_status w4a4_w4a8_gemm_i32(const void *Aq8, const void *Wq4, int32_t M, int32_t N, int32_t K,
+                               int32_t group, int32_t *acc, w4a4_stream stream);
 
 /* Bytes of device workspace w4a4_select_outliers needs (0 for arguments it
  * would reject). A pure function of rows and K. */

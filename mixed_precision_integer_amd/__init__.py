@@ -37,7 +37,8 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_outlier_gemm_i32",
             "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm",
             "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm",
-            "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers")
+            "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers",
+            "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32")
 
 
 class W4A4Error(RuntimeError):
@@ -95,6 +96,10 @@ def lib():
     L.w4a4_select_outliers_workspace_bytes.restype = sz
     L.w4a4_select_outliers.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.w4a4_select_outliers.restype = ctypes.c_int
+    L.w4a4_w4a8_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp]
+    L.w4a4_w4a8_gemm.restype = ctypes.c_int
+    L.w4a4_w4a8_gemm_i32.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    L.w4a4_w4a8_gemm_i32.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -171,14 +176,15 @@ class QuantizedOperand(NamedTuple):
 
 def _quant_args(src, perm, op: QuantizedOperand):
     rows, K = src.shape
-    return (src.data_ptr(), src.stride(0) if rows else K, perm.data_ptr(), rows, K, op.n_out,
+    return (src.data_ptr(), src.stride(0) if rows else K, _ptr(perm), rows, K, op.n_out,
             op.group, _nz(op.q4), _nz(op.q8), _nz(op.s4), _nz(op.s8), _stream())
 
 
 def _quant_rows(fn, name, src, perm, n_out, group):
     torch = _torch()
     _check(src, torch.float16, name, 2)
-    _check(perm, torch.int32, "perm", 1)
+    if perm is not None:                      # None: the identity order
+        _check(perm, torch.int32, "perm", 1)
     op = alloc_operand(src.shape[0], src.shape[1], n_out, group, src.device)
     _ok(fn(*_quant_args(src, perm, op)), name)
     return op
@@ -368,6 +374,54 @@ def select_outliers(Xcal, n_out: int, workspace=None, want_absmax: bool = False)
                                    workspace.data_ptr(), workspace.numel(), _stream()),
         "w4a4_select_outliers")
     return (idx, perm, amax) if want_absmax else (idx, perm)
+
+
+class W4A8Operand(NamedTuple):
+    """W4A8 operand: INT8 activation rows (q [rows, K], s [rows]) or INT4
+    weight rows (q [rows, K / 2] packed, s [rows, G])."""
+    q: object
+    s: object
+    K: int
+    group: int
+
+
+def quant_act_int8(X) -> W4A8Operand:
+    """W4A8 activations: per-token INT8 over all K channels in the original
+    order (the producer with a null permutation and n_out = K)."""
+    op = _quant_rows(lib().w4a4_quant_reorder_act, "w4a4_quant_reorder_act", X, None, X.shape[1], 0)
+    return W4A8Operand(op.q8, op.s8, X.shape[1], 0)
+
+
+def pack_int4_weights_w4a8(W, group: int) -> W4A8Operand:
+    """W4A8 weights: INT4 per output channel (group 0) or per `group`
+    channels, original order (no outliers)."""
+    op = _quant_rows(lib().w4a4_pack_int4_weights, "w4a4_pack_int4_weights", W, None, 0, group)
+    return W4A8Operand(op.q4, op.s4, W.shape[1], group)
+
+
+def w4a8_gemm(a: W4A8Operand, w: W4A8Operand, out=None):
+    """Y [M, N] fp16 = sa8[m] * sum_t sw4[n, t] * (INT8 x INT4 group sums)."""
+    torch = _torch()
+    if a.K != w.K:
+        raise ValueError("activations and weights disagree on K")
+    M, N = a.s.shape[0], w.s.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.s.device)
+    _check(out, torch.float16, "out", 2)
+    _ok(lib().w4a4_w4a8_gemm(_nz(a.q), _nz(a.s), _nz(w.q), _nz(w.s), M, N, a.K, w.group,
+                             out.data_ptr(), out.stride(0) if M else N, _stream()), "w4a4_w4a8_gemm")
+    return out
+
+
+def w4a8_gemm_i32(a: W4A8Operand, w: W4A8Operand):
+    """Accumulator export of the W4A8 main loop: int32 [G, M, N]."""
+    torch = _torch()
+    M, N = a.s.shape[0], w.s.shape[0]
+    G = num_groups(a.K, w.group)
+    acc = torch.zeros((G, M, N), dtype=torch.int32, device=a.s.device)
+    _ok(lib().w4a4_w4a8_gemm_i32(_nz(a.q), _nz(w.q), M, N, a.K, w.group, _nz(acc), _stream()),
+        "w4a4_w4a8_gemm_i32")
+    return acc
 
 
 class W4A4Linear:

@@ -8,6 +8,7 @@
 
 #include "w4a4.h"
 #include "w4a4_internal.h"
+#include "w4a8_internal.h"
 
 namespace {
 
@@ -51,11 +52,11 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
         return W4A4_ERR_INVALID_ARG;
     if (rows == 0)
         return W4A4_OK;                         // empty call: pointers are not used
-    if (!src || !perm)
+    if (!src)                                   // perm may be null: the identity order
         return W4A4_ERR_INVALID_ARG;
     if ((K_n > 0 && (!q4 || !s4)) || (n_out > 0 && (!q8 || !s8)))
         return W4A4_ERR_INVALID_ARG;
-    if (!aligned(src, 16) || ld % 8 != 0 || !aligned(perm, 16) || (q4 && !aligned(q4, 16)) ||
+    if (!aligned(src, 16) || ld % 8 != 0 || (perm && !aligned(perm, 16)) || (q4 && !aligned(q4, 16)) ||
         (q8 && !aligned(q8, 16)) || (s4 && !aligned(s4, 4)) || (s8 && !aligned(s8, 4)))
         return W4A4_ERR_ALIGNMENT;
     if (norm.gamma && (!aligned(norm.gamma, 2) || (norm.rstd && !aligned(norm.rstd, 4))))
@@ -344,6 +345,79 @@ w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, con
                             w4a4_stream stream) {
     return quant_gemm(X, ldx, perm, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, workspace,
                       workspace_bytes, stream, NormArgs{nullptr, 0.0f, nullptr});
+}
+
+static w4a4_status w4a8_check(const void *Aq8, const void *Wq4, int32_t M, int32_t N, int32_t K,
+                              int32_t group) {
+    if (M < 0 || N < 0 || K <= 0 || group < 0 || (group > 0 && K % group != 0))
+        return W4A4_ERR_INVALID_ARG;
+    if (K % 128 != 0 || group % 128 != 0 || (int64_t)K * 16384 >= kAccLimit)
+        return W4A4_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if (!Aq8 || !Wq4)
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(Aq8, 16) || !aligned(Wq4, 16))
+        return W4A4_ERR_ALIGNMENT;
+    return W4A4_OK;
+}
+
+static w4a4::GemmArgs w4a8_args(const void *Aq8, const float *sa8, const void *Wq4, const float *sw4,
+                                int32_t M, int32_t N, int32_t K, int32_t group) {
+    w4a4::GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.a8 = static_cast<const int8_t *>(Aq8);
+    a.w4 = static_cast<const uint8_t *>(Wq4);
+    a.sa8 = sa8;
+    a.sw4 = sw4;
+    a.M = M;
+    a.N = N;
+    a.K_n = K;
+    a.group = group;
+    a.G = w4a4_num_groups(K, group);
+    a.pitch4 = w4a4_pitch4_bytes(K);
+    a.pitch8 = w4a4_pitch8_bytes(K);
+    return a;
+}
+
+w4a4_status w4a4_w4a8_gemm(const void *Aq8, const float *sa8, const void *Wq4, const float *sw4,
+                           int32_t M, int32_t N, int32_t K, int32_t group, void *Y, int64_t ldy,
+                           w4a4_stream stream) {
+    w4a4_status st = w4a8_check(Aq8, Wq4, M, N, K, group);
+    if (st != W4A4_OK)
+        return st;
+    if (ldy < N)
+        return W4A4_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if (!sa8 || !sw4 || !Y)
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(sa8, 4) || !aligned(sw4, 4) || !aligned(Y, 2))
+        return W4A4_ERR_ALIGNMENT;
+    w4a4::GemmArgs a = w4a8_args(Aq8, sa8, Wq4, sw4, M, N, K, group);
+    a.y = static_cast<_Float16 *>(Y);
+    a.ldy = ldy;
+    if (w4a4::launch_gemm_w4a8(a, false, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+w4a4_status w4a4_w4a8_gemm_i32(const void *Aq8, const void *Wq4, int32_t M, int32_t N, int32_t K,
+                               int32_t group, int32_t *acc, w4a4_stream stream) {
+    w4a4_status st = w4a8_check(Aq8, Wq4, M, N, K, group);
+    if (st != W4A4_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if (!acc)
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(acc, 4))
+        return W4A4_ERR_ALIGNMENT;
+    w4a4::GemmArgs a = w4a8_args(Aq8, nullptr, Wq4, nullptr, M, N, K, group);
+    a.acc4_out = acc;
+    if (w4a4::launch_gemm_w4a8(a, true, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
 }
 
 size_t w4a4_select_outliers_workspace_bytes(int32_t rows, int32_t K) {

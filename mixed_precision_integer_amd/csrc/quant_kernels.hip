@@ -196,18 +196,20 @@ void quant_rows_kernel(QuantArgs a) {
         // 16-byte loads (a head unit's 8 entries are two of them; a tail word
         // is one when K_n % 4 == 0), index clamped into the array; entries
         // past the last whole int4 are fixed up with scalar loads after.
+        // (a null permutation is the identity order)
         const int K4 = K / 4;
         const int4 *perm4 = reinterpret_cast<const int4 *>(a.perm);
+        auto entry4 = [&](int q) { return perm4 ? perm4[q] : int4{4 * q, 4 * q + 1, 4 * q + 2, 4 * q + 3}; };
         int4 e[UMAX][2], f[TW];
         if (K4 > 0) {
 #pragma unroll
             for (int i = 0; i < UMAX; ++i)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    e[i][h] = perm4[min(2 * (i * THREADS + tid) + h, K4 - 1)];
+                    e[i][h] = entry4(min(2 * (i * THREADS + tid) + h, K4 - 1));
 #pragma unroll
             for (int i = 0; i < TW; ++i)
-                f[i] = perm4[min(K_n / 4 + i * THREADS + tid, K4 - 1)];
+                f[i] = entry4(min(K_n / 4 + i * THREADS + tid, K4 - 1));
         } else {                                   // K < 4: every entry comes from fix() below
 #pragma unroll
             for (int i = 0; i < UMAX; ++i)
@@ -217,7 +219,8 @@ void quant_rows_kernel(QuantArgs a) {
                 f[i] = int4{0, 0, 0, 0};
         }
         const bool tail4 = (K_n & 3) == 0;
-        auto fix = [&](int v, int j) { return (j >= 4 * K4 && j < K) ? a.perm[j] : v; };
+        auto entry = [&](int j) { return a.perm ? a.perm[j] : j; };
+        auto fix = [&](int v, int j) { return (j >= 4 * K4 && j < K) ? entry(j) : v; };
         auto pack = [](int lo, int hi) { return (uint32_t)(lo & 0xFFFF) | ((uint32_t)hi << 16); };
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
@@ -234,8 +237,8 @@ void quant_rows_kernel(QuantArgs a) {
                 pt[i][0] = pack(fix(f[i].x, j0), fix(f[i].y, j0 + 1));
                 pt[i][1] = pack(fix(f[i].z, j0 + 2), fix(f[i].w, j0 + 3));
             } else {
-                pt[i][0] = pack(j0 < K ? a.perm[j0] : 0, j0 + 1 < K ? a.perm[j0 + 1] : 0);
-                pt[i][1] = pack(j0 + 2 < K ? a.perm[j0 + 2] : 0, j0 + 3 < K ? a.perm[j0 + 3] : 0);
+                pt[i][0] = pack(j0 < K ? entry(j0) : 0, j0 + 1 < K ? entry(j0 + 1) : 0);
+                pt[i][1] = pack(j0 + 2 < K ? entry(j0 + 2) : 0, j0 + 3 < K ? entry(j0 + 3) : 0);
             }
         }
     }
@@ -497,6 +500,7 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
         hi = min(max(hi, 0), K - 1);
         return (uint32_t)lo | ((uint32_t)hi << 16);
     };
+    auto entry = [&](int j) { return a.perm ? a.perm[j] : j; };   // null: the identity order
 
     if (c < NC) {
         // ---- head chunk: units u = c * 64 UPL + 64 i + lane
@@ -505,8 +509,9 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
         for (int i = 0; i < UPL; ++i) {
             const int u = c * 64 * UPL + 64 * i + lane, j0 = 8 * u;
             if (j0 + 8 <= K_n) {
-                const int4 e0 = *reinterpret_cast<const int4 *>(a.perm + j0);
-                const int4 e1 = *reinterpret_cast<const int4 *>(a.perm + j0 + 4);
+                const int4 e0 = a.perm ? *reinterpret_cast<const int4 *>(a.perm + j0) : int4{j0, j0 + 1, j0 + 2, j0 + 3};
+                const int4 e1 = a.perm ? *reinterpret_cast<const int4 *>(a.perm + j0 + 4)
+                                       : int4{j0 + 4, j0 + 5, j0 + 6, j0 + 7};
                 pv[i][0] = pack(e0.x, e0.y);
                 pv[i][1] = pack(e0.z, e0.w);
                 pv[i][2] = pack(e1.x, e1.y);
@@ -514,8 +519,8 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    pv[i][k] = pack(j0 + 2 * k < K_n ? a.perm[j0 + 2 * k] : 0,
-                                    j0 + 2 * k + 1 < K_n ? a.perm[j0 + 2 * k + 1] : 0);
+                    pv[i][k] = pack(j0 + 2 * k < K_n ? entry(j0 + 2 * k) : 0,
+                                    j0 + 2 * k + 1 < K_n ? entry(j0 + 2 * k + 1) : 0);
             }
         }
         uint32_t v[UPL][4];
@@ -586,7 +591,7 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
         const int j0 = K_n + 4 * (64 * i + lane);
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-            pt[i][k] = pack(j0 + 2 * k < K ? a.perm[j0 + 2 * k] : 0, j0 + 2 * k + 1 < K ? a.perm[j0 + 2 * k + 1] : 0);
+            pt[i][k] = pack(j0 + 2 * k < K ? entry(j0 + 2 * k) : 0, j0 + 2 * k + 1 < K ? entry(j0 + 2 * k + 1) : 0);
     }
     uint32_t tv[TW][2];
     {

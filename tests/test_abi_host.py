@@ -101,7 +101,7 @@ def gemm(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(K=0), INVALID), (dict(rows=-1), INVALID), (dict(n_out=300), INVALID),
     (dict(n_out=-1), INVALID), (dict(ld=100), INVALID), (dict(X=None), INVALID),
-    (dict(perm=None), INVALID), (dict(q4=None), INVALID), (dict(q8=None), INVALID),
+    (dict(q4=None), INVALID), (dict(q8=None), INVALID),
     (dict(s4=None), INVALID), (dict(s8=None), INVALID),
     (dict(group=100), INVALID),                    # does not divide K_n = 240
     (dict(K=272, ld=272, group=64), UNSUPPORTED),  # divides, but not a multiple of 128
@@ -173,6 +173,27 @@ def test_select_workspace_query():
     assert w4.select_outliers_workspace_bytes(0, 64) >= 64 * 2          # the keys alone
     big = w4.select_outliers_workspace_bytes(32768, 4096)
     assert 4096 * 2 < big < 64 << 20
+
+
+def w4a8(**kw):
+    args = dict(a8=FAKE, sa8=FAKE, w4=FAKE, sw4=FAKE, M=4, N=8, K=256, group=0, Y=FAKE, ldy=8)
+    args.update(kw)
+    return w4.lib().w4a4_w4a8_gemm(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), INVALID), (dict(K=0), INVALID), (dict(group=100), INVALID), (dict(ldy=4), INVALID),
+    (dict(a8=None), INVALID), (dict(sw4=None), INVALID), (dict(Y=None), INVALID),
+    (dict(K=200), UNSUPPORTED), (dict(K=384, group=192), UNSUPPORTED), (dict(K=131072), UNSUPPORTED),
+    (dict(a8=FAKE + 8), ALIGN), (dict(w4=FAKE + 4), ALIGN), (dict(Y=FAKE + 1), ALIGN),
+])
+def test_w4a8_rejects(kw, code):
+    assert w4a8(**kw) == code
+
+
+def test_w4a8_empty_is_ok():
+    assert w4a8(M=0, a8=None, sa8=None, Y=None) == OK
+    assert w4.lib().w4a4_w4a8_gemm_i32(None, None, 0, 8, 256, 0, None, None) == OK
 
 
 def test_quant_empty_is_ok():
