@@ -169,6 +169,109 @@ def select_bench(torch, w4, args):
     return idx
 
 
+W4A8_WORKLOADS = {
+    # name: (M, N, K, group): the Llama-7B q_proj prefill with 128-channel
+    # weight groups, and up_proj with one weight scale per output channel
+    "qproj": (2048, 4096, 4096, 128),
+    "upproj": (4096, 11008, 4096, 0),
+}
+
+
+def w4a8_bench(torch, w4, args):
+    """W4A8 layer step: per-token INT8 activation producer, then the W4A8
+    GEMM (weights packed before timing). Prints its own JSON line; the
+    roofline is the GEMM's."""
+    M, N, K, group = W4A8_WORKLOADS[args.w4a8]
+    X, W, _ = wl.draw(M, N, K, 0, seed=M + N + group)
+    dev = torch.device("cuda:0")
+    wq = w4.pack_int4_weights_w4a8(torch.from_numpy(W).to(dev), group)
+    one = M * K * 3 + N * K // 2 + M * N * 2
+    n_sets = max(2, math.ceil(ROTATE_BYTES / one) + 1)
+    sets = []
+    for _ in range(n_sets):
+        Xd = torch.from_numpy(X).to(dev)
+        a = w4.quant_act_int8(Xd)
+        wc = w4.W4A8Operand(wq.q.clone(), wq.s.clone(), K, group)
+        sets.append((Xd, a, wc, torch.empty((M, N), dtype=torch.float16, device=dev)))
+    L = w4.lib()
+    stream = w4._stream()
+
+    def produce(st):
+        Xd, a = st[0], st[1]
+        rc = L.w4a4_quant_reorder_act(Xd.data_ptr(), K, None, M, K, K, 0, None, a.q.data_ptr(), None,
+                                      a.s.data_ptr(), stream)
+        if rc:
+            raise SystemExit(f"producer failed: {rc}")
+
+    def gemm(st):
+        a, wc, y = st[1], st[2], st[3]
+        rc = L.w4a4_w4a8_gemm(a.q.data_ptr(), a.s.data_ptr(), wc.q.data_ptr(), wc.s.data_ptr(), M, N, K,
+                              group, y.data_ptr(), N, stream)
+        if rc:
+            raise SystemExit(f"W4A8 GEMM failed: {rc}")
+
+    for i in range(args.warmup):
+        produce(sets[i % n_sets])
+        gemm(sets[i % n_sets])
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, e in enumerate(ev):
+        produce(sets[i % n_sets])
+        e[0].record()
+        gemm(sets[i % n_sets])
+        e[1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gemm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(min(args.steps, 50))]
+    for i, e in enumerate(pev):
+        e[0].record()
+        produce(sets[i % n_sets])
+        e[1].record()
+        gemm(sets[i % n_sets])
+    torch.cuda.synchronize()
+    prod_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ops = 2.0 * M * N * K
+    G = K // group if group else 1
+    prod_bytes = 2 * M * K + M * K + 4 * M
+    ach = ops / (gemm_ms * 1e-3) / 1e12
+    out = {
+        "metric": "W4A8 linear TOPS & % INT8-MFMA peak",
+        "value": ops / (ms_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"w4a8_{args.w4a8}_m{M}_n{N}_k{K}_g{group}", "M": M, "N": N, "K": K,
+                   "group": group, "buffer_sets": n_sets},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": ach / PEAK_INT8_TOPS, "traffic": None, "kernel": "gemm_w4a8_kernel"},
+        "kernels": {"producer_us": prod_ms * 1e3, "producer_GBps": prod_bytes / (prod_ms * 1e-3) / 1e9,
+                    "gemm_us": gemm_ms * 1e3, "gemm_TOPS": ach,
+                    "gemm_GBps": (N * K / 2 + 4 * N * G + M * K + 4 * M + 2 * M * N) / (gemm_ms * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        _, qw = oracle.w4a8_quantize(X[:1], W, group)          # weights quantized beforehand
+        nn = np.arange(N, dtype=np.int32)
+
+        def run(rows):
+            t = time.perf_counter()
+            qa, _ = oracle.w4a8_quantize(X[:rows], W[:1], group)
+            oracle.w4a8_linear_at(qa, qw, group, np.repeat(np.arange(rows, dtype=np.int32), N),
+                                  np.tile(nn, rows))
+            return time.perf_counter() - t
+
+        dt0 = run(8)
+        r = int(min(M, max(8, 8 * args.cpu_budget / max(dt0, 1e-6))))
+        dt = run(r)
+        out["cpu_baseline"] = {"value": 2.0 * r * N * K / dt / 1e12, "unit": "TOPS",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"{r} of {M} token rows x all {N} output channels (weights "
+                                         f"quantized beforehand), {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(torch, nbytes, steps, warmup):
     """A plain copy of known size: it reads and writes exactly `nbytes` of HBM
     per launch, so the hardware counters it produces give the scale from
@@ -203,6 +306,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--select-outliers", default=None, choices=sorted(SELECT_WORKLOADS),
                     help="instead of the layer, time the offline outlier-channel selection")
+    ap.add_argument("--w4a8", default=None, choices=sorted(W4A8_WORKLOADS),
+                    help="instead of the W4A4 layer, time the W4A8 layer (INT8 producer + W4A8 GEMM)")
     ap.add_argument("--norm", action="store_true",
                     help="producer fused with the preceding RMSNorm (eps 1e-6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -224,6 +329,9 @@ def main():
         return
     if args.select_outliers:
         select_bench(torch, w4, args)
+        return
+    if args.w4a8:
+        w4a8_bench(torch, w4, args)
         return
 
     w = WORKLOADS[args.workload]
