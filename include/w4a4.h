@@ -210,7 +210,7 @@ w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamm
                                     int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
                                     void *workspace, size_t workspace_bytes, w4a4_stream stream);
 
-/* W4A8 GEMM (QQQ abstract: 4-bit weights with 8-bit activations, a
+/* W4A8 GEMM (the QQQ abstract on the "smoothquant" tag page: 4-bit weights with 8-bit activations, a
  * per-channel and a per-group GEMM), without outlier channels:
  *   Y[m, n] = fp16( sa8[m] * sum_t sw4[n, t] * acc_t[m, n] ),
  *   acc_t[m, n] = sum over the channels j of group t of qa8[m, j] * qw4[n, j].

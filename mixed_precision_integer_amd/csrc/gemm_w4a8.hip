@@ -3,8 +3,9 @@
 // channels), exact int32 accumulation on the i8 matrix cores, fp32 scale
 // epilogue, fp16 output.
 //
-// Method: the QQQ abstract (4-bit weights with 8-bit activations; a
-// per-channel and a per-group W4A8 GEMM). The operands come from this
+// Method: the QQQ abstract on the "smoothquant" tag page (4-bit weights
+// with 8-bit activations; a per-channel and a per-group W4A8 GEMM). The
+// operands come from this
 // library's own quantizer: activations are the INT8 rows it writes when every
 // channel is an "outlier" in the identity order, weights the INT4 rows it
 // writes with no outliers.

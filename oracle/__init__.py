@@ -270,7 +270,7 @@ def linear(X, W, outlier_idx, group: int):
 
 
 def w4a8_quantize(X, W, group: int):
-    """W4A8 operands (QQQ abstract): per-token INT8 activations over all K
+    """W4A8 operands (the QQQ abstract on the "smoothquant" tag page): per-token INT8 activations over all K
     channels and INT4 weights with one scale per output channel (group 0) or
     per `group` channels, both by the same symmetric quantizer (readings
     R1-R5), in the original channel order. Returns ((q8, s8), (q4, s4))."""

@@ -240,7 +240,7 @@ int w4o_linear_at(const int8_t *qa4, const float *sa4, const int8_t *qa8,
     return bad ? -1 : 0;
 }
 
-/* W4A8 layer (QQQ abstract: 4-bit weights, 8-bit activations, per-channel
+/* W4A8 layer (the QQQ abstract on the "smoothquant" tag page: 4-bit weights, 8-bit activations, per-channel
  * and per-group GEMMs) at selected output positions (m[p], n[p]):
  *   acc[p, t] = sum_{j in block t} qa8[m, j] * qw4[n, j]       (int64, exact)
  *   y[p] = sa8[m] * sum_t sw4[n, t] * acc[p, t]                 (fp64)

@@ -2,7 +2,7 @@
 against the oracle's W4A8 layer: per-token INT8 activation codes and scales,
 packed INT4 weight codes and scales, and the exported group accumulators
 bit-exact; Y within 1e-2 * max |Y_oracle|. W4A8 per channel and per group
-follows the QQQ abstract (4-bit weights, 8-bit activations).
+follows the QQQ abstract on the "smoothquant" tag page (4-bit weights, 8-bit activations).
 """
 import sys
 

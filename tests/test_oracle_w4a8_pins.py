@@ -1,4 +1,4 @@
-"""Pins for the oracle's W4A8 layer (QQQ abstract: 4-bit weights with 8-bit
+"""Pins for the oracle's W4A8 layer (the QQQ abstract on the "smoothquant" tag page: 4-bit weights with 8-bit
 activations, per-channel and per-group GEMMs).
 
 Definition: activations get one INT8 scale per token over all K channels,
