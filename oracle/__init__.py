@@ -313,3 +313,38 @@ def w4a8_linear(X, W, group: int):
     G = acc.shape[1]
     return {"qa": qa, "qw": qw, "acc": acc.reshape(M, N, G).transpose(2, 0, 1).copy(),
             "ystar": y.reshape(M, N), "Y": to_fp16(y.reshape(M, N))}
+
+
+def kv_quantize(X, bits: int):
+    """Low-bit KV cache (reading V1): every (token, head) vector of X [T, H, D]
+    (fp16) is one block of the symmetric quantizer (readings R1-R5), INT4
+    (qmax 7) or INT8 (qmax 127). Atom summary page, Summary paragraph 2: the
+    KV cache is stored in low bit-width. Returns (codes int8 [T, H, D],
+    scales fp32 [T, H])."""
+    X = np.asarray(X)
+    T, H, D = X.shape
+    rows = np.ascontiguousarray(X.reshape(T * H, D))
+    ident = np.arange(D, dtype=np.int32)
+    if bits == 4:
+        q, s, _, _ = quantize_rows(rows, ident, 0, 0)
+        return q.reshape(T, H, D), s.reshape(T, H)
+    if bits == 8:
+        _, _, q, s = quantize_rows(rows, ident, D, 0)
+        return q.reshape(T, H, D), s.reshape(T, H)
+    raise ValueError("bits must be 4 or 8")
+
+
+def kv_dequantize(q, s) -> np.ndarray:
+    """fp16(fl32(s * q)) for codes q [T, H, D] and scales s [T, H] (reading
+    V2): one correctly rounded fp32 product, then round to nearest even."""
+    prod = np.asarray(s, np.float32)[..., None] * np.asarray(q, np.int8).astype(np.float32)
+    return prod.astype(np.float16)
+
+
+def kv_pack(q, bits: int) -> np.ndarray:
+    """Cache bytes of codes q [T, H, D]: INT4 two per byte, low nibble first
+    (the layer's packing); INT8 one per byte. uint8 [T, H, D * bits / 8]."""
+    T, H, D = q.shape
+    if bits == 8:
+        return np.ascontiguousarray(q, np.int8).view(np.uint8)
+    return pack_nibbles(q.reshape(T * H, D), D // 2).reshape(T, H, D // 2)
