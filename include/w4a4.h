@@ -233,6 +233,34 @@ w4a4_status w4a4_w4a8_gemm(const void *Aq8, const float *sa8, const void *Wq4, c
 w4a4_status w4a4_w4a8_gemm_i32(const void *Aq8, const void *Wq4, int32_t M, int32_t N, int32_t K,
                                int32_t group, int32_t *acc, w4a4_stream stream);
 
+/* Low-bit KV cache (Atom summary page, Summary paragraph 2: the KV cache is
+ * kept in low bit-width; the NQKV abstract on the "smoothquant" tag page
+ * quantizes it block by block). Each (token, head) vector of D channels is
+ * one block of the layer's symmetric quantizer: s = fp32(absmax / qmax),
+ * q = round-half-even of the correctly rounded x / s, qmax 7 (bits 4) or 127
+ * (bits 8).
+ *   X       device fp16 [T, ldx]: token t's head h is X[t, h D .. h D + D)
+ *           (ldx >= H D, ldx % 8 == 0, 16-byte aligned)
+ *   slot_mapping device int32 [T]: the cache slot of each token, or NULL for
+ *           slot = t (then num_slots >= T). A slot outside [0, num_slots) is
+ *           skipped (nothing written).
+ *   cache_q device bytes [num_slots, H, D * bits / 8] (16-byte aligned): INT4
+ *           codes two per byte, low nibble first, or INT8 codes
+ *   cache_s device fp32 [num_slots, H]
+ * D in {64, 128, 256} (else UNSUPPORTED); bits in {4, 8}. */
+w4a4_status w4a4_kv_quant(const void *X, int64_t ldx, int32_t T, int32_t H, int32_t D, int32_t bits,
+                          const int32_t *slot_mapping, int64_t num_slots, void *cache_q, float *cache_s,
+                          w4a4_stream stream);
+
+/* Gather of T tokens from the cache back to fp16: Y[t, h D + c] =
+ * fp16(fp32(s * q)) (one correctly rounded fp32 product, then round to
+ * nearest even) for the slot slot_mapping[t] (NULL: slot t); a slot outside
+ * [0, num_slots) reads as zeros. Y device fp16 [T, ldy], ldy >= H D. Same
+ * cache arguments and constraints as w4a4_kv_quant. */
+w4a4_status w4a4_kv_dequant(const void *cache_q, const float *cache_s, int64_t num_slots,
+                            const int32_t *slot_mapping, int32_t T, int32_t H, int32_t D, int32_t bits,
+                            void *Y, int64_t ldy, w4a4_stream stream);
+
 /* Bytes of device workspace w4a4_select_outliers needs (0 for arguments it
  * would reject). A pure function of rows and K. */
 size_t w4a4_select_outliers_workspace_bytes(int32_t rows, int32_t K);

@@ -38,7 +38,7 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm",
             "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm",
             "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers",
-            "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32")
+            "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32", "w4a4_kv_quant", "w4a4_kv_dequant")
 
 
 class W4A4Error(RuntimeError):
@@ -100,6 +100,10 @@ def lib():
     L.w4a4_w4a8_gemm.restype = ctypes.c_int
     L.w4a4_w4a8_gemm_i32.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     L.w4a4_w4a8_gemm_i32.restype = ctypes.c_int
+    L.w4a4_kv_quant.argtypes = [vp, i64, i32, i32, i32, i32, vp, i64, vp, vp, vp]
+    L.w4a4_kv_quant.restype = ctypes.c_int
+    L.w4a4_kv_dequant.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, vp, i64, vp]
+    L.w4a4_kv_dequant.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -422,6 +426,42 @@ def w4a8_gemm_i32(a: W4A8Operand, w: W4A8Operand):
     _ok(lib().w4a4_w4a8_gemm_i32(_nz(a.q), _nz(w.q), M, N, a.K, w.group, _nz(acc), _stream()),
         "w4a4_w4a8_gemm_i32")
     return acc
+
+
+class KVCache:
+    """A slot-mapped low-bit KV cache for one tensor (keys or values):
+    codes uint8 [num_slots, H, D * bits / 8] and scales fp32 [num_slots, H]."""
+
+    def __init__(self, num_slots: int, H: int, D: int, bits: int, device):
+        torch = _torch()
+        self.num_slots, self.H, self.D, self.bits = num_slots, H, D, bits
+        self.q = torch.zeros((num_slots, H, D * bits // 8), dtype=torch.uint8, device=device)
+        self.s = torch.zeros((num_slots, H), dtype=torch.float32, device=device)
+
+    def store(self, X, slots=None):
+        """Quantize X [T, H * D] (fp16) into the slots (int32 [T], or None for 0..T-1)."""
+        torch = _torch()
+        _check(X, torch.float16, "X", 2)
+        if slots is not None:
+            _check(slots, torch.int32, "slots", 1)
+        T = X.shape[0]
+        _ok(lib().w4a4_kv_quant(X.data_ptr() if T else None, X.stride(0) if T else self.H * self.D, T,
+                                self.H, self.D, self.bits, _ptr(slots), self.num_slots, self.q.data_ptr(),
+                                self.s.data_ptr(), _stream()), "w4a4_kv_quant")
+
+    def load(self, slots=None, T=None, out=None):
+        """fp16 [T, H * D] of the given slots (None: slots 0..T-1)."""
+        torch = _torch()
+        if slots is not None:
+            _check(slots, torch.int32, "slots", 1)
+            T = slots.shape[0]
+        if out is None:
+            out = torch.empty((T, self.H * self.D), dtype=torch.float16, device=self.q.device)
+        _check(out, torch.float16, "out", 2)
+        _ok(lib().w4a4_kv_dequant(self.q.data_ptr(), self.s.data_ptr(), self.num_slots, _ptr(slots), T,
+                                  self.H, self.D, self.bits, out.data_ptr() if T else None,
+                                  out.stride(0) if T else self.H * self.D, _stream()), "w4a4_kv_dequant")
+        return out
 
 
 class W4A4Linear:

@@ -7,6 +7,7 @@
 #include <vector>
 
 #include "w4a4.h"
+#include "quant_internal.h"
 #include "w4a4_internal.h"
 #include "w4a8_internal.h"
 
@@ -416,6 +417,83 @@ w4a4_status w4a4_w4a8_gemm_i32(const void *Aq8, const void *Wq4, int32_t M, int3
     w4a4::GemmArgs a = w4a8_args(Aq8, nullptr, Wq4, nullptr, M, N, K, group);
     a.acc4_out = acc;
     if (w4a4::launch_gemm_w4a8(a, true, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+static w4a4_status kv_check(int32_t T, int32_t H, int32_t D, int32_t bits, int64_t num_slots,
+                            const void *cache_q, const float *cache_s, const int32_t *slots) {
+    if (T < 0 || H < 0 || num_slots < 0 || (bits != 4 && bits != 8))
+        return W4A4_ERR_INVALID_ARG;
+    if (D != 64 && D != 128 && D != 256)
+        return W4A4_ERR_UNSUPPORTED;
+    if ((int64_t)T * H == 0)
+        return W4A4_OK;
+    if (num_slots < 1 || !cache_q || !cache_s || (!slots && num_slots < T))
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(cache_q, 16) || !aligned(cache_s, 4) || (slots && !aligned(slots, 4)))
+        return W4A4_ERR_ALIGNMENT;
+    return W4A4_OK;
+}
+
+w4a4_status w4a4_kv_quant(const void *X, int64_t ldx, int32_t T, int32_t H, int32_t D, int32_t bits,
+                          const int32_t *slot_mapping, int64_t num_slots, void *cache_q, float *cache_s,
+                          w4a4_stream stream) {
+    w4a4_status st = kv_check(T, H, D, bits, num_slots, cache_q, cache_s, slot_mapping);
+    if (st != W4A4_OK)
+        return st;
+    if (ldx < (int64_t)H * D)
+        return W4A4_ERR_INVALID_ARG;
+    if ((int64_t)T * H == 0)
+        return W4A4_OK;
+    if (!X)
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || ldx % 8 != 0)
+        return W4A4_ERR_ALIGNMENT;
+    w4a4::KvArgs a;
+    memset(&a, 0, sizeof(a));
+    a.X = static_cast<const _Float16 *>(X);
+    a.ldx = ldx;
+    a.T = T;
+    a.H = H;
+    a.D = D;
+    a.bits = bits;
+    a.slots = slot_mapping;
+    a.num_slots = num_slots;
+    a.cq = static_cast<uint8_t *>(cache_q);
+    a.cs = cache_s;
+    if (w4a4::launch_kv(a, true, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+w4a4_status w4a4_kv_dequant(const void *cache_q, const float *cache_s, int64_t num_slots,
+                            const int32_t *slot_mapping, int32_t T, int32_t H, int32_t D, int32_t bits,
+                            void *Y, int64_t ldy, w4a4_stream stream) {
+    w4a4_status st = kv_check(T, H, D, bits, num_slots, cache_q, cache_s, slot_mapping);
+    if (st != W4A4_OK)
+        return st;
+    if (ldy < (int64_t)H * D)
+        return W4A4_ERR_INVALID_ARG;
+    if ((int64_t)T * H == 0)
+        return W4A4_OK;
+    if (!Y)
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(Y, 2))
+        return W4A4_ERR_ALIGNMENT;
+    w4a4::KvArgs a;
+    memset(&a, 0, sizeof(a));
+    a.Y = static_cast<_Float16 *>(Y);
+    a.ldy = ldy;
+    a.T = T;
+    a.H = H;
+    a.D = D;
+    a.bits = bits;
+    a.slots = slot_mapping;
+    a.num_slots = num_slots;
+    a.cq = static_cast<uint8_t *>(const_cast<void *>(cache_q));
+    a.cs = const_cast<float *>(cache_s);
+    if (w4a4::launch_kv(a, false, static_cast<hipStream_t>(stream)) != hipSuccess)
         return W4A4_ERR_HIP;
     return W4A4_OK;
 }

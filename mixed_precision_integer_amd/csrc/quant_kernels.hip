@@ -45,7 +45,7 @@
 #include <algorithm>
 #include <atomic>
 
-#include "w4a4_internal.h"
+#include "quant_internal.h"
 
 namespace w4a4 {
 namespace quant_impl {

@@ -26,7 +26,7 @@
 //   lower-index rule and give every channel its output position.
 #include <algorithm>
 
-#include "w4a4_internal.h"
+#include "quant_internal.h"
 
 namespace w4a4 {
 namespace select_impl {

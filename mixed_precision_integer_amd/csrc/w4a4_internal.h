@@ -45,27 +45,6 @@ __device__ __forceinline__ void dma4(const void *p, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(p), "s"(sl) : "memory", "m0");
 }
 
-// Arguments of the row quantizer: one launch quantizes `rows` rows of a
-// [rows, ld] fp16 matrix (activations or weights).
-struct QuantArgs {
-    const _Float16 *src;
-    int64_t ld;
-    const int32_t *perm;
-    int32_t rows, K, n_out, K_n, group, G;
-    uint8_t *q4;          // [rows, pitch4]
-    int8_t *q8;           // [rows, pitch8]
-    float *s4;            // [rows, G]
-    float *s8;            // [rows] or nullptr
-    int64_t pitch4, pitch8;
-    // RMSNorm in front of the quantizer (nullptr gamma: none)
-    const _Float16 *gamma;  // [K] norm weight, original channel order
-    float eps;
-    float *rstd;          // [rows] norm factor per row, or nullptr
-};
-
-hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream);
-int quant_rows_max_k();   // longest row (channels) the quantizer takes
-
 // Arguments of the mixed-precision GEMM.
 struct GemmArgs {
     const uint8_t *a4;    // [M, pitch4] packed INT4 activations
@@ -115,26 +94,5 @@ hipError_t launch_gemm_group(const GemmArgs &a, hipStream_t stream);
 // 256 x 256 tile kernel for one scale group per row (gemm_big.hip).
 bool gemm_big_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t G);
 hipError_t launch_gemm_big(const GemmArgs &a, bool export_acc, hipStream_t stream);
-
-// Offline outlier-channel selection (select_kernels.hip).
-struct SelectArgs {
-    const void *X;        // [rows, ld] fp16 calibration batch
-    int64_t ld;
-    int32_t rows, K, n_out;
-    int32_t *outlier_idx; // [n_out] or nullptr
-    int32_t *perm;        // [K]
-    void *absmax;         // [K] fp16 or nullptr
-    void *workspace;      // plan_select(rows, K).workspace_bytes, 256-byte aligned
-};
-
-struct SelectPlan {
-    int stripes, chunks, rows_per_chunk;
-    int64_t kp;                   // channels rounded up to 8
-    size_t keys_offset, workspace_bytes;
-};
-
-SelectPlan plan_select(int32_t rows, int32_t K);
-int select_max_k();
-hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 
 }  // namespace w4a4

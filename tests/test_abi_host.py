@@ -196,6 +196,27 @@ def test_w4a8_empty_is_ok():
     assert w4.lib().w4a4_w4a8_gemm_i32(None, None, 0, 8, 256, 0, None, None) == OK
 
 
+def kvq(**kw):
+    args = dict(X=FAKE, ldx=512, T=4, H=4, D=128, bits=4, slots=None, num_slots=8, cq=FAKE, cs=FAKE)
+    args.update(kw)
+    return w4.lib().w4a4_kv_quant(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=5), INVALID), (dict(D=96), UNSUPPORTED), (dict(num_slots=0), INVALID), (dict(num_slots=3), INVALID),
+    (dict(ldx=256), INVALID), (dict(X=None), INVALID), (dict(cq=None), INVALID), (dict(T=-1), INVALID),
+    (dict(X=FAKE + 2), ALIGN), (dict(ldx=516), ALIGN), (dict(cq=FAKE + 4), ALIGN), (dict(cs=FAKE + 2), ALIGN),
+])
+def test_kv_quant_rejects(kw, code):
+    assert kvq(**kw) == code
+
+
+def test_kv_empty_is_ok():
+    assert kvq(T=0, X=None, cq=None, cs=None) == OK
+    assert w4.lib().w4a4_kv_dequant(None, None, 0, None, 0, 4, 128, 4, None, 512, None) == OK
+    assert w4.lib().w4a4_kv_dequant(FAKE, FAKE, 8, None, 4, 4, 128, 8, FAKE, 256, None) == INVALID  # ldy < H D
+
+
 def test_quant_empty_is_ok():
     assert quant(rows=0, X=None, perm=None, q4=None, q8=None, s4=None, s8=None) == OK
 
