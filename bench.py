@@ -272,6 +272,75 @@ def w4a8_bench(torch, w4, args):
     print(json.dumps(out), flush=True)
 
 
+KV_WORKLOADS = {
+    # name: (tokens, heads, head dim, bits): a Llama-65B-style prefill of
+    # 8 x 2048 tokens appended to the key (or value) cache
+    "int4": (16384, 64, 128, 4),
+    "int8": (16384, 64, 128, 8),
+}
+
+
+def kv_bench(torch, w4, args):
+    """Low-bit KV cache: a step quantizes one tensor's new tokens into the
+    cache (w4a4_kv_quant) and gathers them back (w4a4_kv_dequant). Prints its
+    own JSON line; value = bytes both calls must move / step time."""
+    T, H, D, bits = KV_WORKLOADS[args.kv]
+    rng = np.random.default_rng(T + bits)
+    X = (rng.standard_normal((T, H * D), dtype=np.float32)
+         * rng.choice([0.05, 1.0, 30.0], (T, H)).repeat(D, axis=1).astype(np.float32)).astype(np.float16)
+    dev = torch.device("cuda:0")
+    n_sets = max(2, math.ceil(ROTATE_BYTES / (T * H * D * 2 * 2)))
+    slots = torch.from_numpy(np.random.default_rng(1).permutation(2 * T)[:T].astype(np.int32)).to(dev)
+    sets = [(torch.from_numpy(X).to(dev), w4.KVCache(2 * T, H, D, bits, dev),
+             torch.empty((T, H * D), dtype=torch.float16, device=dev)) for _ in range(n_sets)]
+    for i in range(args.warmup):
+        x, c, y = sets[i % n_sets]
+        c.store(x, slots)
+        c.load(slots, out=y)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, e in enumerate(ev):
+        x, c, y = sets[i % n_sets]
+        e[0].record()
+        c.store(x, slots)
+        e[1].record()
+        c.load(slots, out=y)
+        e[2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    d_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    code_bytes = T * H * (D * bits // 8 + 4)
+    q_bytes = T * H * D * 2 + code_bytes + 4 * T
+    d_bytes = code_bytes + T * H * D * 2 + 4 * T
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    out = {
+        "metric": "low-bit KV cache GB/s (quantize into the cache + gather back) & % HBM",
+        "value": (q_bytes + d_bytes) / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": f"int{bits}", "data": "synthetic",
+        "config": {"workload": f"kv_cache_t{T}_h{H}_d{D}_int{bits}", "T": T, "H": H, "D": D, "bits": bits,
+                   "buffer_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": q_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": q_gbs / PEAK_HBM_GBS, "traffic": None, "kernel": f"kv_quant_kernel<2, {bits}>"},
+        "kernels": {"quant_us": q_ms * 1e3, "quant_GBps": q_gbs, "dequant_us": d_ms * 1e3,
+                    "dequant_GBps": d_bytes / (d_ms * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        r = min(T, 2048)
+        t = time.perf_counter()
+        q, s = oracle.kv_quantize(X[:r].reshape(r, H, D), bits)
+        oracle.kv_dequantize(q, s)
+        dt = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": r * H * D * 2 * 2 / dt / 1e9, "unit": "GB/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"{r} of {T} tokens, quantize + dequantize, {dt:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(torch, nbytes, steps, warmup):
     """A plain copy of known size: it reads and writes exactly `nbytes` of HBM
     per launch, so the hardware counters it produces give the scale from
@@ -308,6 +377,8 @@ def main():
                     help="instead of the layer, time the offline outlier-channel selection")
     ap.add_argument("--w4a8", default=None, choices=sorted(W4A8_WORKLOADS),
                     help="instead of the W4A4 layer, time the W4A8 layer (INT8 producer + W4A8 GEMM)")
+    ap.add_argument("--kv", default=None, choices=sorted(KV_WORKLOADS),
+                    help="instead of the layer, time the low-bit KV cache (quantize + gather)")
     ap.add_argument("--norm", action="store_true",
                     help="producer fused with the preceding RMSNorm (eps 1e-6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -332,6 +403,9 @@ def main():
         return
     if args.w4a8:
         w4a8_bench(torch, w4, args)
+        return
+    if args.kv:
+        kv_bench(torch, w4, args)
         return
 
     w = WORKLOADS[args.workload]

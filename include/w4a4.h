@@ -255,8 +255,9 @@ w4a4_status w4a4_kv_quant(const void *X, int64_t ldx, int32_t T, int32_t H, int3
 /* Gather of T tokens from the cache back to fp16: Y[t, h D + c] =
  * fp16(fp32(s * q)) (one correctly rounded fp32 product, then round to
  * nearest even) for the slot slot_mapping[t] (NULL: slot t); a slot outside
- * [0, num_slots) reads as zeros. Y device fp16 [T, ldy], ldy >= H D. Same
- * cache arguments and constraints as w4a4_kv_quant. */
+ * [0, num_slots) reads as zeros. Y device fp16 [T, ldy], ldy >= H D,
+ * 16-byte aligned with ldy % 8 == 0. Same cache arguments and constraints as
+ * w4a4_kv_quant. */
 w4a4_status w4a4_kv_dequant(const void *cache_q, const float *cache_s, int64_t num_slots,
                             const int32_t *slot_mapping, int32_t T, int32_t H, int32_t D, int32_t bits,
                             void *Y, int64_t ldy, w4a4_stream stream);

@@ -479,7 +479,7 @@ w4a4_status w4a4_kv_dequant(const void *cache_q, const float *cache_s, int64_t n
         return W4A4_OK;
     if (!Y)
         return W4A4_ERR_INVALID_ARG;
-    if (!aligned(Y, 2))
+    if (!aligned(Y, 16) || ldy % 8 != 0)
         return W4A4_ERR_ALIGNMENT;
     w4a4::KvArgs a;
     memset(&a, 0, sizeof(a));

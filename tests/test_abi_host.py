@@ -215,6 +215,8 @@ def test_kv_empty_is_ok():
     assert kvq(T=0, X=None, cq=None, cs=None) == OK
     assert w4.lib().w4a4_kv_dequant(None, None, 0, None, 0, 4, 128, 4, None, 512, None) == OK
     assert w4.lib().w4a4_kv_dequant(FAKE, FAKE, 8, None, 4, 4, 128, 8, FAKE, 256, None) == INVALID  # ldy < H D
+    assert w4.lib().w4a4_kv_dequant(FAKE, FAKE, 8, None, 4, 4, 128, 8, FAKE + 2, 512, None) == ALIGN
+    assert w4.lib().w4a4_kv_dequant(FAKE, FAKE, 8, None, 4, 4, 128, 8, FAKE, 516, None) == ALIGN
 
 
 def test_quant_empty_is_ok():
