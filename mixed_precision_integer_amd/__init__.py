@@ -465,9 +465,11 @@ class KVCache:
 
 
 class W4A4Linear:
-    """A linear layer y = x W^T with W held as packed INT4 + INT8 outlier columns."""
+    """A linear layer y = x W^T with W held as packed INT4 + INT8 outlier
+    columns; with norm_weight (fp16 [K]) the layer first applies the RMSNorm
+    in front of it, fused into its producer."""
 
-    def __init__(self, weight, outlier_idx, group: int = 0):
+    def __init__(self, weight, outlier_idx, group: int = 0, norm_weight=None, eps: float = 1e-6):
         torch = _torch()
         K = weight.shape[1]
         self.outlier_idx = np.asarray(outlier_idx, np.int32)
@@ -475,6 +477,7 @@ class W4A4Linear:
         self.n_out = int(self.outlier_idx.size)
         self.group = group
         self.weight = pack_int4_weights(weight, self.perm, self.n_out, group)
+        self.norm_weight, self.eps = norm_weight, eps
         self._ws = None
 
     def __call__(self, X, out=None):
@@ -482,6 +485,9 @@ class W4A4Linear:
                                           self.n_out, self.group)
         if self._ws is None or self._ws.numel() < need:
             self._ws = _torch().zeros(max(need, 1), dtype=_torch().uint8, device=X.device)
+        if self.norm_weight is not None:
+            return rmsnorm_quant_gemm(X, self.norm_weight, self.eps, self.perm, self.weight, out=out,
+                                      workspace=self._ws)
         return quant_gemm(X, self.perm, self.weight, out=out, workspace=self._ws)
 
 

@@ -172,6 +172,21 @@ def test_norm_full_size_qproj_layer(oracle):
     assert np.abs(got.astype(np.float64) - ref).max() <= TOL * np.abs(ref).max()
 
 
+def test_norm_layer_object(oracle):
+    """W4A4Linear with a norm weight runs the fused RMSNorm layer."""
+    M, N, K, n_out, group = 24, 96, 512, 128, 128
+    _say("norm W4A4Linear")
+    X, W, o = wl.draw(M, N, K, n_out, seed=77, outlier_factor=30.0)
+    g = wl.draw_norm_weight(K, seed=77)
+    gd = torch.from_numpy(g).to(DEV)
+    layer = w4.W4A4Linear(torch.from_numpy(W).to(DEV), o, group, norm_weight=gd, eps=1e-6)
+    Xd = torch.from_numpy(X).to(DEV)
+    y = layer(Xd)
+    y2 = w4.rmsnorm_quant_gemm(Xd, gd, 1e-6, layer.perm, layer.weight)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
 def test_norm_empty_batch():
     K = 256
     X = torch.zeros((0, K), dtype=torch.float16, device=DEV)

@@ -50,6 +50,8 @@ SELECT = [
     (5, 300, 300),          # everything selected
     (3, 32768, 700),        # the widest row the selection takes
     (1, 8, 1),
+    (4, 1, 1),              # one channel (a partial 8-channel group)
+    (9, 7, 3),              # fewer channels than one 16-byte load
 ]
 
 
