@@ -141,7 +141,9 @@ struct RowLds {
 
 // WIDE_TAIL: the outlier tail may need more than one 4-channel word per lane.
 // Up to 512 lanes a workgroup is register-limited: 64 VGPRs (eight waves per
-// SIMD) keep every workgroup the occupancy query counts resident at once.
+// SIMD) keep every workgroup the occupancy query counts resident at once;
+// the FULL layout takes up to 84 VGPRs (six waves per SIMD), which measured
+// faster than spilling at 64.
 //
 // NORM: the row is RMS-normalized first (the norm that precedes the layer,
 // fused so that its fp16 output never goes to memory). The lane's gathered
@@ -153,9 +155,16 @@ struct RowLds {
 // operations, normalizes its values in registers and only then takes the
 // absmax. The norm weights of the lane's channels are gathered once per
 // workgroup, like the permutation.
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL && !NORM ? 8 : 4)))
+//
+// FULL: K and K_n are multiples of 8 (so n_out is too) and the tail fits one
+// word per lane: every head unit and tail word lies wholly inside the row,
+// so no entry needs a bounds check of its own. One mask per unit replaces
+// the per-channel conditions, whose exec masks would otherwise stay live
+// across the row loop and spill.
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL && !NORM ? (FULL ? 6 : 8) : 4)))
 void quant_rows_kernel(QuantArgs a) {
+    static_assert(!(FULL && WIDE_TAIL), "a full-row layout has one tail word per lane");
     using L = RowLds<KMAX, THREADS>;
     constexpr int NW = THREADS / 64;
     constexpr int UMAX = (KMAX / 8 + THREADS - 1) / THREADS;    // head units (8 channels) per lane
@@ -220,7 +229,7 @@ void quant_rows_kernel(QuantArgs a) {
         }
         const bool tail4 = (K_n & 3) == 0;
         auto entry = [&](int j) { return a.perm ? a.perm[j] : j; };
-        auto fix = [&](int v, int j) { return (j >= 4 * K4 && j < K) ? entry(j) : v; };
+        auto fix = [&](int v, int j) { return (!FULL && j >= 4 * K4 && j < K) ? entry(j) : v; };
         auto pack = [](int lo, int hi) { return (uint32_t)(lo & 0xFFFF) | ((uint32_t)hi << 16); };
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
@@ -233,7 +242,7 @@ void quant_rows_kernel(QuantArgs a) {
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
             const int j0 = K_n + (i * THREADS + tid) * 4;
-            if (tail4) {
+            if (FULL || tail4) {
                 pt[i][0] = pack(fix(f[i].x, j0), fix(f[i].y, j0 + 1));
                 pt[i][1] = pack(fix(f[i].z, j0 + 2), fix(f[i].w, j0 + 3));
             } else {
@@ -318,7 +327,12 @@ void quant_rows_kernel(QuantArgs a) {
         for (int i = 0; i < UMAX; ++i) {
             const int u = i * THREADS + tid;
             const int j0 = u * 8;
-            if (u < U && j0 + 8 <= K_n) {
+            if constexpr (FULL) {                  // entries are valid row positions even past U
+                const uint32_t keep = u < U ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    v[i][k] = ((uint32_t)xs[pv[i][k] & 0xFFFF] | ((uint32_t)xs[pv[i][k] >> 16] << 16)) & keep;
+            } else if (u < U && j0 + 8 <= K_n) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     v[i][k] = (uint32_t)xs[pv[i][k] & 0xFFFF] | ((uint32_t)xs[pv[i][k] >> 16] << 16);
@@ -337,12 +351,19 @@ void quant_rows_kernel(QuantArgs a) {
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
             const int w = i * THREADS + tid;
+            if constexpr (FULL) {
+                const uint32_t keep = 4 * w < n_out ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int j = K_n + 4 * w + 2 * k;
-                const uint32_t lo = j < K ? xs[pt[i][k] & 0xFFFF] : 0u;
-                const uint32_t hi = j + 1 < K ? xs[pt[i][k] >> 16] : 0u;
-                tv[i][k] = lo | (hi << 16);
+                for (int k = 0; k < 2; ++k)
+                    tv[i][k] = ((uint32_t)xs[pt[i][k] & 0xFFFF] | ((uint32_t)xs[pt[i][k] >> 16] << 16)) & keep;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int j = K_n + 4 * w + 2 * k;
+                    const uint32_t lo = j < K ? xs[pt[i][k] & 0xFFFF] : 0u;
+                    const uint32_t hi = j + 1 < K ? xs[pt[i][k] >> 16] : 0u;
+                    tv[i][k] = lo | (hi << 16);
+                }
             }
             if (!NORM)
                 tail_absmax(i);
@@ -453,14 +474,16 @@ void quant_rows_kernel(QuantArgs a) {
                 const int w = i * THREADS + tid;
                 if (w < W8) {
                     uint32_t word = 0;
+                    if (!FULL || 4 * w < n_out) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int j = K_n + 4 * w + k;
-                        if (j < K) {
-                            const uint32_t h = (k & 1) ? (tv[i][k >> 1] >> 16) : (tv[i][k >> 1] & 0xFFFF);
-                            const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-                            const int q = (int)__builtin_rintf(exact_quotient(x, s8, r8));
-                            word |= (uint32_t)(q & 0xFF) << (8 * k);
+                        for (int k = 0; k < 4; ++k) {
+                            const int j = K_n + 4 * w + k;
+                            if (FULL || j < K) {
+                                const uint32_t h = (k & 1) ? (tv[i][k >> 1] >> 16) : (tv[i][k >> 1] & 0xFFFF);
+                                const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+                                const int q = (int)__builtin_rintf(exact_quotient(x, s8, r8));
+                                word |= (uint32_t)(q & 0xFF) << (8 * k);
+                            }
                         }
                     }
                     q8row[w] = word;
@@ -649,7 +672,7 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
 
 // Resident workgroups of one instantiation on the current device, queried on
 // first use (a launch then costs no runtime queries).
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM>
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL>
 long resident_slots() {
     static std::atomic<long> cached[kMaxDevices];
     int dev = 0;
@@ -663,7 +686,7 @@ long resident_slots() {
     int cus = 256, per_cu = 1;
     if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL>,
                                                      THREADS, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
     const long slots = (long)cus * per_cu;
@@ -672,19 +695,21 @@ long resident_slots() {
     return slots;
 }
 
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM>
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL>
 hipError_t launch_tail(const QuantArgs &a, hipStream_t stream) {
-    const int grid = (int)std::min<long>(a.rows, resident_slots<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM>());
-    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM>), dim3(grid), dim3(THREADS),
-                       0, stream, a);
+    const int grid = (int)std::min<long>(a.rows, resident_slots<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL>());
+    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL>), dim3(grid),
+                       dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int KMAX, int THREADS, bool GROUPED, bool NORM>
 hipError_t launch(const QuantArgs &a, hipStream_t stream) {
     if (a.pitch8 / 4 > THREADS)                   // more than one tail word per lane
-        return launch_tail<KMAX, THREADS, GROUPED, true, NORM>(a, stream);
-    return launch_tail<KMAX, THREADS, GROUPED, false, NORM>(a, stream);
+        return launch_tail<KMAX, THREADS, GROUPED, true, NORM, false>(a, stream);
+    if (a.K % 8 == 0 && a.K_n % 8 == 0)           // every unit and tail word inside the row
+        return launch_tail<KMAX, THREADS, GROUPED, false, NORM, true>(a, stream);
+    return launch_tail<KMAX, THREADS, GROUPED, false, NORM, false>(a, stream);
 }
 
 // Row-length buckets: (longest row, lanes per workgroup).
