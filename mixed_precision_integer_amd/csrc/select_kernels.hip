@@ -160,7 +160,9 @@ __device__ void find_crossing(const uint32_t *hist, uint32_t need, int *bin_out,
             incl += o;
     }
     const uint64_t hit = __ballot(incl >= need);
-    const int first = __builtin_ctzll(hit);    // a crossing exists: the counts sum to >= need
+    // the counts sum to at least `need`, so some lane crosses; the guard keeps
+    // the bit scan defined even if that did not hold
+    const int first = hit ? __builtin_ctzll(hit) : 63;
     if (lane == first) {
         uint32_t above = incl - s;
         int j = 0;
