@@ -138,8 +138,8 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "") -> s
              "are not part of a step.\n")
     k = bj["kernels"]
     roof = bj["roofline"]
-    L.append("bench.py line printed in the same run (HIP events on the launch stream around each GEMM "
-             "launch of the timed region): producer %.2f µs, GEMM %.2f µs, step %.2f µs, value %.1f %s; "
+    L.append("bench.py line printed in the same run (HIP events on the launch stream around every eighth "
+             "GEMM launch of the timed region): producer %.2f µs, GEMM %.2f µs, step %.2f µs, value %.1f %s; "
              "roofline: %.1f of %.0f %s (%.1f%%, %s-bound).\n"
              % (k["producer_us"], k["gemm_us"], bj["ms_per_step"] * 1e3, bj["value"], bj["unit"],
                 roof["achieved"], roof["peak"], roof["unit"], 100 * roof["frac"], roof["bound"]))
