@@ -220,9 +220,7 @@ def summarize_kernels(d: str, bench_args: str, title: str, out: str) -> str:
             f"{roof['peak']:.0f} {roof['unit']} ({100 * roof['frac']:.1f}%, {roof['bound']}-bound, "
             f"{roof['kernel']})")
     if "kernels" in bj:
-        k = bj["kernels"]
-        line += (f"; producer {k['producer_us']:.2f} µs ({k['producer_GBps']:.0f} GB/s), "
-                 f"GEMM {k['gemm_us']:.2f} µs")
+        line += "; " + ", ".join(f"{key} {val:.2f}" for key, val in bj["kernels"].items())
     L.append(line + ".\n")
     L.append("## HBM traffic (rocprofv3 --pmc, one counter per run)\n")
     cmds = [("FETCH_SIZE", "fetch", f"{run} --steps 5 --warmup 2 --no-cpu-baseline"),
