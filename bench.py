@@ -334,7 +334,7 @@ def kv_bench(torch, w4, args):
         "config": {"workload": f"kv_cache_t{T}_h{H}_d{D}_int{bits}", "T": T, "H": H, "D": D, "bits": bits,
                    "buffer_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": q_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": q_gbs / PEAK_HBM_GBS, "traffic": None, "kernel": f"kv_quant_kernel<2, {bits}>"},
+                     "frac": q_gbs / PEAK_HBM_GBS, "traffic": None, "kernel": f"kv_quant_kernel<16, {bits}>"},
         "kernels": {"quant_us": q_ms * 1e3, "quant_GBps": q_gbs, "dequant_us": d_ms * 1e3,
                     "dequant_GBps": d_bytes / (d_ms * 1e-3) / 1e9},
     }

@@ -45,7 +45,7 @@ __device__ __forceinline__ float hi_f(uint32_t p) { return (float)__builtin_bit_
 
 // SEG = D / 8 lanes per head vector; HPW = 64 / SEG head vectors per step.
 template <int SEG, int BITS>
-__global__ __launch_bounds__(256) void kv_quant_kernel(const _Float16 *X, int64_t ldx, int T, int H,
+__global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t *X, int64_t ldx, int T, int H,
                                                        const int32_t *slots, int64_t num_slots, uint8_t *cq,
                                                        float *cs) {
     constexpr int D = 8 * SEG, HPW = 64 / SEG;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const _Float16 *X, int64_
 
 template <int SEG, int BITS>
 __global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t *cq, const float *cs, int64_t num_slots,
-                                                         const int32_t *slots, int T, int H, _Float16 *Y,
+                                                         const int32_t *slots, int T, int H, uint16_t *Y,
                                                          int64_t ldy) {
 #pragma clang fp contract(off)
     constexpr int D = 8 * SEG, HPW = 64 / SEG;
@@ -161,6 +161,10 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t *cq, cons
     }
 }
 
+// fp16 data passes to the kernels as its bit patterns (uint16_t), so that
+// kernel names in traces demangle.
+inline const uint16_t *fp16_bits(const _Float16 *p) { return reinterpret_cast<const uint16_t *>(p); }
+
 template <int SEG>
 hipError_t launch_seg(const KvArgs &a, bool quant, hipStream_t stream) {
     constexpr int HPW = 64 / SEG;
@@ -169,18 +173,18 @@ hipError_t launch_seg(const KvArgs &a, bool quant, hipStream_t stream) {
     const int grid = (int)((nvec + per_group - 1) / per_group);
     if (quant) {
         if (a.bits == 4)
-            hipLaunchKernelGGL((kv_quant_kernel<SEG, 4>), dim3(grid), dim3(256), 0, stream, a.X, a.ldx, a.T, a.H,
+            hipLaunchKernelGGL((kv_quant_kernel<SEG, 4>), dim3(grid), dim3(256), 0, stream, fp16_bits(a.X), a.ldx, a.T, a.H,
                                a.slots, a.num_slots, a.cq, a.cs);
         else
-            hipLaunchKernelGGL((kv_quant_kernel<SEG, 8>), dim3(grid), dim3(256), 0, stream, a.X, a.ldx, a.T, a.H,
+            hipLaunchKernelGGL((kv_quant_kernel<SEG, 8>), dim3(grid), dim3(256), 0, stream, fp16_bits(a.X), a.ldx, a.T, a.H,
                                a.slots, a.num_slots, a.cq, a.cs);
     } else {
         if (a.bits == 4)
             hipLaunchKernelGGL((kv_dequant_kernel<SEG, 4>), dim3(grid), dim3(256), 0, stream, a.cq, a.cs,
-                               a.num_slots, a.slots, a.T, a.H, a.Y, a.ldy);
+                               a.num_slots, a.slots, a.T, a.H, reinterpret_cast<uint16_t *>(a.Y), a.ldy);
         else
             hipLaunchKernelGGL((kv_dequant_kernel<SEG, 8>), dim3(grid), dim3(256), 0, stream, a.cq, a.cs,
-                               a.num_slots, a.slots, a.T, a.H, a.Y, a.ldy);
+                               a.num_slots, a.slots, a.T, a.H, reinterpret_cast<uint16_t *>(a.Y), a.ldy);
     }
     return hipGetLastError();
 }
