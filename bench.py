@@ -62,7 +62,10 @@ def work_counts(w, M, norm=False):
     a_bytes = M * K_n / 2 + M * n_out + 4 * M * G + 4 * M
     gemm_bytes = w_bytes + a_bytes + 2 * M * N
     producer_bytes = 2 * M * K + a_bytes + (2 * K if norm else 0)
-    return ops, gemm_bytes, producer_bytes
+    # one launch (quantizer inside the GEMM): fp16 tokens and the permutation
+    # in place of the codes
+    one_launch_bytes = w_bytes + 2 * M * K + 4 * K + 2 * M * N
+    return ops, gemm_bytes, producer_bytes, one_launch_bytes
 
 
 def traffic_record(workload_name, M):
@@ -444,11 +447,18 @@ def main():
     if args.norm:
         norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
     plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq), norm=norm) for _ in range(n_sets)]
+    # Small decode batches run the layer as one launch (the quantizer inside
+    # the GEMM's workgroups); every other shape as producer + GEMM.
+    one_launch = norm is None and \
+        w4.quant_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group) == "decode_fused_kernel"
 
     for i in range(args.warmup):
         p = plans[i % n_sets]
-        p.produce()
-        p.gemm()
+        if one_launch:
+            p.fused()
+        else:
+            p.produce()
+            p.gemm()
     torch.cuda.synchronize()
 
     # Timed region: K whole steps. Only the dominant kernel (the GEMM) is
@@ -461,11 +471,15 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         p = plans[i % n_sets]
-        p.produce()
+        if not one_launch:
+            p.produce()
         e = ev.get(i)
         if e:
             e[0].record()
-        p.gemm()
+        if one_launch:
+            p.fused()
+        else:
+            p.gemm()
         if e:
             e[1].record()
     torch.cuda.synchronize()
@@ -474,7 +488,7 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
     gemm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev.values()]))
     # the producer's share, from events around it alone (after the timed region)
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(min(K, 50))]
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(0 if one_launch else min(K, 50))]
     for i, e in enumerate(pev):
         p = plans[i % n_sets]
         e[0].record()
@@ -482,8 +496,10 @@ def main():
         e[1].record()
         p.gemm()
     torch.cuda.synchronize()
-    prod_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
-    ops, gemm_bytes, prod_bytes = work_counts(w, M, args.norm)
+    prod_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev])) if pev else None
+    ops, gemm_bytes, prod_bytes, one_bytes = work_counts(w, M, args.norm)
+    if one_launch:
+        gemm_bytes = one_bytes
     value = ops / (ms_step * 1e-3) / 1e12
 
     mem_bound = ops / gemm_bytes < PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -495,15 +511,19 @@ def main():
         ach = ops / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "frac": ach / PEAK_INT8_TOPS}
-    roof["kernel"] = w4.outlier_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group)
+    roof["kernel"] = (w4.quant_gemm_kernel_name if one_launch else w4.outlier_gemm_kernel_name)(
+        M, w.N, w.K, w.n_out, w.group)
     roof["traffic"] = traffic_record(w.name, M)
 
-    # the result is checked against a fused call (same kernels, same bits)
+    # the result is checked: the fused call against producer + GEMM (the same
+    # bits whether the fused call takes one launch or two)
     yf = torch.empty_like(plans[0].out)
     if norm is None:
         w4.quant_gemm(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
     else:
         w4.rmsnorm_quant_gemm(plans[0]._keep[0], norm[0], norm[1], perm, plans[0]._keep[2], out=yf)
+    plans[0].produce()
+    plans[0].gemm()
     torch.cuda.synchronize()
     if not torch.equal(yf, plans[0].out):
         raise SystemExit("fused call and producer + GEMM disagree")
@@ -523,12 +543,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": w.N, "K": w.K, "n_out": w.n_out,
                    "group": w.group, "buffer_sets": n_sets,
-                   "producer": "rmsnorm_fused" if args.norm else "plain"},
+                   "producer": "rmsnorm_fused" if args.norm else ("in_gemm" if one_launch else "plain")},
         "roofline": roof,
         "kernels": {
-            "producer_us": prod_ms * 1e3,
-            "producer_GBps": prod_bytes / (prod_ms * 1e-3) / 1e9,
-            "producer_hbm_frac": prod_bytes / (prod_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "producer_us": prod_ms * 1e3 if prod_ms else None,
+            "producer_GBps": prod_bytes / (prod_ms * 1e-3) / 1e9 if prod_ms else None,
+            "producer_hbm_frac": prod_bytes / (prod_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if prod_ms else None,
             "gemm_us": gemm_ms * 1e3,
             "gemm_TOPS": ops / (gemm_ms * 1e-3) / 1e12,
             "gemm_GBps": gemm_bytes / (gemm_ms * 1e-3) / 1e9,

@@ -184,6 +184,13 @@ w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *
                                   int32_t n_out, int32_t group, int32_t *acc4,
                                   int32_t *acc8, w4a4_stream stream);
 
+/* Name of the GPU kernel that computes w4a4_quant_gemm's product for this
+ * shape: "decode_fused_kernel" when the quantizer is fused into it (see
+ * w4a4_quant_gemm), else the kernel w4a4_outlier_gemm launches. A static
+ * string owned by the library, or NULL for a shape the call would reject. */
+const char *w4a4_quant_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                        int32_t group);
+
 /* Bytes of device workspace w4a4_quant_gemm needs: the quantized activations
  * (Aq4, Aq8, sa4, sa8 for M rows) plus the GEMM's own workspace, under the
  * same zero-on-first-use rule as w4a4_outlier_gemm's workspace. */
@@ -193,7 +200,11 @@ size_t w4a4_quant_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t 
 /* The fused layer (Atom summary page, Interesting ideas I2: quantization and
  * reordering run as part of the layer's own launches): w4a4_quant_reorder_act
  * on X into the caller's workspace, then w4a4_outlier_gemm with the
- * pre-packed weights, both on `stream`. */
+ * pre-packed weights, both on `stream`. Small decode batches (M <= 2,
+ * group 128, n_out <= 128, K_n <= 16384) take one launch instead: the GEMM's
+ * workgroups gather and quantize the token rows themselves, with the same
+ * arithmetic, so Y is bit-identical to the two-launch result; the workspace is
+ * then left untouched. */
 w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
                             const void *Wq8, const float *sw4, const float *sw8, int32_t M,
                             int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,

@@ -35,7 +35,7 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_make_perm", "w4a4_quant_reorder_act", "w4a4_pack_int4_weights",
             "w4a4_outlier_gemm_workspace_bytes", "w4a4_outlier_gemm_kernel_name", "w4a4_outlier_gemm",
             "w4a4_outlier_gemm_i32",
-            "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm",
+            "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm_kernel_name", "w4a4_quant_gemm",
             "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm",
             "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers",
             "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32", "w4a4_kv_quant", "w4a4_kv_dequant")
@@ -75,8 +75,10 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [i32, i32, i32, i32, i32]
         f.restype = sz
-    L.w4a4_outlier_gemm_kernel_name.argtypes = [i32, i32, i32, i32, i32]
-    L.w4a4_outlier_gemm_kernel_name.restype = ctypes.c_char_p
+    for name in ("w4a4_outlier_gemm_kernel_name", "w4a4_quant_gemm_kernel_name"):
+        f = getattr(L, name)
+        f.argtypes = [i32, i32, i32, i32, i32]
+        f.restype = ctypes.c_char_p
     L.w4a4_outlier_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     vp, i64, vp, sz, vp]
     L.w4a4_outlier_gemm.restype = ctypes.c_int
@@ -271,6 +273,13 @@ def outlier_gemm_workspace_bytes(M: int, N: int, K: int, n_out: int, group: int)
 def outlier_gemm_kernel_name(M: int, N: int, K: int, n_out: int, group: int):
     """Kernel the GEMM launches for this shape (as named in a kernel trace), or None."""
     r = lib().w4a4_outlier_gemm_kernel_name(M, N, K, n_out, group)
+    return None if r is None else r.decode()
+
+
+def quant_gemm_kernel_name(M: int, N: int, K: int, n_out: int, group: int):
+    """Kernel that computes the fused layer call's product for this shape:
+    "decode_fused_kernel" when the quantizer runs inside it, else the GEMM's."""
+    r = lib().w4a4_quant_gemm_kernel_name(M, N, K, n_out, group)
     return None if r is None else r.decode()
 
 

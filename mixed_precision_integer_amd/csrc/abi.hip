@@ -221,6 +221,12 @@ const char *w4a4_outlier_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32
     return w4a4::gemm_kernel_name(w4a4::plan_gemm(M, N, K - n_out, n_out, group, false));
 }
 
+const char *w4a4_quant_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
+    if (M > 0 && N > 0 && w4a4::decode_fused_fits(M, N, K, n_out, group))
+        return "decode_fused_kernel";
+    return w4a4_outlier_gemm_kernel_name(M, N, K, n_out, group);
+}
+
 w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
                               const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
                               int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group,
@@ -323,6 +329,28 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
     const size_t need = w4a4_quant_gemm_workspace_bytes(M, N, K, n_out, group);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return W4A4_ERR_WORKSPACE;
+    if (!norm.gamma && w4a4::decode_fused_fits(M, N, K, n_out, group)) {
+        // small decode batch: the quantizer runs inside the GEMM's workgroups
+        w4a4::DecodeFusedArgs f{};
+        f.x = static_cast<const uint16_t *>(X);
+        f.perm = perm;
+        f.w4 = static_cast<const uint8_t *>(Wq4);
+        f.w8 = static_cast<const int8_t *>(Wq8);
+        f.sw4 = sw4;
+        f.sw8 = sw8;
+        f.y = static_cast<_Float16 *>(Y);
+        f.M = M;
+        f.N = N;
+        f.K = K;
+        f.K_n = K_n;
+        f.n_out = n_out;
+        f.ldx = ldx;
+        f.pitch4 = w4a4_pitch4_bytes(K_n);
+        f.pitch8 = w4a4_pitch8_bytes(n_out);
+        f.ldy = ldy;
+        return w4a4::launch_decode_fused(f, static_cast<hipStream_t>(stream)) == hipSuccess ? W4A4_OK
+                                                                                        : W4A4_ERR_HIP;
+    }
     size_t off[5];
     quant_gemm_layout(M, K, n_out, group, off);
     char *ws = static_cast<char *>(workspace);

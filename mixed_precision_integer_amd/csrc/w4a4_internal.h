@@ -87,6 +87,21 @@ hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipS
 bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
 hipError_t launch_gemm_decode(const GemmArgs &a, hipStream_t stream);
 
+// Decode layer call with the quantizer fused in (gemm_decode_fused.hip): at
+// most 2 token rows, 128-channel groups, at most 128 outlier channels.
+struct DecodeFusedArgs {
+    const uint16_t *x;    // [M, ldx] fp16 activations (bit patterns)
+    const int32_t *perm;  // [K] reordered channel -> source channel
+    const uint8_t *w4;    // [N, pitch4]
+    const int8_t *w8;     // [N, pitch8]
+    const float *sw4, *sw8;
+    _Float16 *y;          // [M, ldy]
+    int32_t M, N, K, K_n, n_out;
+    int64_t ldx, pitch4, pitch8, ldy;
+};
+bool decode_fused_fits(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group);
+hipError_t launch_decode_fused(const DecodeFusedArgs &a, hipStream_t stream);
+
 // 128 x 128 tile kernel for 128-channel scale groups (gemm_group.hip).
 bool gemm_group_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
 hipError_t launch_gemm_group(const GemmArgs &a, hipStream_t stream);

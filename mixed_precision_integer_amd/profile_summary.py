@@ -34,7 +34,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 GEMM_SOURCES = ("gemm_kernels.hip", "gemm_big.hip", "gemm_group.hip", "gemm_decode.hip",
-                "gemm_common.h", "w4a4_internal.h")
+                "gemm_decode_fused.hip", "gemm_common.h", "w4a4_internal.h")
 COPY_KIB = 512 * 1024
 
 
@@ -138,10 +138,12 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "") -> s
              "are not part of a step.\n")
     k = bj["kernels"]
     roof = bj["roofline"]
+    prod = ("producer %.2f µs" % k["producer_us"] if k["producer_us"] is not None
+            else "producer inside the GEMM kernel (one launch)")
     L.append("bench.py line printed in the same run (HIP events on the launch stream around every eighth "
-             "GEMM launch of the timed region): producer %.2f µs, GEMM %.2f µs, step %.2f µs, value %.1f %s; "
+             "GEMM launch of the timed region): %s, GEMM %.2f µs, step %.2f µs, value %.1f %s; "
              "roofline: %.1f of %.0f %s (%.1f%%, %s-bound).\n"
-             % (k["producer_us"], k["gemm_us"], bj["ms_per_step"] * 1e3, bj["value"], bj["unit"],
+             % (prod, k["gemm_us"], bj["ms_per_step"] * 1e3, bj["value"], bj["unit"],
                 roof["achieved"], roof["peak"], roof["unit"], 100 * roof["frac"], roof["bound"]))
     L.append("## HBM traffic (rocprofv3 --pmc, one counter per run)\n")
     cmds = [("FETCH_SIZE", "fetch", f"{run} --steps 5 --warmup 2 --no-cpu-baseline"),

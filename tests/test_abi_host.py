@@ -277,3 +277,18 @@ def test_device_calls_fail_loudly_without_gpu():
 ])
 def test_gemm_kernel_name(shape, name):
     assert w4.outlier_gemm_kernel_name(*shape) == name
+
+
+def test_one_launch_decode_path_bounds():
+    """The fused layer call takes one launch for at most 2 rows, 128-channel
+    groups, at most 128 outliers and K_n <= 16384; other shapes keep the
+    producer + GEMM launches (a pure function of the shape)."""
+    assert w4.quant_gemm_kernel_name(1, 8192, 8192, 128, 128) == "decode_fused_kernel"
+    assert w4.quant_gemm_kernel_name(2, 256, 16384 + 64, 64, 128) == "decode_fused_kernel"
+    assert w4.quant_gemm_kernel_name(3, 256, 1152, 128, 128) == "gemm_decode_kernel"
+    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 0) == "gemm_decode_kernel"
+    assert w4.quant_gemm_kernel_name(2, 256, 1280, 256, 128) == "gemm_decode_kernel"
+    assert w4.quant_gemm_kernel_name(2, 256, 16384 + 256, 128, 128) != "decode_fused_kernel"
+    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 256) == "gemm_decode_kernel"
+    assert w4.quant_gemm_kernel_name(2048, 4096, 4096, 128, 128) == w4.outlier_gemm_kernel_name(2048, 4096, 4096, 128, 128)
+    assert w4.quant_gemm_kernel_name(0, 256, 1152, 128, 128) is None

@@ -1,0 +1,118 @@
+"""GPU parity of the one-launch decode layer call (quantizer fused into the
+decode GEMM, at most 2 token rows, 128-channel groups, at most 128 outliers).
+
+Bars: every output within 1e-2 of max |Y| of the oracle, and bit-identical to
+the two-launch path (producer, then GEMM): the fused kernel computes the same
+codes and scales with the same arithmetic and folds in the same order.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import mixed_precision_integer_amd as w4
+from mixed_precision_integer_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 1e-2
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    sys.stderr.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def _layer(X, W, outliers, group, ldx=None, ldy=None):
+    """Fused call, two-launch call and oracle on the same inputs."""
+    M, K = X.shape
+    N = W.shape[0]
+    n_out = len(outliers)
+    perm = torch.from_numpy(w4.make_perm(K, outliers)).to(DEV)
+    Xs = torch.zeros((M, ldx or K), dtype=torch.float16, device=DEV)
+    Xs[:, :K] = torch.from_numpy(X).to(DEV)
+    Xd = Xs[:, :K]
+    w = w4.pack_int4_weights(torch.from_numpy(W).to(DEV), perm, n_out, group)
+    Ys = torch.full((M, ldy or N), float("nan"), dtype=torch.float16, device=DEV)
+    need = w4.quant_gemm_workspace_bytes(M, N, K, n_out, group)
+    ws = torch.full((max(need, 1),), 0x5A, dtype=torch.uint8, device=DEV)
+    y_fused = w4.quant_gemm(Xd, perm, w, out=Ys[:, :N], workspace=ws)
+    a = w4.quant_reorder_act(Xd, perm, n_out, group)
+    y_two = w4.w4a4_outlier_gemm(a, w)
+    torch.cuda.synchronize()
+    return perm, a, w, y_fused, y_two, Ys, ws
+
+
+def _oracle_y(oracle, X, W, perm_h, n_out, group):
+    M, N = X.shape[0], W.shape[0]
+    qa = oracle.quantize_rows(X, perm_h, n_out, group)
+    qw = oracle.quantize_rows(W, perm_h, n_out, group)
+    mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")
+    _, _, ystar = oracle.linear_at(qa, qw, group, mm.reshape(-1), nn.reshape(-1))
+    return oracle.to_fp16(ystar).reshape(M, N)
+
+
+FUSED = [
+    # M, N, K, n_out, ldx, ldy
+    (1, 96, 256, 128, None, None),        # one INT4 tile: only wave 0 has tiles
+    (2, 200, 1152, 0, None, None),        # no outlier tail, ragged N
+    (1, 136, 1120, 96, 1136, 144),        # tail of 96 padded to 128, padded row strides
+    (2, 64, 640, 128, None, None),        # four tiles: waves 4-7 idle in the head
+    (2, 320, 16448, 64, None, None),      # K_n = 16384: sixteen tiles per wave, one tail tile
+    (1, 384, 4224, 128, None, None),      # two tail tiles
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out,ldx,ldy", FUSED)
+def test_fused_decode_parity(oracle, M, N, K, n_out, ldx, ldy):
+    group = 128
+    assert w4.quant_gemm_kernel_name(M, N, K, n_out, group) == "decode_fused_kernel"
+    X, W, o = wl.draw(M, N, K, n_out, seed=7 * M + K, outlier_factor=30.0)
+    perm, a, w, yf, y2, Ys, ws = _layer(X, W, o, group, ldx, ldy)
+    assert torch.equal(yf, y2), "fused call differs from producer + GEMM"
+    if ldy:
+        assert torch.isnan(Ys[:, N:]).all(), "wrote past N"
+    assert bool((ws == 0x5A).all()), "the one-launch path writes no workspace"
+    ref = _oracle_y(oracle, X, W, perm.cpu().numpy(), n_out, group)
+    got = yf.cpu().numpy().astype(np.float64)
+    amax = np.abs(ref.astype(np.float64)).max()
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - ref).max() <= TOL * amax
+
+
+def test_fused_decode_zero_rows_and_groups(oracle):
+    """Zero rows, a zero group and a zero tail (scale 0, codes 0) next to
+    ordinary rows: identical to the two-launch path and to the oracle."""
+    M, N, K, n_out = 2, 128, 1152, 128
+    X, W, o = wl.draw(M, N, K, n_out, seed=31, outlier_factor=30.0)
+    perm_h = w4.make_perm(K, o)
+    X[0, perm_h[256:384]] = 0                   # one whole INT4 group of row 0
+    X[0, o] = 0                                 # and its outlier channels
+    X[1] = 0
+    perm, a, w, yf, y2, _, _ = _layer(X, W, o, 128)
+    assert torch.equal(yf, y2)
+    assert bool((yf[1] == 0).all())
+    assert np.array_equal(a.s8.cpu().numpy(), np.zeros(2, np.float32))
+    assert a.s4.cpu().numpy()[0, 2] == 0
+    ref = _oracle_y(oracle, X, W, perm_h, n_out, 128)
+    amax = np.abs(ref.astype(np.float64)).max()
+    assert np.abs(yf.cpu().numpy().astype(np.float64) - ref).max() <= TOL * amax
+
+
+def test_fused_decode_rows_far_apart(oracle):
+    """Rows whose magnitudes differ by 2^12 keep their own scales."""
+    M, N, K, n_out = 2, 256, 2176, 128
+    X, W, o = wl.draw(M, N, K, n_out, seed=32, outlier_factor=30.0)
+    X = (X.astype(np.float32) * np.array([2.0 ** -6, 2.0 ** 6], np.float32)[:, None]).astype(np.float16)
+    perm, a, w, yf, y2, _, _ = _layer(X, W, o, 128)
+    assert torch.equal(yf, y2)
+    ref = _oracle_y(oracle, X, W, perm.cpu().numpy(), n_out, 128)
+    for m in range(M):                          # the bar per row: each row has its own scale
+        amax = np.abs(ref[m].astype(np.float64)).max()
+        assert np.abs(yf[m].cpu().numpy().astype(np.float64) - ref[m]).max() <= TOL * amax
+
