@@ -63,8 +63,8 @@ def work_counts(w, M, norm=False):
     gemm_bytes = w_bytes + a_bytes + 2 * M * N
     producer_bytes = 2 * M * K + a_bytes + (2 * K if norm else 0)
     # one launch (quantizer inside the GEMM): fp16 tokens and the permutation
-    # in place of the codes
-    one_launch_bytes = w_bytes + 2 * M * K + 4 * K + 2 * M * N
+    # (and the norm weights) in place of the codes
+    one_launch_bytes = w_bytes + 2 * M * K + 4 * K + (2 * K if norm else 0) + 2 * M * N
     return ops, gemm_bytes, producer_bytes, one_launch_bytes
 
 
@@ -447,10 +447,11 @@ def main():
     if args.norm:
         norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
     plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq), norm=norm) for _ in range(n_sets)]
-    # Small decode batches run the layer as one launch (the quantizer inside
-    # the GEMM's workgroups); every other shape as producer + GEMM.
-    one_launch = norm is None and \
-        w4.quant_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group) == "decode_fused_kernel"
+    # Small decode batches run the layer as one launch (the quantizer, and the
+    # RMSNorm with --norm, inside the GEMM's workgroups); every other shape as
+    # producer + GEMM.
+    one_launch = w4.quant_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group) == "decode_fused_kernel" and \
+        (not args.norm or M == 1)
 
     for i in range(args.warmup):
         p = plans[i % n_sets]
@@ -543,7 +544,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": w.N, "K": w.K, "n_out": w.n_out,
                    "group": w.group, "buffer_sets": n_sets,
-                   "producer": "rmsnorm_fused" if args.norm else ("in_gemm" if one_launch else "plain")},
+                   "producer": ("rmsnorm_" if args.norm else "") + ("in_gemm" if one_launch else
+                                                                     ("fused" if args.norm else "plain"))},
         "roofline": roof,
         "kernels": {
             "producer_us": prod_ms * 1e3 if prod_ms else None,

@@ -185,7 +185,7 @@ w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *
                                   int32_t *acc8, w4a4_stream stream);
 
 /* Name of the GPU kernel that computes w4a4_quant_gemm's product for this
- * shape: "decode_fused_kernel" when the quantizer is fused into it (see
+ * shape (and w4a4_rmsnorm_quant_gemm's when M == 1): "decode_fused_kernel" when the quantizer is fused into it (see
  * w4a4_quant_gemm), else the kernel w4a4_outlier_gemm launches. A static
  * string owned by the library, or NULL for a shape the call would reject. */
 const char *w4a4_quant_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out,
@@ -214,7 +214,10 @@ w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, con
 /* The fused layer behind an RMSNorm: w4a4_rmsnorm_quant_reorder_act on X
  * into the caller's workspace (the same size as w4a4_quant_gemm's), then
  * w4a4_outlier_gemm, both on `stream`. gamma and eps as in
- * w4a4_rmsnorm_quant_reorder_act. */
+ * w4a4_rmsnorm_quant_reorder_act. A single decode token (M == 1) in the
+ * shapes where w4a4_quant_gemm takes one launch takes one launch here too
+ * (norm, quantizer and GEMM in the same workgroups, the same arithmetic, a
+ * bit-identical Y). */
 w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamma, float eps,
                                     const int32_t *perm, const void *Wq4, const void *Wq8,
                                     const float *sw4, const float *sw8, int32_t M, int32_t N,

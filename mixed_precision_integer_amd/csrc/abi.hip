@@ -329,10 +329,14 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
     const size_t need = w4a4_quant_gemm_workspace_bytes(M, N, K, n_out, group);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return W4A4_ERR_WORKSPACE;
-    if (!norm.gamma && w4a4::decode_fused_fits(M, N, K, n_out, group)) {
-        // small decode batch: the quantizer runs inside the GEMM's workgroups
+    // small decode batches: the quantizer (and the norm, for one token: a
+    // second row already costs more than the norm producer's launch) run
+    // inside the GEMM's workgroups
+    if (w4a4::decode_fused_fits(M, N, K, n_out, group) && (!norm.gamma || M == 1)) {
         w4a4::DecodeFusedArgs f{};
         f.x = static_cast<const uint16_t *>(X);
+        f.gamma = static_cast<const uint16_t *>(norm.gamma);
+        f.eps = norm.eps;
         f.perm = perm;
         f.w4 = static_cast<const uint8_t *>(Wq4);
         f.w8 = static_cast<const int8_t *>(Wq8);

@@ -32,6 +32,12 @@
 // * The INT8 tail (at most 128 channels, one tile per wave 0 and 1): a tail
 //   wave gathers all tail channels of every token row for the row's absmax,
 //   then codes the 64 channels of its own tile into LDS.
+// * With the RMSNorm in front (NORM): each wave adds the squares of its own
+//   channels exactly, as 128-bit integers of x^2 * 2^48 (wave 0 also the
+//   tail's), the eight partial sums meet in LDS behind one barrier, and every
+//   lane derives rstd = fl32(1 / sqrt(fl64(S) / K + eps)) in binary64 and
+//   normalizes its values as fl16(gamma * fl16(fl32(x * rstd))) before the
+//   absmax: the producer's arithmetic, so the codes stay bit-identical.
 // * Loads complete in order, so the waits are counted by hand around the
 //   weight DMA: the first two pairs are requested before the permutation
 //   entries arrive (their HBM latency overlaps the quantizer); with a deeper
@@ -61,7 +67,8 @@ constexpr int TOK = MAXM * TROW;           // INT4 token codes of one wave
 constexpr int TAIL = MAXM * kTileBytes;    // INT8 codes of the wave's tail tile
 constexpr int SCL = MAXM * MAXT * 4 + MAXM * 4;   // group scales, then tail scales
 constexpr int WAVE_AREA = TOK + TAIL + SCL;
-constexpr int LDS_BYTES = RING + WAVES * WAVE_AREA;
+constexpr int SUMS = WAVES * MAXM * 16;      // partial sums of squares (RMSNorm), 128 bits each
+constexpr int LDS_BYTES = RING + WAVES * WAVE_AREA + SUMS;
 constexpr int RED_BYTES = WAVES * 16 * 64 * 4;
 static_assert(RING >= RED_BYTES, "the reduction reuses the ring");
 static_assert(LDS_BYTES <= 160 * 1024, "one workgroup per CU");
@@ -83,6 +90,37 @@ __device__ __forceinline__ float recip_or_zero(float s) { return s == 0.0f ? 0.0
 
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// x^2 * 2^48 of an fp16 value, exactly, as an integer below 2^80: with
+// x = Mx * 2^(sh - 24) (Mx the significand with its hidden bit, sh = 0 for
+// subnormals), x^2 * 2^48 = Mx^2 * 2^(2 sh).
+__device__ __forceinline__ unsigned __int128 square_q48(uint16_t h) {
+    const uint32_t e = (h >> 10) & 31, m = h & 1023;
+    const uint32_t mx = e ? (m | 1024u) : m, sh = e ? e - 1 : 0;
+    return (unsigned __int128)(mx * mx) << (2 * sh);
+}
+
+__device__ __forceinline__ unsigned __int128 wave_sum_u128(unsigned __int128 s) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w[k] = (uint32_t)__shfl_xor((int)(uint32_t)(s >> (32 * k)), off, 64);
+        s += (unsigned __int128)w[0] | ((unsigned __int128)w[1] << 32) | ((unsigned __int128)w[2] << 64) |
+             ((unsigned __int128)w[3] << 96);
+    }
+    return s;
+}
+
+// fl16(gamma * fl16(fl32(x * rstd))): the fp16 product of two fp16 values is
+// exact in fp32, so one rounding to fp16 gives the fp16 multiply.
+__device__ __forceinline__ uint16_t norm_one(uint16_t x, uint16_t g, float rstd) {
+#pragma clang fp contract(off)
+    const _Float16 h = (_Float16)(h2f(x) * rstd);
+    return __builtin_bit_cast(uint16_t, (_Float16)((float)h * h2f(g)));
+}
+
+template <bool NORM>
 __global__ __launch_bounds__(THREADS) void decode_fused_kernel(DecodeFusedArgs a) {
     __shared__ __align__(16) unsigned char lds[LDS_BYTES];
 
@@ -206,11 +244,89 @@ __global__ __launch_bounds__(THREADS) void decode_fused_kernel(DecodeFusedArgs a
                 xt[r][i] = X[(int64_t)r * a.ldx + min((uint32_t)pt[i], kmax)];
         }
     }
+    uint16_t gv[UCW][8], gt[2] = {0, 0};                      // norm weights of the same channels
+    if constexpr (NORM) {
+#pragma unroll
+        for (int i = 0; i < UCW; ++i) {
+            if (64 * i >= ucols)
+                break;                                        // uniform
+            const int p[8] = {pe[i][0].x, pe[i][0].y, pe[i][0].z, pe[i][0].w,
+                              pe[i][1].x, pe[i][1].y, pe[i][1].z, pe[i][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                gv[i][e] = a.gamma[min((uint32_t)p[e], kmax)];
+        }
+        if (tail_wave) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                gt[i] = a.gamma[min((uint32_t)pt[i], kmax)];
+        }
+    }
     for (int j = early; j < early + late; ++j)
         issue(j);
     compiler_fence();
     wait_pairs(late);                                         // the token loads and every older load
     compiler_fence();
+
+    if constexpr (NORM) {
+        // exact sums of squares: this wave's head channels, and wave 0 adds the tail
+        uint32_t *sums = reinterpret_cast<uint32_t *>(lds + RING + WAVES * WAVE_AREA);   // [WAVES][MAXM][4]
+#pragma unroll
+        for (int r = 0; r < MAXM; ++r) {
+            if (r >= a.M)
+                break;                                        // uniform
+            unsigned __int128 ss = 0;
+#pragma unroll
+            for (int i = 0; i < UCW; ++i) {
+                if (64 * i >= ucols)
+                    break;                                    // uniform
+                if (lane + 64 * i < ucols)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        ss += square_q48(xv[r][i][e]);
+            }
+            if (wave == 0 && tail_wave)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    if (lane + 64 * i < a.n_out)
+                        ss += square_q48(xt[r][i]);
+            ss = wave_sum_u128(ss);
+            if (lane == 0)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    sums[(wave * MAXM + r) * 4 + k] = (uint32_t)(ss >> (32 * k));
+        }
+        // a barrier that orders LDS only: the weight DMA keeps running across it
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+#pragma unroll
+        for (int r = 0; r < MAXM; ++r) {
+            if (r >= a.M)
+                break;                                        // uniform
+            unsigned __int128 S = 0;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const uint32_t *q = sums + (w * MAXM + r) * 4;
+                S += (unsigned __int128)q[0] | ((unsigned __int128)q[1] << 32) | ((unsigned __int128)q[2] << 64) |
+                     ((unsigned __int128)q[3] << 96);
+            }
+            const double var = (double)S * 0x1p-48 / (double)a.K + (double)a.eps;
+            const float rstd = var == 0.0 ? 0.0f : (float)(1.0 / __builtin_sqrt(var));
+#pragma unroll
+            for (int i = 0; i < UCW; ++i) {
+                if (64 * i >= ucols)
+                    break;                                    // uniform
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xv[r][i][e] = norm_one(xv[r][i][e], gv[i][e], rstd);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                xt[r][i] = norm_one(xt[r][i], gt[i], rstd);
+        }
+    }
 
     // ---- INT4 codes and group scales of this wave's tiles ---------------------------
 #pragma unroll
@@ -382,6 +498,8 @@ __global__ __launch_bounds__(THREADS) void decode_fused_kernel(DecodeFusedArgs a
 using namespace decode_fused_impl;
 
 bool decode_fused_fits(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
+    if (K > 32768)
+        return false;                                         // the exact sum of squares stays below 2^95
     const int32_t K_n = K - n_out;
     if (M < 1 || M > MAXM || group != 128 || K_n < 128 || K_n % 128 != 0 || n_out < 0 || n_out > MAXOUT)
         return false;
@@ -393,7 +511,10 @@ bool decode_fused_fits(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t g
 }
 
 hipError_t launch_decode_fused(const DecodeFusedArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_fused_kernel, dim3((a.N + BN - 1) / BN), dim3(THREADS), 0, stream, a);
+    if (a.gamma)
+        hipLaunchKernelGGL(decode_fused_kernel<true>, dim3((a.N + BN - 1) / BN), dim3(THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL(decode_fused_kernel<false>, dim3((a.N + BN - 1) / BN), dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

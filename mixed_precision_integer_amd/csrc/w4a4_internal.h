@@ -91,6 +91,8 @@ hipError_t launch_gemm_decode(const GemmArgs &a, hipStream_t stream);
 // most 2 token rows, 128-channel groups, at most 128 outlier channels.
 struct DecodeFusedArgs {
     const uint16_t *x;    // [M, ldx] fp16 activations (bit patterns)
+    const uint16_t *gamma;  // [K] fp16 RMSNorm weights in front of the layer, or nullptr
+    float eps;            // RMSNorm epsilon (with gamma)
     const int32_t *perm;  // [K] reordered channel -> source channel
     const uint8_t *w4;    // [N, pitch4]
     const int8_t *w8;     // [N, pitch8]

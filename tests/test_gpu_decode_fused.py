@@ -116,3 +116,40 @@ def test_fused_decode_rows_far_apart(oracle):
         amax = np.abs(ref[m].astype(np.float64)).max()
         assert np.abs(yf[m].cpu().numpy().astype(np.float64) - ref[m]).max() <= TOL * amax
 
+
+
+@pytest.mark.parametrize("M,N,K,n_out,eps,zero_row", [
+    (1, 200, 1152, 128, 1e-6, False),       # one token
+    (1, 320, 8320, 128, 1e-5, False),       # 64 groups, two tail tiles
+    (1, 64, 640, 0, 0.0, True),             # no tail; an all-zero row with eps 0 (rstd 0)
+    (2, 96, 1152, 128, 1e-6, False),        # two rows: norm producer + GEMM (same bits)
+])
+def test_fused_decode_rmsnorm_parity(oracle, M, N, K, n_out, eps, zero_row):
+    """The RMSNorm-fused layer call, one launch for one token: bit-identical
+    to the norm producer + GEMM, and within the bar of the oracle's norm +
+    quantizer."""
+    group = 128
+    assert w4.quant_gemm_kernel_name(M, N, K, n_out, group) == "decode_fused_kernel"
+    X, W, o = wl.draw(M, N, K, n_out, seed=5 * M + K, outlier_factor=30.0)
+    if zero_row:
+        X[M - 1] = 0
+    g = wl.draw_norm_weight(K, seed=K)
+    perm = torch.from_numpy(w4.make_perm(K, o)).to(DEV)
+    Xd = torch.from_numpy(X).to(DEV)
+    gam = torch.from_numpy(g).to(DEV)
+    w = w4.pack_int4_weights(torch.from_numpy(W).to(DEV), perm, n_out, group)
+    yf = w4.rmsnorm_quant_gemm(Xd, gam, eps, perm, w)
+    a = w4.rmsnorm_quant_reorder_act(Xd, gam, eps, perm, n_out, group)
+    y2 = w4.w4a4_outlier_gemm(a, w)
+    torch.cuda.synchronize()
+    assert torch.equal(yf, y2), "one-launch norm call differs from norm producer + GEMM"
+    perm_h = perm.cpu().numpy()
+    qa = oracle.rmsnorm_quantize_rows(X, g, eps, perm_h, n_out, group)
+    qw = oracle.quantize_rows(W, perm_h, n_out, group)
+    mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")
+    _, _, ystar = oracle.linear_at(qa, qw, group, mm.reshape(-1), nn.reshape(-1))
+    ref = oracle.to_fp16(ystar).reshape(M, N).astype(np.float64)
+    got = yf.cpu().numpy().astype(np.float64)
+    assert np.abs(got - ref).max() <= TOL * np.abs(ref).max()
+    if zero_row:
+        assert bool((yf[M - 1] == 0).all())
