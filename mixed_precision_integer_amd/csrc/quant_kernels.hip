@@ -10,7 +10,8 @@
 //
 // Design (HBM-bound: every input byte is read once, every code written once)
 // * Persistent workgroups loop over rows. Rows stream in by direct
-//   global->LDS DMA (16 bytes per lane), double buffered: the first two rows
+//   global->LDS DMA (16 bytes per lane, non-temporal: each row is read once),
+//   double buffered: the first two rows
 //   are requested at once, then each next row's DMA is in flight while the
 //   current row is quantized. LDS holds only the two row buffers and small
 //   reduction tables, sized statically per row-length bucket (K <= 4096,
@@ -113,6 +114,18 @@ __device__ __forceinline__ uint32_t norm_pair(uint32_t xv, uint32_t g, float rst
     return __builtin_bit_cast(uint32_t, h * __builtin_bit_cast(half2, g));
 }
 
+// The row DMA of dma16 with the non-temporal cache policy: every X row is read
+// exactly once, so it streams past the caches. (Measured 5-12% faster on the
+// producer; the GEMMs keep cached DMA, which their tile reuse needs.)
+__device__ __forceinline__ void dma16_stream(const void *base, uint32_t voff, uint32_t lds) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sb), "s"(sl)
+                 : "memory", "m0");
+}
+
 // s_waitcnt immediates (gfx9 encoding): all counters zero, or LDS only.
 constexpr int kWaitAll = 0;
 constexpr int kWaitLds = 0xF | (0x3 << 14) | (0x7 << 4);   // vmcnt max, expcnt max, lgkmcnt 0
@@ -182,7 +195,7 @@ void quant_rows_kernel(QuantArgs a) {
         const uint32_t d = lds_addr(sm.x[b]) + wave_u * 1024;
         for (int j = 0; j < rounds; ++j) {
             const int c = j * THREADS + tid;
-            dma16(src, (uint32_t)(c < nfull ? c : 0) * 16, d + j * L::ROUND);
+            dma16_stream(src, (uint32_t)(c < nfull ? c : 0) * 16, d + j * L::ROUND);
         }
     };
 
