@@ -31,6 +31,8 @@
 namespace w4a4 {
 namespace select_impl {
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 constexpr int kStripe = 512;          // columns per workgroup
 constexpr int kWaves = 4;             // waves per column-absmax workgroup
 constexpr int kRowsInFlight = 4;      // rows each lane loads before it reduces
@@ -60,7 +62,12 @@ __global__ __launch_bounds__(kWaves * 64) void colmax_kernel(const uint16_t *X, 
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u) {
                 const int rr = r + u * kWaves;
-                v[u] = rr < r1 ? *reinterpret_cast<const uint4 *>(X + (int64_t)rr * ld + c0) : uint4{0u, 0u, 0u, 0u};
+                if (rr < r1) {                           // each value is read once: streamed past the caches
+                    const v4u q = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(X + (int64_t)rr * ld + c0));
+                    v[u] = uint4{q.x, q.y, q.z, q.w};
+                } else {
+                    v[u] = uint4{0u, 0u, 0u, 0u};
+                }
             }
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u) {
