@@ -3,6 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M] [--norm]
 
+The default workload is the largest prefill projection (the Llama-65B
+down_proj, M = 8192, K = 22016, N = 8192, per-row scales, 256 INT8 outlier
+channels); --workload qproj|upproj|decode|tiny selects the others.
+
 One step is one pass of the layer's run-time path over one batch: the
 activation producer (reorder + INT4/INT8 quantize, ``w4a4_quant_reorder_act``)
 then the mixed-precision GEMM with its fp32 epilogue (``w4a4_outlier_gemm``);
@@ -21,11 +25,14 @@ Prints one JSON line. ``value`` is the whole-step throughput in TOPS
 (2 M N K integer ops per step). ``roofline`` describes the dominant kernel,
 the GEMM: its algorithmic ops (or bytes, for memory-bound decode shapes) per
 launch divided by its mean duration, measured with HIP events recorded on
-the launch stream around every EVENT_EVERY-th GEMM launch inside the timed
-region (an event pair on every step added about 5 us to each step on this
-box, so the wall-clock step time would carry measurement overhead); the
-producer is timed by events in a short loop after it, so that no event sits
-between the two kernels of a timed step.
+the launch stream around the GEMM launches inside the timed region: every
+launch when a step takes longer than LONG_STEP_MS, else every EVENT_EVERY-th
+(an event pair costs about 5 us, which short steps would carry); the line
+reports their mean, p10, p50 and p90. The producer is timed by events in a
+short loop after it, so that no event sits between the two kernels of a timed
+step. The shader clock is sampled during the timed region (amdsmi, else
+rocm-smi) and reported with the line, since the matrix-core rate on this chip
+depends on the clock it holds under load.
 ``cpu_baseline`` times the CPU oracle on the host cores on a bounded row
 sample of the same workload.
 """
@@ -44,7 +51,8 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5033.2      # 256 CU x 2.4 GHz x 8192 dense int8 ops / clk / CU
 PEAK_HBM_GBS = 8000.0        # HBM3E
 ROTATE_BYTES = 512 << 20
-EVENT_EVERY = 8              # timed steps per HIP event pair around the GEMM
+EVENT_EVERY = 8              # timed steps per HIP event pair around the GEMM (short steps)
+LONG_STEP_MS = 0.2           # steps at least this long get an event pair every step
 
 from mixed_precision_integer_amd import workloads as wl  # noqa: E402
 
@@ -66,6 +74,68 @@ def work_counts(w, M, norm=False):
     # (and the norm weights) in place of the codes
     one_launch_bytes = w_bytes + 2 * M * K + 4 * K + (2 * K if norm else 0) + 2 * M * N
     return ops, gemm_bytes, producer_bytes, one_launch_bytes
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (MHz) on a host thread while the
+    timed region runs; reports the median of the readings and where they came
+    from. Nothing here touches the GPU's work."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+        self.period_s, self.samples, self.source = period_s, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handle = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read():
+                info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+                return float(info.get("clk", info.get("cur_clk")))
+            read()
+            self._read, self.source = read, "amdsmi_get_clock_info(GFX)"
+        except Exception:
+            self._read = None
+        if self._read is None:
+            self._read, self.source = self._rocm_smi, "rocm-smi --showclocks"
+
+    @staticmethod
+    def _rocm_smi():
+        import re
+        import subprocess
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=10).stdout
+        m = re.search(r"sclk.*?\((\d+)Mhz\)", out, re.I)
+        return float(m.group(1)) if m else None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except Exception:
+                pass
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        import threading
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+
+    def report(self):
+        if not self.samples:
+            return {"mhz": None, "samples": 0, "source": self.source}
+        return {"mhz": float(np.median(self.samples)), "min_mhz": float(min(self.samples)),
+                "max_mhz": float(max(self.samples)), "samples": len(self.samples), "source": self.source}
 
 
 def traffic_record(workload_name, M):
@@ -380,7 +450,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="qproj", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="downproj", choices=sorted(WORKLOADS))
     ap.add_argument("--m", type=int, default=None, help="token rows (decode sweep)")
     ap.add_argument("--custom", default=None,
                     help="M,N,K,n_out,group: a synthetic shape instead of a named workload")
@@ -462,32 +532,50 @@ def main():
             p.gemm()
     torch.cuda.synchronize()
 
+    # How long is a step? One event-timed step after the warmup decides how
+    # densely the timed region carries event pairs.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    p = plans[0]
+    if one_launch:
+        p.fused()
+    else:
+        p.produce()
+        p.gemm()
+    e1.record()
+    torch.cuda.synchronize()
+    every = 1 if e0.elapsed_time(e1) >= LONG_STEP_MS else EVENT_EVERY
+
     # Timed region: K whole steps. Only the dominant kernel (the GEMM) is
     # bracketed by events, on its launch stream (torch's current stream, which
     # the binding launches on); an event between the producer and the GEMM
     # would itself add a gap to every step.
     K = args.steps
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, K, EVENT_EVERY)}
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, K, every)}
+    clock = ClockSampler()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        p = plans[i % n_sets]
-        if not one_launch:
-            p.produce()
-        e = ev.get(i)
-        if e:
-            e[0].record()
-        if one_launch:
-            p.fused()
-        else:
-            p.gemm()
-        if e:
-            e[1].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with clock:
+        t0 = time.perf_counter()
+        for i in range(K):
+            p = plans[i % n_sets]
+            if not one_launch:
+                p.produce()
+            e = ev.get(i)
+            if e:
+                e[0].record()
+            if one_launch:
+                p.fused()
+            else:
+                p.gemm()
+            if e:
+                e[1].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
 
     ms_step = (t1 - t0) * 1e3 / K
-    gemm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev.values()]))
+    gemm_all = np.array([e[0].elapsed_time(e[1]) for e in ev.values()])
+    gemm_ms = float(np.mean(gemm_all))
+    p10, p50, p90 = (float(v) * 1e3 for v in np.percentile(gemm_all, [10, 50, 90]))
     # the producer's share, from events around it alone (after the timed region)
     pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(0 if one_launch else min(K, 50))]
     for i, e in enumerate(pev):
@@ -552,9 +640,13 @@ def main():
             "producer_GBps": prod_bytes / (prod_ms * 1e-3) / 1e9 if prod_ms else None,
             "producer_hbm_frac": prod_bytes / (prod_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if prod_ms else None,
             "gemm_us": gemm_ms * 1e3,
+            "gemm_us_p10_p50_p90": [p10, p50, p90],
+            "gemm_event_pairs": int(gemm_all.size),
             "gemm_TOPS": ops / (gemm_ms * 1e-3) / 1e12,
             "gemm_GBps": gemm_bytes / (gemm_ms * 1e-3) / 1e9,
+            "gemm_frac_of_int8_mfma_peak": ops / (gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
         },
+        "sclk": clock.report(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X, W, outliers, args.cpu_budget,

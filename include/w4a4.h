@@ -146,10 +146,12 @@ w4a4_status w4a4_pack_int4_weights(const void *W, int64_t ldw, const int32_t *pe
 size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
                                          int32_t group);
 
-/* Name of the GPU kernel w4a4_outlier_gemm launches for this shape (as in a
- * kernel trace), for profiling and benchmarks: a static string owned by the
- * library, or NULL for a shape the call would reject. A pure function of the
- * shape, like the workspace size. */
+/* Name of the GPU kernel w4a4_outlier_gemm launches for this shape, as a
+ * kernel trace prints it (the template arguments the shape fixes included;
+ * for the 256 x 256 tile kernel, whose edge instantiation also depends on Y,
+ * the name without them), for profiling and benchmarks: a static string owned
+ * by the library, or NULL for a shape the call would reject. A pure function
+ * of the shape, like the workspace size. */
 const char *w4a4_outlier_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out,
                                           int32_t group);
 
@@ -159,8 +161,11 @@ const char *w4a4_outlier_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32
  * accumulation, fp32 scale epilogue, fp16 output
  *   Y[m, n] = fp16( sum_t sa4[m,t] sw4[n,t] acc4_t[m,n] + sa8[m] sw8[n] acc8[m,n] ).
  * Operands in the layouts above (from the two calls above). Y device fp16
- * [M, ldy], ldy >= N. GPU constraint (UNSUPPORTED otherwise): K_n * 16384 <
- * 2^31 and n_out * 16384 < 2^31 (int32 range of the widened accumulators).
+ * [M, ldy], ldy >= N. GPU constraints (UNSUPPORTED otherwise): K_n * 16384 <
+ * 2^31 and n_out * 16384 < 2^31 (int32 range of the widened accumulators);
+ * max(M, N) * max(pitch4, pitch8) < 2^32 (32-bit row offsets); group 0 or a
+ * multiple of 128 (the pages fix no group size; one GPU K-tile of 128 INT4
+ * channels then never straddles two groups, and the workloads use 0 and 128).
  * workspace: device memory of at least w4a4_outlier_gemm_workspace_bytes
  * bytes, 256-byte aligned (ALIGNMENT otherwise; WORKSPACE if too small). It
  * must be all zero before the first call that uses it (allocate it zeroed
@@ -175,14 +180,20 @@ w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4
                               int64_t ldy, void *workspace, size_t workspace_bytes,
                               w4a4_stream stream);
 
-/* Test export of the same main loop: instead of Y, writes the exact integer
- * accumulators acc4 device int32 [G, M, N] (one slice per scale group) and
- * acc8 device int32 [M, N] (NULL allowed when n_out == 0). Same constraints
- * as w4a4_outlier_gemm. */
-w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *Wq4,
-                                  const void *Wq8, int32_t M, int32_t N, int32_t K,
-                                  int32_t n_out, int32_t group, int32_t *acc4,
-                                  int32_t *acc8, w4a4_stream stream);
+/* The same call with the accumulator export (test path): it launches the
+ * kernel w4a4_outlier_gemm launches for the shape, with the same main loop,
+ * writes the same Y, and also stores the exact integer accumulators
+ *   acc4 device int32 [G, M, N] (one slice per scale group; NULL allowed when K_n == 0)
+ *   acc8 device int32 [M, N]    (NULL allowed when n_out == 0)
+ * (zeroed by the call first: kernels whose waves or workgroups each hold part
+ * of a group's sum add their parts). Same arguments and constraints as
+ * w4a4_outlier_gemm otherwise. */
+w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const float *sa4,
+                                  const float *sa8, const void *Wq4, const void *Wq8,
+                                  const float *sw4, const float *sw8, int32_t M, int32_t N,
+                                  int32_t K, int32_t n_out, int32_t group, void *Y,
+                                  int64_t ldy, void *workspace, size_t workspace_bytes,
+                                  int32_t *acc4, int32_t *acc8, w4a4_stream stream);
 
 /* Name of the GPU kernel that computes w4a4_quant_gemm's product for this
  * shape (and w4a4_rmsnorm_quant_gemm's when M == 1): "decode_fused_kernel" when the quantizer is fused into it (see
@@ -191,9 +202,11 @@ w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *
 const char *w4a4_quant_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out,
                                         int32_t group);
 
-/* Bytes of device workspace w4a4_quant_gemm needs: the quantized activations
- * (Aq4, Aq8, sa4, sa8 for M rows) plus the GEMM's own workspace, under the
- * same zero-on-first-use rule as w4a4_outlier_gemm's workspace. */
+/* Bytes of device workspace w4a4_quant_gemm needs: the GEMM's own workspace
+ * first (its 2048-byte arrival-counter block at offset 0, reserved for every
+ * shape, so one workspace can serve calls of any shape in turn), then the
+ * quantized activations (Aq4, Aq8, sa4, sa8 for M rows). The same
+ * zero-on-first-use rule as w4a4_outlier_gemm's workspace. */
 size_t w4a4_quant_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
                                        int32_t group);
 

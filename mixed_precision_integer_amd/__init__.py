@@ -82,7 +82,8 @@ def lib():
     L.w4a4_outlier_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     vp, i64, vp, sz, vp]
     L.w4a4_outlier_gemm.restype = ctypes.c_int
-    L.w4a4_outlier_gemm_i32.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.w4a4_outlier_gemm_i32.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                        vp, i64, vp, sz, vp, vp, vp]
     L.w4a4_outlier_gemm_i32.restype = ctypes.c_int
     L.w4a4_quant_gemm.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64,
                                   vp, sz, vp]
@@ -296,18 +297,26 @@ def w4a4_outlier_gemm(a: QuantizedOperand, w: QuantizedOperand, out=None):
     return out
 
 
-def w4a4_outlier_gemm_i32(a: QuantizedOperand, w: QuantizedOperand):
-    """Accumulator export of the same main loop: (acc4 int32 [G, M, N], acc8 int32 [M, N])."""
+def w4a4_outlier_gemm_i32(a: QuantizedOperand, w: QuantizedOperand, out=None):
+    """The GEMM with its accumulator export: the same kernel and main loop as
+    w4a4_outlier_gemm. Returns (acc4 int32 [G, M, N], acc8 int32 [M, N], Y fp16
+    [M, N])."""
     torch = _torch()
     M, N = a.s8.shape[0], w.s8.shape[0]
     G = num_groups(a.K - a.n_out, a.group)
     dev = a.s8.device
-    acc4 = torch.zeros((G, M, N), dtype=torch.int32, device=dev)
-    acc8 = torch.zeros((M, N), dtype=torch.int32, device=dev)
-    _ok(lib().w4a4_outlier_gemm_i32(_nz(a.q4), _nz(a.q8), _nz(w.q4), _nz(w.q8), M, N, a.K,
-                                    a.n_out, a.group, _nz(acc4), _nz(acc8) if a.n_out else None,
-                                    _stream()), "w4a4_outlier_gemm_i32")
-    return acc4, acc8
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _check(out, torch.float16, "out", 2)
+    acc4 = torch.empty((G, M, N), dtype=torch.int32, device=dev)
+    acc8 = torch.empty((M, N), dtype=torch.int32, device=dev)
+    ws_bytes = outlier_gemm_workspace_bytes(M, N, a.K, a.n_out, a.group)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    _ok(lib().w4a4_outlier_gemm_i32(*_gemm_args(a, w, out, ws)[:-1], _nz(acc4),
+                                    _nz(acc8) if a.n_out else None, _stream()), "w4a4_outlier_gemm_i32")
+    if not a.n_out:
+        acc8.zero_()
+    return acc4, acc8, out
 
 
 def quant_gemm_workspace_bytes(M: int, N: int, K: int, n_out: int, group: int) -> int:

@@ -13,6 +13,7 @@ lane, which only fit as AGPRs, and is built without that option.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import shutil
@@ -52,13 +53,18 @@ def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
     tmp = LIB + ".tmp"
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with tempfile.TemporaryDirectory(prefix="w4a4_build_") as objdir:
-        objs = []
+        cmds, objs = [], []
         for src in srcs:
             name = os.path.basename(src)
             obj = os.path.join(objdir, name + ".o")
-            _run([hipcc(), *COMMON, *EXTRA.get(name, VGPR_FORM), *inc, "-c", src, "-o", obj], verbose)
+            cmds.append([hipcc(), *COMMON, *EXTRA.get(name, VGPR_FORM), *inc, "-c", src, "-o", obj])
             objs.append(obj)
+        # one process per source, at most MAX_JOBS (or the CPU count) at a time
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
         _run([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "w4a4.h"
@@ -32,6 +33,15 @@ w4a4_status check_shape(int32_t rows, int32_t K, int32_t n_out, int32_t group) {
     if ((int64_t)K_n * 64 * 256 >= kAccLimit || (int64_t)n_out * 16384 >= kAccLimit)
         return W4A4_ERR_UNSUPPORTED;
     return W4A4_OK;
+}
+
+// The GEMM kernels address operand rows by a 32-bit byte offset from the
+// operand's base (row * pitch + column), so every packed row must start below
+// 4 GiB.
+bool dma_offsets_fit(int64_t M, int64_t N, int32_t K_n, int32_t n_out) {
+    const int64_t rows = M > N ? M : N;
+    const int64_t pitch = std::max(w4a4_pitch4_bytes(K_n), w4a4_pitch8_bytes(n_out));
+    return rows * pitch < (int64_t(1) << 32);
 }
 
 // Optional RMSNorm in front of the quantizer (gamma == nullptr: none).
@@ -113,6 +123,8 @@ w4a4_status gemm_check(const void *Aq4, const void *Aq8, const void *Wq4, const 
     if ((Aq4 && !aligned(Aq4, 16)) || (Wq4 && !aligned(Wq4, 16)) || (Aq8 && !aligned(Aq8, 16)) ||
         (Wq8 && !aligned(Wq8, 16)))
         return W4A4_ERR_ALIGNMENT;
+    if (!dma_offsets_fit(M, N, K_n, n_out))
+        return W4A4_ERR_UNSUPPORTED;
     return W4A4_OK;
 }
 
@@ -212,13 +224,13 @@ size_t w4a4_outlier_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_
                                          int32_t group) {
     if (M <= 0 || N <= 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
         return 0;
-    return w4a4::plan_gemm(M, N, K - n_out, n_out, group, false).workspace_bytes;
+    return w4a4::plan_gemm(M, N, K - n_out, n_out, group).workspace_bytes;
 }
 
 const char *w4a4_outlier_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
     if (M <= 0 || N <= 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
         return nullptr;
-    return w4a4::gemm_kernel_name(w4a4::plan_gemm(M, N, K - n_out, n_out, group, false));
+    return w4a4::gemm_kernel_name(w4a4::plan_gemm(M, N, K - n_out, n_out, group));
 }
 
 const char *w4a4_quant_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
@@ -227,11 +239,13 @@ const char *w4a4_quant_gemm_kernel_name(int32_t M, int32_t N, int32_t K, int32_t
     return w4a4_outlier_gemm_kernel_name(M, N, K, n_out, group);
 }
 
-w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
-                              const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
-                              int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group,
-                              void *Y, int64_t ldy, void *workspace, size_t workspace_bytes,
-                              w4a4_stream stream) {
+}  // extern "C"
+
+static w4a4_status outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
+                                const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
+                                int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                                int64_t ldy, void *workspace, size_t workspace_bytes, int32_t *acc4,
+                                int32_t *acc8, bool export_acc, w4a4_stream stream) {
     w4a4_status st = gemm_check(Aq4, Aq8, Wq4, Wq8, M, N, K, n_out, group);
     if (st != W4A4_OK)
         return st;
@@ -242,8 +256,11 @@ w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4
         return W4A4_OK;
     if (!Y || (K_n > 0 && (!sa4 || !sw4)) || (n_out > 0 && (!sa8 || !sw8)))
         return W4A4_ERR_INVALID_ARG;
+    if (export_acc && ((K_n > 0 && !acc4) || (n_out > 0 && !acc8)))
+        return W4A4_ERR_INVALID_ARG;
     if (!aligned(Y, 2) || (sa4 && !aligned(sa4, 4)) || (sw4 && !aligned(sw4, 4)) ||
-        (sa8 && !aligned(sa8, 4)) || (sw8 && !aligned(sw8, 4)))
+        (sa8 && !aligned(sa8, 4)) || (sw8 && !aligned(sw8, 4)) ||
+        (export_acc && ((acc4 && !aligned(acc4, 4)) || (acc8 && !aligned(acc8, 4)))))
         return W4A4_ERR_ALIGNMENT;
     const size_t need = w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group);
     if (workspace_bytes < need || (need > 0 && !workspace))
@@ -253,40 +270,45 @@ w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4
     w4a4::GemmArgs a = gemm_args(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group);
     a.y = static_cast<_Float16 *>(Y);
     a.ldy = ldy;
-    if (w4a4::launch_gemm(a, false, workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (export_acc) {
+        a.acc4_out = K_n > 0 ? acc4 : nullptr;
+        a.acc8_out = n_out > 0 ? acc8 : nullptr;
+    }
+    if (w4a4::launch_gemm(a, export_acc, workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
         return W4A4_ERR_HIP;
     return W4A4_OK;
 }
 
-w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const void *Wq4,
-                                  const void *Wq8, int32_t M, int32_t N, int32_t K, int32_t n_out,
-                                  int32_t group, int32_t *acc4, int32_t *acc8,
-                                  w4a4_stream stream) {
-    w4a4_status st = gemm_check(Aq4, Aq8, Wq4, Wq8, M, N, K, n_out, group);
-    if (st != W4A4_OK)
-        return st;
-    const int32_t K_n = K - n_out;
-    if (M == 0 || N == 0)
-        return W4A4_OK;
-    if ((K_n > 0 && !acc4) || (n_out > 0 && !acc8))
-        return W4A4_ERR_INVALID_ARG;
-    if ((acc4 && !aligned(acc4, 4)) || (acc8 && !aligned(acc8, 4)))
-        return W4A4_ERR_ALIGNMENT;
-    w4a4::GemmArgs a = gemm_args(Aq4, Aq8, nullptr, nullptr, Wq4, Wq8, nullptr, nullptr, M, N, K,
-                                 n_out, group);
-    a.acc4_out = acc4;
-    a.acc8_out = acc8;
-    if (w4a4::launch_gemm(a, true, nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return W4A4_ERR_HIP;
-    return W4A4_OK;
+extern "C" {
+
+w4a4_status w4a4_outlier_gemm(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
+                              const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
+                              int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group,
+                              void *Y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                              w4a4_stream stream) {
+    return outlier_gemm(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, workspace,
+                        workspace_bytes, nullptr, nullptr, false, stream);
 }
 
-// Workspace of the fused call: Aq4 | Aq8 | sa4 | sa8, each 256-byte aligned,
-// then the GEMM's own workspace.
-static void quant_gemm_layout(int32_t M, int32_t K, int32_t n_out, int32_t group, size_t off[5]) {
+w4a4_status w4a4_outlier_gemm_i32(const void *Aq4, const void *Aq8, const float *sa4, const float *sa8,
+                                  const void *Wq4, const void *Wq8, const float *sw4, const float *sw8,
+                                  int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group,
+                                  void *Y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                                  int32_t *acc4, int32_t *acc8, w4a4_stream stream) {
+    return outlier_gemm(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, workspace,
+                        workspace_bytes, acc4, acc8, true, stream);
+}
+
+// Workspace of the fused call: first the GEMM's own workspace, whose
+// arrival-counter block always sits at offset 0 and is always reserved (also
+// for shapes that do not split K), so the activation operands of one call
+// never land on the counters of a later one; then Aq4 | Aq8 | sa4 | sa8,
+// each 256-byte aligned. off[0..3] are the operand offsets, off[4] the size.
+static void quant_gemm_layout(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group, size_t off[5]) {
     const int32_t K_n = K - n_out;
     const int32_t G = w4a4_num_groups(K_n, group);
-    off[0] = 0;
+    const size_t gemm = std::max(w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group), w4a4::gemm_counter_bytes());
+    off[0] = round_up((int64_t)gemm, 256);
     off[1] = off[0] + round_up((int64_t)M * w4a4_pitch4_bytes(K_n), 256);
     off[2] = off[1] + round_up((int64_t)M * w4a4_pitch8_bytes(n_out), 256);
     off[3] = off[2] + round_up((int64_t)M * (G > 0 ? G : 0) * 4, 256);
@@ -298,8 +320,8 @@ size_t w4a4_quant_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t 
     if (M < 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
         return 0;
     size_t off[5];
-    quant_gemm_layout(M, K, n_out, group, off);
-    return off[4] + w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group);
+    quant_gemm_layout(M, N, K, n_out, group, off);
+    return off[4];
 }
 
 }  // extern "C"
@@ -319,6 +341,8 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
         return W4A4_ERR_INVALID_ARG;
     if (M == 0 || N == 0)
         return W4A4_OK;
+    if (!dma_offsets_fit(M, N, K_n, n_out))
+        return W4A4_ERR_UNSUPPORTED;
     if (!X || !perm || !Y || (K_n > 0 && (!Wq4 || !sw4)) ||
         (n_out > 0 && (!Wq8 || !sw8)))
         return W4A4_ERR_INVALID_ARG;
@@ -356,7 +380,7 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
                                                                                         : W4A4_ERR_HIP;
     }
     size_t off[5];
-    quant_gemm_layout(M, K, n_out, group, off);
+    quant_gemm_layout(M, N, K, n_out, group, off);
     char *ws = static_cast<char *>(workspace);
     void *Aq4 = K_n > 0 ? ws + off[0] : nullptr;
     void *Aq8 = n_out > 0 ? ws + off[1] : nullptr;
@@ -366,7 +390,7 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
     if (st != W4A4_OK)
         return st;
     return w4a4_outlier_gemm(Aq4, Aq8, sa4, sa8, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy,
-                             ws + off[4], workspace_bytes - off[4], stream);
+                             ws, off[0], stream);
 }
 
 extern "C" {

@@ -135,7 +135,8 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
-// Epilogue of edge tiles and of the accumulator export, block by block
+// Epilogue of edge tiles (and, in the accumulator export, of every tile: the
+// exact sums are stored, then Y as in the production epilogue), block by block
 // (column block outer, so the weight side of the tail is read once per
 // column): the INT4 sums of the block are copied out (and converted to the
 // fp32 partial acc4 * (sa4 * sw4 / 256), or exported), the INT8 tail product
@@ -177,6 +178,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, v16i (&acc)[FM][FN],
                     acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(pb8[j][s], x, acc[fm][fn], 0, 0, 0);
                 }
             if constexpr (EXPORT) {
+                // accumulator export (test path): this workgroup owns the sums
                 if (m < a.M) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -189,7 +191,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, v16i (&acc)[FM][FN],
                         }
                     }
                 }
-            } else {
+            }
+            {
                 const float rs4 = sS[ml] * (1.0f / 256.0f);
                 const float rs8 = T8 > 0 ? sS[BM + ml] : 0.0f;   // tail scales are not loaded when T8 == 0
 #pragma unroll
@@ -357,7 +360,7 @@ __device__ __forceinline__ void gemm_big_tile(const GemmArgs &a, unsigned char *
     // ---- scales of the tile, ahead of every K-tile ---------------------------------
     // Issued first, so the wait for K-tile 0 covers them as well (loads
     // complete in order). Lane tid carries row row0 + tid and column col0 + tid.
-    if constexpr (!EXPORT) {
+    {
         const uint32_t ss = lds_addr(sS) + wave_u * 256;
         const int64_t mr = min(row0 + tid, a.M - 1), nc = min(col0 + tid, a.N - 1);
         dma4(a.sa4 + mr * a.G, ss);

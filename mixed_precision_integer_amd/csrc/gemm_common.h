@@ -24,6 +24,13 @@ constexpr int lgkmcnt_only(int n) { return 0xF | (0x3 << 14) | (0x7 << 4) | ((n 
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// Accumulator export (test path of every GEMM kernel): the exact integer
+// partial sum a lane holds is added into the zeroed export array. Integer
+// additions are exact and commute, so the parts of one scale group that
+// different waves or workgroups hold give the same total in any order. The
+// adds share vmcnt with the DMA, so a kernel waits for vmcnt(0) after them.
+__device__ __forceinline__ void export_add(int32_t *dst, int v) { atomicAdd(dst, v); }
+
 // Byte offset of 16-byte chunk c of row r inside a K-tile of 64-byte rows.
 // Chunk c of row r is stored at slot (c ^ (r >> 1) ^ (r >> 2)) & 3: any 8
 // consecutive rows then land on 8 distinct 16-byte slots modulo 128 bytes and

@@ -57,6 +57,25 @@ __device__ __forceinline__ v4i as_v4i(uint4 p) { return v4i{(int)p.x, (int)p.y, 
 // 16-byte chunk c of row r of a pair slot sits at chunk position c ^ (r & 7)
 __device__ __forceinline__ int pair_off(int r, int c) { return r * PAIR + ((c ^ (r & 7)) << 4); }
 
+// Accumulator export (test path): add the exact integer sums of one 32 x 32
+// block (token rows m0 + li, columns n0 + 8 (e / 4) + 4 lh + e % 4) into the
+// zeroed export slice `dst` [M, N]; the waves that share a scale group add
+// their parts.
+__device__ __forceinline__ void export_block(const v16i &acc, int32_t *dst, int shift, const GemmArgs &a, int m0,
+                                             int n0, int li, int lh) {
+    const int m = m0 + li;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int n = n0 + 8 * (e / 4) + 4 * lh + e % 4;
+        if (m < a.M && n < a.N)
+            export_add(dst + (int64_t)m * a.N + n, acc[e] >> shift);
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    compiler_fence();
+}
+
+template <bool EXPORT>
 __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
     __shared__ __align__(16) unsigned char lds[WAVES * WAVE_LDS];
 
@@ -140,6 +159,8 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0, x0, s == 0 ? zi : acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1, x1, acc, 0, 0, 0);
         }
+        if constexpr (EXPORT)
+            export_block(acc, a.acc4_out + (int64_t)((tb + k) / tiles_per_group) * a.M * a.N, 8, a, 0, n0, li, lh);
         // scale products S[n][m] = sw[n] * sa[m] / 256 (the k = 1 lanes give zero)
         const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw[k], lh ? 0.0f : sa[k], zf, 0, 0, 0);
 #pragma unroll
@@ -187,6 +208,8 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
             acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w0), as_v4i(x0), acc8, 0, 0, 0);
             acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(w1), as_v4i(x1), acc8, 0, 0, 0);
         }
+        if constexpr (EXPORT)
+            export_block(acc8, a.acc8_out, 0, a, 0, n0, li, lh);
         const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : a.sw8[nrow], lh ? 0.0f : a.sa8[mrow], zf,
                                                              0, 0, 0);
 #pragma unroll
@@ -251,7 +274,7 @@ struct RowsRing {
     static constexpr int BYTES = WAVES * WAVE > WAVES * 16 * 64 * 4 ? WAVES * WAVE : WAVES * 16 * 64 * 4;
 };
 
-template <int MB>
+template <int MB, bool EXPORT>
 __global__ __launch_bounds__(THREADS) void gemm_decode_rows_kernel(GemmArgs a) {
     using R = RowsRing<MB>;
     __shared__ __align__(16) unsigned char lds[R::BYTES];
@@ -382,6 +405,13 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_rows_kernel(GemmArgs a) {
                     if (i < nb)
                         acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[q >> 1][q & 1], x[i][q >> 1][q & 1],
                                                                        q == 0 ? zi : acc[i], 0, 0, 0);
+            if constexpr (EXPORT) {
+#pragma unroll
+                for (int i = 0; i < kPair; ++i)
+                    if (i < nb)
+                        export_block(acc[i], a.acc4_out + (int64_t)((tb + k) / tiles_per_group) * a.M * a.N, 8, a,
+                                     32 * (b0 + i), n0, li, lh);
+            }
             // scale products one block at a time (16 registers live)
 #pragma unroll
             for (int i = 0; i < kPair; ++i)
@@ -427,6 +457,8 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_rows_kernel(GemmArgs a) {
             }
             v16i acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(tw[0]), as_v4i(tx[0]), zi, 0, 0, 0);
             acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(tw[1]), as_v4i(tx[1]), acc8, 0, 0, 0);
+            if constexpr (EXPORT)
+                export_block(acc8, a.acc8_out, 0, a, 32 * b, n0, li, lh);
             const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw8, lh ? 0.0f : a.sa8[min(32 * b + li, a.M - 1)],
                                                                  zf, 0, 0, 0);
             // the block index is uniform: select y[b] without indexing a register array
@@ -489,17 +521,34 @@ bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t 
            ((M <= MAXM && per <= MAXT) || (M <= 4 * MAXM && per <= MAXT_ROWS));
 }
 
-hipError_t launch_gemm_decode(const GemmArgs &a, hipStream_t stream) {
+const char *decode_kernel_name(int row_blocks) {
+    switch (row_blocks) {
+    case 1: return "gemm_decode_kernel<false>";
+    case 2: return "gemm_decode_rows_kernel<2, false>";
+    case 3: return "gemm_decode_rows_kernel<3, false>";
+    default: return "gemm_decode_rows_kernel<4, false>";
+    }
+}
+
+template <bool EXPORT>
+static void launch_decode(const GemmArgs &a, hipStream_t stream) {
     const int blocks = (a.N + BN - 1) / BN;
     const int mb = (a.M + MAXM - 1) / MAXM;
     if (mb <= 1)
-        hipLaunchKernelGGL(gemm_decode_kernel, dim3(blocks), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL(gemm_decode_kernel<EXPORT>, dim3(blocks), dim3(THREADS), 0, stream, a);
     else if (mb == 2)
-        hipLaunchKernelGGL(gemm_decode_rows_kernel<2>, dim3(blocks), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_decode_rows_kernel<2, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
     else if (mb == 3)
-        hipLaunchKernelGGL(gemm_decode_rows_kernel<3>, dim3(blocks), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_decode_rows_kernel<3, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL(gemm_decode_rows_kernel<4>, dim3(blocks), dim3(THREADS), 0, stream, a);
+        hipLaunchKernelGGL((gemm_decode_rows_kernel<4, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
+}
+
+hipError_t launch_gemm_decode(const GemmArgs &a, bool export_acc, hipStream_t stream) {
+    if (export_acc)
+        launch_decode<true>(a, stream);
+    else
+        launch_decode<false>(a, stream);
     return hipGetLastError();
 }
 

@@ -69,6 +69,30 @@ __device__ __forceinline__ void fold_half(float (&y)[F][F][16], const v16i (&acc
     }
 }
 
+// Accumulator export (test path): the exact integer sums of one group of a
+// wave's 2 x 2 blocks; lane (li, lh) of block (fm, fn) holds token row li and
+// the columns 8 (r / 4) + 4 lh + r % 4. This workgroup owns every sum of the
+// group for its tile, so the adds never meet another workgroup's.
+__device__ __forceinline__ void export_sums(const v16i (&acc)[F][F], int32_t *dst, int shift, const GemmArgs &a,
+                                            int row0, int col0, int wm, int wn, int li, int lh) {
+#pragma unroll
+    for (int fm = 0; fm < F; ++fm) {
+        const int m = row0 + wm * WT + fm * 32 + li;
+#pragma unroll
+        for (int fn = 0; fn < F; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = col0 + wn * WT + fn * 32 + 8 * (r / 4) + 4 * lh + r % 4;
+                if (m < a.M && n < a.N)
+                    export_add(dst + (int64_t)m * a.N + n, acc[fm][fn][r] >> shift);
+            }
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    compiler_fence();
+}
+
+template <bool EXPORT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_group_kernel(GemmArgs a) {
     __shared__ __align__(16) unsigned char lds[STAGES * STAGE];
@@ -240,8 +264,11 @@ void gemm_group_kernel(GemmArgs a) {
         }
         const float r0 = rs, a0 = ca, b0 = cb;
         next_tile(tt, false);
-        if (tt == T8 - 1)
+        if (tt == T8 - 1) {
+            if constexpr (EXPORT)
+                export_sums(acc, a.acc8_out, 0, a, row0, col0, wm, wn, li, lh);
             fold_group(r0, a0, b0);
+        }
     }
 
     // ---- INT4 tiles, one 128-channel group each ------------------------------------
@@ -267,6 +294,8 @@ void gemm_group_kernel(GemmArgs a) {
         }
         const float r0 = rs * (1.0f / 256.0f), a0 = ca, b0 = cb;
         next_tile(tt, true);
+        if constexpr (EXPORT)
+            export_sums(acc, a.acc4_out + (int64_t)(tt - T8) * a.M * a.N, 8, a, row0, col0, wm, wn, li, lh);
         fold_group(r0, a0, b0);
     }
     // the reloads past the last tile land in LDS this workgroup still owns
@@ -318,9 +347,12 @@ bool gemm_group_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t g
     return group == 128 && K_n >= 128 && M > 64;
 }
 
-hipError_t launch_gemm_group(const GemmArgs &a, hipStream_t stream) {
+hipError_t launch_gemm_group(const GemmArgs &a, bool export_acc, hipStream_t stream) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_group_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
+    if (export_acc)
+        hipLaunchKernelGGL(gemm_group_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(gemm_group_kernel<false>, dim3(tiles), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -160,7 +160,8 @@ __device__ __forceinline__ void dequant_group(const v16i (&acc)[C::FM][C::FN],
     }
 }
 
-// Accumulator export (test path): write the exact integer sums of a group.
+// Accumulator export (test path): add the exact integer sums of a group (or,
+// under a K split, of the part of the group this split covers).
 template <class C, bool TAIL>
 __device__ __forceinline__ void export_group(const v16i (&acc)[C::FM][C::FN], const GemmArgs &a,
                                              int gidx, int row0, int col0, int wm, int wn, int li,
@@ -176,17 +177,20 @@ __device__ __forceinline__ void export_group(const v16i (&acc)[C::FM][C::FN], co
                 const int m = row0 + wm * C::WTM + fm * 32 + (r / 4) * 8 + lh * 4 + (r % 4);
                 const int v = acc[fm][fn][r];
                 if (m < a.M && n < a.N)
-                    dst[(int64_t)m * a.N + n] = TAIL ? v : (v >> 8);
+                    export_add(dst + (int64_t)m * a.N + n, TAIL ? v : (v >> 8));
             }
         }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    compiler_fence();
 }
 
 template <class C, bool EXPORT, bool SPLIT>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     constexpr int BM = C::BM, BN = C::BN, FM = C::FM, FN = C::FN;
     constexpr int STAGES = C::STAGES, PREFETCH = C::PREFETCH;
-    constexpr int STAGE = C::A_BYTES + C::B_BYTES + (EXPORT ? 0 : C::S_BYTES);
-    constexpr int D = C::DA + C::DB + (EXPORT ? 0 : C::DS);   // DMA instructions per tile per lane
+    constexpr int STAGE = C::A_BYTES + C::B_BYTES + C::S_BYTES;
+    constexpr int D = C::DA + C::DB + C::DS;                   // DMA instructions per tile per lane
 
     __shared__ __align__(16) unsigned char lds[STAGES * STAGE];
     __shared__ int last_split;
@@ -260,11 +264,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 #pragma unroll
             for (int j = 0; j < C::DB; ++j)
                 dma16(B, b8o[j], sb + j * 4096);
-            if constexpr (!EXPORT) {
 #pragma unroll
-                for (int j = 0; j < C::DS; ++j)
-                    dma4((s_is_a[j] ? a.sa8 : a.sw8) + s_row[j], ss + j * 1024);
-            }
+            for (int j = 0; j < C::DS; ++j)
+                dma4((s_is_a[j] ? a.sa8 : a.sw8) + s_row[j], ss + j * 1024);
         } else {
             const int t4 = tt - T8;
             const uint8_t *A = a.a4 + t4 * kTileBytes;
@@ -275,12 +277,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 #pragma unroll
             for (int j = 0; j < C::DB; ++j)
                 dma16(B, b4o[j], sb + j * 4096);
-            if constexpr (!EXPORT) {
-                const int g = t4 / tiles_per_group;
+            const int g = t4 / tiles_per_group;
 #pragma unroll
-                for (int j = 0; j < C::DS; ++j)
-                    dma4((s_is_a[j] ? a.sa4 : a.sw4) + s_row[j] * (uint32_t)a.G + g, ss + j * 1024);
-            }
+            for (int j = 0; j < C::DS; ++j)
+                dma4((s_is_a[j] ? a.sa4 : a.sw4) + s_row[j] * (uint32_t)a.G + g, ss + j * 1024);
         }
     };
 
@@ -332,8 +332,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         }
         if constexpr (EXPORT)
             export_group<C, true>(acc, a, 0, row0, col0, wm, wn, li, lh);
-        else
-            dequant_group<C, true>(acc, yacc, st, wm, wn, li, lh);
+        dequant_group<C, true>(acc, yacc, st, wm, wn, li, lh);
     }
     while (tt < t_end) {
         const int g = (tt - T8) / tiles_per_group;
@@ -346,11 +345,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         }
         if constexpr (EXPORT)
             export_group<C, false>(acc, a, g, row0, col0, wm, wn, li, lh);
-        else
-            dequant_group<C, false>(acc, yacc, st, wm, wn, li, lh);
+        dequant_group<C, false>(acc, yacc, st, wm, wn, li, lh);
     }
 
-    if constexpr (!EXPORT) {
+    {
         if constexpr (!SPLIT) {
             // ---- epilogue: fp16 store --------------------------------------------------
 #pragma unroll
@@ -455,18 +453,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     gemm_body<Cfg<BM, BN, WAVES_M, WAVES_N, STAGES>, EXPORT, SPLIT>(a);
 }
 
-template <class C>
-hipError_t launch_cfg(const GemmArgs &a, bool export_acc, hipStream_t stream) {
+template <class C, bool EXPORT>
+hipError_t launch_cfg(const GemmArgs &a, hipStream_t stream) {
     const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
     const dim3 grid(tiles * a.splits);
-    if (export_acc)
-        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, true, false>), grid,
-                           dim3(kThreads), 0, stream, a);
-    else if (a.splits > 1)
-        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, false, true>), grid,
+    if (a.splits > 1)
+        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, EXPORT, true>), grid,
                            dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, false, false>), grid,
+        hipLaunchKernelGGL((gemm_kernel<C::BM, C::BN, C::WAVES_M, C::WAVES_N, C::STAGES, EXPORT, false>), grid,
                            dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -488,25 +483,31 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
-// Tile shape and K split for a shape. Pure function of the shape, so the
-// workspace query and the launch always agree.
+size_t gemm_counter_bytes() { return kSplitCounterBytes; }
+
+// Name of the production kernel of a plan as the kernel trace prints it
+// (template arguments included where they are fixed by the shape).
 const char *gemm_kernel_name(const GemmPlan &p) {
     switch (p.cfg) {
-    case 0: return p.splits > 1 ? "gemm_kernel<64, 64> (split K)" : "gemm_kernel<64, 64>";
-    case 1: return p.splits > 1 ? "gemm_kernel<128, 128> (split K)" : "gemm_kernel<128, 128>";
+    case 0: return p.splits > 1 ? "gemm_kernel<64, 64, 2, 2, 4, false, true>" : "gemm_kernel<64, 64, 2, 2, 4, false, false>";
+    case 1: return p.splits > 1 ? "gemm_kernel<128, 128, 2, 2, 4, false, true>" : "gemm_kernel<128, 128, 2, 2, 4, false, false>";
     case 2: return "gemm_big_kernel";
-    case 3: return "gemm_group_kernel";
-    case 4: return "gemm_decode_kernel";
+    case 3: return "gemm_group_kernel<false>";
+    case 4: return decode_kernel_name(p.mb);
     default: return "unknown";
     }
 }
 
-GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc) {
+// Tile shape and K split for a shape. A pure function of the shape, so the
+// workspace query and the launch always agree, and the accumulator export
+// runs the same kernel as the product.
+GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
     GemmPlan p{};
-    if (!export_acc && gemm_decode_fits(M, N, K_n, n_out, group)) {
+    if (gemm_decode_fits(M, N, K_n, n_out, group)) {
         p.cfg = 4;
         p.tiles = ceil_div(N, 32);
         p.splits = 1;
+        p.mb = ceil_div(M, 32);
         return p;
     }
     if (gemm_big_fits(M, N, K_n, n_out, w4a4_num_groups(K_n, group))) {
@@ -523,7 +524,7 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
     const int T = (int)(w4a4_pitch4_bytes(K_n) / 64 + w4a4_pitch8_bytes(n_out) / 64);
     int S = 1;
     const int slots = kDeviceCUs * per_cu;
-    if (!export_acc && p.tiles > 0 && p.tiles * 2 <= slots && p.tiles <= kMaxSplitTiles) {
+    if (p.tiles > 0 && p.tiles * 2 <= slots && p.tiles <= kMaxSplitTiles) {
         // about half the resident slots: measured on the 8192 x 8192 decode
         // shapes, more splits cost more in partial-sum traffic and arrival
         // latency than they gain in memory parallelism. At least two K-tiles
@@ -536,7 +537,7 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
         S = std::max(S, 1);
     }
     p.splits = S;
-    if (S == 1 && !export_acc && gemm_group_fits(M, N, K_n, n_out, group)) {
+    if (S == 1 && gemm_group_fits(M, N, K_n, n_out, group)) {
         p.cfg = 3;
         p.tiles = ceil_div(M, 128) * ceil_div(N, 128);
         return p;
@@ -553,25 +554,55 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
     return p;
 }
 
+namespace {
+
+__global__ void zero_i32_kernel(int32_t *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t j = i; j < n; j += stride)
+        p[j] = 0;
+}
+
+hipError_t zero_i32(int32_t *p, int64_t n, hipStream_t stream) {
+    if (!p || n <= 0)
+        return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const GemmArgs &a_in, bool export_acc, void *workspace, hipStream_t stream) {
     if (a_in.M == 0 || a_in.N == 0)
         return hipSuccess;
     GemmArgs a = a_in;
-    const GemmPlan p = plan_gemm(a.M, a.N, a.K_n, a.n_out, a.group, export_acc);
+    const GemmPlan p = plan_gemm(a.M, a.N, a.K_n, a.n_out, a.group);
     a.splits = p.splits;
     if (p.splits > 1) {
         a.ctr = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.part_offset);
     }
+    if (export_acc) {
+        // the export adds partial sums: both arrays start at zero
+        hipError_t e = zero_i32(a.acc4_out, (int64_t)a.G * a.M * a.N, stream);
+        if (e == hipSuccess && a.n_out > 0)
+            e = zero_i32(a.acc8_out, (int64_t)a.M * a.N, stream);
+        if (e != hipSuccess)
+            return e;
+    } else {
+        a.acc4_out = nullptr;
+        a.acc8_out = nullptr;
+    }
     if (p.cfg == 2)
         return launch_gemm_big(a, export_acc, stream);
     if (p.cfg == 3)
-        return launch_gemm_group(a, stream);
+        return launch_gemm_group(a, export_acc, stream);
     if (p.cfg == 4)
-        return launch_gemm_decode(a, stream);
+        return launch_gemm_decode(a, export_acc, stream);
     if (p.cfg == 0)
-        return launch_cfg<CfgSmall>(a, export_acc, stream);
-    return launch_cfg<CfgMid>(a, export_acc, stream);
+        return export_acc ? launch_cfg<CfgSmall, true>(a, stream) : launch_cfg<CfgSmall, false>(a, stream);
+    return export_acc ? launch_cfg<CfgMid, true>(a, stream) : launch_cfg<CfgMid, false>(a, stream);
 }
 
 }  // namespace w4a4

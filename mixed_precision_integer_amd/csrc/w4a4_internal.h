@@ -69,23 +69,30 @@ struct GemmPlan {
                               // 4 decode (M <= 128, weights streamed once)
     int tiles;                // output tiles
     int splits;               // K splits per output tile
+    int mb;                   // decode: 32-row token blocks (1: gemm_decode_kernel)
     size_t part_offset;       // byte offset of the fp32 partial sums (counters first)
     size_t part_bytes;        // fp32 partial sums
     size_t workspace_bytes;   // 0 when splits == 1
 };
 
-GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group, bool export_acc);
+GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
+
+// Bytes of the arrival-counter block at the start of every split-K workspace.
+size_t gemm_counter_bytes();
 
 // Kernel of a plan, as named in a kernel trace (static string).
 const char *gemm_kernel_name(const GemmPlan &p);
 
 // `workspace` holds plan_gemm(...).workspace_bytes bytes; its counter part
-// must be zero on entry and is zero again when the kernel completes.
+// must be zero on entry and is zero again when the kernel completes. With
+// export_acc the same kernel also adds its exact integer sums into
+// a.acc4_out / a.acc8_out, which this call zeroes first.
 hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipStream_t stream);
 
 // Decode kernels for M <= 128 token rows (gemm_decode.hip).
 bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
-hipError_t launch_gemm_decode(const GemmArgs &a, hipStream_t stream);
+const char *decode_kernel_name(int row_blocks);
+hipError_t launch_gemm_decode(const GemmArgs &a, bool export_acc, hipStream_t stream);
 
 // Decode layer call with the quantizer fused in (gemm_decode_fused.hip): at
 // most 2 token rows, 128-channel groups, at most 128 outlier channels.
@@ -106,7 +113,7 @@ hipError_t launch_decode_fused(const DecodeFusedArgs &a, hipStream_t stream);
 
 // 128 x 128 tile kernel for 128-channel scale groups (gemm_group.hip).
 bool gemm_group_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
-hipError_t launch_gemm_group(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_gemm_group(const GemmArgs &a, bool export_acc, hipStream_t stream);
 
 // 256 x 256 tile kernel for one scale group per row (gemm_big.hip).
 bool gemm_big_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t G);

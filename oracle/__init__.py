@@ -238,6 +238,40 @@ def linear_at(qa, qw, group: int, m_idx, n_idx):
     return acc4, acc8, y
 
 
+def linear_dense(qa, qw, group: int):
+    """Integer GEMM + fp64 dequant at every output position (the same steps
+    as linear_at, for whole-matrix checks).
+
+    The group sums (step O6) are taken with a library float64 matrix product
+    of the codes: every product and partial sum is an integer below 2^53, so
+    the product is exact whatever order the library sums in. The dequant
+    (O7) evaluates y* = sum_t (sa4 * sw4) * acc4_t + (sa8 * sw8) * acc8 in
+    fp64 in the same order and association as linear_at.
+    Returns (acc4 int32 [G, M, N], acc8 int32 [M, N], ystar float64 [M, N]).
+    """
+    qa4, sa4, qa8, sa8 = qa
+    qw4, sw4, qw8, sw8 = qw
+    M, K_n = qa4.shape
+    N, n_out = qw4.shape[0], qa8.shape[1]
+    G = num_groups(K_n, group)
+    gl = group if group > 0 else K_n
+
+    def exact_sums(a, b):
+        s = np.asarray(a, np.float64) @ np.asarray(b, np.float64).T
+        if s.size and (s.max() > 2**31 - 1 or s.min() < -2**31):
+            raise OverflowError("accumulator outside int32")
+        return s.astype(np.int32)
+
+    acc4 = np.zeros((G, M, N), np.int32)
+    y = np.zeros((M, N), np.float64)
+    for t in range(G):
+        acc4[t] = exact_sums(qa4[:, t * gl:(t + 1) * gl], qw4[:, t * gl:(t + 1) * gl])
+        y += (np.asarray(sa4[:, t], np.float64)[:, None] * np.asarray(sw4[:, t], np.float64)[None, :]) * acc4[t]
+    acc8 = exact_sums(qa8, qw8) if n_out else np.zeros((M, N), np.int32)
+    y += (np.asarray(sa8, np.float64)[:, None] * np.asarray(sw8, np.float64)[None, :]) * acc8
+    return acc4, acc8, y
+
+
 def to_fp16(ystar) -> np.ndarray:
     """fp64 -> fp16, round to nearest even (numpy's direct double->half cast)."""
     return np.asarray(ystar, np.float64).astype(np.float16)

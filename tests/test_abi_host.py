@@ -267,16 +267,70 @@ def test_device_calls_fail_loudly_without_gpu():
 
 
 @pytest.mark.parametrize("shape,name", [
-    ((1, 8192, 8192, 128, 128), "gemm_decode_kernel"),         # decode batch: weights streamed once
-    ((2048, 4096, 4096, 128, 128), "gemm_group_kernel"),       # 128-channel groups
-    ((2048, 11008, 4096, 256, 0), "gemm_big_kernel"),          # per-row scales, >= 256 large tiles
-    ((48, 384, 4224, 128, 128), "gemm_decode_kernel"),         # decode batch of two row blocks
-    ((48, 384, 17536, 128, 128), "gemm_kernel<64, 64> (split K)"),   # K_n past the decode kernel's range
-    ((0, 1, 1, 0, 0), None),                                   # rejected shapes
+    ((1, 8192, 8192, 128, 128), "gemm_decode_kernel<false>"),   # decode batch: weights streamed once
+    ((32, 8192, 8192, 128, 128), "gemm_decode_kernel<false>"),
+    ((16, 256, 256, 16, 0), "gemm_decode_kernel<false>"),       # the tiny per-row layer
+    ((2048, 4096, 4096, 128, 128), "gemm_group_kernel<false>"), # 128-channel groups
+    ((2048, 11008, 4096, 256, 0), "gemm_big_kernel"),           # per-row scales, >= 256 large tiles
+    ((48, 384, 4224, 128, 128), "gemm_decode_rows_kernel<2, false>"),   # two row blocks
+    ((96, 384, 4224, 128, 128), "gemm_decode_rows_kernel<3, false>"),
+    ((128, 8192, 8192, 128, 128), "gemm_decode_rows_kernel<4, false>"),
+    ((256, 8192, 8192, 128, 128), "gemm_kernel<128, 128, 2, 2, 4, false, true>"),   # split K
+    ((48, 384, 17536, 128, 128), "gemm_kernel<64, 64, 2, 2, 4, false, true>"),      # K_n past the decode range
+    ((200, 300, 1024, 32, 0), "gemm_kernel<128, 128, 2, 2, 4, false, false>"),
+    ((0, 1, 1, 0, 0), None),                                    # rejected shapes
     ((4, 4, 130, 0, 128), None),
 ])
 def test_gemm_kernel_name(shape, name):
     assert w4.outlier_gemm_kernel_name(*shape) == name
+
+
+def test_gemm_rejects_rows_past_32bit_offsets():
+    """Operand rows are addressed by 32-bit byte offsets: a shape whose last
+    packed row would start at 4 GiB or more is rejected before any launch."""
+    # K_n = 21760 -> 10880-byte rows; 394759 rows reach 2^32
+    K, n_out = 22016, 256
+    assert gemm(M=394800, N=8, K=K, n_out=n_out, ldy=8) == UNSUPPORTED
+    assert gemm(M=4, N=394800, K=K, n_out=n_out, ldy=394800) == UNSUPPORTED
+    L = w4.lib()
+    need = w4.quant_gemm_workspace_bytes(394800, 8, K, n_out, 0)
+    assert L.w4a4_quant_gemm(FAKE, K, FAKE, FAKE, FAKE, FAKE, FAKE, 394800, 8, K, n_out, 0, FAKE, 8,
+                             FAKE, need, None) == UNSUPPORTED
+
+
+def gemm_i32(**kw):
+    args = dict(a4=FAKE, a8=FAKE, sa4=FAKE, sa8=FAKE, w4=FAKE, w8=FAKE, sw4=FAKE, sw8=FAKE,
+                M=4, N=8, K=256, n_out=16, group=0, Y=FAKE, ldy=8, ws=None, ws_bytes=0,
+                acc4=FAKE, acc8=FAKE)
+    args.update(kw)
+    return w4.lib().w4a4_outlier_gemm_i32(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(acc4=None), INVALID), (dict(acc8=None), INVALID), (dict(Y=None), INVALID),
+    (dict(sa4=None), INVALID), (dict(acc4=FAKE + 2), ALIGN), (dict(K=272, group=64), UNSUPPORTED),
+])
+def test_gemm_i32_rejects(kw, code):
+    assert gemm_i32(**kw) == code
+
+
+def test_gemm_i32_empty_is_ok():
+    assert gemm_i32(M=0, a4=None, a8=None, sa4=None, sa8=None, Y=None, acc4=None, acc8=None) == OK
+
+
+def test_quant_gemm_workspace_keeps_the_counters_first():
+    """The fused call's workspace reserves the GEMM's arrival-counter block at
+    offset 0 for every shape, so the activation codes of one call never land
+    on the counters of a later split-K call sharing the workspace."""
+    for shape in [(256, 8192, 8192, 128, 128), (200, 8192, 8192, 128, 128), (64, 8192, 8192, 128, 128),
+                  (16, 256, 256, 16, 0)]:
+        M, N, K, n_out, g = shape
+        gemm_ws = w4.outlier_gemm_workspace_bytes(*shape)
+        act = (M * w4.pitch4_bytes(K - n_out) + M * w4.pitch8_bytes(n_out) + 4 * M * max(w4.num_groups(K - n_out, g), 0)
+               + 4 * M)
+        assert w4.quant_gemm_workspace_bytes(*shape) >= max(gemm_ws, 2048) + act
+    assert w4.outlier_gemm_workspace_bytes(256, 8192, 8192, 128, 128) > 0      # these two split K
+    assert w4.outlier_gemm_workspace_bytes(200, 8192, 8192, 128, 128) > 0
 
 
 def test_one_launch_decode_path_bounds():
@@ -285,10 +339,10 @@ def test_one_launch_decode_path_bounds():
     producer + GEMM launches (a pure function of the shape)."""
     assert w4.quant_gemm_kernel_name(1, 8192, 8192, 128, 128) == "decode_fused_kernel"
     assert w4.quant_gemm_kernel_name(2, 256, 16384 + 64, 64, 128) == "decode_fused_kernel"
-    assert w4.quant_gemm_kernel_name(3, 256, 1152, 128, 128) == "gemm_decode_kernel"
-    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 0) == "gemm_decode_kernel"
-    assert w4.quant_gemm_kernel_name(2, 256, 1280, 256, 128) == "gemm_decode_kernel"
+    assert w4.quant_gemm_kernel_name(3, 256, 1152, 128, 128) == "gemm_decode_kernel<false>"
+    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 0) == "gemm_decode_kernel<false>"
+    assert w4.quant_gemm_kernel_name(2, 256, 1280, 256, 128) == "gemm_decode_kernel<false>"
     assert w4.quant_gemm_kernel_name(2, 256, 16384 + 256, 128, 128) != "decode_fused_kernel"
-    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 256) == "gemm_decode_kernel"
+    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 256) == "gemm_decode_kernel<false>"
     assert w4.quant_gemm_kernel_name(2048, 4096, 4096, 128, 128) == w4.outlier_gemm_kernel_name(2048, 4096, 4096, 128, 128)
     assert w4.quant_gemm_kernel_name(0, 256, 1152, 128, 128) is None

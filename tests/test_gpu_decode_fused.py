@@ -78,7 +78,7 @@ def test_fused_decode_parity(oracle, M, N, K, n_out, ldx, ldy):
     if ldy:
         assert torch.isnan(Ys[:, N:]).all(), "wrote past N"
     assert bool((ws == 0x5A).all()), "the one-launch path writes no workspace"
-    ref = _oracle_y(oracle, X, W, perm.cpu().numpy(), n_out, group)
+    ref = _oracle_y(oracle, X, W, oracle.make_perm(K, o), n_out, group)
     got = yf.cpu().numpy().astype(np.float64)
     amax = np.abs(ref.astype(np.float64)).max()
     assert np.all(np.isfinite(got))
@@ -90,7 +90,7 @@ def test_fused_decode_zero_rows_and_groups(oracle):
     ordinary rows: identical to the two-launch path and to the oracle."""
     M, N, K, n_out = 2, 128, 1152, 128
     X, W, o = wl.draw(M, N, K, n_out, seed=31, outlier_factor=30.0)
-    perm_h = w4.make_perm(K, o)
+    perm_h = oracle.make_perm(K, o)
     X[0, perm_h[256:384]] = 0                   # one whole INT4 group of row 0
     X[0, o] = 0                                 # and its outlier channels
     X[1] = 0
@@ -111,7 +111,7 @@ def test_fused_decode_rows_far_apart(oracle):
     X = (X.astype(np.float32) * np.array([2.0 ** -6, 2.0 ** 6], np.float32)[:, None]).astype(np.float16)
     perm, a, w, yf, y2, _, _ = _layer(X, W, o, 128)
     assert torch.equal(yf, y2)
-    ref = _oracle_y(oracle, X, W, perm.cpu().numpy(), n_out, 128)
+    ref = _oracle_y(oracle, X, W, oracle.make_perm(K, o), n_out, 128)
     for m in range(M):                          # the bar per row: each row has its own scale
         amax = np.abs(ref[m].astype(np.float64)).max()
         assert np.abs(yf[m].cpu().numpy().astype(np.float64) - ref[m]).max() <= TOL * amax
@@ -143,7 +143,7 @@ def test_fused_decode_rmsnorm_parity(oracle, M, N, K, n_out, eps, zero_row):
     y2 = w4.w4a4_outlier_gemm(a, w)
     torch.cuda.synchronize()
     assert torch.equal(yf, y2), "one-launch norm call differs from norm producer + GEMM"
-    perm_h = perm.cpu().numpy()
+    perm_h = oracle.make_perm(K, o)
     qa = oracle.rmsnorm_quantize_rows(X, g, eps, perm_h, n_out, group)
     qw = oracle.quantize_rows(W, perm_h, n_out, group)
     mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")

@@ -52,8 +52,8 @@ def to_dev(X, ld=None):
 def check_norm_producer(oracle, X, gamma, eps, outliers, group, ld=None):
     rows, K = X.shape
     n_out = len(outliers)
-    perm_h = w4.make_perm(K, outliers)
-    perm = torch.from_numpy(perm_h).to(DEV)
+    perm_h = oracle.make_perm(K, outliers)                  # the oracle's own permutation
+    perm = torch.from_numpy(w4.make_perm(K, outliers)).to(DEV)
     op, rstd = w4.rmsnorm_quant_reorder_act(to_dev(X, ld), torch.from_numpy(gamma).to(DEV), eps,
                                             perm, n_out, group, want_rstd=True)
     q4, s4, q8, s8 = oracle.rmsnorm_quantize_rows(X, gamma, eps, perm_h, n_out, group)
@@ -128,8 +128,8 @@ def test_norm_fused_layer(oracle):
     _say(f"norm fused layer M={M} N={N} K={K}")
     X, W, o = wl.draw(M, N, K, n_out, seed=41, outlier_factor=30.0)
     g = wl.draw_norm_weight(K, seed=41)
-    perm_h = w4.make_perm(K, o)
-    perm = torch.from_numpy(perm_h).to(DEV)
+    perm_h = oracle.make_perm(K, o)
+    perm = torch.from_numpy(w4.make_perm(K, o)).to(DEV)
     Xd, gd = torch.from_numpy(X).to(DEV), torch.from_numpy(g).to(DEV)
     w = w4.pack_int4_weights(torch.from_numpy(W).to(DEV), perm, n_out, group)
     y = w4.rmsnorm_quant_gemm(Xd, gd, 1e-6, perm, w)
@@ -154,8 +154,8 @@ def test_norm_full_size_qproj_layer(oracle):
     _say(f"norm fused layer {work.name}")
     X, W, o = wl.draw_workload(work)
     g = wl.draw_norm_weight(work.K, seed=work.seed)
-    perm_h = w4.make_perm(work.K, o)
-    perm = torch.from_numpy(perm_h).to(DEV)
+    perm_h = oracle.make_perm(work.K, o)
+    perm = torch.from_numpy(w4.make_perm(work.K, o)).to(DEV)
     w = w4.pack_int4_weights(torch.from_numpy(W).to(DEV), perm, work.n_out, work.group)
     y = w4.rmsnorm_quant_gemm(torch.from_numpy(X).to(DEV), torch.from_numpy(g).to(DEV), 1e-6,
                               perm, w)

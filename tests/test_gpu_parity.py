@@ -2,14 +2,21 @@
 
 Bars (from the layer's definition; the oracle is pinned separately):
 * codes, padding bytes and fp32 scales of the producer: bit-exact;
-* int32 accumulators of the GEMM (exported from the production main loop):
-  bit-exact;
+* int32 accumulators of the GEMM: bit-exact. They come from
+  w4a4_outlier_gemm_i32, which launches the kernel w4a4_outlier_gemm launches
+  for the shape (one shape-only plan serves both) and writes the same Y; the
+  tests check that Y bit for bit;
 * fp16 output: max |Y - Y_oracle| <= 1e-2 * max |Y_oracle| (the GPU sums the
   scaled groups in fp32 in its own order; the oracle sums in fp64).
 
-Mid-size cases compare every output and span several 128 x 128 tiles with
-ragged M, N and K edges. The five named workloads run at full size and are
-compared on every producer byte and on sampled GEMM outputs.
+The oracle side always takes its own permutation (oracle.make_perm), so a
+wrong permutation from the library's host helper would show.
+
+Mid-size cases span several tiles with ragged M, N and K edges. The five
+named workloads and the large-tile and group-tile shapes run at full size.
+Every case compares every output: accumulators against the oracle's
+whole-matrix GEMM (oracle.linear_dense, pinned to the per-position C oracle)
+and Y against its fp64 dequant.
 """
 import sys
 
@@ -93,38 +100,39 @@ def full_compare(oracle, X, W, outliers, group):
     N = W.shape[0]
     n_out = len(outliers)
     perm, Xd, a, w = run_layer(X, W, outliers, group)
-    perm_h = perm.cpu().numpy()
-    qa = check_producer(oracle, a, X, perm_h, n_out, group)
-    qw = check_producer(oracle, w, W, perm_h, n_out, group)
-    mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")
-    acc4, acc8, ystar = oracle.linear_at(qa, qw, group, mm.reshape(-1), nn.reshape(-1))
-    G = acc4.shape[1]
-    g4, g8 = w4.w4a4_outlier_gemm_i32(a, w)
-    torch.cuda.synchronize()
-    assert np.array_equal(g4.cpu().numpy(), acc4.reshape(M, N, G).transpose(2, 0, 1)), "acc4"
-    if n_out:
-        assert np.array_equal(g8.cpu().numpy(), acc8.reshape(M, N)), "acc8"
+    perm_o = oracle.make_perm(K, outliers)
+    qa = check_producer(oracle, a, X, perm_o, n_out, group)
+    qw = check_producer(oracle, w, W, perm_o, n_out, group)
+    acc4, acc8, ystar = oracle.linear_dense(qa, qw, group)
+    g4, g8, y_exp = w4.w4a4_outlier_gemm_i32(a, w)
     y = w4.w4a4_outlier_gemm(a, w)
-    rel, ndiff = check_y(y.cpu().numpy(), oracle.to_fp16(ystar).reshape(M, N))
     yf = w4.quant_gemm(Xd, perm, w)
     torch.cuda.synchronize()
+    assert torch.equal(y, y_exp), "the accumulator export's launch wrote a different Y"
+    G = acc4.shape[0]
+    for t in range(G):                      # one group at a time (bounded host memory)
+        assert np.array_equal(g4[t].cpu().numpy(), acc4[t]), f"acc4 group {t}"
+    del g4
+    if n_out:
+        assert np.array_equal(g8.cpu().numpy(), acc8), "acc8"
+    rel, ndiff = check_y(y.cpu().numpy(), oracle.to_fp16(ystar))
     assert torch.equal(yf, y), "fused call differs from producer + GEMM"
     return rel, ndiff
 
 
 MID = [
-    # M, N, K, n_out, group
-    (16, 256, 256, 16, 0),          # the tiny workload's shape, other seed
-    (200, 300, 1024, 32, 0),        # ragged M and N, K_n = 992 not a tile multiple
-    (130, 257, 1152, 128, 128),     # group 128, G = 8, ragged N
-    (300, 130, 2176, 128, 256),     # group 256 spans two K-tiles
-    (37, 200, 640, 100, 0),         # tail of 100 padded to 128
-    (1, 128, 512, 0, 0),            # one token, no outliers
-    (64, 64, 256, 256, 0),          # every channel an outlier: plain W8A8
-    (70, 90, 384, 0, 128),          # group mode without outliers
-    (512, 512, 4096, 128, 128),     # several full tiles in both directions
-    (600, 300, 2304, 256, 0),       # large-tile path with ragged M and N
-    (520, 260, 1664, 128, 128),     # large-tile path, group mode, ragged
+    # M, N, K, n_out, group                 kernel the shape runs
+    (16, 256, 256, 16, 0),          # decode kernel: the tiny workload's shape, other seed
+    (200, 300, 1024, 32, 0),        # 128 x 128 generic kernel, ragged M and N, K_n = 992
+    (130, 257, 1152, 128, 128),     # group-tile kernel, G = 8, ragged N
+    (300, 130, 2176, 128, 256),     # 128 x 128 generic kernel: group 256 spans two K-tiles
+    (37, 200, 640, 100, 0),         # row-block decode kernel (2 blocks): tail of 100 padded to 128
+    (1, 128, 512, 0, 0),            # decode kernel: one token, no outliers
+    (64, 64, 256, 256, 0),          # 64 x 64 generic kernel: every channel an outlier (plain W8A8)
+    (70, 90, 384, 0, 128),          # row-block decode kernel (3 blocks): group mode, no outliers
+    (512, 512, 4096, 128, 128),     # group-tile kernel, several full tiles each way
+    (600, 300, 2304, 256, 0),       # 128 x 128 generic kernel (under 256 large tiles), ragged
+    (520, 260, 1664, 128, 128),     # group-tile kernel with ragged M and N
 ]
 
 
@@ -195,7 +203,7 @@ DECODE = [
 @pytest.mark.parametrize("M,N,K,n_out,group", DECODE)
 def test_decode_parity(oracle, M, N, K, n_out, group):
     assert w4.outlier_gemm_workspace_bytes(M, N, K, n_out, group) == 0
-    assert w4.outlier_gemm_kernel_name(M, N, K, n_out, group) == "gemm_decode_kernel"
+    assert w4.outlier_gemm_kernel_name(M, N, K, n_out, group).startswith("gemm_decode")
     X, W, o = wl.draw(M, N, K, n_out, seed=M * 13 + K, outlier_factor=30.0)
     full_compare(oracle, X, W, o, group)
 
@@ -255,58 +263,26 @@ def test_gemm_extreme_codes(oracle, mode):
     mm, nn = np.meshgrid(np.arange(M, dtype=np.int32), np.arange(N, dtype=np.int32), indexing="ij")
     acc4, acc8, ystar = oracle.linear_at((qa4, sa4, qa8, sa8), (qw4, sw4, qw8, sw8), 0,
                                          mm.reshape(-1), nn.reshape(-1))
-    g4, g8 = w4.w4a4_outlier_gemm_i32(a, w)
+    g4, g8, y_exp = w4.w4a4_outlier_gemm_i32(a, w)
+    y = w4.w4a4_outlier_gemm(a, w)
     torch.cuda.synchronize()
+    assert torch.equal(y, y_exp)
     assert np.array_equal(g4.cpu().numpy()[0], acc4[:, 0].reshape(M, N))
     assert np.array_equal(g8.cpu().numpy(), acc8.reshape(M, N))
-    y = w4.w4a4_outlier_gemm(a, w)
     check_y(y.cpu().numpy(), oracle.to_fp16(ystar).reshape(M, N))
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads: every producer byte, sampled GEMM outputs
+# full-size workloads: every producer byte and every GEMM output
 # ---------------------------------------------------------------------------
-def sample_pairs(M, N, P, seed):
-    rng = np.random.default_rng(seed)
-    m = rng.integers(0, M, P).astype(np.int32)
-    n = rng.integers(0, N, P).astype(np.int32)
-    corners = np.array([[0, 0], [M - 1, N - 1], [0, N - 1], [M - 1, 0]], np.int32)
-    return np.concatenate([m, corners[:, 0]]), np.concatenate([n, corners[:, 1]])
-
-
-def full_size_check(oracle, X, W, o, group, P=4096):
-    M, K = X.shape
-    N = W.shape[0]
-    n_out = len(o)
-    perm, Xd, a, w = run_layer(X, W, o, group)
-    perm_h = perm.cpu().numpy()
-    qa = check_producer(oracle, a, X, perm_h, n_out, group)
-    qw = check_producer(oracle, w, W, perm_h, n_out, group)
-    mi, ni = sample_pairs(M, N, P, seed=M + N)
-    acc4, acc8, ystar = oracle.linear_at(qa, qw, group, mi, ni)
-    g4, g8 = w4.w4a4_outlier_gemm_i32(a, w)
-    mt, nt = torch.from_numpy(mi).long().to(DEV), torch.from_numpy(ni).long().to(DEV)
-    got4 = g4[:, mt, nt].cpu().numpy().T
-    got8 = g8[mt, nt].cpu().numpy()
-    del g4, g8
-    assert np.array_equal(got4, acc4), "acc4 (sampled)"
-    assert np.array_equal(got8, acc8), "acc8 (sampled)"
-    y = w4.quant_gemm(Xd, perm, w)
-    y_s = y[mt, nt].cpu().numpy()
-    ref = oracle.to_fp16(ystar)
-    # the tolerance scale is max |Y_oracle| over the sampled outputs
-    rel, _ = check_y(y_s, ref)
-    y2 = w4.w4a4_outlier_gemm(a, w)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y2)
-    return rel
-
-
 @pytest.mark.parametrize("work", [wl.QPROJ_7B, wl.UPPROJ_7B, wl.DOWNPROJ_65B],
                          ids=lambda w: w.name)
 def test_full_size_workload(oracle, work):
     X, W, o = wl.draw_workload(work)
-    full_size_check(oracle, X, W, o, work.group)
+    sys.stderr.write(f"[gpu case] full size {work.name}: "
+                     f"{w4.outlier_gemm_kernel_name(work.M, work.N, work.K, work.n_out, work.group)}\n")
+    sys.stderr.flush()
+    full_compare(oracle, X, W, o, work.group)
 
 
 # The activation producer on its own (codes, scales and padding bit-exact
@@ -337,7 +313,7 @@ def test_producer_parity(oracle, rows, K, n_out, group):
     X, _, o = wl.draw(rows, 1, K, n_out, seed=rows + K + n_out, outlier_factor=30.0)
     perm = torch.from_numpy(w4.make_perm(K, o)).to(DEV)
     a = w4.quant_reorder_act(torch.from_numpy(X).to(DEV), perm, n_out, group)
-    check_producer(oracle, a, X, perm.cpu().numpy(), n_out, group)
+    check_producer(oracle, a, X, oracle.make_perm(K, o), n_out, group)
 
 
 # The longest row the producer takes (24576 channels, the 1024-lane bucket)
@@ -365,8 +341,9 @@ BIG_TILE = [
 
 @pytest.mark.parametrize("M,N,K,n_out,group", BIG_TILE)
 def test_big_tile_parity(oracle, M, N, K, n_out, group):
+    assert w4.outlier_gemm_kernel_name(M, N, K, n_out, group) == "gemm_big_kernel"
     X, W, o = wl.draw(M, N, K, n_out, seed=M + N + K, outlier_factor=40.0)
-    full_size_check(oracle, X, W, o, group, P=6144)
+    full_compare(oracle, X, W, o, group)
 
 
 # Shapes with 128-channel scale groups and more than 256 output tiles of
@@ -385,20 +362,78 @@ GROUP_TILE = [
 @pytest.mark.parametrize("M,N,K,n_out,group", GROUP_TILE)
 def test_group_tile_parity(oracle, M, N, K, n_out, group):
     assert w4.outlier_gemm_workspace_bytes(M, N, K, n_out, group) == 0, "shape splits K"
+    assert w4.outlier_gemm_kernel_name(M, N, K, n_out, group) == "gemm_group_kernel<false>"
     X, W, o = wl.draw(M, N, K, n_out, seed=M + 3 * N + K, outlier_factor=30.0)
-    rel = full_size_check(oracle, X, W, o, group, P=6144)
+    rel, _ = full_compare(oracle, X, W, o, group)
     # The fp32 dequantization of every group adds far less than the fp16
     # rounding of the output (2^-11 of max |Y|), well inside the layer
     # tolerance: a fold that loses precision shows here first.
     assert rel <= 1e-3, f"group fold error {rel:.2e} of max |Y|"
 
 
-def test_decode_sweep(oracle):
-    X, W, o = wl.draw_workload(wl.DECODE_65B)
-    for M in wl.DECODE_M:
-        sys.stderr.write(f"[gpu case] decode M={M}\n")
-        sys.stderr.flush()
-        full_size_check(oracle, np.ascontiguousarray(X[:M]), W, o, wl.DECODE_65B.group, P=2048)
+@pytest.mark.parametrize("M", wl.DECODE_M)
+def test_decode_sweep(oracle, M):
+    """The 65B decode sweep at full size, every output, on the kernel each
+    batch size runs in production (decode, row-block decode, split K)."""
+    d = wl.DECODE_65B
+    X, W, o = wl.draw_workload(d)
+    sys.stderr.write(f"[gpu case] decode M={M}: {w4.outlier_gemm_kernel_name(M, d.N, d.K, d.n_out, d.group)}\n")
+    sys.stderr.flush()
+    full_compare(oracle, np.ascontiguousarray(X[:M]), W, o, d.group)
+
+
+# Every production kernel class is reached by the cases of this file; the
+# export runs the same plan, so its kernel is the production kernel.
+PRODUCTION_KERNELS = {
+    (16, 256, 256, 16, 0): "gemm_decode_kernel<false>",             # the tiny layer
+    (2048, 4096, 4096, 128, 128): "gemm_group_kernel<false>",       # q_proj prefill
+    (4096, 11008, 4096, 256, 0): "gemm_big_kernel",                 # up_proj prefill
+    (8192, 8192, 22016, 256, 0): "gemm_big_kernel",                 # down_proj prefill
+    (1, 8192, 8192, 128, 128): "gemm_decode_kernel<false>",         # decode sweep
+    (8, 8192, 8192, 128, 128): "gemm_decode_kernel<false>",
+    (32, 8192, 8192, 128, 128): "gemm_decode_kernel<false>",
+    (128, 8192, 8192, 128, 128): "gemm_decode_rows_kernel<4, false>",
+    (256, 8192, 8192, 128, 128): "gemm_kernel<128, 128, 2, 2, 4, false, true>",
+}
+
+
+def test_workload_kernels():
+    for shape, name in PRODUCTION_KERNELS.items():
+        assert w4.outlier_gemm_kernel_name(*shape) == name, shape
+
+
+def test_quant_gemm_workspace_reuse(oracle):
+    """One fused-call workspace for M = 256, 64, 200, 256 on the 65B decode
+    shape (split K, decode kernel, split K): the activation codes of a
+    non-split call must not land on the arrival counters of the next split
+    one. Y starts as NaN so that a split that never reduces would show."""
+    d = wl.DECODE_65B
+    X, W, o = wl.draw_workload(d)
+    perm = torch.from_numpy(w4.make_perm(d.K, o)).to(DEV)
+    w = w4.pack_int4_weights(torch.from_numpy(W).to(DEV), perm, d.n_out, d.group)
+    Ms = [256, 64, 200, 256]
+    need = max(w4.quant_gemm_workspace_bytes(M, d.N, d.K, d.n_out, d.group) for M in Ms)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for M in Ms:
+        Xd = torch.from_numpy(np.ascontiguousarray(X[:M])).to(DEV)
+        fresh = w4.quant_gemm(Xd, perm, w)
+        y = torch.full_like(fresh, float("nan"))
+        w4.quant_gemm(Xd, perm, w, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, fresh), f"M={M}: the reused workspace gives a different Y"
+
+
+def test_layer_object_reuses_its_workspace(oracle):
+    """W4A4Linear keeps one workspace across calls of different batch sizes."""
+    d = wl.DECODE_65B
+    X, W, o = wl.draw_workload(d)
+    layer = w4.W4A4Linear(torch.from_numpy(W).to(DEV), o, d.group)
+    for M in [256, 32, 200, 256, 1]:
+        Xd = torch.from_numpy(np.ascontiguousarray(X[:M])).to(DEV)
+        y = layer(Xd)
+        ref = w4.quant_gemm(Xd, layer.perm, layer.weight)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"M={M}"
 
 
 def test_repeatable(oracle):

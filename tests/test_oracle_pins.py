@@ -206,6 +206,22 @@ def test_int_gemm_equals_library_matmul(oracle, group):
     assert np.array_equal(out["acc8"], (qa8.astype(np.float64) @ qw8.T.astype(np.float64)).astype(np.int64))
 
 
+@pytest.mark.parametrize("M,N,K,n_out,group", [(9, 13, 96, 16, 16), (7, 5, 64, 0, 0), (6, 10, 40, 40, 0),
+                                               (12, 8, 200, 8, 48), (3, 4, 130, 2, 0)])
+def test_linear_dense_equals_linear_at(oracle, M, N, K, n_out, group):
+    """The whole-matrix form of the GEMM and dequant agrees with the C oracle's
+    per-position loops bit for bit: accumulators and fp64 y*."""
+    rng = np.random.default_rng(M * N + K + group)
+    X = (rng.standard_normal((M, K)) * rng.choice([1.0, 30.0], K)).astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    O = rng.choice(K, n_out, replace=False)
+    ref = oracle.linear(X, W, O, group)
+    acc4, acc8, ystar = oracle.linear_dense(ref["qa"], ref["qw"], group)
+    assert np.array_equal(acc4, ref["acc4"])
+    assert np.array_equal(acc8, ref["acc8"])
+    assert np.array_equal(ystar, ref["ystar"])
+
+
 def test_all_outliers_is_w8a8(oracle):
     rng = np.random.default_rng(3)
     M, N, K = 4, 5, 32
