@@ -129,6 +129,20 @@ __device__ __forceinline__ void chunk_order() {
     }
 }
 
+// y = acc4 * s4 + acc8 * s8 with the roundings spelled out (one product,
+// then one fused multiply-add, rounded to fp32 before the fp16 conversion),
+// so that both epilogues, and the accumulator export's launch, give the same
+// bits whatever the compiler would contract (left alone, it fuses the last
+// FMA of one epilogue with the fp16 conversion into v_fma_mixlo_f16, one
+// rounding instead of two).
+__device__ __forceinline__ float y_value(int acc4, int acc8, float s4, float s8) {
+#pragma clang fp contract(off)
+    const float p4 = (float)acc4 * s4;
+    float y = __builtin_fmaf((float)acc8, s8, p4);
+    asm volatile("" : "+v"(y));
+    return y;
+}
+
 // fp16 pair, round to nearest even, packed low | high << 16
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
     const _Float16 l = (_Float16)lo, h = (_Float16)hi;
@@ -204,8 +218,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, v16i (&acc)[FM][FN],
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        v[e] = (float)a4[q * 4 + e] * (rs4 * cs4[e]) +
-                               (float)(acc[fm][fn][q * 4 + e] - a4[q * 4 + e]) * (rs8 * cs8[e]);
+                        v[e] = y_value(a4[q * 4 + e], acc[fm][fn][q * 4 + e] - a4[q * 4 + e], rs4 * cs4[e],
+                                       rs8 * cs8[e]);
                     const int n = col0 + nl + q * 8;
                     _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
                     if (m < a.M) {
@@ -289,8 +303,8 @@ __device__ __forceinline__ void epilogue_interior(const GemmArgs &a, v16i (&acc)
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        v[e] = (float)a4[q * 4 + e] * (rs4 * cs4[e]) +
-                               (float)(acc[fm][fn][q * 4 + e] - a4[q * 4 + e]) * (rs8 * cs8[e]);
+                        v[e] = y_value(a4[q * 4 + e], acc[fm][fn][q * 4 + e] - a4[q * 4 + e], rs4 * cs4[e],
+                                       rs8 * cs8[e]);
                     *reinterpret_cast<uint2 *>(stg + li * STG_PITCH + (f2 * 32 + q * 8 + lh * 4) * 2) =
                         uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
                 }

@@ -156,7 +156,7 @@ __device__ __forceinline__ void dequant_group(const v16i (&acc)[C::FM][C::FN],
         for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                yacc[fm][fn][r] += (float)acc[fm][fn][r] * (rs[r] * cs[fn]);
+                yacc[fm][fn][r] = __builtin_fmaf((float)acc[fm][fn][r], rs[r] * cs[fn], yacc[fm][fn][r]);
     }
 }
 
