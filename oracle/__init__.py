@@ -211,6 +211,72 @@ def pack_nibbles(q4, pitch: int) -> np.ndarray:
     return out
 
 
+# ---------------------------------------------------------------------------
+# FP6 (E3M2) packing of INT4 codes for the prefill GEMM
+# ---------------------------------------------------------------------------
+def e3m2_value(code: int) -> float:
+    """Value of a 6-bit FP6 E3M2 code (OCP Microscaling Formats v1.0): sign
+    bit 5, exponent bits 4..2 with bias 3, mantissa bits 1..0; exponent 0 is
+    subnormal, 2^-2 * m/4; no infinities or NaNs."""
+    s, e, m = (code >> 5) & 1, (code >> 2) & 7, code & 3
+    v = 2.0 ** (e - 3) * (1 + m / 4) if e else 2.0 ** -2 * (m / 4)
+    return -v if s else v
+
+
+def e3m2_code(q: int) -> int:
+    """The E3M2 code whose value is the integer q (|q| <= 8 here: every INT4
+    code and its negation are exact in E3M2). Zero is +0 (code 0)."""
+    if q == 0:
+        return 0
+    hits = [c for c in range(64) if e3m2_value(c) == q]
+    if len(hits) != 1:
+        raise ValueError(f"{q} is not exactly representable in E3M2")
+    return hits[0]
+
+
+def pack_u6(q4, pitch4: int):
+    """INT4 codes [rows, K_n] -> the FP6 operand of the prefill GEMM.
+
+    Each 32-channel chunk c of a row (channels 32c .. 32c+31, zero past K_n
+    up to 2 * pitch4 channels) becomes a 192-bit image holding E3M2 code i
+    at bits 6i .. 6i+5 (little-endian); image bytes 0..15 go to the lo plane
+    at bytes 16c .. 16c+15 of the row, bytes 16..23 to the hi plane at bytes
+    8c .. 8c+7. Returns (lo uint8 [rows, pitch4], hi uint8 [rows, pitch4 // 2]).
+    """
+    q4 = np.asarray(q4, np.int8)
+    rows, K_n = q4.shape
+    C = 2 * pitch4 // 32                      # chunks per row
+    table = np.array([e3m2_code(v) for v in range(-8, 8)], np.uint64)
+    codes = np.zeros((rows, C * 32), np.uint64)
+    codes[:, :K_n] = table[q4.astype(np.int64) + 8]
+    codes = codes.reshape(rows, C, 32)
+    words = np.zeros((rows, C, 3), np.uint64)
+    for i in range(32):
+        bit = 6 * i
+        w, off = bit // 64, bit % 64
+        words[:, :, w] |= (codes[:, :, i] << np.uint64(off)) & np.uint64(0xFFFFFFFFFFFFFFFF)
+        if off > 58:                          # the code straddles two 64-bit words
+            words[:, :, w + 1] |= codes[:, :, i] >> np.uint64(64 - off)
+    image = words.astype("<u8").view(np.uint8).reshape(rows, C, 24)
+    lo = np.ascontiguousarray(image[:, :, :16]).reshape(rows, C * 16)
+    hi = np.ascontiguousarray(image[:, :, 16:]).reshape(rows, C * 8)
+    return lo, hi
+
+
+def unpack_u6(lo, hi, K_n: int) -> np.ndarray:
+    """Inverse of pack_u6: the INT4 codes [rows, K_n] (values of the E3M2 codes)."""
+    lo, hi = np.asarray(lo, np.uint8), np.asarray(hi, np.uint8)
+    rows, C = lo.shape[0], lo.shape[1] // 16
+    image = np.concatenate([lo.reshape(rows, C, 16), hi.reshape(rows, C, 8)], axis=2)
+    out = np.zeros((rows, C * 32), np.int8)
+    for r in range(rows):
+        for c in range(C):
+            bits = int.from_bytes(image[r, c].tobytes(), "little")
+            for i in range(32):
+                out[r, 32 * c + i] = int(e3m2_value((bits >> (6 * i)) & 63))
+    return out[:, :K_n]
+
+
 def linear_at(qa, qw, group: int, m_idx, n_idx):
     """Integer GEMM + fp64 dequant at output pairs (m_idx[p], n_idx[p]).
 

@@ -369,3 +369,61 @@ def test_fp64_to_fp16_rounding_is_nearest_even(oracle):
     assert np.array_equal(oracle.to_fp16(np.nextafter(mid, np.inf)),
                           np.nextafter(h, np.float16(np.inf)))
     assert np.array_equal(oracle.to_fp16(np.nextafter(mid, -np.inf)), h)
+
+
+# ---------------------------------------------------------------------------
+# FP6 (E3M2) packing of INT4 codes for the prefill GEMM
+# ---------------------------------------------------------------------------
+E3M2 = os.path.join(os.path.dirname(__file__), "golden", "e3m2_int4.json")
+
+
+def test_e3m2_codes_match_hand_derived(oracle):
+    want = json.load(open(E3M2))["codes"]
+    for q, code in want.items():
+        assert oracle.e3m2_code(int(q)) == code, q
+        assert oracle.e3m2_value(code) == int(q)
+
+
+def test_e3m2_value_closed_forms(oracle):
+    assert oracle.e3m2_value(0b011111) == 28.0          # the largest finite value: 2^4 * 1.75
+    assert oracle.e3m2_value(0b011100) == 16.0
+    assert oracle.e3m2_value(0b000001) == 1 / 16        # the smallest subnormal
+    assert oracle.e3m2_value(0b000100) == 0.25          # the smallest normal
+    assert oracle.e3m2_value(0b100000) == 0.0           # -0
+    vals = sorted(oracle.e3m2_value(c) for c in range(32))
+    assert len(set(vals)) == 32 and vals[0] == 0.0      # 32 distinct non-negative values
+
+
+def test_pack_u6_bit_positions(oracle):
+    """Code i of chunk c sits at bits 6i of the chunk's 192-bit image, whose
+    bytes 0..15 are the lo plane's bytes 16c.. and bytes 16..23 the hi
+    plane's bytes 8c..; channels past K_n are code 0."""
+    rng = np.random.default_rng(7)
+    q = rng.integers(-8, 8, (3, 200), dtype=np.int8)
+    pitch4 = 128                                        # 256 channels: 8 chunks
+    lo, hi = oracle.pack_u6(q, pitch4)
+    assert lo.shape == (3, 128) and hi.shape == (3, 64)
+    for r in range(3):
+        for c in range(8):
+            img = int.from_bytes(bytes(lo[r, 16 * c:16 * c + 16]) + bytes(hi[r, 8 * c:8 * c + 8]), "little")
+            for i in range(32):
+                j = 32 * c + i
+                want = oracle.e3m2_code(int(q[r, j])) if j < 200 else 0
+                assert (img >> (6 * i)) & 63 == want
+
+
+def test_pack_u6_round_trip(oracle):
+    rng = np.random.default_rng(8)
+    q = rng.integers(-8, 8, (4, 100), dtype=np.int8)
+    lo, hi = oracle.pack_u6(q, 64)
+    assert np.array_equal(oracle.unpack_u6(lo, hi, 100), q)
+
+
+def test_pack_u6_known_bytes(oracle):
+    """One chunk by hand: q = [1, -1, 7, -8, 0, ...]: codes 12, 44, 23, 56 at
+    bits 0, 6, 12, 18 -> 12 | 44 << 6 | 23 << 12 | 56 << 18 = 0xE17B0C."""
+    q = np.zeros((1, 32), np.int8)
+    q[0, :4] = [1, -1, 7, -8]
+    lo, hi = oracle.pack_u6(q, 64)
+    assert lo[0, :4].tolist() == [0x0C, 0x7B, 0xE1, 0x00]
+    assert not lo[0, 4:].any() and not hi.any()
