@@ -49,6 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5033.2      # 256 CU x 2.4 GHz x 8192 dense int8 ops / clk / CU
+PEAK_FP6_TOPS = 10066.3      # 256 CU x 2.4 GHz x 16384 dense fp6 (f8f6f4) ops / clk / CU
 PEAK_HBM_GBS = 8000.0        # HBM3E
 ROTATE_BYTES = 512 << 20
 EVENT_EVERY = 8              # timed steps per HIP event pair around the GEMM (short steps)
@@ -462,6 +463,10 @@ def main():
                     help="instead of the W4A4 layer, time the W4A8 layer (INT8 producer + W4A8 GEMM)")
     ap.add_argument("--kv", default=None, choices=sorted(KV_WORKLOADS),
                     help="instead of the layer, time the low-bit KV cache (quantize + gather)")
+    ap.add_argument("--path", default="auto", choices=("auto", "fp6", "i8"),
+                    help="prefill GEMM path: fp6 (INT4 codes as FP6 E3M2 on the FP6 matrix cores) or i8 "
+                         "(widened nibbles on the i8 matrix cores); auto takes fp6 wherever it applies "
+                         "and no RMSNorm is fused")
     ap.add_argument("--norm", action="store_true",
                     help="producer fused with the preceding RMSNorm (eps 1e-6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -516,11 +521,24 @@ def main():
     norm = None
     if args.norm:
         norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
-    plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq), norm=norm) for _ in range(n_sets)]
+    fp6_fits = w4.outlier_gemm_fp6_kernel_name(M, w.N, w.K, w.n_out, w.group) is not None and M > 128
+    if args.path == "fp6" and (not fp6_fits or args.norm):
+        raise SystemExit("the FP6 path takes per-row scales (group 0), over 128 rows, no fused RMSNorm")
+    use_fp6 = args.path == "fp6" or (args.path == "auto" and fp6_fits and not args.norm)
+    if use_fp6:
+        wf6 = w4.to_fp6(wq)
+
+        def clone_fp6(op):
+            return w4.Fp6Operand(*[None if t is None else t.clone() for t in op[:4]], *op[4:])
+        plans = [w4.Fp6LayerPlan(Xd.clone(), perm, clone_fp6(wf6)) for _ in range(n_sets)]
+    else:
+        plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq), norm=norm) for _ in range(n_sets)]
     # Small decode batches run the layer as one launch (the quantizer, and the
     # RMSNorm with --norm, inside the GEMM's workgroups); every other shape as
-    # producer + GEMM.
-    one_launch = w4.quant_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group) == "decode_fused_kernel" and \
+    # producer + GEMM (on the FP6 path: producer + repack of the activation
+    # codes + FP6 GEMM).
+    one_launch = not use_fp6 and \
+        w4.quant_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group) == "decode_fused_kernel" and \
         (not args.norm or M == 1)
 
     for i in range(args.warmup):
@@ -598,16 +616,27 @@ def main():
                 "frac": ach / PEAK_HBM_GBS}
     else:
         ach = ops / (gemm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                "frac": ach / PEAK_INT8_TOPS}
-    roof["kernel"] = (w4.quant_gemm_kernel_name if one_launch else w4.outlier_gemm_kernel_name)(
-        M, w.N, w.K, w.n_out, w.group)
+        # a contraction's peak is that of its own operand type: on the FP6 path
+        # the INT4 head runs at the FP6 rate and the INT8 tail at the i8 rate,
+        # so the peak is the ops-weighted harmonic combination of the two
+        peak = PEAK_INT8_TOPS
+        if use_fp6:
+            head, tail = 2.0 * M * w.N * w.K_n, 2.0 * M * w.N * w.n_out
+            peak = ops / (head / PEAK_FP6_TOPS + tail / PEAK_INT8_TOPS)
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TOP/s", "frac": ach / peak}
+    if use_fp6:
+        roof["kernel"] = w4.outlier_gemm_fp6_kernel_name(M, w.N, w.K, w.n_out, w.group)
+    else:
+        roof["kernel"] = (w4.quant_gemm_kernel_name if one_launch else w4.outlier_gemm_kernel_name)(
+            M, w.N, w.K, w.n_out, w.group)
     roof["traffic"] = traffic_record(w.name, M)
 
     # the result is checked: the fused call against producer + GEMM (the same
     # bits whether the fused call takes one launch or two)
     yf = torch.empty_like(plans[0].out)
-    if norm is None:
+    if use_fp6:
+        w4.quant_gemm_fp6(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
+    elif norm is None:
         w4.quant_gemm(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
     else:
         w4.rmsnorm_quant_gemm(plans[0]._keep[0], norm[0], norm[1], perm, plans[0]._keep[2], out=yf)
@@ -628,15 +657,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "int4 as fp6 e3m2 (exact) + int8 tail" if use_fp6 else "int4 widened to int8 + int8 tail",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": w.N, "K": w.K, "n_out": w.n_out,
-                   "group": w.group, "buffer_sets": n_sets,
+                   "group": w.group, "buffer_sets": n_sets, "gemm_path": "fp6" if use_fp6 else "i8",
                    "producer": ("rmsnorm_" if args.norm else "") + ("in_gemm" if one_launch else
                                                                      ("fused" if args.norm else "plain"))},
         "roofline": roof,
         "kernels": {
             "producer_us": prod_ms * 1e3 if prod_ms else None,
+            "producer_includes_u6_repack": bool(use_fp6),
             "producer_GBps": prod_bytes / (prod_ms * 1e-3) / 1e9 if prod_ms else None,
             "producer_hbm_frac": prod_bytes / (prod_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if prod_ms else None,
             "gemm_us": gemm_ms * 1e3,

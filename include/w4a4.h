@@ -237,6 +237,78 @@ w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamm
                                     int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
                                     void *workspace, size_t workspace_bytes, w4a4_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * FP6 prefill path. The layer's INT4 x INT4 sums (Atom summary page, Summary
+ * paragraph 2 and Key points item 5) formed on CDNA4's FP6 matrix
+ * instruction: every INT4 code q is held as the FP6 E3M2 value q (sign bit 5,
+ * exponent bits 4..2 with bias 3, mantissa bits 1..0, as the OCP Microscaling
+ * Formats v1.0 define E3M2; exact for |q| <= 8), products and partial sums
+ * are integers below 2^24, so the fp32 accumulators hold the exact integer
+ * sums: the results are those of w4a4_outlier_gemm, with the same int32
+ * accumulators. The INT8 outlier tail is unchanged.
+ *
+ * u6 operand of `rows` rows (K_n head channels): rows in blocks of 32
+ * (rows past the last are code 0) and channels in tiles of 64 (T = pitch4 /
+ * 32 tiles, code 0 past K_n); the block of row block b and tile t is 1536
+ * bytes at offset (b * T + t) * 1536. Each row's two 32-channel chunks h = 0,
+ * 1 of the tile are 192-bit images holding code i of the chunk at bits 6i ..
+ * 6i+5 (little-endian); image bytes 0..15 of row r's chunk h sit at 512 h +
+ * 16 r of the block and image bytes 16..23 at 1024 + 256 h + 8 r (the layout
+ * the GEMM's LDS reads want, so whole blocks are copied).
+ * --------------------------------------------------------------------------- */
+
+/* Bytes of a u6 operand: ceil(rows / 32) * (pitch4 / 32) * 1536 (0 when rows
+ * or K_n is 0; -1 for negative sizes). */
+int64_t w4a4_u6_bytes(int32_t rows, int32_t K_n);
+
+/* Convert packed INT4 nibbles Q4 device uint8 [rows, pitch4] (the layout of
+ * Aq4 / Wq4 above) to a u6 operand U6 device uint8 [w4a4_u6_bytes(rows,
+ * K_n)]. Weights are converted once, offline; the fused FP6 call converts the
+ * activation codes itself. Both pointers 16-byte aligned (ALIGNMENT). */
+w4a4_status w4a4_repack_u6(const void *Q4, int32_t rows, int32_t K_n, void *U6, w4a4_stream stream);
+
+/* Name of the kernel w4a4_outlier_gemm_fp6 launches for this shape (as a
+ * kernel trace prints it), or NULL for a shape it rejects. */
+const char *w4a4_outlier_gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                              int32_t group);
+
+/* The mixed-precision GEMM with u6 INT4 operands (Au6 for the M activation
+ * rows, Wu6 for the N weight rows); the INT8 tails and the scales as for
+ * w4a4_outlier_gemm, and the same Y definition. Constraints: group 0 (one
+ * INT4 scale per row), K_n > 0, at most 256 outlier channels
+ * (UNSUPPORTED otherwise), plus those of w4a4_outlier_gemm. No workspace. */
+w4a4_status w4a4_outlier_gemm_fp6(const void *Au6, const void *Aq8, const float *sa4,
+                                  const float *sa8, const void *Wu6, const void *Wq8,
+                                  const float *sw4, const float *sw8, int32_t M, int32_t N,
+                                  int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
+                                  w4a4_stream stream);
+
+/* The same call with the accumulator export (test path): the same kernel and
+ * main loop, the same Y, and the exact integer sums acc4 device int32 [1, M,
+ * N] and acc8 device int32 [M, N] (NULL allowed when n_out == 0). */
+w4a4_status w4a4_outlier_gemm_fp6_i32(const void *Au6, const void *Aq8, const float *sa4,
+                                      const float *sa8, const void *Wu6, const void *Wq8,
+                                      const float *sw4, const float *sw8, int32_t M, int32_t N,
+                                      int32_t K, int32_t n_out, int32_t group, void *Y,
+                                      int64_t ldy, int32_t *acc4, int32_t *acc8,
+                                      w4a4_stream stream);
+
+/* Workspace bytes of w4a4_quant_gemm_fp6 (no contents required on entry). */
+size_t w4a4_quant_gemm_fp6_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out,
+                                           int32_t group);
+
+/* The fused prefill layer on the FP6 path (Atom summary page, Interesting
+ * ideas I2): w4a4_quant_reorder_act on X, the conversion of its INT4 codes to
+ * a u6 operand, and w4a4_outlier_gemm_fp6 with the pre-converted weights Wu6
+ * (w4a4_repack_u6 of Wq4), all on `stream`, with the caller's workspace. The
+ * codes, scales and integer sums are those of w4a4_quant_gemm. Constraints of
+ * w4a4_outlier_gemm_fp6. */
+w4a4_status w4a4_quant_gemm_fp6(const void *X, int64_t ldx, const int32_t *perm, const void *Wu6,
+                                const void *Wq8, const float *sw4, const float *sw8, int32_t M,
+                                int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                                int64_t ldy, void *workspace, size_t workspace_bytes,
+                                w4a4_stream stream);
+
 /* W4A8 GEMM (the QQQ abstract on the "smoothquant" tag page: 4-bit weights with 8-bit activations, a
  * per-channel and a per-group GEMM), without outlier channels:
  *   Y[m, n] = fp16( sa8[m] * sum_t sw4[n, t] * acc_t[m, n] ),

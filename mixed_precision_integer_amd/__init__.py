@@ -38,7 +38,10 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_quant_gemm_workspace_bytes", "w4a4_quant_gemm_kernel_name", "w4a4_quant_gemm",
             "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm",
             "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers",
-            "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32", "w4a4_kv_quant", "w4a4_kv_dequant")
+            "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32", "w4a4_kv_quant", "w4a4_kv_dequant",
+            "w4a4_u6_bytes", "w4a4_repack_u6", "w4a4_outlier_gemm_fp6_kernel_name",
+            "w4a4_outlier_gemm_fp6", "w4a4_outlier_gemm_fp6_i32", "w4a4_quant_gemm_fp6_workspace_bytes",
+            "w4a4_quant_gemm_fp6")
 
 
 class W4A4Error(RuntimeError):
@@ -107,6 +110,21 @@ def lib():
     L.w4a4_kv_quant.restype = ctypes.c_int
     L.w4a4_kv_dequant.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, vp, i64, vp]
     L.w4a4_kv_dequant.restype = ctypes.c_int
+    L.w4a4_u6_bytes.argtypes = [i32, i32]
+    L.w4a4_u6_bytes.restype = i64
+    L.w4a4_repack_u6.argtypes = [vp, i32, i32, vp, vp]
+    L.w4a4_repack_u6.restype = ctypes.c_int
+    L.w4a4_outlier_gemm_fp6_kernel_name.argtypes = [i32, i32, i32, i32, i32]
+    L.w4a4_outlier_gemm_fp6_kernel_name.restype = ctypes.c_char_p
+    L.w4a4_outlier_gemm_fp6.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64, vp]
+    L.w4a4_outlier_gemm_fp6.restype = ctypes.c_int
+    L.w4a4_outlier_gemm_fp6_i32.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64,
+                                            vp, vp, vp]
+    L.w4a4_outlier_gemm_fp6_i32.restype = ctypes.c_int
+    L.w4a4_quant_gemm_fp6_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.w4a4_quant_gemm_fp6_workspace_bytes.restype = sz
+    L.w4a4_quant_gemm_fp6.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64, vp, sz, vp]
+    L.w4a4_quant_gemm_fp6.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -398,6 +416,115 @@ def select_outliers(Xcal, n_out: int, workspace=None, want_absmax: bool = False)
     return (idx, perm, amax) if want_absmax else (idx, perm)
 
 
+# ---------------------------------------------------------------------------
+# FP6 prefill path: INT4 codes held as FP6 E3M2 values ("u6" operands)
+# ---------------------------------------------------------------------------
+def u6_bytes(rows: int, K_n: int) -> int:
+    return int(lib().w4a4_u6_bytes(rows, K_n))
+
+
+def repack_u6(q4, K_n: int):
+    """Packed INT4 nibbles [rows, pitch4] -> the u6 operand of the FP6 GEMM
+    (uint8 [u6_bytes]: 32-row x 64-channel blocks of 1536 bytes)."""
+    torch = _torch()
+    _check(q4, torch.uint8, "q4", 2)
+    rows = q4.shape[0]
+    out = torch.empty(max(u6_bytes(rows, K_n), 1), dtype=torch.uint8, device=q4.device)
+    _ok(lib().w4a4_repack_u6(_nz(q4), rows, K_n, out.data_ptr(), _stream()), "w4a4_repack_u6")
+    return out
+
+
+class Fp6Operand(NamedTuple):
+    """An operand of the FP6 GEMM: the INT4 head as u6 bytes, the INT8 tail
+    and the scales as in QuantizedOperand."""
+    u6: object
+    q8: object
+    s4: object
+    s8: object
+    K: int
+    n_out: int
+    group: int
+
+
+def to_fp6(op: QuantizedOperand) -> Fp6Operand:
+    """Repack a quantized operand's INT4 head for the FP6 GEMM."""
+    return Fp6Operand(repack_u6(op.q4, op.K - op.n_out), op.q8, op.s4, op.s8, op.K, op.n_out, op.group)
+
+
+def pack_weights_fp6(W, perm, n_out: int, group: int) -> Fp6Operand:
+    """Offline weight preparation for the FP6 prefill path."""
+    return to_fp6(pack_int4_weights(W, perm, n_out, group))
+
+
+def outlier_gemm_fp6_kernel_name(M: int, N: int, K: int, n_out: int, group: int):
+    r = lib().w4a4_outlier_gemm_fp6_kernel_name(M, N, K, n_out, group)
+    return None if r is None else r.decode()
+
+
+def _fp6_args(a: Fp6Operand, w: Fp6Operand, out):
+    if (a.K, a.n_out, a.group) != (w.K, w.n_out, w.group):
+        raise ValueError("activation and weight quantization parameters differ")
+    M, N = a.s8.shape[0], w.s8.shape[0]
+    return (_nz(a.u6), _nz(a.q8), _nz(a.s4), _nz(a.s8), _nz(w.u6), _nz(w.q8), _nz(w.s4), _nz(w.s8), M, N, a.K,
+            a.n_out, a.group, out.data_ptr(), out.stride(0) if M else N)
+
+
+def outlier_gemm_fp6(a: Fp6Operand, w: Fp6Operand, out=None):
+    """Y[M, N] fp16 from FP6-held INT4 operands (the same integer sums as
+    w4a4_outlier_gemm)."""
+    torch = _torch()
+    M, N = a.s8.shape[0], w.s8.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.s8.device)
+    _check(out, torch.float16, "out", 2)
+    _ok(lib().w4a4_outlier_gemm_fp6(*_fp6_args(a, w, out), _stream()), "w4a4_outlier_gemm_fp6")
+    return out
+
+
+def outlier_gemm_fp6_i32(a: Fp6Operand, w: Fp6Operand, out=None):
+    """The FP6 GEMM with its accumulator export: (acc4 int32 [G, M, N], acc8
+    int32 [M, N], Y)."""
+    torch = _torch()
+    M, N = a.s8.shape[0], w.s8.shape[0]
+    G = num_groups(a.K - a.n_out, a.group)
+    dev = a.s8.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    acc4 = torch.zeros((G, M, N), dtype=torch.int32, device=dev)
+    acc8 = torch.zeros((M, N), dtype=torch.int32, device=dev)
+    _ok(lib().w4a4_outlier_gemm_fp6_i32(*_fp6_args(a, w, out), _nz(acc4), _nz(acc8) if a.n_out else None,
+                                        _stream()), "w4a4_outlier_gemm_fp6_i32")
+    return acc4, acc8, out
+
+
+def quant_gemm_fp6_workspace_bytes(M: int, N: int, K: int, n_out: int, group: int) -> int:
+    return int(lib().w4a4_quant_gemm_fp6_workspace_bytes(M, N, K, n_out, group))
+
+
+def quant_gemm_fp6(X, perm, w: Fp6Operand, out=None, workspace=None):
+    """The fused prefill layer on the FP6 path: producer, repack of the
+    activation codes, FP6 GEMM, on one stream."""
+    torch = _torch()
+    _check(X, torch.float16, "X", 2)
+    _check(perm, torch.int32, "perm", 1)
+    M, K = X.shape
+    N = w.s8.shape[0]
+    if K != w.K:
+        raise ValueError("X and weights disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(out, torch.float16, "out", 2)
+    need = quant_gemm_fp6_workspace_bytes(M, N, K, w.n_out, w.group)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+    _check(workspace, torch.uint8, "workspace", 1)
+    _ok(lib().w4a4_quant_gemm_fp6(X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.u6), _nz(w.q8),
+                                  _nz(w.s4), _nz(w.s8), M, N, K, w.n_out, w.group, out.data_ptr(),
+                                  out.stride(0) if M else N, workspace.data_ptr(), workspace.numel(), _stream()),
+        "w4a4_quant_gemm_fp6")
+    return out
+
+
 class W4A8Operand(NamedTuple):
     """W4A8 operand: INT8 activation rows (q [rows, K], s [rows]) or INT4
     weight rows (q [rows, K / 2] packed, s [rows, G])."""
@@ -568,3 +695,55 @@ class LayerPlan:
         if st:
             raise W4A4Error(st, self._fname)
         return self.out
+
+
+class Fp6LayerPlan:
+    """Arguments of one FP6-path layer call, marshalled once (the FP6
+    counterpart of LayerPlan): ``produce()`` runs w4a4_quant_reorder_act and
+    w4a4_repack_u6 into pre-allocated operands, ``gemm()`` runs
+    w4a4_outlier_gemm_fp6, ``fused()`` is w4a4_quant_gemm_fp6 (the same
+    launches)."""
+
+    def __init__(self, X, perm, w: Fp6Operand, out=None):
+        torch = _torch()
+        _check(X, torch.float16, "X", 2)
+        _check(perm, torch.int32, "perm", 1)
+        M, K = X.shape
+        N = w.s8.shape[0]
+        K_n = K - w.n_out
+        self.out = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
+        self.a = alloc_operand(M, K, w.n_out, w.group, X.device)
+        self.u6 = torch.empty(max(u6_bytes(M, K_n), 1), dtype=torch.uint8, device=X.device)
+        need = quant_gemm_fp6_workspace_bytes(M, N, K, w.n_out, w.group)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+        self._keep = (X, perm, w)
+        L = lib()
+        st = _stream()
+        self._q, self._qa = L.w4a4_quant_reorder_act, _quant_args(X, perm, self.a)
+        self._r, self._ra = L.w4a4_repack_u6, (_nz(self.a.q4), M, K_n, self.u6.data_ptr(), st)
+        af = Fp6Operand(self.u6, self.a.q8, self.a.s4, self.a.s8, K, w.n_out, w.group)
+        self._g, self._ga = L.w4a4_outlier_gemm_fp6, (*_fp6_args(af, w, self.out), st)
+        self._f = L.w4a4_quant_gemm_fp6
+        self._fa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.u6), _nz(w.q8), _nz(w.s4),
+                    _nz(w.s8), M, N, K, w.n_out, w.group, self.out.data_ptr(), self.out.stride(0) if M else N,
+                    self.ws.data_ptr(), self.ws.numel(), st)
+
+    def produce(self):
+        st = self._q(*self._qa)
+        if st:
+            raise W4A4Error(st, "w4a4_quant_reorder_act")
+        st = self._r(*self._ra)
+        if st:
+            raise W4A4Error(st, "w4a4_repack_u6")
+
+    def gemm(self):
+        st = self._g(*self._ga)
+        if st:
+            raise W4A4Error(st, "w4a4_outlier_gemm_fp6")
+
+    def fused(self):
+        st = self._f(*self._fa)
+        if st:
+            raise W4A4Error(st, "w4a4_quant_gemm_fp6")
+        return self.out
+

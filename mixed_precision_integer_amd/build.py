@@ -8,8 +8,9 @@ Packed-FP32 instructions are disabled for all device code (-packed-fp32-ops);
 hipcc's host pass warns that it does not know that target feature, which is
 harmless. The 64 x 64 and 128 x 128 GEMM keeps MFMA accumulators in
 architectural VGPRs (-amdgpu-mfma-vgpr-form), since its fp32 epilogue reads
-them every scale group; the 256 x 256 GEMM holds 256 accumulator registers per
-lane, which only fit as AGPRs, and is built without that option.
+them every scale group; the 256 x 256 GEMMs (i8 and FP6) hold 256 accumulator
+registers per lane, which only fit as AGPRs, and are built without that option.
+Sources are compiled in parallel (at most MAX_JOBS, else the CPU count).
 """
 from __future__ import annotations
 
@@ -30,7 +31,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Wno-unused-command-line-argument"]
 # per-source extra flags (default: accumulators in architectural VGPRs)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"gemm_big.hip": []}
+EXTRA = {"gemm_big.hip": [], "gemm_fp6.hip": []}
 
 
 def hipcc() -> str:

@@ -11,6 +11,7 @@
 #include "quant_internal.h"
 #include "w4a4_internal.h"
 #include "w4a8_internal.h"
+#include "gemm_fp6_internal.h"
 
 namespace {
 
@@ -603,6 +604,171 @@ w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamm
         return st;
     return quant_gemm(X, ldx, perm, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, workspace,
                       workspace_bytes, stream, NormArgs{gamma, eps, nullptr});
+}
+
+// ---------------------------------------------------------------------------
+// FP6 prefill GEMM
+// ---------------------------------------------------------------------------
+
+int64_t w4a4_u6_bytes(int32_t rows, int32_t K_n) {
+    if (rows < 0 || K_n < 0)
+        return -1;
+    return w4a4::u6_operand_bytes(rows, w4a4_pitch4_bytes(K_n));
+}
+
+w4a4_status w4a4_repack_u6(const void *Q4, int32_t rows, int32_t K_n, void *U6, w4a4_stream stream) {
+    if (rows < 0 || K_n < 0)
+        return W4A4_ERR_INVALID_ARG;
+    const int64_t p4 = w4a4_pitch4_bytes(K_n);
+    if ((int64_t)rows * p4 == 0)
+        return W4A4_OK;
+    if (!Q4 || !U6)
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(Q4, 16) || !aligned(U6, 16))
+        return W4A4_ERR_ALIGNMENT;
+    if (w4a4::launch_repack_u6(static_cast<const uint8_t *>(Q4), rows, p4, static_cast<uint8_t *>(U6),
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+const char *w4a4_outlier_gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
+    if (M <= 0 || N <= 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
+        return nullptr;
+    return w4a4::gemm_fp6_kernel_name(M, N, K - n_out, n_out, group);
+}
+
+}  // extern "C"
+
+static w4a4_status fp6_gemm(const void *Au6, const void *Aq8, const float *sa4, const float *sa8,
+                            const void *Wu6, const void *Wq8, const float *sw4, const float *sw8, int32_t M,
+                            int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
+                            int32_t *acc4, int32_t *acc8, bool export_acc, w4a4_stream stream) {
+    w4a4_status st = gemm_check(Au6, Aq8, Wu6, Wq8, M, N, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    const int32_t K_n = K - n_out;
+    if (ldy < N)
+        return W4A4_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if (!w4a4::gemm_fp6_fits(M, N, K_n, n_out, group))
+        return W4A4_ERR_UNSUPPORTED;
+    if (!Y || !sa4 || !sw4 || (n_out > 0 && (!sa8 || !sw8)))
+        return W4A4_ERR_INVALID_ARG;
+    if (export_acc && (!acc4 || (n_out > 0 && !acc8)))
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(Y, 2) || !aligned(sa4, 4) || !aligned(sw4, 4) || (sa8 && !aligned(sa8, 4)) ||
+        (sw8 && !aligned(sw8, 4)) || (export_acc && (!aligned(acc4, 4) || (acc8 && !aligned(acc8, 4)))))
+        return W4A4_ERR_ALIGNMENT;
+    const int64_t p4 = w4a4_pitch4_bytes(K_n);
+    // u6 blocks are addressed by 32-bit offsets too
+    if (w4a4_u6_bytes(M > N ? M : N, K_n) >= (int64_t(1) << 32))
+        return W4A4_ERR_UNSUPPORTED;
+    w4a4::Fp6GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.a_u6 = static_cast<const uint8_t *>(Au6);
+    a.w_u6 = static_cast<const uint8_t *>(Wu6);
+    a.a8 = static_cast<const int8_t *>(Aq8);
+    a.w8 = static_cast<const int8_t *>(Wq8);
+    a.sa4 = sa4;
+    a.sa8 = sa8;
+    a.sw4 = sw4;
+    a.sw8 = sw8;
+    a.y = static_cast<_Float16 *>(Y);
+    a.acc4_out = export_acc ? acc4 : nullptr;
+    a.acc8_out = export_acc && n_out > 0 ? acc8 : nullptr;
+    a.M = M;
+    a.N = N;
+    a.K_n = K_n;
+    a.n_out = n_out;
+    a.pitch4 = p4;
+    a.pitch8 = n_out > 0 ? w4a4_pitch8_bytes(n_out) : 0;
+    a.ldy = ldy;
+    if (w4a4::launch_gemm_fp6(a, export_acc, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
+    return W4A4_OK;
+}
+
+extern "C" {
+
+w4a4_status w4a4_outlier_gemm_fp6(const void *Au6, const void *Aq8, const float *sa4, const float *sa8,
+                                  const void *Wu6, const void *Wq8, const float *sw4, const float *sw8,
+                                  int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                                  int64_t ldy, w4a4_stream stream) {
+    return fp6_gemm(Au6, Aq8, sa4, sa8, Wu6, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, nullptr, nullptr,
+                    false, stream);
+}
+
+w4a4_status w4a4_outlier_gemm_fp6_i32(const void *Au6, const void *Aq8, const float *sa4, const float *sa8,
+                                      const void *Wu6, const void *Wq8, const float *sw4, const float *sw8,
+                                      int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                                      int64_t ldy, int32_t *acc4, int32_t *acc8, w4a4_stream stream) {
+    return fp6_gemm(Au6, Aq8, sa4, sa8, Wu6, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, acc4, acc8, true,
+                    stream);
+}
+
+// Workspace of the fused FP6 call: Aq4 (nibbles) | Au6 | Aq8 | sa4 | sa8,
+// each 256-byte aligned; off[5] is the size.
+static void quant_gemm_fp6_layout(int32_t M, int32_t K, int32_t n_out, int32_t group, size_t off[6]) {
+    const int32_t K_n = K - n_out;
+    const int32_t G = w4a4_num_groups(K_n, group);
+    off[0] = 0;
+    off[1] = off[0] + round_up((int64_t)M * w4a4_pitch4_bytes(K_n), 256);
+    off[2] = off[1] + round_up(std::max<int64_t>(w4a4_u6_bytes(M, K_n), 0), 256);
+    off[3] = off[2] + round_up((int64_t)M * w4a4_pitch8_bytes(n_out), 256);
+    off[4] = off[3] + round_up((int64_t)M * (G > 0 ? G : 0) * 4, 256);
+    off[5] = off[4] + round_up((int64_t)M * 4, 256);
+}
+
+size_t w4a4_quant_gemm_fp6_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
+    (void)N;
+    if (M < 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
+        return 0;
+    size_t off[6];
+    quant_gemm_fp6_layout(M, K, n_out, group, off);
+    return off[5];
+}
+
+w4a4_status w4a4_quant_gemm_fp6(const void *X, int64_t ldx, const int32_t *perm, const void *Wu6,
+                                const void *Wq8, const float *sw4, const float *sw8, int32_t M, int32_t N,
+                                int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy, void *workspace,
+                                size_t workspace_bytes, w4a4_stream stream) {
+    if (N < 0)
+        return W4A4_ERR_INVALID_ARG;
+    w4a4_status st = check_shape(M, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    const int32_t K_n = K - n_out;
+    if (ldx < K || ldy < N)
+        return W4A4_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return W4A4_OK;
+    if (!w4a4::gemm_fp6_fits(M, N, K_n, n_out, group) || !dma_offsets_fit(M, N, K_n, n_out))
+        return W4A4_ERR_UNSUPPORTED;
+    if (!X || !perm || !Y || !Wu6 || !sw4 || (n_out > 0 && (!Wq8 || !sw8)))
+        return W4A4_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(perm, 16) || !aligned(Y, 2) || !aligned(Wu6, 16) ||
+        (Wq8 && !aligned(Wq8, 16)) || !aligned(sw4, 4) || (sw8 && !aligned(sw8, 4)) || !aligned(workspace, 256))
+        return W4A4_ERR_ALIGNMENT;
+    const size_t need = w4a4_quant_gemm_fp6_workspace_bytes(M, N, K, n_out, group);
+    if (workspace_bytes < need || !workspace)
+        return W4A4_ERR_WORKSPACE;
+    size_t off[6];
+    quant_gemm_fp6_layout(M, K, n_out, group, off);
+    char *ws = static_cast<char *>(workspace);
+    void *Aq4 = ws + off[0];
+    void *Au6 = ws + off[1];
+    void *Aq8 = n_out > 0 ? ws + off[2] : nullptr;
+    float *sa4 = reinterpret_cast<float *>(ws + off[3]);
+    float *sa8 = reinterpret_cast<float *>(ws + off[4]);
+    st = quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream);
+    if (st != W4A4_OK)
+        return st;
+    st = w4a4_repack_u6(Aq4, M, K_n, Au6, stream);
+    if (st != W4A4_OK)
+        return st;
+    return w4a4_outlier_gemm_fp6(Au6, Aq8, sa4, sa8, Wu6, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, stream);
 }
 
 }  // extern "C"

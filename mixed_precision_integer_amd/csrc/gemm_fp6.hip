@@ -1,0 +1,436 @@
+// Prefill GEMM on the FP6 matrix cores: INT4 x INT4 head with the INT4 codes
+// held as FP6 E3M2 values, exact fp32 accumulation; INT8 x INT8 outlier tail
+// on the i8 matrix cores; fp32 scale epilogue to fp16.
+//
+// Method: Atom summary page (Summary paragraph 2: INT4 main part plus an
+// 8-bit outlier part over reordered channels; Key points item 5: symmetric
+// scales factor out of the integer sums) and the QUIK abstract (hybrid 4-bit
+// layer with higher-precision outliers). The integer sums are those of the
+// i8 kernels; only the matrix instruction that forms them differs.
+//
+// CDNA4 design
+// * CDNA4 has no INT4 matrix instruction, but its FP6 one
+//   (v_mfma_scale_f32_32x32x64_f8f6f4, E3M2 operands) runs at twice the i8
+//   rate, and E3M2 holds every INT4 code exactly (q = +-2^(e-3) (1 + m/4)
+//   for |q| <= 8). Products of two codes are integers below 2^7 and every
+//   partial sum an integer below 2^24 in magnitude (|sum| <= 64 K_n), so the
+//   fp32 accumulator holds the exact integer sum whatever order the matrix
+//   core adds in: the accumulator export converts it to int32 unchanged.
+// * The FP6 operand of a lane is a 192-bit image of 32 codes (code i at bits
+//   6i). Unpacking nibbles into it costs more VALU per MFMA than the FP6
+//   rate leaves, so the operands arrive already in that form, in a "u6"
+//   layout built for this kernel: 32-row x 64-channel blocks of 1536
+//   contiguous bytes, each laid out as LDS wants it (row r's chunk h: image
+//   bytes 0..15 at 512 h + 16 r, bytes 16..23 at 1024 + 256 h + 8 r). A DMA
+//   instruction then moves whole cache lines, and the b128 / b64 fragment
+//   reads of 16 lanes cover 128 contiguous bytes (no bank conflicts).
+//   repack_u6_kernel converts packed nibbles to it (once for weights; per
+//   call for activations).
+// * 256 x 256 output tile per workgroup, four waves of 128 x 128 (4 x 4
+//   blocks of 32 x 32), fp32 accumulators in AGPRs, one wave per SIMD. A
+//   K-tile is 64 channels (one FP6 k-step): eight u6 blocks of each operand,
+//   24 KB per stage; a 6-stage ring, DMA four tiles ahead, one barrier per
+//   tile. Fragments are read from LDS one row of MFMAs ahead of their use.
+// * The INT8 tail (at most 256 channels) is staged into the ring once the
+//   head is done and multiplied block by block on the i8 matrix cores into a
+//   16-register int32 accumulator; y = fp16(acc4 * (sa4 sw4) + acc8 * (sa8
+//   sw8)).
+#include <algorithm>
+
+#include "w4a4.h"
+#include "gemm_common.h"
+#include "gemm_fp6_internal.h"
+
+namespace w4a4 {
+namespace gemm_fp6_impl {
+
+constexpr int64_t kU6Block = 1536;                 // bytes of a 32-row x 64-channel u6 block
+
+using namespace gemm_impl;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// repack: packed two's complement nibbles -> u6 planes
+// ---------------------------------------------------------------------------
+
+// E3M2 magnitude codes of 0..8, six bits each: 0, 1 = 2^0 (e 3), 2 = 2^1,
+// 3 = 2^1 * 1.5, 4 = 2^2, 5 = 2^2 * 1.25, 6 = 2^2 * 1.5, 7 = 2^2 * 1.75,
+// 8 = 2^3; the sign is bit 5.
+constexpr uint64_t kMagCodes = (0ull << 0) | (12ull << 6) | (16ull << 12) | (18ull << 18) | (20ull << 24) |
+                               (21ull << 30) | (22ull << 36) | (23ull << 42) | (24ull << 48);
+
+__device__ __forceinline__ uint32_t e3m2_of_nibble(uint32_t n) {
+    const uint32_t neg = (n >> 3) & 1;
+    const uint32_t mag = neg ? 16u - n : n;                  // |q| of the two's complement nibble
+    return (neg << 5) | (uint32_t)((kMagCodes >> (6 * mag)) & 63);
+}
+
+// One lane per (row, 64-channel tile): 32 nibble bytes in, the two chunk
+// images out. Lanes are ordered row-fastest inside a 32-row block, so the
+// image stores of consecutive lanes are consecutive; rows past the last one
+// of the operand are written as code 0.
+__global__ __launch_bounds__(256) void repack_u6_kernel(const uint8_t *q4, int64_t rows, int64_t pitch4,
+                                                         uint8_t *u6) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int64_t T = pitch4 / 32, RB = (rows + 31) / 32;
+    const int64_t total = RB * T * 32;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t rr = i & 31, bt = i >> 5;            // row inside the block, block index
+        const int64_t b = bt / T, t = bt % T;
+        const int64_t r = b * 32 + rr;
+        unsigned char *blk = u6 + bt * kU6Block;           // block (b, t) is block b * T + t
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+            if (r < rows) {
+                const u32x4 p = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(q4 + r * pitch4 + t * 32 + h * 16));
+                const uint32_t pw[4] = {p[0], p[1], p[2], p[3]};
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const uint32_t code = e3m2_of_nibble((pw[j >> 3] >> (4 * (j & 7))) & 15);
+                    const int bit = 6 * j, d = bit >> 5, off = bit & 31;
+                    w[d] |= code << off;
+                    if (off > 26)
+                        w[d + 1] |= code >> (32 - off);
+                }
+            }
+            *reinterpret_cast<uint4 *>(blk + 512 * h + 16 * rr) = uint4{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<uint2 *>(blk + 1024 + 256 * h + 8 * rr) = uint2{w[4], w[5]};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 256 x 256 FP6 GEMM for one scale per row (group 0)
+// ---------------------------------------------------------------------------
+constexpr int BM = 256, BN = 256, WTM = 128, WTN = 128, FM = 4, FN = 4;
+constexpr int STAGES = 6;                          // ring depth
+constexpr int BLK = (int)kU6Block;                 // one 32-row block of a K-tile (64 channels)
+constexpr int A_OFF = 0, B_OFF = (BM / 32) * BLK;  // eight blocks of each operand per stage
+constexpr int STAGE = B_OFF + (BN / 32) * BLK;     // 24 KB
+constexpr int DPO = (BM / 32) * BLK / 16 / kThreads;   // DMA instructions per operand per K-tile
+constexpr int D = 2 * DPO;                         // DMA instructions per K-tile per lane
+constexpr int MAX_TAIL_TILES = 4;                  // INT8 tail <= 256 channels
+constexpr int TAIL_TILE = (BM + BN) * kTileBytes;  // 32 KB: A rows, then B rows (swizzled 64-byte rows)
+constexpr int SCALES = STAGES * STAGE;             // sa4, sa8, sw4, sw8 of the tile
+constexpr int LDS_BYTES = SCALES + 4 * BM * 4;
+static_assert(MAX_TAIL_TILES * TAIL_TILE <= STAGES * STAGE, "the tail fits in the ring");
+static_assert(STAGE == 24576 && DPO == 3, "stage layout");
+static_assert((STAGES - 1) * D <= 63, "vmcnt range");
+
+// One FP6 operand: 32 codes per lane in registers 0..5 (lo chunk, then the
+// hi bytes); the instruction reads only those six for FP6. Kept in VGPRs:
+// the AGPRs hold the sums.
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v8i load_operand(const unsigned char *lo, const unsigned char *hi) {
+    v4i l = *reinterpret_cast<const v4i *>(lo);
+    v2i h = *reinterpret_cast<const v2i *>(hi);
+    asm("" : "+v"(l));
+    asm("" : "+v"(h));
+    v8i v;
+    v[0] = l[0];
+    v[1] = l[1];
+    v[2] = l[2];
+    v[3] = l[3];
+    v[4] = h[0];
+    v[5] = h[1];
+    return v;                                      // registers 6 and 7 left undefined
+}
+
+// One row of blocks of a K-tile: block (fm, fn) takes the weight fragment as
+// the first operand, so lane (li, lh) holds token row li and the columns
+// 8 (r / 4) + 4 lh + r % 4 of the block.
+__device__ __forceinline__ void mma_row(v16f (&acc)[FN], const v8i &x, const v8i (&w)[FN]) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        acc[fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[fn], x, acc[fn], 3, 3, 0, 127, 0, 127);
+}
+
+// y = acc4 * s4 + acc8 * s8: one product, one fused multiply-add, rounded to
+// fp32 before the fp16 conversion (the same bits in every launch).
+__device__ __forceinline__ float y_value(float acc4, int acc8, float s4, float s8) {
+#pragma clang fp contract(off)
+    const float p4 = acc4 * s4;
+    float y = __builtin_fmaf((float)acc8, s8, p4);
+    asm volatile("" : "+v"(y));
+    return y;
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    const _Float16 l = (_Float16)lo, h = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+template <bool EXPORT>
+__global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
+    __shared__ __align__(16) unsigned char lds[LDS_BYTES];
+    float *sS = reinterpret_cast<float *>(lds + SCALES);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int li = lane & 31, lh = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, true, tm, tn);
+    const int row0 = tm * BM, col0 = tn * BN;
+
+    // ---- DMA sources of this lane (fixed for the K loop) -------------------------
+    // A stage holds the eight 32-row blocks of each operand for one K-tile,
+    // copied whole: unit q = j * 256 + tid of an operand is bytes 16 (q % 96)
+    // of block q / 96 (clamped to the last block of the operand).
+    const int RBA = (a.M + 31) / 32, RBB = (a.N + 31) / 32;
+    const int T = (int)(a.pitch4 / 32);            // head K-tiles of 64 channels
+    const int T8 = (int)(a.pitch8 / kTileBytes);   // tail K-tiles of 64 INT8 channels
+    uint32_t oa[DPO], ob[DPO];
+#pragma unroll
+    for (int j = 0; j < DPO; ++j) {
+        const int q = j * kThreads + tid, i = q / 96, u = q % 96;
+        oa[j] = (uint32_t)min(row0 / 32 + i, RBA - 1) * (uint32_t)(T * BLK) + 16 * u;
+        ob[j] = (uint32_t)min(col0 / 32 + i, RBB - 1) * (uint32_t)(T * BLK) + 16 * u;
+    }
+
+    // ring tile tt (past the last head tile: a reload of the last one into a
+    // stage nothing reads again, so every iteration issues the same DMA)
+    auto issue = [&](int tt) {
+        const int t = min(tt, T - 1);
+        const uint32_t st = lds_addr(lds) + (tt % STAGES) * STAGE + wave_u * 1024;
+        const uint8_t *A = a.a_u6 + (int64_t)t * BLK, *B = a.w_u6 + (int64_t)t * BLK;
+#pragma unroll
+        for (int j = 0; j < DPO; ++j)
+            dma16(A, oa[j], st + A_OFF + j * 4096);
+#pragma unroll
+        for (int j = 0; j < DPO; ++j)
+            dma16(B, ob[j], st + B_OFF + j * 4096);
+    };
+
+    // ---- scales of the tile, ahead of every K-tile (the first wait covers them)
+    {
+        const uint32_t ss = lds_addr(sS) + wave_u * 256;
+        const int64_t mr = min(row0 + tid, a.M - 1), nc = min(col0 + tid, a.N - 1);
+        dma4(a.sa4 + mr, ss);
+        dma4(a.sw4 + nc, ss + 2 * BM * 4);
+        if (T8 > 0) {
+            dma4(a.sa8 + mr, ss + BM * 4);
+            dma4(a.sw8 + nc, ss + 3 * BM * 4);
+        }
+    }
+
+    v16f acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[fm][fn][r] = 0.0f;
+
+    // Per-lane LDS offsets of this wave's fragments inside a stage: lane
+    // (li, lh) of row block i reads chunk lh of row li of block 4 wm + i (A)
+    // or 4 wn + i (B); a row block adds BLK bytes (an immediate offset).
+    const uint32_t la = A_OFF + (wm * 4) * BLK, lb = B_OFF + (wn * 4) * BLK;
+    const uint32_t llo = 512 * lh + 16 * li, lhi = 1024 + 256 * lh + 8 * li;
+    auto a_frag = [&](uint32_t st, int i) {
+        return load_operand(lds + st + la + llo + i * BLK, lds + st + la + lhi + i * BLK);
+    };
+    auto b_frag = [&](uint32_t st, int i) {
+        return load_operand(lds + st + lb + llo + i * BLK, lds + st + lb + lhi + i * BLK);
+    };
+
+    // ---- head -------------------------------------------------------------------------
+    // Software pipeline per wave: at the top of tile t the registers hold the
+    // four weight fragments of tile t and the first activation row; during
+    // row fm of tile t the next activation row (tile t's row fm + 1, or tile
+    // t + 1's first) and weight fragment fm of tile t + 1 are read, so every
+    // read has a row of MFMAs (128 cycles) to arrive. DMA runs four tiles
+    // ahead: at tile t, after the barrier that has every wave done with tile
+    // t - 1, tile t + 5 goes into tile t - 1's stage.
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+        issue(p);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * D));     // tile 0 (and the scales)
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    v8i wc[FN], wn_[FN], x0, x1;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+        wc[i] = b_frag(0, i);
+    x0 = a_frag(0, 0);
+
+    auto tile = [&](int t, v8i (&wcur)[FN], v8i (&wnext)[FN]) {
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 3) * D));   // tile t + 1 has landed
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));               // tile t - 1's reads are back
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        issue(t + STAGES - 1);                                      // into tile t - 1's stage
+        const uint32_t sc = (uint32_t)((t % STAGES) * STAGE), sn = (uint32_t)(((t + 1) % STAGES) * STAGE);
+        x1 = a_frag(sc, 1);
+        wnext[0] = b_frag(sn, 0);
+        mma_row(acc[0], x0, wcur);
+        x0 = a_frag(sc, 2);
+        wnext[1] = b_frag(sn, 1);
+        mma_row(acc[1], x1, wcur);
+        x1 = a_frag(sc, 3);
+        wnext[2] = b_frag(sn, 2);
+        mma_row(acc[2], x0, wcur);
+        x0 = a_frag(sn, 0);
+        wnext[3] = b_frag(sn, 3);
+        mma_row(acc[3], x1, wcur);
+    };
+    for (int t = 0; t < T; t += 2) {
+        tile(t, wc, wn_);
+        if (t + 1 < T)
+            tile(t + 1, wn_, wc);
+    }
+
+    // ---- the INT8 tail: staged into the ring once every wave is done with it ----------
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    if (T8 > 0) {
+        // tail tile j: A rows at j * TAIL_TILE, B rows after them; 16-byte
+        // chunk c of row r at swz(r, c), lane q of a DMA instruction row q / 4
+#pragma unroll
+        for (int j = 0; j < MAX_TAIL_TILES; ++j) {
+            if (j >= T8)
+                break;                                             // uniform
+            const uint32_t st = lds_addr(lds) + j * TAIL_TILE + wave_u * 1024;
+            const uint8_t *A8 = reinterpret_cast<const uint8_t *>(a.a8) + j * kTileBytes;
+            const uint8_t *B8 = reinterpret_cast<const uint8_t *>(a.w8) + j * kTileBytes;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int q = k * kThreads + tid, r = q >> 2;
+                dma16(A8, (uint32_t)min(row0 + r, a.M - 1) * (uint32_t)a.pitch8 + dma_chunk_offset(q), st + k * 4096);
+                dma16(B8, (uint32_t)min(col0 + r, a.N - 1) * (uint32_t)a.pitch8 + dma_chunk_offset(q),
+                      st + BM * kTileBytes + k * 4096);
+            }
+        }
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+    }
+
+    // ---- epilogue, block by block -----------------------------------------------------
+    const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const bool vec_store = ((reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2)) & 7) == 0;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int nl = wn * WTN + fn * 32 + lh * 4;       // tile-local first column of the lane
+        v4i pb8[MAX_TAIL_TILES][2];
+#pragma unroll
+        for (int j = 0; j < MAX_TAIL_TILES; ++j)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                uint4 p = uint4{0, 0, 0, 0};
+                if (j < T8)
+                    p = *reinterpret_cast<const uint4 *>(lds + j * TAIL_TILE + BM * kTileBytes +
+                                                        swz(wn * WTN + fn * 32 + li, 2 * s + lh));
+                pb8[j][s] = v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w};
+            }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int ml = wm * WTM + fm * 32 + li;
+            const int m = row0 + ml;
+            v16i acc8 = zi;
+#pragma unroll
+            for (int j = 0; j < MAX_TAIL_TILES; ++j) {
+                if (j >= T8)
+                    break;                                 // uniform
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint4 p = *reinterpret_cast<const uint4 *>(lds + j * TAIL_TILE + swz(ml, 2 * s + lh));
+                    acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(pb8[j][s], v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w},
+                                                                 acc8, 0, 0, 0);
+                }
+            }
+            if constexpr (EXPORT) {
+                // accumulator export (test path): this workgroup owns the sums
+                if (m < a.M) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int n = col0 + nl + (r / 4) * 8 + (r % 4);
+                        if (n < a.N) {
+                            const int64_t e = (int64_t)m * a.N + n;
+                            a.acc4_out[e] = (int32_t)acc[fm][fn][r];
+                            if (a.acc8_out)
+                                a.acc8_out[e] = acc8[r];
+                        }
+                    }
+                }
+            }
+            const float rs4 = sS[ml];
+            const float rs8 = T8 > 0 ? sS[BM + ml] : 0.0f;    // tail scales are not loaded when T8 == 0
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(sS + 2 * BM + nl + q * 8);
+                const float4 c8v = *reinterpret_cast<const float4 *>(sS + 3 * BM + nl + q * 8);
+                const float4 c8 = T8 > 0 ? c8v : float4{0.0f, 0.0f, 0.0f, 0.0f};
+                const float cs4[4] = {c4.x, c4.y, c4.z, c4.w}, cs8[4] = {c8.x, c8.y, c8.z, c8.w};
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = y_value(acc[fm][fn][q * 4 + e], acc8[q * 4 + e], rs4 * cs4[e], rs8 * cs8[e]);
+                const int n = col0 + nl + q * 8;
+                if (m < a.M) {
+                    _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
+                    if (vec_store && n + 3 < a.N) {
+                        *reinterpret_cast<uint2 *>(dst) = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < a.N)
+                                dst[e] = (_Float16)v[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace gemm_fp6_impl
+
+using namespace gemm_fp6_impl;
+
+int64_t u6_operand_bytes(int64_t rows, int64_t pitch4) { return (rows + 31) / 32 * (pitch4 / 32) * kU6Block; }
+
+hipError_t launch_repack_u6(const uint8_t *q4, int64_t rows, int64_t pitch4, uint8_t *u6, hipStream_t stream) {
+    const int64_t total = (rows + 31) / 32 * (pitch4 / 32) * 32;
+    if (total <= 0)
+        return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(repack_u6_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q4, rows, pitch4, u6);
+    return hipGetLastError();
+}
+
+bool gemm_fp6_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
+    (void)M;
+    (void)N;
+    return group == 0 && K_n > 0 && w4a4_pitch8_bytes(n_out) / kTileBytes <= MAX_TAIL_TILES;
+}
+
+const char *gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
+    return gemm_fp6_fits(M, N, K_n, n_out, group) ? "gemm_fp6_big_kernel<false>" : nullptr;
+}
+
+hipError_t launch_gemm_fp6(const Fp6GemmArgs &a, bool export_acc, hipStream_t stream) {
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    if (export_acc)
+        hipLaunchKernelGGL(gemm_fp6_big_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(gemm_fp6_big_kernel<false>, dim3(tiles), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace w4a4

@@ -234,15 +234,13 @@ def e3m2_code(q: int) -> int:
     return hits[0]
 
 
-def pack_u6(q4, pitch4: int):
-    """INT4 codes [rows, K_n] -> the FP6 operand of the prefill GEMM.
+U6_BLOCK = 1536    # bytes of one 32-row x 64-channel block of a u6 operand
 
-    Each 32-channel chunk c of a row (channels 32c .. 32c+31, zero past K_n
-    up to 2 * pitch4 channels) becomes a 192-bit image holding E3M2 code i
-    at bits 6i .. 6i+5 (little-endian); image bytes 0..15 go to the lo plane
-    at bytes 16c .. 16c+15 of the row, bytes 16..23 to the hi plane at bytes
-    8c .. 8c+7. Returns (lo uint8 [rows, pitch4], hi uint8 [rows, pitch4 // 2]).
-    """
+
+def u6_chunk_images(q4, pitch4: int) -> np.ndarray:
+    """The 192-bit image of every 32-channel chunk of every row: code i of
+    chunk c (channel 32c + i, code 0 past K_n up to 2 * pitch4 channels) at
+    bits 6i .. 6i+5, little-endian. Returns uint8 [rows, chunks, 24]."""
     q4 = np.asarray(q4, np.int8)
     rows, K_n = q4.shape
     C = 2 * pitch4 // 32                      # chunks per row
@@ -257,23 +255,49 @@ def pack_u6(q4, pitch4: int):
         words[:, :, w] |= (codes[:, :, i] << np.uint64(off)) & np.uint64(0xFFFFFFFFFFFFFFFF)
         if off > 58:                          # the code straddles two 64-bit words
             words[:, :, w + 1] |= codes[:, :, i] >> np.uint64(64 - off)
-    image = words.astype("<u8").view(np.uint8).reshape(rows, C, 24)
-    lo = np.ascontiguousarray(image[:, :, :16]).reshape(rows, C * 16)
-    hi = np.ascontiguousarray(image[:, :, 16:]).reshape(rows, C * 8)
-    return lo, hi
+    return words.astype("<u8").view(np.uint8).reshape(rows, C, 24)
 
 
-def unpack_u6(lo, hi, K_n: int) -> np.ndarray:
-    """Inverse of pack_u6: the INT4 codes [rows, K_n] (values of the E3M2 codes)."""
-    lo, hi = np.asarray(lo, np.uint8), np.asarray(hi, np.uint8)
-    rows, C = lo.shape[0], lo.shape[1] // 16
-    image = np.concatenate([lo.reshape(rows, C, 16), hi.reshape(rows, C, 8)], axis=2)
-    out = np.zeros((rows, C * 32), np.int8)
+def pack_u6(q4, pitch4: int) -> np.ndarray:
+    """INT4 codes [rows, K_n] -> the u6 operand of the FP6 GEMM (uint8).
+
+    Rows go in blocks of 32 (rows past the last one are code 0) and channels
+    in tiles of 64 (two 32-channel chunks, h = 0, 1); the block of row block
+    b and tile t is 1536 bytes at (b * T + t) * 1536, T = pitch4 / 32. Inside
+    it, row r's chunk h has image bytes 0..15 at 512 h + 16 r and image bytes
+    16..23 at 1024 + 256 h + 8 r.
+    """
+    img = u6_chunk_images(q4, pitch4)
+    rows = img.shape[0]
+    RB, T = (rows + 31) // 32, pitch4 // 32
+    out = np.zeros((RB, T, U6_BLOCK), np.uint8)
     for r in range(rows):
-        for c in range(C):
-            bits = int.from_bytes(image[r, c].tobytes(), "little")
-            for i in range(32):
-                out[r, 32 * c + i] = int(e3m2_value((bits >> (6 * i)) & 63))
+        b, rr = divmod(r, 32)
+        for t in range(T):
+            for h in range(2):
+                c = img[r, 2 * t + h]
+                out[b, t, 512 * h + 16 * rr:512 * h + 16 * rr + 16] = c[:16]
+                out[b, t, 1024 + 256 * h + 8 * rr:1024 + 256 * h + 8 * rr + 8] = c[16:]
+    return out.reshape(-1)
+
+
+def unpack_u6(u6, rows: int, K_n: int) -> np.ndarray:
+    """Inverse of pack_u6: the INT4 codes [rows, K_n] (values of the E3M2 codes)."""
+    u6 = np.asarray(u6, np.uint8)
+    pitch4 = (K_n + 127) // 128 * 64
+    T = pitch4 // 32
+    blocks = u6.reshape(-1, T, U6_BLOCK)
+    out = np.zeros((rows, 2 * pitch4), np.int8)
+    for r in range(rows):
+        b, rr = divmod(r, 32)
+        for t in range(T):
+            for h in range(2):
+                blk = blocks[b, t]
+                img = bytes(blk[512 * h + 16 * rr:512 * h + 16 * rr + 16]) + \
+                    bytes(blk[1024 + 256 * h + 8 * rr:1024 + 256 * h + 8 * rr + 8])
+                bits = int.from_bytes(img, "little")
+                for i in range(32):
+                    out[r, 64 * t + 32 * h + i] = int(e3m2_value((bits >> (6 * i)) & 63))
     return out[:, :K_n]
 
 

@@ -1,0 +1,143 @@
+"""GPU parity of the FP6 prefill path (INT4 codes held as FP6 E3M2 values)
+through the C ABI, against the CPU oracle.
+
+* The u6 conversion (w4a4_repack_u6) is checked byte for byte against the
+  oracle's pack_u6 of the oracle's own codes.
+* The FP6 GEMM's integer sums are the layer's accumulators: its export
+  (w4a4_outlier_gemm_fp6_i32, the same kernel and main loop as the product)
+  must equal the oracle's acc4 / acc8 exactly, and its Y the product's Y bit
+  for bit; Y is within 1e-2 * max |Y_oracle| of the oracle's fp64 dequant.
+* The fused FP6 layer call equals producer + repack + FP6 GEMM bit for bit.
+Every case compares every output.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import mixed_precision_integer_amd as w4
+from mixed_precision_integer_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 1e-2
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    sys.stderr.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def check_y(y_gpu, y_ref_fp16):
+    ref = y_ref_fp16.astype(np.float64)
+    got = y_gpu.astype(np.float64)
+    amax = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    assert np.all(np.isfinite(got))
+    assert err <= TOL * amax, f"max err {err} vs bound {TOL * amax}"
+    return err / max(amax, 1e-30)
+
+
+def fp6_compare(oracle, X, W, outliers, group=0):
+    M, K = X.shape
+    N = W.shape[0]
+    n_out = len(outliers)
+    K_n = K - n_out
+    perm = torch.from_numpy(w4.make_perm(K, outliers)).to(DEV)
+    Xd, Wd = torch.from_numpy(X).to(DEV), torch.from_numpy(W).to(DEV)
+    a = w4.quant_reorder_act(Xd, perm, n_out, group)
+    wq = w4.pack_int4_weights(Wd, perm, n_out, group)
+    af, wf = w4.to_fp6(a), w4.to_fp6(wq)
+    perm_o = oracle.make_perm(K, outliers)
+    qa = oracle.quantize_rows(X, perm_o, n_out, group)
+    qw = oracle.quantize_rows(W, perm_o, n_out, group)
+    torch.cuda.synchronize()
+    # the u6 conversion, byte for byte, for both operands
+    for op, q, rows in ((af, qa[0], M), (wf, qw[0], N)):
+        want = oracle.pack_u6(q, w4.pitch4_bytes(K_n))
+        assert op.u6.numel() == want.size == w4.u6_bytes(rows, K_n)
+        assert np.array_equal(op.u6.cpu().numpy(), want), "u6 bytes"
+    acc4, acc8, ystar = oracle.linear_dense(qa, qw, group)
+    g4, g8, y_exp = w4.outlier_gemm_fp6_i32(af, wf)
+    y = w4.outlier_gemm_fp6(af, wf)
+    yf = w4.quant_gemm_fp6(Xd, perm, wf)
+    y_i8 = w4.w4a4_outlier_gemm(a, wq)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_exp), "the accumulator export's launch wrote a different Y"
+    assert np.array_equal(g4[0].cpu().numpy(), acc4[0]), "acc4"
+    if n_out:
+        assert np.array_equal(g8.cpu().numpy(), acc8), "acc8"
+    rel = check_y(y.cpu().numpy(), oracle.to_fp16(ystar))
+    assert torch.equal(yf, y), "fused FP6 call differs from producer + repack + FP6 GEMM"
+    # the i8 path forms the same integer sums; Y may differ only by the fp32 order
+    check_y(y_i8.cpu().numpy(), y.cpu().numpy())
+    return rel
+
+
+CASES = [
+    # M, N, K, n_out
+    (256, 256, 320, 64),            # one tile, K_n = 256: two K-tiles, one tail tile
+    (300, 520, 1152, 128),          # ragged M and N (edge tiles), two tail tiles
+    (37, 200, 640, 100),            # one partial tile, tail of 100 padded to 128
+    (1, 128, 512, 0),               # one token, no outliers
+    (512, 768, 2304, 256),          # several tiles, four tail tiles
+    (513, 257, 4160, 64),           # ragged by one in both directions, 65 K-tiles (odd)
+    (96, 160, 21760 + 256, 256),    # the longest K of the workloads
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out", CASES)
+def test_fp6_parity(oracle, M, N, K, n_out):
+    X, W, o = wl.draw(M, N, K, n_out, seed=M + 5 * N + K, outlier_factor=40.0)
+    fp6_compare(oracle, X, W, o)
+
+
+def test_fp6_extreme_codes(oracle):
+    """All -8 codes (magnitude 8, the largest E3M2 value used) and random
+    full-range codes over the longest K: the sums reach 21760 * 64."""
+    rng = np.random.default_rng(321)
+    M, N, K_n, n_out = 64, 96, 21760, 256
+    for mode in ("all_min", "random"):
+        if mode == "all_min":
+            qa4 = np.full((M, K_n), -8, np.int8); qw4 = np.full((N, K_n), -8, np.int8)
+        else:
+            qa4 = rng.integers(-8, 8, (M, K_n), dtype=np.int8); qw4 = rng.integers(-8, 8, (N, K_n), dtype=np.int8)
+        qa8 = rng.integers(-128, 128, (M, n_out), dtype=np.int8)
+        qw8 = rng.integers(-128, 128, (N, n_out), dtype=np.int8)
+        sa4 = rng.uniform(0.5, 2, (M, 1)).astype(np.float32); sw4 = rng.uniform(1e-3, 2e-3, (N, 1)).astype(np.float32)
+        sa8 = rng.uniform(0.5, 2, M).astype(np.float32); sw8 = rng.uniform(1e-4, 2e-4, N).astype(np.float32)
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)  # noqa: E731
+
+        def operand(q4, s4, q8, s8):
+            rows = q4.shape[0]
+            u6 = t(oracle.pack_u6(q4, w4.pitch4_bytes(K_n)))
+            p8 = np.zeros((rows, 256), np.int8); p8[:, :n_out] = q8
+            return w4.Fp6Operand(u6, t(p8), t(s4), t(s8), K_n + n_out, n_out, 0)
+
+        a = operand(qa4, sa4, qa8, sa8)
+        w = operand(qw4, sw4, qw8, sw8)
+        acc4, acc8, ystar = oracle.linear_dense((qa4, sa4, qa8, sa8), (qw4, sw4, qw8, sw8), 0)
+        g4, g8, y = w4.outlier_gemm_fp6_i32(a, w)
+        torch.cuda.synchronize()
+        assert np.array_equal(g4[0].cpu().numpy(), acc4[0]), mode
+        assert np.array_equal(g8.cpu().numpy(), acc8), mode
+        check_y(y.cpu().numpy(), oracle.to_fp16(ystar))
+
+
+@pytest.mark.parametrize("work", [wl.UPPROJ_7B, wl.DOWNPROJ_65B], ids=lambda w: w.name)
+def test_fp6_full_size_workload(oracle, work):
+    X, W, o = wl.draw_workload(work)
+    sys.stderr.write(f"[gpu case] FP6 full size {work.name}: "
+                     f"{w4.outlier_gemm_fp6_kernel_name(work.M, work.N, work.K, work.n_out, work.group)}\n")
+    sys.stderr.flush()
+    fp6_compare(oracle, X, W, o, work.group)
+
+
+def test_fp6_rejects_group_mode():
+    assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4096, 128, 128) is None
+    assert w4.outlier_gemm_fp6_kernel_name(4096, 11008, 4096, 256, 0) == "gemm_fp6_big_kernel<false>"

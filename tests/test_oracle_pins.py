@@ -395,35 +395,42 @@ def test_e3m2_value_closed_forms(oracle):
 
 
 def test_pack_u6_bit_positions(oracle):
-    """Code i of chunk c sits at bits 6i of the chunk's 192-bit image, whose
-    bytes 0..15 are the lo plane's bytes 16c.. and bytes 16..23 the hi
-    plane's bytes 8c..; channels past K_n are code 0."""
+    """Code i of a row's chunk (32 channels) sits at bits 6i of the chunk's
+    192-bit image; image bytes 0..15 and 16..23 sit where the block layout
+    puts them; channels past K_n and rows past the last are code 0."""
     rng = np.random.default_rng(7)
-    q = rng.integers(-8, 8, (3, 200), dtype=np.int8)
-    pitch4 = 128                                        # 256 channels: 8 chunks
-    lo, hi = oracle.pack_u6(q, pitch4)
-    assert lo.shape == (3, 128) and hi.shape == (3, 64)
-    for r in range(3):
+    rows, K_n, pitch4 = 40, 200, 128                   # 2 row blocks, 4 tiles of 64 channels
+    q = rng.integers(-8, 8, (rows, K_n), dtype=np.int8)
+    u6 = oracle.pack_u6(q, pitch4)
+    assert u6.shape == (2 * 4 * 1536,)
+    blk = u6.reshape(2, 4, 1536)
+    for r in range(64):
+        b, rr = divmod(r, 32)
         for c in range(8):
-            img = int.from_bytes(bytes(lo[r, 16 * c:16 * c + 16]) + bytes(hi[r, 8 * c:8 * c + 8]), "little")
+            t, h = divmod(c, 2)
+            img = bytes(blk[b, t, 512 * h + 16 * rr:512 * h + 16 * rr + 16]) + \
+                bytes(blk[b, t, 1024 + 256 * h + 8 * rr:1024 + 256 * h + 8 * rr + 8])
+            bits = int.from_bytes(img, "little")
             for i in range(32):
                 j = 32 * c + i
-                want = oracle.e3m2_code(int(q[r, j])) if j < 200 else 0
-                assert (img >> (6 * i)) & 63 == want
+                want = oracle.e3m2_code(int(q[r, j])) if r < rows and j < K_n else 0
+                assert (bits >> (6 * i)) & 63 == want
 
 
 def test_pack_u6_round_trip(oracle):
     rng = np.random.default_rng(8)
-    q = rng.integers(-8, 8, (4, 100), dtype=np.int8)
-    lo, hi = oracle.pack_u6(q, 64)
-    assert np.array_equal(oracle.unpack_u6(lo, hi, 100), q)
+    q = rng.integers(-8, 8, (37, 100), dtype=np.int8)
+    u6 = oracle.pack_u6(q, 64)
+    assert np.array_equal(oracle.unpack_u6(u6, 37, 100), q)
 
 
 def test_pack_u6_known_bytes(oracle):
-    """One chunk by hand: q = [1, -1, 7, -8, 0, ...]: codes 12, 44, 23, 56 at
-    bits 0, 6, 12, 18 -> 12 | 44 << 6 | 23 << 12 | 56 << 18 = 0xE17B0C."""
+    """One chunk by hand: q = [1, -1, 7, -8, 0, ...] in row 0: codes 12, 44,
+    23, 56 at bits 0, 6, 12, 18 -> 12 | 44 << 6 | 23 << 12 | 56 << 18 =
+    0xE17B0C, the first bytes of block (0, 0)."""
     q = np.zeros((1, 32), np.int8)
     q[0, :4] = [1, -1, 7, -8]
-    lo, hi = oracle.pack_u6(q, 64)
-    assert lo[0, :4].tolist() == [0x0C, 0x7B, 0xE1, 0x00]
-    assert not lo[0, 4:].any() and not hi.any()
+    u6 = oracle.pack_u6(q, 64)
+    assert u6.size == 2 * 1536
+    assert u6[:4].tolist() == [0x0C, 0x7B, 0xE1, 0x00]
+    assert not u6[4:].any()
