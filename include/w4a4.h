@@ -224,6 +224,23 @@ w4a4_status w4a4_quant_gemm(const void *X, int64_t ldx, const int32_t *perm, con
                             int64_t ldy, void *workspace, size_t workspace_bytes,
                             w4a4_stream stream);
 
+/* w4a4_quant_gemm without a caller workspace, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a library-owned device
+ * array of w4a4_quant_gemm_static_max_bytes() bytes (32 MiB), one copy per
+ * GPU, held until the process ends; the call allocates nothing. Arguments,
+ * results and kernels are those of w4a4_quant_gemm; UNSUPPORTED when
+ * w4a4_quant_gemm_workspace_bytes for the shape exceeds the array. Every call
+ * on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams or host threads) race. The array keeps the last call's contents;
+ * the split-K arrival counters at its start are cleared by a kernel on
+ * `stream` before the launches that use them. */
+size_t w4a4_quant_gemm_static_max_bytes(void);
+w4a4_status w4a4_quant_gemm_static(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
+                                   const void *Wq8, const float *sw4, const float *sw8, int32_t M,
+                                   int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
+                                   int64_t ldy, w4a4_stream stream);
+
 /* The fused layer behind an RMSNorm: w4a4_rmsnorm_quant_reorder_act on X
  * into the caller's workspace (the same size as w4a4_quant_gemm's), then
  * w4a4_outlier_gemm, both on `stream`. gamma and eps as in

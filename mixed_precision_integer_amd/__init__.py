@@ -41,7 +41,7 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32", "w4a4_kv_quant", "w4a4_kv_dequant",
             "w4a4_u6_bytes", "w4a4_repack_u6", "w4a4_outlier_gemm_fp6_kernel_name",
             "w4a4_outlier_gemm_fp6", "w4a4_outlier_gemm_fp6_i32", "w4a4_quant_gemm_fp6_workspace_bytes",
-            "w4a4_quant_gemm_fp6")
+            "w4a4_quant_gemm_fp6", "w4a4_quant_gemm_static_max_bytes", "w4a4_quant_gemm_static")
 
 
 class W4A4Error(RuntimeError):
@@ -110,6 +110,10 @@ def lib():
     L.w4a4_kv_quant.restype = ctypes.c_int
     L.w4a4_kv_dequant.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, vp, i64, vp]
     L.w4a4_kv_dequant.restype = ctypes.c_int
+    L.w4a4_quant_gemm_static_max_bytes.argtypes = []
+    L.w4a4_quant_gemm_static_max_bytes.restype = sz
+    L.w4a4_quant_gemm_static.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64, vp]
+    L.w4a4_quant_gemm_static.restype = ctypes.c_int
     L.w4a4_u6_bytes.argtypes = [i32, i32]
     L.w4a4_u6_bytes.restype = i64
     L.w4a4_repack_u6.argtypes = [vp, i32, i32, vp, vp]
@@ -361,6 +365,26 @@ def quant_gemm(X, perm, w: QuantizedOperand, out=None, workspace=None):
                               _nz(w.q8), _nz(w.s4), _nz(w.s8), M, N, K, w.n_out, w.group,
                               out.data_ptr(), out.stride(0) if M else N, workspace.data_ptr(),
                               workspace.numel(), _stream()), "w4a4_quant_gemm")
+    return out
+
+
+def quant_gemm_static(X, perm, w: QuantizedOperand, out=None):
+    """The fused layer with the library's static per-GPU workspace (no device
+    allocation by the call; calls that overlap on one GPU race)."""
+    torch = _torch()
+    _check(X, torch.float16, "X", 2)
+    _check(perm, torch.int32, "perm", 1)
+    M, K = X.shape
+    N = w.s8.shape[0]
+    if K != w.K:
+        raise ValueError("X and weights disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(out, torch.float16, "out", 2)
+    _ok(lib().w4a4_quant_gemm_static(X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.q4),
+                                     _nz(w.q8), _nz(w.s4), _nz(w.s8), M, N, K, w.n_out, w.group,
+                                     out.data_ptr(), out.stride(0) if M else N, _stream()),
+        "w4a4_quant_gemm_static")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "w4a4.h"
@@ -331,7 +332,7 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
                               const void *Wq8, const float *sw4, const float *sw8, int32_t M,
                               int32_t N, int32_t K, int32_t n_out, int32_t group, void *Y,
                               int64_t ldy, void *workspace, size_t workspace_bytes,
-                              w4a4_stream stream, const NormArgs &norm) {
+                              w4a4_stream stream, const NormArgs &norm, bool clear_counters = false) {
     if (N < 0)
         return W4A4_ERR_INVALID_ARG;
     w4a4_status st = check_shape(M, K, n_out, group);
@@ -354,6 +355,8 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
     const size_t need = w4a4_quant_gemm_workspace_bytes(M, N, K, n_out, group);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return W4A4_ERR_WORKSPACE;
+    if (K > w4a4::quant_rows_max_k())            // the producer's longest row (checked before any launch)
+        return W4A4_ERR_UNSUPPORTED;
     // small decode batches: the quantizer (and the norm, for one token: a
     // second row already costs more than the norm producer's launch) run
     // inside the GEMM's workgroups
@@ -383,6 +386,11 @@ static w4a4_status quant_gemm(const void *X, int64_t ldx, const int32_t *perm, c
     size_t off[5];
     quant_gemm_layout(M, N, K, n_out, group, off);
     char *ws = static_cast<char *>(workspace);
+    // a workspace that keeps earlier contents (the static one) gets its
+    // split-K arrival counters cleared first, by a kernel on the stream
+    if (clear_counters && w4a4_outlier_gemm_workspace_bytes(M, N, K, n_out, group) > 0 &&
+        w4a4::clear_gemm_counters(ws, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return W4A4_ERR_HIP;
     void *Aq4 = K_n > 0 ? ws + off[0] : nullptr;
     void *Aq8 = n_out > 0 ? ws + off[1] : nullptr;
     float *sa4 = K_n > 0 ? reinterpret_cast<float *>(ws + off[2]) : nullptr;
@@ -772,3 +780,69 @@ w4a4_status w4a4_quant_gemm_fp6(const void *X, int64_t ldx, const int32_t *perm,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The fused layer call without a caller workspace: for callers that cannot
+// allocate device memory (code under graph capture, tight serving loops,
+// harnesses that forbid hipMalloc). Its workspace is a file-scope device
+// array, one copy per GPU, held until the process ends.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current (the host-side name is not a device address).
+w4a4_status scratch_for_current_device(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return W4A4_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return W4A4_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a4_quant_gemm_static_max_bytes(void) { return kScratchBytes; }
+
+w4a4_status w4a4_quant_gemm_static(const void *X, int64_t ldx, const int32_t *perm, const void *Wq4,
+                                   const void *Wq8, const float *sw4, const float *sw8, int32_t M, int32_t N,
+                                   int32_t K, int32_t n_out, int32_t group, void *Y, int64_t ldy,
+                                   w4a4_stream stream) {
+    if (N < 0)
+        return W4A4_ERR_INVALID_ARG;
+    w4a4_status st = check_shape(M, K, n_out, group);
+    if (st != W4A4_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return quant_gemm(X, ldx, perm, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, nullptr, 0, stream,
+                          NormArgs{nullptr, 0.0f, nullptr});
+    if (w4a4_quant_gemm_workspace_bytes(M, N, K, n_out, group) > kScratchBytes)
+        return W4A4_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != W4A4_OK)
+        return st;
+    // the array keeps the last call's contents: the split-K arrival counters
+    // at its start are cleared on the stream after the argument checks and
+    // before the launches (every other byte a call reads it has written first)
+    return quant_gemm(X, ldx, perm, Wq4, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, ws, kScratchBytes, stream,
+                      NormArgs{nullptr, 0.0f, nullptr}, true);
+}
+
+}  // extern "C"
+

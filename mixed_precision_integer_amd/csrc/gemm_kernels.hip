@@ -573,6 +573,10 @@ hipError_t zero_i32(int32_t *p, int64_t n, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t clear_gemm_counters(void *workspace, hipStream_t stream) {
+    return zero_i32(static_cast<int32_t *>(workspace), (int64_t)(kSplitCounterBytes / sizeof(int32_t)), stream);
+}
+
 hipError_t launch_gemm(const GemmArgs &a_in, bool export_acc, void *workspace, hipStream_t stream) {
     if (a_in.M == 0 || a_in.N == 0)
         return hipSuccess;

@@ -77,8 +77,10 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
 
-// Bytes of the arrival-counter block at the start of every split-K workspace.
+// Bytes of the arrival-counter block at the start of every split-K workspace,
+// and a kernel that zeroes that block on a stream (no memset node).
 size_t gemm_counter_bytes();
+hipError_t clear_gemm_counters(void *workspace, hipStream_t stream);
 
 // Kernel of a plan, as named in a kernel trace (static string).
 const char *gemm_kernel_name(const GemmPlan &p);
