@@ -29,8 +29,9 @@
 // * 256 x 256 output tile per workgroup, four waves of 128 x 128 (4 x 4
 //   blocks of 32 x 32), fp32 accumulators in AGPRs, one wave per SIMD. A
 //   K-tile is 64 channels (one FP6 k-step): eight u6 blocks of each operand,
-//   24 KB per stage; a 6-stage ring, DMA four tiles ahead, one barrier per
-//   tile. Fragments are read from LDS one row of MFMAs ahead of their use.
+//   24 KB per stage; a 6-stage ring, DMA five tiles ahead, one barrier per
+//   tile. The fragments of tile t + 1 are read from LDS into a second
+//   register set while the sixteen MFMAs of tile t run.
 // * The INT8 tail (at most 256 channels) is staged into the ring once the
 //   head is done and multiplied block by block on the i8 matrix cores into a
 //   16-register int32 accumulator; y = fp16(acc4 * (sa4 sw4) + acc8 * (sa8
@@ -126,29 +127,29 @@ static_assert((STAGES - 1) * D <= 63, "vmcnt range");
 // hi bytes); the instruction reads only those six for FP6. Kept in VGPRs:
 // the AGPRs hold the sums.
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 
-__device__ __forceinline__ v8i load_operand(const unsigned char *lo, const unsigned char *hi) {
-    v4i l = *reinterpret_cast<const v4i *>(lo);
-    v2i h = *reinterpret_cast<const v2i *>(hi);
-    asm("" : "+v"(l));
-    asm("" : "+v"(h));
-    v8i v;
-    v[0] = l[0];
-    v[1] = l[1];
-    v[2] = l[2];
-    v[3] = l[3];
-    v[4] = h[0];
-    v[5] = h[1];
-    return v;                                      // registers 6 and 7 left undefined
+// One operand fragment: 64 FP6 values of one row, as six dwords (the
+// 16-byte lo part of the chunk image, then its 8-byte hi part).
+__device__ __forceinline__ v6i load_operand(const unsigned char *lo, const unsigned char *hi) {
+    const v4i l = *reinterpret_cast<const v4i *>(lo);
+    const v2i h = *reinterpret_cast<const v2i *>(hi);
+    v6i v;
+    v.s0123 = l;
+    v.s45 = h;
+    return v;
 }
 
-// One row of blocks of a K-tile: block (fm, fn) takes the weight fragment as
-// the first operand, so lane (li, lh) holds token row li and the columns
-// 8 (r / 4) + 4 lh + r % 4 of the block.
-__device__ __forceinline__ void mma_row(v16f (&acc)[FN], const v8i &x, const v8i (&w)[FN]) {
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-        acc[fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[fn], x, acc[fn], 3, 3, 0, 127, 0, 127);
+// acc += w^T x for one 32 x 32 block (both operands FP6 E3M2, unit scales).
+// Block (fm, fn) takes the weight fragment as the first operand, so lane
+// (li, lh) holds token row li and the columns 8 (r / 4) + 4 lh + r % 4.
+// Written as an instruction so that the accumulators stay in AGPRs and the
+// fragments in VGPRs with no copies; the compiler places the waits for the
+// fragments' LDS reads in front of it.
+__device__ __forceinline__ void mma(v16f &acc, const v6i &w, const v6i &x) {
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:3 blgp:3"
+                 : "+a"(acc)
+                 : "v"(w), "v"(x), "v"(127));
 }
 
 // y = acc4 * s4 + acc8 * s8: one product, one fused multiply-add, rounded to
@@ -198,17 +199,20 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
     }
 
     // ring tile tt (past the last head tile: a reload of the last one into a
-    // stage nothing reads again, so every iteration issues the same DMA)
-    auto issue = [&](int tt) {
+    // stage nothing reads again, so every iteration issues the same DMA);
+    // part j < DPO is unit j of A, part DPO + j unit j of B
+    auto issue_part = [&](int tt, int j) {
         const int t = min(tt, T - 1);
         const uint32_t st = lds_addr(lds) + (tt % STAGES) * STAGE + wave_u * 1024;
-        const uint8_t *A = a.a_u6 + (int64_t)t * BLK, *B = a.w_u6 + (int64_t)t * BLK;
+        if (j < DPO)
+            dma16(a.a_u6 + (int64_t)t * BLK, oa[j], st + A_OFF + j * 4096);
+        else
+            dma16(a.w_u6 + (int64_t)t * BLK, ob[j - DPO], st + B_OFF + (j - DPO) * 4096);
+    };
+    auto issue = [&](int tt) {
 #pragma unroll
-        for (int j = 0; j < DPO; ++j)
-            dma16(A, oa[j], st + A_OFF + j * 4096);
-#pragma unroll
-        for (int j = 0; j < DPO; ++j)
-            dma16(B, ob[j], st + B_OFF + j * 4096);
+        for (int j = 0; j < D; ++j)
+            issue_part(tt, j);
     };
 
     // ---- scales of the tile, ahead of every K-tile (the first wait covers them)
@@ -237,60 +241,81 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
     // or 4 wn + i (B); a row block adds BLK bytes (an immediate offset).
     const uint32_t la = A_OFF + (wm * 4) * BLK, lb = B_OFF + (wn * 4) * BLK;
     const uint32_t llo = 512 * lh + 16 * li, lhi = 1024 + 256 * lh + 8 * li;
+    // The 8-byte reads each get a base register of their own: two of them a
+    // block apart on one base would be merged into a single four-register
+    // read, which cannot land inside two operand tuples.
+    uint32_t ha[FM], hb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        ha[i] = la + lhi + i * BLK;
+        asm("" : "+v"(ha[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+        hb[i] = lb + lhi + i * BLK;
+        asm("" : "+v"(hb[i]));
+    }
     auto a_frag = [&](uint32_t st, int i) {
-        return load_operand(lds + st + la + llo + i * BLK, lds + st + la + lhi + i * BLK);
+        return load_operand(lds + st + la + llo + i * BLK, lds + st + ha[i]);
     };
     auto b_frag = [&](uint32_t st, int i) {
-        return load_operand(lds + st + lb + llo + i * BLK, lds + st + lb + lhi + i * BLK);
+        return load_operand(lds + st + lb + llo + i * BLK, lds + st + hb[i]);
     };
 
     // ---- head -------------------------------------------------------------------------
-    // Software pipeline per wave: at the top of tile t the registers hold the
-    // four weight fragments of tile t and the first activation row; during
-    // row fm of tile t the next activation row (tile t's row fm + 1, or tile
-    // t + 1's first) and weight fragment fm of tile t + 1 are read, so every
-    // read has a row of MFMAs (128 cycles) to arrive. DMA runs four tiles
-    // ahead: at tile t, after the barrier that has every wave done with tile
-    // t - 1, tile t + 5 goes into tile t - 1's stage.
+    // Register double buffer: at the top of tile t the registers hold all
+    // eight fragments of tile t. After the barrier that has every wave holding
+    // tile t (so its stage is free) and tile t + 1 landed, tile t + 6 goes into
+    // tile t's stage, the sixteen reads of tile t + 1 are issued, and the
+    // sixteen MFMAs of tile t run while they are in flight.
 #pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
+    for (int p = 0; p < STAGES; ++p)
         issue(p);
     compiler_fence();
-    __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * D));     // tile 0 (and the scales)
+    __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 1) * D));     // tile 0 (and the scales)
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    v8i wc[FN], wn_[FN], x0, x1;
+    v6i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        fa0[i] = a_frag(0, i);
 #pragma unroll
     for (int i = 0; i < FN; ++i)
-        wc[i] = b_frag(0, i);
-    x0 = a_frag(0, 0);
+        fb0[i] = b_frag(0, i);
 
-    auto tile = [&](int t, v8i (&wcur)[FN], v8i (&wnext)[FN]) {
+    auto tile = [&](int t, const v6i (&xa)[FM], const v6i (&xb)[FN], v6i (&na)[FM], v6i (&nb)[FN]) {
         compiler_fence();
-        __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 3) * D));   // tile t + 1 has landed
-        __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));               // tile t - 1's reads are back
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * D));   // tile t + 1 has landed
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));               // tile t is in registers
         __builtin_amdgcn_s_barrier();
         compiler_fence();
-        issue(t + STAGES - 1);                                      // into tile t - 1's stage
-        const uint32_t sc = (uint32_t)((t % STAGES) * STAGE), sn = (uint32_t)(((t + 1) % STAGES) * STAGE);
-        x1 = a_frag(sc, 1);
-        wnext[0] = b_frag(sn, 0);
-        mma_row(acc[0], x0, wcur);
-        x0 = a_frag(sc, 2);
-        wnext[1] = b_frag(sn, 1);
-        mma_row(acc[1], x1, wcur);
-        x1 = a_frag(sc, 3);
-        wnext[2] = b_frag(sn, 2);
-        mma_row(acc[2], x0, wcur);
-        x0 = a_frag(sn, 0);
-        wnext[3] = b_frag(sn, 3);
-        mma_row(acc[3], x1, wcur);
+        // The sixteen MFMAs of tile t, each followed by one fragment read of
+        // tile t + 1 (the first eight) or one DMA unit of tile t + 6 into tile
+        // t's stage (the next six), so that every other instruction issues
+        // while an MFMA executes.
+        const uint32_t sn = (uint32_t)(((t + 1) % STAGES) * STAGE);
+#pragma unroll
+        for (int k = 0; k < FM * FN; ++k) {
+            const int fm = k / FN, fn = k % FN;
+            mma(acc[fm][fn], xb[fn], xa[fm]);
+            if (k < FM)
+                na[k] = a_frag(sn, k);
+            else if (k < FM + FN)
+                nb[k - FM] = b_frag(sn, k - FM);
+            else if (k < FM + FN + D)
+                issue_part(t + STAGES, k - FM - FN);
+        }
     };
     for (int t = 0; t < T; t += 2) {
-        tile(t, wc, wn_);
+        tile(t, fa0, fb0, fa1, fb1);
         if (t + 1 < T)
-            tile(t + 1, wn_, wc);
+            tile(t + 1, fa1, fb1, fa0, fb0);
     }
+
+    // The MFMAs above are instructions the compiler does not see as such: give
+    // the last ones the wait states their AGPR results need before the VALU
+    // reads them.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     // ---- the INT8 tail: staged into the ring once every wave is done with it ----------
     compiler_fence();
