@@ -212,25 +212,26 @@ def pack_nibbles(q4, pitch: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# FP6 (E3M2) packing of INT4 codes for the prefill GEMM
+# FP6 (E2M3) packing of INT4 codes for the prefill GEMM
 # ---------------------------------------------------------------------------
-def e3m2_value(code: int) -> float:
-    """Value of a 6-bit FP6 E3M2 code (OCP Microscaling Formats v1.0): sign
-    bit 5, exponent bits 4..2 with bias 3, mantissa bits 1..0; exponent 0 is
-    subnormal, 2^-2 * m/4; no infinities or NaNs."""
-    s, e, m = (code >> 5) & 1, (code >> 2) & 7, code & 3
-    v = 2.0 ** (e - 3) * (1 + m / 4) if e else 2.0 ** -2 * (m / 4)
+def e2m3_value(code: int) -> float:
+    """Value of a 6-bit FP6 E2M3 code (OCP Microscaling Formats v1.0): sign
+    bit 5, exponent bits 4..3 with bias 1, mantissa bits 2..0; exponent 0 is
+    subnormal, 2^0 * m/8; no infinities or NaNs."""
+    s, e, m = (code >> 5) & 1, (code >> 3) & 3, code & 7
+    v = 2.0 ** (e - 1) * (1 + m / 8) if e else m / 8
     return -v if s else v
 
 
-def e3m2_code(q: int) -> int:
-    """The E3M2 code whose value is the integer q (|q| <= 8 here: every INT4
-    code and its negation are exact in E3M2). Zero is +0 (code 0)."""
+def e2m3_code(q: int) -> int:
+    """The E2M3 code of the INT4 code q: the code whose value is q / 2 (|q| <=
+    8 here; every half-integer of magnitude <= 4 is exact in E2M3, and the
+    operand scale 2 of the matrix instruction restores q). Zero is +0."""
     if q == 0:
         return 0
-    hits = [c for c in range(64) if e3m2_value(c) == q]
+    hits = [c for c in range(64) if e2m3_value(c) == q / 2]
     if len(hits) != 1:
-        raise ValueError(f"{q} is not exactly representable in E3M2")
+        raise ValueError(f"{q} / 2 is not exactly representable in E2M3")
     return hits[0]
 
 
@@ -244,7 +245,7 @@ def u6_chunk_images(q4, pitch4: int) -> np.ndarray:
     q4 = np.asarray(q4, np.int8)
     rows, K_n = q4.shape
     C = 2 * pitch4 // 32                      # chunks per row
-    table = np.array([e3m2_code(v) for v in range(-8, 8)], np.uint64)
+    table = np.array([e2m3_code(v) for v in range(-8, 8)], np.uint64)
     codes = np.zeros((rows, C * 32), np.uint64)
     codes[:, :K_n] = table[q4.astype(np.int64) + 8]
     codes = codes.reshape(rows, C, 32)
@@ -282,7 +283,7 @@ def pack_u6(q4, pitch4: int) -> np.ndarray:
 
 
 def unpack_u6(u6, rows: int, K_n: int) -> np.ndarray:
-    """Inverse of pack_u6: the INT4 codes [rows, K_n] (values of the E3M2 codes)."""
+    """Inverse of pack_u6: the INT4 codes [rows, K_n] (twice the values of the E2M3 codes)."""
     u6 = np.asarray(u6, np.uint8)
     pitch4 = (K_n + 127) // 128 * 64
     T = pitch4 // 32
@@ -297,7 +298,7 @@ def unpack_u6(u6, rows: int, K_n: int) -> np.ndarray:
                     bytes(blk[1024 + 256 * h + 8 * rr:1024 + 256 * h + 8 * rr + 8])
                 bits = int.from_bytes(img, "little")
                 for i in range(32):
-                    out[r, 64 * t + 32 * h + i] = int(e3m2_value((bits >> (6 * i)) & 63))
+                    out[r, 64 * t + 32 * h + i] = int(2 * e2m3_value((bits >> (6 * i)) & 63))
     return out[:, :K_n]
 
 

@@ -372,26 +372,31 @@ def test_fp64_to_fp16_rounding_is_nearest_even(oracle):
 
 
 # ---------------------------------------------------------------------------
-# FP6 (E3M2) packing of INT4 codes for the prefill GEMM
+# FP6 (E2M3) packing of INT4 codes for the prefill GEMM
 # ---------------------------------------------------------------------------
-E3M2 = os.path.join(os.path.dirname(__file__), "golden", "e3m2_int4.json")
+E2M3 = os.path.join(os.path.dirname(__file__), "golden", "e2m3_int4.json")
 
 
-def test_e3m2_codes_match_hand_derived(oracle):
-    want = json.load(open(E3M2))["codes"]
+def test_e2m3_codes_match_hand_derived(oracle):
+    want = json.load(open(E2M3))["codes"]
     for q, code in want.items():
-        assert oracle.e3m2_code(int(q)) == code, q
-        assert oracle.e3m2_value(code) == int(q)
+        assert oracle.e2m3_code(int(q)) == code, q
+        assert oracle.e2m3_value(code) == int(q) / 2
 
 
-def test_e3m2_value_closed_forms(oracle):
-    assert oracle.e3m2_value(0b011111) == 28.0          # the largest finite value: 2^4 * 1.75
-    assert oracle.e3m2_value(0b011100) == 16.0
-    assert oracle.e3m2_value(0b000001) == 1 / 16        # the smallest subnormal
-    assert oracle.e3m2_value(0b000100) == 0.25          # the smallest normal
-    assert oracle.e3m2_value(0b100000) == 0.0           # -0
-    vals = sorted(oracle.e3m2_value(c) for c in range(32))
+def test_e2m3_value_closed_forms(oracle):
+    assert oracle.e2m3_value(0b011111) == 7.5           # the largest finite value: 2^2 * 1.875
+    assert oracle.e2m3_value(0b011000) == 4.0           # 2^2: -8 / 2 in magnitude
+    assert oracle.e2m3_value(0b000001) == 1 / 8         # the smallest subnormal
+    assert oracle.e2m3_value(0b000111) == 7 / 8         # the largest subnormal
+    assert oracle.e2m3_value(0b001000) == 1.0           # the smallest normal
+    assert oracle.e2m3_value(0b100000) == 0.0           # -0
+    assert oracle.e2m3_value(0b110100) == -3.0          # -2^1 * 1.5
+    vals = sorted(oracle.e2m3_value(c) for c in range(32))
     assert len(set(vals)) == 32 and vals[0] == 0.0      # 32 distinct non-negative values
+    # the values are the multiples of 1/8 up to 1, of 1/4 up to 4 and of 1/2 up to 7.5
+    assert vals == [i / 8 for i in range(8)] + [1 + i / 8 for i in range(8)] + \
+        [2 + i / 4 for i in range(8)] + [4 + i / 2 for i in range(8)]
 
 
 def test_pack_u6_bit_positions(oracle):
@@ -413,7 +418,7 @@ def test_pack_u6_bit_positions(oracle):
             bits = int.from_bytes(img, "little")
             for i in range(32):
                 j = 32 * c + i
-                want = oracle.e3m2_code(int(q[r, j])) if r < rows and j < K_n else 0
+                want = oracle.e2m3_code(int(q[r, j])) if r < rows and j < K_n else 0
                 assert (bits >> (6 * i)) & 63 == want
 
 
@@ -425,12 +430,12 @@ def test_pack_u6_round_trip(oracle):
 
 
 def test_pack_u6_known_bytes(oracle):
-    """One chunk by hand: q = [1, -1, 7, -8, 0, ...] in row 0: codes 12, 44,
-    23, 56 at bits 0, 6, 12, 18 -> 12 | 44 << 6 | 23 << 12 | 56 << 18 =
-    0xE17B0C, the first bytes of block (0, 0)."""
+    """One chunk by hand: q = [1, -1, 7, -8, 0, ...] in row 0: the E2M3 codes
+    of 0.5, -0.5, 3.5, -4 are 4, 36, 22, 56, at bits 0, 6, 12, 18 ->
+    4 | 36 << 6 | 22 << 12 | 56 << 18 = 0xE16904, the first bytes of block (0, 0)."""
     q = np.zeros((1, 32), np.int8)
     q[0, :4] = [1, -1, 7, -8]
     u6 = oracle.pack_u6(q, 64)
     assert u6.size == 2 * 1536
-    assert u6[:4].tolist() == [0x0C, 0x7B, 0xE1, 0x00]
+    assert u6[:4].tolist() == [0x04, 0x69, 0xE1, 0x00]
     assert not u6[4:].any()
