@@ -281,9 +281,21 @@ int64_t w4a4_u6_bytes(int32_t rows, int32_t K_n);
 
 /* Convert packed INT4 nibbles Q4 device uint8 [rows, pitch4] (the layout of
  * Aq4 / Wq4 above) to a u6 operand U6 device uint8 [w4a4_u6_bytes(rows,
- * K_n)]. Weights are converted once, offline; the fused FP6 call converts the
- * activation codes itself. Both pointers 16-byte aligned (ALIGNMENT). */
+ * K_n)]. Weights are converted once, offline. Both pointers 16-byte aligned
+ * (ALIGNMENT). */
 w4a4_status w4a4_repack_u6(const void *Q4, int32_t rows, int32_t K_n, void *U6, w4a4_stream stream);
+
+/* The activation producer of the FP6 path (QUIK abstract; Atom summary page,
+ * Summary paragraph 2 and Interesting ideas I2): w4a4_quant_reorder_act with
+ * the INT4 head written straight into a u6 operand Au6 device uint8
+ * [w4a4_u6_bytes(M, K_n)] (rows past M up to the end of their 32-row block
+ * are written as code 0) instead of packed nibbles. Codes, scales and the
+ * INT8 tail are those of w4a4_quant_reorder_act; Au6 equals w4a4_repack_u6
+ * of its Aq4 byte for byte. Group 0 only (UNSUPPORTED otherwise); Au6
+ * 16-byte aligned; other arguments as w4a4_quant_reorder_act. */
+w4a4_status w4a4_quant_reorder_act_u6(const void *X, int64_t ldx, const int32_t *perm, int32_t M,
+                                      int32_t K, int32_t n_out, int32_t group, void *Au6, void *Aq8,
+                                      float *sa4, float *sa8, w4a4_stream stream);
 
 /* Name of the kernel w4a4_outlier_gemm_fp6 launches for this shape (as a
  * kernel trace prints it), or NULL for a shape it rejects. */
@@ -316,9 +328,9 @@ size_t w4a4_quant_gemm_fp6_workspace_bytes(int32_t M, int32_t N, int32_t K, int3
                                            int32_t group);
 
 /* The fused prefill layer on the FP6 path (Atom summary page, Interesting
- * ideas I2): w4a4_quant_reorder_act on X, the conversion of its INT4 codes to
- * a u6 operand, and w4a4_outlier_gemm_fp6 with the pre-converted weights Wu6
- * (w4a4_repack_u6 of Wq4), all on `stream`, with the caller's workspace. The
+ * ideas I2): w4a4_quant_reorder_act_u6 on X and w4a4_outlier_gemm_fp6 with
+ * the pre-converted weights Wu6 (w4a4_repack_u6 of Wq4), both on `stream`,
+ * with the caller's workspace. The
  * codes, scales and integer sums are those of w4a4_quant_gemm. Constraints of
  * w4a4_outlier_gemm_fp6. */
 w4a4_status w4a4_quant_gemm_fp6(const void *X, int64_t ldx, const int32_t *perm, const void *Wu6,

@@ -39,7 +39,7 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm",
             "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers",
             "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32", "w4a4_kv_quant", "w4a4_kv_dequant",
-            "w4a4_u6_bytes", "w4a4_repack_u6", "w4a4_outlier_gemm_fp6_kernel_name",
+            "w4a4_u6_bytes", "w4a4_repack_u6", "w4a4_quant_reorder_act_u6", "w4a4_outlier_gemm_fp6_kernel_name",
             "w4a4_outlier_gemm_fp6", "w4a4_outlier_gemm_fp6_i32", "w4a4_quant_gemm_fp6_workspace_bytes",
             "w4a4_quant_gemm_fp6", "w4a4_quant_gemm_static_max_bytes", "w4a4_quant_gemm_static")
 
@@ -118,6 +118,8 @@ def lib():
     L.w4a4_u6_bytes.restype = i64
     L.w4a4_repack_u6.argtypes = [vp, i32, i32, vp, vp]
     L.w4a4_repack_u6.restype = ctypes.c_int
+    L.w4a4_quant_reorder_act_u6.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.w4a4_quant_reorder_act_u6.restype = ctypes.c_int
     L.w4a4_outlier_gemm_fp6_kernel_name.argtypes = [i32, i32, i32, i32, i32]
     L.w4a4_outlier_gemm_fp6_kernel_name.restype = ctypes.c_char_p
     L.w4a4_outlier_gemm_fp6.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64, vp]
@@ -475,6 +477,38 @@ def to_fp6(op: QuantizedOperand) -> Fp6Operand:
     return Fp6Operand(repack_u6(op.q4, op.K - op.n_out), op.q8, op.s4, op.s8, op.K, op.n_out, op.group)
 
 
+def quant_reorder_act_u6(X, perm, n_out: int, group: int = 0, out: Fp6Operand = None) -> Fp6Operand:
+    """Runtime activation producer of the FP6 path: reorder + quantize every
+    token row, the INT4 head written straight into a u6 operand (into `out`'s
+    buffers when given)."""
+    torch = _torch()
+    _check(X, torch.float16, "X", 2)
+    _check(perm, torch.int32, "perm", 1)
+    M, K = X.shape
+    a = out if out is not None else alloc_fp6_operand(M, K, n_out, group, X.device)
+    if a.u6.numel() < u6_bytes(M, K - n_out) or a.s8.shape[0] < M:
+        raise ValueError("out is too small")
+    _ok(lib().w4a4_quant_reorder_act_u6(X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), M, K, n_out,
+                                        group, a.u6.data_ptr(), _nz(a.q8), a.s4.data_ptr(), a.s8.data_ptr(),
+                                        _stream()),
+        "w4a4_quant_reorder_act_u6")
+    return a
+
+
+def alloc_fp6_operand(rows: int, K: int, n_out: int, group: int, device) -> Fp6Operand:
+    """Empty device buffers of an FP6-path operand of `rows` rows."""
+    torch = _torch()
+    K_n = K - n_out
+    G = num_groups(K_n, group)
+    if G < 0:
+        raise ValueError("group must divide K - n_out")
+    return Fp6Operand(
+        torch.empty(max(u6_bytes(rows, K_n), 1), dtype=torch.uint8, device=device),
+        torch.empty((rows, pitch8_bytes(n_out)), dtype=torch.int8, device=device) if n_out else None,
+        torch.empty((rows, G), dtype=torch.float32, device=device),
+        torch.empty((rows,), dtype=torch.float32, device=device), K, n_out, group)
+
+
 def pack_weights_fp6(W, perm, n_out: int, group: int) -> Fp6Operand:
     """Offline weight preparation for the FP6 prefill path."""
     return to_fp6(pack_int4_weights(W, perm, n_out, group))
@@ -723,10 +757,9 @@ class LayerPlan:
 
 class Fp6LayerPlan:
     """Arguments of one FP6-path layer call, marshalled once (the FP6
-    counterpart of LayerPlan): ``produce()`` runs w4a4_quant_reorder_act and
-    w4a4_repack_u6 into pre-allocated operands, ``gemm()`` runs
-    w4a4_outlier_gemm_fp6, ``fused()`` is w4a4_quant_gemm_fp6 (the same
-    launches)."""
+    counterpart of LayerPlan): ``produce()`` runs w4a4_quant_reorder_act_u6
+    into pre-allocated operands, ``gemm()`` runs w4a4_outlier_gemm_fp6,
+    ``fused()`` is w4a4_quant_gemm_fp6 (the same launches)."""
 
     def __init__(self, X, perm, w: Fp6Operand, out=None):
         torch = _torch()
@@ -734,19 +767,17 @@ class Fp6LayerPlan:
         _check(perm, torch.int32, "perm", 1)
         M, K = X.shape
         N = w.s8.shape[0]
-        K_n = K - w.n_out
         self.out = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
-        self.a = alloc_operand(M, K, w.n_out, w.group, X.device)
-        self.u6 = torch.empty(max(u6_bytes(M, K_n), 1), dtype=torch.uint8, device=X.device)
+        self.a = alloc_fp6_operand(M, K, w.n_out, w.group, X.device)
         need = quant_gemm_fp6_workspace_bytes(M, N, K, w.n_out, w.group)
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
         self._keep = (X, perm, w)
         L = lib()
         st = _stream()
-        self._q, self._qa = L.w4a4_quant_reorder_act, _quant_args(X, perm, self.a)
-        self._r, self._ra = L.w4a4_repack_u6, (_nz(self.a.q4), M, K_n, self.u6.data_ptr(), st)
-        af = Fp6Operand(self.u6, self.a.q8, self.a.s4, self.a.s8, K, w.n_out, w.group)
-        self._g, self._ga = L.w4a4_outlier_gemm_fp6, (*_fp6_args(af, w, self.out), st)
+        self._q = L.w4a4_quant_reorder_act_u6
+        self._qa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), M, K, w.n_out, w.group,
+                    self.a.u6.data_ptr(), _nz(self.a.q8), _nz(self.a.s4), _nz(self.a.s8), st)
+        self._g, self._ga = L.w4a4_outlier_gemm_fp6, (*_fp6_args(self.a, w, self.out), st)
         self._f = L.w4a4_quant_gemm_fp6
         self._fa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.u6), _nz(w.q8), _nz(w.s4),
                     _nz(w.s8), M, N, K, w.n_out, w.group, self.out.data_ptr(), self.out.stride(0) if M else N,
@@ -755,10 +786,7 @@ class Fp6LayerPlan:
     def produce(self):
         st = self._q(*self._qa)
         if st:
-            raise W4A4Error(st, "w4a4_quant_reorder_act")
-        st = self._r(*self._ra)
-        if st:
-            raise W4A4Error(st, "w4a4_repack_u6")
+            raise W4A4Error(st, "w4a4_quant_reorder_act_u6")
 
     def gemm(self):
         st = self._g(*self._ga)

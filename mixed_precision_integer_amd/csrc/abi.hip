@@ -53,9 +53,12 @@ struct NormArgs {
     float *rstd;
 };
 
+// q4: packed nibbles [rows, pitch4]; or, with u6 set (q4 unused), the head
+// as the FP6 GEMM's u6 operand (per-row scales only, no norm).
 w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t rows,
                        int32_t K, int32_t n_out, int32_t group, void *q4, void *q8, float *s4,
-                       float *s8, w4a4_stream stream, const NormArgs &norm = NormArgs{nullptr, 0.0f, nullptr}) {
+                       float *s8, w4a4_stream stream, const NormArgs &norm = NormArgs{nullptr, 0.0f, nullptr},
+                       void *u6 = nullptr) {
     w4a4_status st = check_shape(rows, K, n_out, group);
     if (st != W4A4_OK)
         return st;
@@ -67,10 +70,12 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
         return W4A4_OK;                         // empty call: pointers are not used
     if (!src)                                   // perm may be null: the identity order
         return W4A4_ERR_INVALID_ARG;
-    if ((K_n > 0 && (!q4 || !s4)) || (n_out > 0 && (!q8 || !s8)))
+    if (u6 && (group != 0 || norm.gamma))
+        return W4A4_ERR_UNSUPPORTED;
+    if ((K_n > 0 && (!(u6 ? u6 : q4) || !s4)) || (n_out > 0 && (!q8 || !s8)))
         return W4A4_ERR_INVALID_ARG;
     if (!aligned(src, 16) || ld % 8 != 0 || (perm && !aligned(perm, 16)) || (q4 && !aligned(q4, 16)) ||
-        (q8 && !aligned(q8, 16)) || (s4 && !aligned(s4, 4)) || (s8 && !aligned(s8, 4)))
+        (u6 && !aligned(u6, 16)) || (q8 && !aligned(q8, 16)) || (s4 && !aligned(s4, 4)) || (s8 && !aligned(s8, 4)))
         return W4A4_ERR_ALIGNMENT;
     if (norm.gamma && (!aligned(norm.gamma, 2) || (norm.rstd && !aligned(norm.rstd, 4))))
         return W4A4_ERR_ALIGNMENT;
@@ -84,7 +89,8 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
     a.K_n = K_n;
     a.group = group;
     a.G = G;
-    a.q4 = static_cast<uint8_t *>(q4);
+    a.q4 = u6 ? nullptr : static_cast<uint8_t *>(q4);
+    a.u6 = static_cast<uint8_t *>(u6);
     a.q8 = static_cast<int8_t *>(q8);
     a.s4 = s4;
     a.s8 = s8;
@@ -640,6 +646,13 @@ w4a4_status w4a4_repack_u6(const void *Q4, int32_t rows, int32_t K_n, void *U6, 
     return W4A4_OK;
 }
 
+w4a4_status w4a4_quant_reorder_act_u6(const void *X, int64_t ldx, const int32_t *perm, int32_t M, int32_t K,
+                                      int32_t n_out, int32_t group, void *Au6, void *Aq8, float *sa4,
+                                      float *sa8, w4a4_stream stream) {
+    return quant_rows(X, ldx, perm, M, K, n_out, group, nullptr, Aq8, sa4, sa8, stream,
+                      NormArgs{nullptr, 0.0f, nullptr}, Au6);
+}
+
 const char *w4a4_outlier_gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
     if (M <= 0 || N <= 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
         return nullptr;
@@ -716,26 +729,25 @@ w4a4_status w4a4_outlier_gemm_fp6_i32(const void *Au6, const void *Aq8, const fl
                     stream);
 }
 
-// Workspace of the fused FP6 call: Aq4 (nibbles) | Au6 | Aq8 | sa4 | sa8,
-// each 256-byte aligned; off[5] is the size.
-static void quant_gemm_fp6_layout(int32_t M, int32_t K, int32_t n_out, int32_t group, size_t off[6]) {
+// Workspace of the fused FP6 call: Au6 | Aq8 | sa4 | sa8, each 256-byte
+// aligned; off[4] is the size.
+static void quant_gemm_fp6_layout(int32_t M, int32_t K, int32_t n_out, int32_t group, size_t off[5]) {
     const int32_t K_n = K - n_out;
     const int32_t G = w4a4_num_groups(K_n, group);
     off[0] = 0;
-    off[1] = off[0] + round_up((int64_t)M * w4a4_pitch4_bytes(K_n), 256);
-    off[2] = off[1] + round_up(std::max<int64_t>(w4a4_u6_bytes(M, K_n), 0), 256);
-    off[3] = off[2] + round_up((int64_t)M * w4a4_pitch8_bytes(n_out), 256);
-    off[4] = off[3] + round_up((int64_t)M * (G > 0 ? G : 0) * 4, 256);
-    off[5] = off[4] + round_up((int64_t)M * 4, 256);
+    off[1] = off[0] + round_up(std::max<int64_t>(w4a4_u6_bytes(M, K_n), 0), 256);
+    off[2] = off[1] + round_up((int64_t)M * w4a4_pitch8_bytes(n_out), 256);
+    off[3] = off[2] + round_up((int64_t)M * (G > 0 ? G : 0) * 4, 256);
+    off[4] = off[3] + round_up((int64_t)M * 4, 256);
 }
 
 size_t w4a4_quant_gemm_fp6_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {
     (void)N;
     if (M < 0 || K <= 0 || n_out < 0 || n_out > K || w4a4_num_groups(K - n_out, group) < 0)
         return 0;
-    size_t off[6];
+    size_t off[5];
     quant_gemm_fp6_layout(M, K, n_out, group, off);
-    return off[5];
+    return off[4];
 }
 
 w4a4_status w4a4_quant_gemm_fp6(const void *X, int64_t ldx, const int32_t *perm, const void *Wu6,
@@ -762,18 +774,15 @@ w4a4_status w4a4_quant_gemm_fp6(const void *X, int64_t ldx, const int32_t *perm,
     const size_t need = w4a4_quant_gemm_fp6_workspace_bytes(M, N, K, n_out, group);
     if (workspace_bytes < need || !workspace)
         return W4A4_ERR_WORKSPACE;
-    size_t off[6];
+    size_t off[5];
     quant_gemm_fp6_layout(M, K, n_out, group, off);
     char *ws = static_cast<char *>(workspace);
-    void *Aq4 = ws + off[0];
-    void *Au6 = ws + off[1];
-    void *Aq8 = n_out > 0 ? ws + off[2] : nullptr;
-    float *sa4 = reinterpret_cast<float *>(ws + off[3]);
-    float *sa8 = reinterpret_cast<float *>(ws + off[4]);
-    st = quant_rows(X, ldx, perm, M, K, n_out, group, Aq4, Aq8, sa4, sa8, stream);
-    if (st != W4A4_OK)
-        return st;
-    st = w4a4_repack_u6(Aq4, M, K_n, Au6, stream);
+    void *Au6 = ws + off[0];
+    void *Aq8 = n_out > 0 ? ws + off[1] : nullptr;
+    float *sa4 = reinterpret_cast<float *>(ws + off[2]);
+    float *sa8 = reinterpret_cast<float *>(ws + off[3]);
+    st = quant_rows(X, ldx, perm, M, K, n_out, group, nullptr, Aq8, sa4, sa8, stream,
+                    NormArgs{nullptr, 0.0f, nullptr}, Au6);
     if (st != W4A4_OK)
         return st;
     return w4a4_outlier_gemm_fp6(Au6, Aq8, sa4, sa8, Wu6, Wq8, sw4, sw8, M, N, K, n_out, group, Y, ldy, stream);

@@ -15,7 +15,8 @@ struct QuantArgs {
     int64_t ld;
     const int32_t *perm;
     int32_t rows, K, n_out, K_n, group, G;
-    uint8_t *q4;          // [rows, pitch4]
+    uint8_t *q4;          // [rows, pitch4] packed nibbles, or nullptr when u6 is set
+    uint8_t *u6;          // the head as the FP6 GEMM's u6 operand instead of nibbles (group 0 only), or nullptr
     int8_t *q8;           // [rows, pitch8]
     float *s4;            // [rows, G]
     float *s8;            // [rows] or nullptr

@@ -139,6 +139,42 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// u6 operand of the FP6 GEMM: rows in blocks of 32 and channels in tiles of
+// 64 (two 32-channel chunks); the block of row block b and tile t is 1536
+// bytes at (b * T + t) * 1536, T = pitch4 / 32. Each chunk of a row is a
+// 192-bit image holding the code of channel i at bits 6i; image bytes 0..15
+// of row r's chunk h sit at 512 h + 16 r of the block, bytes 16..23 at
+// 1024 + 256 h + 8 r.
+constexpr int64_t kU6Block = 1536;
+
+// The E2M3 code of q / 2 for an integer-valued q in [-8, 8]: for m = |q|,
+// 4 m below 4 (0.5 is the subnormal 4/8, then 1 and 1.5 on exponent 1) and
+// 2 m + 8 from 4 on (exponents 2 and 3, mantissa steps of 2), i.e.
+// 2 m + min(2 m, 8); sign at bit 5; q = 0 (also -0) is code 0.
+__device__ __forceinline__ uint32_t e2m3_half_code(float q) {
+    const float m2 = 2.0f * __builtin_fabsf(q);
+    const uint32_t mag = (uint32_t)(m2 + __builtin_fminf(m2, 8.0f));
+    return q < 0.0f ? mag | 32u : mag;
+}
+
+// Store the 48 bits of head unit u (channels 8u .. 8u + 7, code i at bit 6i)
+// of row rr of a row block into their place in the chunk image: unit p = u % 4
+// of chunk h = (u / 4) % 2 of tile u / 8 covers image bytes 6p .. 6p + 5,
+// written as one 4-byte and one 2-byte store (both aligned).
+__device__ __forceinline__ void store_u6_unit(unsigned char *blocks, int u, int rr, uint64_t img) {
+    const int p = u & 3, h = (u >> 2) & 1;
+    unsigned char *blk = blocks + (int64_t)(u >> 3) * kU6Block;
+    unsigned char *lo = blk + 512 * h + 16 * rr, *hi = blk + 1024 + 256 * h + 8 * rr;
+    const uint32_t w0 = (uint32_t)img, w1 = (uint32_t)(img >> 32);
+    const bool odd = p & 1;
+    // 4-byte part: bytes 0..3 (p 0), 8..11 (p 1), 12..15 (p 2), hi 4..7 (p 3)
+    unsigned char *d4 = p == 0 ? lo : p == 1 ? lo + 8 : p == 2 ? lo + 12 : hi + 4;
+    // 2-byte part: bytes 4..5 (p 0), 6..7 (p 1), hi 0..1 (p 2), hi 2..3 (p 3)
+    unsigned char *d2 = p == 0 ? lo + 4 : p == 1 ? lo + 6 : p == 2 ? hi : hi + 2;
+    *reinterpret_cast<uint32_t *>(d4) = odd ? (w0 >> 16) | (w1 << 16) : w0;
+    *reinterpret_cast<uint16_t *>(d2) = (uint16_t)(odd ? w0 : w1);
+}
+
 // Static LDS for rows of up to KMAX channels: two row buffers (whole DMA
 // rounds), the group maxima of two consecutive rows and the wave maxima.
 template <int KMAX, int THREADS>
@@ -174,10 +210,11 @@ struct RowLds {
 // so no entry needs a bounds check of its own. One mask per unit replaces
 // the per-channel conditions, whose exec masks would otherwise stay live
 // across the row loop and spill.
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL>
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL, bool U6>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL && !NORM ? (FULL ? 6 : 8) : 4)))
 void quant_rows_kernel(QuantArgs a) {
     static_assert(!(FULL && WIDE_TAIL), "a full-row layout has one tail word per lane");
+    static_assert(!(U6 && (GROUPED || NORM)), "the u6 head is written for per-row scales without the norm");
     using L = RowLds<KMAX, THREADS>;
     constexpr int NW = THREADS / 64;
     constexpr int UMAX = (KMAX / 8 + THREADS - 1) / THREADS;    // head units (8 channels) per lane
@@ -202,7 +239,14 @@ void quant_rows_kernel(QuantArgs a) {
     const int U = (K_n + 7) / 8;
     const int W4 = (int)(a.pitch4 / 4), W8 = (int)(a.pitch8 / 4);
 
+    // First row of this workgroup. For the u6 head, the rows that are in
+    // flight together on one XCD are consecutive: workgroups are handed to
+    // the eight XCDs in turn, so workgroup w takes the place (w % 8) P + w / 8
+    // (P = grid / 8), and a 32-row block's partial-line stores meet in one
+    // L2 instead of being written back piecewise from eight.
     int row = blockIdx.x;
+    if (U6 && gridDim.x % 8 == 0)
+        row = (int)((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8);
     if (row < a.rows)
         issue_row(row, 0);
     if (row + (int)gridDim.x < a.rows)         // the second row streams in at once as well
@@ -452,6 +496,29 @@ void quant_rows_kernel(QuantArgs a) {
 
         // (4) INT4 head: codes + 8 as bytes, even channels in one dword and odd
         //     ones in another, then one nibble interleave and an xor with 8
+        //     (or, for the u6 operand, the FP6 E2M3 codes of q / 2)
+        if constexpr (U6) {
+            const int64_t T6 = a.pitch4 / 32;
+            unsigned char *blocks = a.u6 + (int64_t)(row >> 5) * T6 * kU6Block;
+            const int rr = row & 31;
+#pragma unroll
+            for (int i = 0; i < UMAX; ++i) {
+                const int u = i * THREADS + tid;
+                if (u < U) {
+                    uint64_t img = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float q0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), s_row, r_row));
+                        const float q1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), s_row, r_row));
+                        img |= (uint64_t)e2m3_half_code(q0) << (12 * k);
+                        img |= (uint64_t)e2m3_half_code(q1) << (12 * k + 6);
+                    }
+                    store_u6_unit(blocks, u, rr, img);
+                }
+            }
+            for (int u = U + tid; u < W4; u += THREADS)   // code 0 up to the end of the last tile
+                store_u6_unit(blocks, u, rr, 0);
+        } else {
         uint32_t *q4row = reinterpret_cast<uint32_t *>(a.q4 + (int64_t)row * a.pitch4);
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
@@ -478,6 +545,7 @@ void quant_rows_kernel(QuantArgs a) {
         }
         for (int u = U + tid; u < W4; u += THREADS)   // zero padding of the row pitch
             q4row[u] = 0u;
+        }
 
         // (5) INT8 tail: 4 codes -> one dword (zero past the last outlier)
         if (a.q8) {
@@ -502,6 +570,16 @@ void quant_rows_kernel(QuantArgs a) {
                     q8row[w] = word;
                 }
             }
+        }
+    }
+    if constexpr (U6) {
+        // rows past the last one, up to the end of its 32-row block: code 0
+        const int64_t T6 = a.pitch4 / 32;
+        const int rows_padded = (a.rows + 31) & ~31;
+        for (int zr = a.rows + (int)blockIdx.x; zr < rows_padded; zr += (int)gridDim.x) {
+            unsigned char *blocks = a.u6 + (int64_t)(zr >> 5) * T6 * kU6Block;
+            for (int u = tid; u < W4; u += THREADS)
+                store_u6_unit(blocks, u, zr & 31, 0);
         }
     }
 }
@@ -685,7 +763,7 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
 
 // Resident workgroups of one instantiation on the current device, queried on
 // first use (a launch then costs no runtime queries).
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL>
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL, bool U6>
 long resident_slots() {
     static std::atomic<long> cached[kMaxDevices];
     int dev = 0;
@@ -699,7 +777,7 @@ long resident_slots() {
     int cus = 256, per_cu = 1;
     if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL, U6>,
                                                      THREADS, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
     const long slots = (long)cus * per_cu;
@@ -708,30 +786,30 @@ long resident_slots() {
     return slots;
 }
 
-template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL>
+template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL, bool U6>
 hipError_t launch_tail(const QuantArgs &a, hipStream_t stream) {
-    const int grid = (int)std::min<long>(a.rows, resident_slots<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL>());
-    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL>), dim3(grid),
+    const int grid = (int)std::min<long>(a.rows, resident_slots<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL, U6>());
+    hipLaunchKernelGGL((quant_rows_kernel<KMAX, THREADS, GROUPED, WIDE_TAIL, NORM, FULL, U6>), dim3(grid),
                        dim3(THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int KMAX, int THREADS, bool GROUPED, bool NORM>
+template <int KMAX, int THREADS, bool GROUPED, bool NORM, bool U6>
 hipError_t launch(const QuantArgs &a, hipStream_t stream) {
     if (a.pitch8 / 4 > THREADS)                   // more than one tail word per lane
-        return launch_tail<KMAX, THREADS, GROUPED, true, NORM, false>(a, stream);
+        return launch_tail<KMAX, THREADS, GROUPED, true, NORM, false, U6>(a, stream);
     if (a.K % 8 == 0 && a.K_n % 8 == 0)           // every unit and tail word inside the row
-        return launch_tail<KMAX, THREADS, GROUPED, false, NORM, true>(a, stream);
-    return launch_tail<KMAX, THREADS, GROUPED, false, NORM, false>(a, stream);
+        return launch_tail<KMAX, THREADS, GROUPED, false, NORM, true, U6>(a, stream);
+    return launch_tail<KMAX, THREADS, GROUPED, false, NORM, false, U6>(a, stream);
 }
 
 // Row-length buckets: (longest row, lanes per workgroup).
-template <bool GROUPED, bool NORM>
+template <bool GROUPED, bool NORM, bool U6 = false>
 hipError_t launch_grouping(const QuantArgs &a, hipStream_t stream) {
-    if (a.K <= 4096) return launch<4096, 256, GROUPED, NORM>(a, stream);
-    if (a.K <= 8192) return launch<8192, 512, GROUPED, NORM>(a, stream);
-    if (a.K <= 16384) return launch<16384, 1024, GROUPED, NORM>(a, stream);
-    if (a.K <= 24576) return launch<24576, 1024, GROUPED, NORM>(a, stream);
+    if (a.K <= 4096) return launch<4096, 256, GROUPED, NORM, U6>(a, stream);
+    if (a.K <= 8192) return launch<8192, 512, GROUPED, NORM, U6>(a, stream);
+    if (a.K <= 16384) return launch<16384, 1024, GROUPED, NORM, U6>(a, stream);
+    if (a.K <= 24576) return launch<24576, 1024, GROUPED, NORM, U6>(a, stream);
     return hipErrorInvalidValue;
 }
 
@@ -759,6 +837,9 @@ int quant_rows_max_k() { return 24576; }
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream) {
     if (a.rows == 0)
         return hipSuccess;
+    if (a.u6)                                     // u6 head: per-row scales, no norm
+        return a.group == 0 && !a.gamma ? quant_impl::launch_grouping<false, false, true>(a, stream)
+                                        : hipErrorInvalidValue;
     if (a.gamma)                                  // the norm needs whole rows: row kernel
         return a.group > 0 ? quant_impl::launch_grouping<true, true>(a, stream)
                            : quant_impl::launch_grouping<false, true>(a, stream);

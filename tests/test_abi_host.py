@@ -115,6 +115,27 @@ def test_quant_rejects(kw, code):
     assert quant(**kw) == code
 
 
+def quant_u6(**kw):
+    args = dict(X=FAKE, ld=256, perm=FAKE, rows=4, K=256, n_out=16, group=0,
+                u6=FAKE, q8=FAKE, s4=FAKE, s8=FAKE)
+    args.update(kw)
+    return w4.lib().w4a4_quant_reorder_act_u6(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(group=128, K=272, ld=272), UNSUPPORTED),    # the u6 head takes per-row scales only
+    (dict(u6=None), INVALID), (dict(q8=None), INVALID), (dict(s4=None), INVALID),
+    (dict(u6=FAKE + 8), ALIGN), (dict(X=FAKE + 2), ALIGN), (dict(K=0), INVALID),
+    (dict(K=24584, ld=24584, n_out=0), UNSUPPORTED),
+])
+def test_quant_u6_rejects(kw, code):
+    assert quant_u6(**kw) == code
+
+
+def test_quant_u6_empty_is_ok():
+    assert quant_u6(rows=0, X=None, u6=None, q8=None, s4=None, s8=None) == 0
+
+
 def norm_quant(**kw):
     args = dict(X=FAKE, ld=256, gamma=FAKE, eps=1e-6, perm=FAKE, rows=4, K=256, n_out=16, group=0,
                 q4=FAKE, q8=FAKE, s4=FAKE, s8=FAKE, rstd=None)

@@ -62,6 +62,12 @@ def fp6_compare(oracle, X, W, outliers, group=0):
         want = oracle.pack_u6(q, w4.pitch4_bytes(K_n))
         assert op.u6.numel() == want.size == w4.u6_bytes(rows, K_n)
         assert np.array_equal(op.u6.cpu().numpy(), want), "u6 bytes"
+    # the producer that writes u6 directly: the same bytes, codes and scales
+    au = w4.quant_reorder_act_u6(Xd, perm, n_out, group)
+    assert torch.equal(au.u6, af.u6), "u6 producer differs from producer + repack"
+    assert torch.equal(au.s4, af.s4) and torch.equal(au.s8, af.s8)
+    if n_out:
+        assert torch.equal(au.q8, af.q8)
     acc4, acc8, ystar = oracle.linear_dense(qa, qw, group)
     g4, g8, y_exp = w4.outlier_gemm_fp6_i32(af, wf)
     y = w4.outlier_gemm_fp6(af, wf)
@@ -136,6 +142,37 @@ def test_fp6_full_size_workload(oracle, work):
                      f"{w4.outlier_gemm_fp6_kernel_name(work.M, work.N, work.K, work.n_out, work.group)}\n")
     sys.stderr.flush()
     fp6_compare(oracle, X, W, o, work.group)
+
+
+@pytest.mark.parametrize("M,K,n_out", [
+    (37, 640, 100),        # rows past M in the last block; tail of 100
+    (64, 1003, 11),        # K and K_n not multiples of 8 (ragged row end)
+    (1, 256, 0),           # one row, no outliers
+    (200, 4096, 128),      # the 4096 row bucket, several row blocks
+    (33, 22016, 256),      # the longest rows (24576 bucket)
+])
+def test_u6_producer(oracle, M, K, n_out):
+    """w4a4_quant_reorder_act_u6 against the oracle: u6 bytes (rows past M up
+    to the end of their block written as code 0 over garbage), INT8 tail and
+    scales bit-exact."""
+    X, _, o = wl.draw(M, 8, K, n_out, seed=M * 7 + K, outlier_factor=40.0)
+    perm_o = oracle.make_perm(K, o)
+    perm = torch.from_numpy(perm_o).to(DEV)
+    K_n = K - n_out
+    out = w4.alloc_fp6_operand(M, K, n_out, 0, DEV)
+    out.u6.fill_(0xFF)
+    ld = (K + 7) // 8 * 8                  # row pitch: a multiple of 8 halves
+    Xd = torch.zeros((M, ld), dtype=torch.float16, device=DEV)
+    Xd[:, :K] = torch.from_numpy(X).to(DEV)
+    a = w4.quant_reorder_act_u6(Xd[:, :K], perm, n_out, 0, out=out)
+    torch.cuda.synchronize()
+    q4, s4, q8, s8 = oracle.quantize_rows(X, perm_o, n_out, 0)
+    assert np.array_equal(a.u6.cpu().numpy(), oracle.pack_u6(q4, w4.pitch4_bytes(K_n)))
+    assert np.array_equal(a.s4.cpu().numpy(), s4)
+    assert np.array_equal(a.s8.cpu().numpy(), s8)
+    if n_out:
+        assert np.array_equal(a.q8.cpu().numpy()[:, :n_out], q8)
+        assert not a.q8.cpu().numpy()[:, n_out:].any()
 
 
 def test_fp6_rejects_group_mode():
