@@ -147,14 +147,28 @@ __device__ __forceinline__ void lds_barrier() {
 // 1024 + 256 h + 8 r.
 constexpr int64_t kU6Block = 1536;
 
-// The E2M3 code of q / 2 for an integer-valued q in [-8, 8]: for m = |q|,
-// 4 m below 4 (0.5 is the subnormal 4/8, then 1 and 1.5 on exponent 1) and
-// 2 m + 8 from 4 on (exponents 2 and 3, mantissa steps of 2), i.e.
-// 2 m + min(2 m, 8); sign at bit 5; q = 0 (also -0) is code 0.
-__device__ __forceinline__ uint32_t e2m3_half_code(float q) {
-    const float m2 = 2.0f * __builtin_fabsf(q);
-    const uint32_t mag = (uint32_t)(m2 + __builtin_fminf(m2, 8.0f));
-    return q < 0.0f ? mag | 32u : mag;
+// E2M3 codes of q / 2 for four offset codes c = q + 8 (bytes, 0..15): two
+// 8-entry byte tables (c < 8 and c >= 8) looked up by v_perm with c & 7,
+// then a third v_perm takes each byte from the second table where bit 3 of
+// c is set. Tables: q = -8..-1 -> 56 54 52 50 48 44 40 36; q = 0..7 -> 0 4 8
+// 12 16 18 20 22.
+__device__ __forceinline__ uint32_t e2m3_of_offset4(uint32_t c) {
+    const uint32_t sel = c & 0x07070707u;
+    const uint32_t neg = __builtin_amdgcn_perm(0x24282C30u, 0x32343638u, sel);
+    const uint32_t pos = __builtin_amdgcn_perm(0x16141210u, 0x0C080400u, sel);
+    return __builtin_amdgcn_perm(pos, neg, ((c >> 1) & 0x04040404u) | 0x03020100u);
+}
+
+// Four 6-bit codes in the low bits of four bytes -> 24 contiguous bits.
+__device__ __forceinline__ uint32_t pack6x4(uint32_t x) {
+    const uint32_t v = (x & 0x003F003Fu) | ((x >> 2) & 0x0FC00FC0u);   // fields at bits 0, 6, 16, 22
+    return (v & 0xFFFu) | ((v >> 4) & 0xFFF000u);
+}
+
+// The value of `v` in lane SRC (0..3) of this lane's quad.
+template <int SRC>
+__device__ __forceinline__ uint32_t quad_read(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, SRC * 0x55, 0xF, 0xF, false);   // quad_perm [SRC x 4]
 }
 
 // Store the 48 bits of head unit u (channels 8u .. 8u + 7, code i at bit 6i)
@@ -498,26 +512,43 @@ void quant_rows_kernel(QuantArgs a) {
         //     ones in another, then one nibble interleave and an xor with 8
         //     (or, for the u6 operand, the FP6 E2M3 codes of q / 2)
         if constexpr (U6) {
+            // The four units of a 32-channel chunk sit in one quad of lanes
+            // (units i * THREADS + tid, THREADS and W4 multiples of 4): each
+            // lane forms its unit's 48 bits, lane 0 of the quad collects the
+            // other three by DPP and stores the chunk image as 16 + 8 bytes.
+            // Units from U up to W4 hold zeros, i.e. code 0.
             const int64_t T6 = a.pitch4 / 32;
-            unsigned char *blocks = a.u6 + (int64_t)(row >> 5) * T6 * kU6Block;
-            const int rr = row & 31;
+            unsigned char *blocks = a.u6 + (int64_t)(row >> 5) * T6 * kU6Block + 16 * (row & 31);
 #pragma unroll
             for (int i = 0; i < UMAX; ++i) {
                 const int u = i * THREADS + tid;
-                if (u < U) {
-                    uint64_t img = 0;
+                if (u < W4) {                      // uniform over each quad
+                    uint32_t c[2] = {0u, 0u};      // offset codes q + 8, elements 0..3 and 4..7
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const float q0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), s_row, r_row));
-                        const float q1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), s_row, r_row));
-                        img |= (uint64_t)e2m3_half_code(q0) << (12 * k);
-                        img |= (uint64_t)e2m3_half_code(q1) << (12 * k + 6);
+                        const float q0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), s_row, r_row)) + 8.0f;
+                        const float q1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), s_row, r_row)) + 8.0f;
+                        c[k >> 1] = __builtin_amdgcn_cvt_pk_u8_f32(q0, 2 * (k & 1), c[k >> 1]);
+                        c[k >> 1] = __builtin_amdgcn_cvt_pk_u8_f32(q1, 2 * (k & 1) + 1, c[k >> 1]);
                     }
-                    store_u6_unit(blocks, u, rr, img);
+                    const uint32_t y0 = pack6x4(e2m3_of_offset4(c[0])), y1 = pack6x4(e2m3_of_offset4(c[1]));
+                    const uint32_t w0 = y0 | (y1 << 24), w1 = y1 >> 8;
+                    const uint32_t a1 = quad_read<1>(w0), b1 = quad_read<1>(w1);
+                    const uint32_t a2 = quad_read<2>(w0), b2 = quad_read<2>(w1);
+                    const uint32_t a3 = quad_read<3>(w0), b3 = quad_read<3>(w1);
+                    if ((tid & 3) == 0) {
+                        unsigned char *blk = blocks + (int64_t)(u >> 3) * kU6Block;
+                        const int h = (u >> 2) & 1;
+                        // image bytes 0..15: unit 0, unit 1, the first four bytes of unit 2
+                        *reinterpret_cast<uint4 *>(blk + 512 * h) =
+                            uint4{w0, __builtin_amdgcn_perm(a1, w1, 0x05040100u),
+                                  __builtin_amdgcn_perm(b1, a1, 0x05040302u), a2};
+                        // bytes 16..23: the last two bytes of unit 2, unit 3
+                        *reinterpret_cast<uint2 *>(blk + 1024 + 256 * h - 8 * (row & 31)) =
+                            uint2{__builtin_amdgcn_perm(a3, b2, 0x05040100u), __builtin_amdgcn_perm(b3, a3, 0x05040302u)};
+                    }
                 }
             }
-            for (int u = U + tid; u < W4; u += THREADS)   // code 0 up to the end of the last tile
-                store_u6_unit(blocks, u, rr, 0);
         } else {
         uint32_t *q4row = reinterpret_cast<uint32_t *>(a.q4 + (int64_t)row * a.pitch4);
 #pragma unroll
