@@ -61,14 +61,16 @@ WORKLOADS = {"tiny": wl.TINY, "qproj": wl.QPROJ_7B, "upproj": wl.UPPROJ_7B,
              "decode": wl.DECODE_65B, "downproj": wl.DOWNPROJ_65B}
 
 
-def work_counts(w, M, norm=False):
+def work_counts(w, M, norm=False, fp6=False):
     """Algorithmic ops and bytes of one layer call (zero padding not counted);
-    the norm-fused producer also reads the K fp16 norm weights."""
+    the norm-fused producer also reads the K fp16 norm weights. The INT4 head
+    is half a byte per code, or 6 bits on the FP6 path (its u6 operands)."""
     N, K, n_out, K_n = w.N, w.K, w.n_out, w.K_n
     G = (K_n // w.group if w.group else 1) if K_n else 0
     ops = 2 * M * N * K
-    w_bytes = N * K_n / 2 + N * n_out + 4 * N * G + 4 * N
-    a_bytes = M * K_n / 2 + M * n_out + 4 * M * G + 4 * M
+    code = 0.75 if fp6 else 0.5
+    w_bytes = N * K_n * code + N * n_out + 4 * N * G + 4 * N
+    a_bytes = M * K_n * code + M * n_out + 4 * M * G + 4 * M
     gemm_bytes = w_bytes + a_bytes + 2 * M * N
     producer_bytes = 2 * M * K + a_bytes + (2 * K if norm else 0)
     # one launch (quantizer inside the GEMM): fp16 tokens and the permutation
@@ -523,7 +525,7 @@ def main():
         norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
     fp6_fits = w4.outlier_gemm_fp6_kernel_name(M, w.N, w.K, w.n_out, w.group) is not None and M > 128
     if args.path == "fp6" and (not fp6_fits or args.norm):
-        raise SystemExit("the FP6 path takes per-row scales (group 0), over 128 rows, no fused RMSNorm")
+        raise SystemExit("the FP6 path takes per-row scales or 128-channel groups, over 128 rows, no fused RMSNorm")
     use_fp6 = args.path == "fp6" or (args.path == "auto" and fp6_fits and not args.norm)
     if use_fp6:
         wf6 = w4.to_fp6(wq)
@@ -535,8 +537,7 @@ def main():
         plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq), norm=norm) for _ in range(n_sets)]
     # Small decode batches run the layer as one launch (the quantizer, and the
     # RMSNorm with --norm, inside the GEMM's workgroups); every other shape as
-    # producer + GEMM (on the FP6 path: producer + repack of the activation
-    # codes + FP6 GEMM).
+    # producer + GEMM (on the FP6 path the producer writes the u6 operand).
     one_launch = not use_fp6 and \
         w4.quant_gemm_kernel_name(M, w.N, w.K, w.n_out, w.group) == "decode_fused_kernel" and \
         (not args.norm or M == 1)
@@ -604,7 +605,7 @@ def main():
         p.gemm()
     torch.cuda.synchronize()
     prod_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev])) if pev else None
-    ops, gemm_bytes, prod_bytes, one_bytes = work_counts(w, M, args.norm)
+    ops, gemm_bytes, prod_bytes, one_bytes = work_counts(w, M, args.norm, use_fp6)
     if one_launch:
         gemm_bytes = one_bytes
     value = ops / (ms_step * 1e-3) / 1e12
@@ -666,7 +667,7 @@ def main():
         "roofline": roof,
         "kernels": {
             "producer_us": prod_ms * 1e3 if prod_ms else None,
-            "producer_includes_u6_repack": bool(use_fp6),
+            "producer_writes_u6": bool(use_fp6),
             "producer_GBps": prod_bytes / (prod_ms * 1e-3) / 1e9 if prod_ms else None,
             "producer_hbm_frac": prod_bytes / (prod_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if prod_ms else None,
             "gemm_us": gemm_ms * 1e3,

@@ -70,7 +70,7 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
         return W4A4_OK;                         // empty call: pointers are not used
     if (!src)                                   // perm may be null: the identity order
         return W4A4_ERR_INVALID_ARG;
-    if (u6 && (group != 0 || norm.gamma))
+    if (u6 && norm.gamma)
         return W4A4_ERR_UNSUPPORTED;
     if ((K_n > 0 && (!(u6 ? u6 : q4) || !s4)) || (n_out > 0 && (!q8 || !s8)))
         return W4A4_ERR_INVALID_ARG;
@@ -706,7 +706,7 @@ static w4a4_status fp6_gemm(const void *Au6, const void *Aq8, const float *sa4, 
     a.pitch4 = p4;
     a.pitch8 = n_out > 0 ? w4a4_pitch8_bytes(n_out) : 0;
     a.ldy = ldy;
-    if (w4a4::launch_gemm_fp6(a, export_acc, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (w4a4::launch_gemm_fp6(a, group, export_acc, static_cast<hipStream_t>(stream)) != hipSuccess)
         return W4A4_ERR_HIP;
     return W4A4_OK;
 }

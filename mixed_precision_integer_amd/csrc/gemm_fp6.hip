@@ -42,18 +42,11 @@
 #include <algorithm>
 
 #include "w4a4.h"
-#include "gemm_common.h"
+#include "gemm_fp6_common.h"
 #include "gemm_fp6_internal.h"
 
 namespace w4a4 {
 namespace gemm_fp6_impl {
-
-constexpr int64_t kU6Block = 1536;                 // bytes of a 32-row x 64-channel u6 block
-
-using namespace gemm_impl;
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // repack: packed two's complement nibbles -> u6 planes
@@ -113,35 +106,16 @@ __global__ __launch_bounds__(256) void repack_u6_kernel(const uint8_t *q4, int64
 // ---------------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, WTM = 128, WTN = 128, FM = 4, FN = 4;
 constexpr int STAGES = 6;                          // ring depth
-constexpr int BLK = (int)kU6Block;                 // one 32-row block of a K-tile (64 channels)
 constexpr int A_OFF = 0, B_OFF = (BM / 32) * BLK;  // eight blocks of each operand per stage
 constexpr int STAGE = B_OFF + (BN / 32) * BLK;     // 24 KB
 constexpr int DPO = (BM / 32) * BLK / 16 / kThreads;   // DMA instructions per operand per K-tile
 constexpr int D = 2 * DPO;                         // DMA instructions per K-tile per lane
-constexpr int MAX_TAIL_TILES = 4;                  // INT8 tail <= 256 channels
 constexpr int TAIL_TILE = (BM + BN) * kTileBytes;  // 32 KB: A rows, then B rows (swizzled 64-byte rows)
 constexpr int SCALES = STAGES * STAGE;             // sa4, sa8, sw4, sw8 of the tile
 constexpr int LDS_BYTES = SCALES + 4 * BM * 4;
 static_assert(MAX_TAIL_TILES * TAIL_TILE <= STAGES * STAGE, "the tail fits in the ring");
 static_assert(STAGE == 24576 && DPO == 3, "stage layout");
 static_assert((STAGES - 1) * D <= 63, "vmcnt range");
-
-// One FP6 operand: 32 codes per lane in registers 0..5 (lo chunk, then the
-// hi bytes); the instruction reads only those six for FP6. Kept in VGPRs:
-// the AGPRs hold the sums.
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v6i __attribute__((ext_vector_type(6)));
-
-// One operand fragment: 64 FP6 values of one row, as six dwords (the
-// 16-byte lo part of the chunk image, then its 8-byte hi part).
-__device__ __forceinline__ v6i load_operand(const unsigned char *lo, const unsigned char *hi) {
-    const v4i l = *reinterpret_cast<const v4i *>(lo);
-    const v2i h = *reinterpret_cast<const v2i *>(hi);
-    v6i v;
-    v.s0123 = l;
-    v.s45 = h;
-    return v;
-}
 
 // acc += w^T x for one 32 x 32 block (both operands FP6 E2M3 holding q / 2,
 // block scale exponent 128 = 2^1 on each).
@@ -164,11 +138,6 @@ __device__ __forceinline__ float y_value(float acc4, int acc8, float s4, float s
     float y = __builtin_fmaf((float)acc8, s8, p4);
     asm volatile("" : "+v"(y));
     return y;
-}
-
-__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
-    const _Float16 l = (_Float16)lo, h = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
 template <bool EXPORT>
@@ -446,14 +415,19 @@ hipError_t launch_repack_u6(const uint8_t *q4, int64_t rows, int64_t pitch4, uin
 bool gemm_fp6_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
     (void)M;
     (void)N;
-    return group == 0 && K_n > 0 && w4a4_pitch8_bytes(n_out) / kTileBytes <= MAX_TAIL_TILES;
+    return (group == 0 || (group == 128 && K_n % 128 == 0)) && K_n > 0 &&
+           w4a4_pitch8_bytes(n_out) / kTileBytes <= MAX_TAIL_TILES;
 }
 
 const char *gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
-    return gemm_fp6_fits(M, N, K_n, n_out, group) ? "gemm_fp6_big_kernel<false>" : nullptr;
+    if (!gemm_fp6_fits(M, N, K_n, n_out, group))
+        return nullptr;
+    return group == 0 ? "gemm_fp6_big_kernel<false>" : "gemm_fp6_group_kernel<false>";
 }
 
-hipError_t launch_gemm_fp6(const Fp6GemmArgs &a, bool export_acc, hipStream_t stream) {
+hipError_t launch_gemm_fp6(const Fp6GemmArgs &a, int32_t group, bool export_acc, hipStream_t stream) {
+    if (group == 128)
+        return launch_gemm_fp6_group(a, export_acc, stream);
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (export_acc)
         hipLaunchKernelGGL(gemm_fp6_big_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream, a);

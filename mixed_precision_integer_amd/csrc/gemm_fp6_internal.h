@@ -28,6 +28,8 @@ hipError_t launch_repack_u6(const uint8_t *q4, int64_t rows, int64_t pitch4, uin
 // Shapes the FP6 GEMM takes, and the kernel it launches for them.
 bool gemm_fp6_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
 const char *gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
-hipError_t launch_gemm_fp6(const Fp6GemmArgs &a, bool export_acc, hipStream_t stream);
+hipError_t launch_gemm_fp6(const Fp6GemmArgs &a, int32_t group, bool export_acc, hipStream_t stream);
+// The group-scale kernel (group 128; gemm_fp6_group.hip).
+hipError_t launch_gemm_fp6_group(const Fp6GemmArgs &a, bool export_acc, hipStream_t stream);
 
 }  // namespace w4a4

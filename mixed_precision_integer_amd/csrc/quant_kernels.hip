@@ -228,7 +228,7 @@ template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool F
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL && !NORM ? (FULL ? 6 : 8) : 4)))
 void quant_rows_kernel(QuantArgs a) {
     static_assert(!(FULL && WIDE_TAIL), "a full-row layout has one tail word per lane");
-    static_assert(!(U6 && (GROUPED || NORM)), "the u6 head is written for per-row scales without the norm");
+    static_assert(!(U6 && NORM), "the u6 head is written without the norm");
     using L = RowLds<KMAX, THREADS>;
     constexpr int NW = THREADS / 64;
     constexpr int UMAX = (KMAX / 8 + THREADS - 1) / THREADS;    // head units (8 channels) per lane
@@ -523,11 +523,19 @@ void quant_rows_kernel(QuantArgs a) {
             for (int i = 0; i < UMAX; ++i) {
                 const int u = i * THREADS + tid;
                 if (u < W4) {                      // uniform over each quad
+                    float sc = s_row, rc = r_row;
+                    if (GROUPED && u < U) {
+                        const int t = (u * 8) / a.group;
+                        sc = __uint_as_float(gm[t]) / 7.0f;
+                        rc = recip_or_zero(sc);
+                        if ((u * 8) % a.group == 0)    // the group's first unit stores its scale
+                            a.s4[(int64_t)row * G + t] = sc;
+                    }
                     uint32_t c[2] = {0u, 0u};      // offset codes q + 8, elements 0..3 and 4..7
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const float q0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), s_row, r_row)) + 8.0f;
-                        const float q1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), s_row, r_row)) + 8.0f;
+                        const float q0 = __builtin_rintf(exact_quotient((float)lo_half(v[i][k]), sc, rc)) + 8.0f;
+                        const float q1 = __builtin_rintf(exact_quotient((float)hi_half(v[i][k]), sc, rc)) + 8.0f;
                         c[k >> 1] = __builtin_amdgcn_cvt_pk_u8_f32(q0, 2 * (k & 1), c[k >> 1]);
                         c[k >> 1] = __builtin_amdgcn_cvt_pk_u8_f32(q1, 2 * (k & 1) + 1, c[k >> 1]);
                     }
@@ -868,9 +876,12 @@ int quant_rows_max_k() { return 24576; }
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream) {
     if (a.rows == 0)
         return hipSuccess;
-    if (a.u6)                                     // u6 head: per-row scales, no norm
-        return a.group == 0 && !a.gamma ? quant_impl::launch_grouping<false, false, true>(a, stream)
-                                        : hipErrorInvalidValue;
+    if (a.u6) {                                   // u6 head (no norm): the row kernel
+        if (a.gamma)
+            return hipErrorInvalidValue;
+        return a.group > 0 ? quant_impl::launch_grouping<true, false, true>(a, stream)
+                           : quant_impl::launch_grouping<false, false, true>(a, stream);
+    }
     if (a.gamma)                                  // the norm needs whole rows: row kernel
         return a.group > 0 ? quant_impl::launch_grouping<true, true>(a, stream)
                            : quant_impl::launch_grouping<false, true>(a, stream);

@@ -123,7 +123,7 @@ def quant_u6(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(group=128, K=272, ld=272), UNSUPPORTED),    # the u6 head takes per-row scales only
+    (dict(group=64, K=272, ld=272), UNSUPPORTED),     # groups are multiples of 128
     (dict(u6=None), INVALID), (dict(q8=None), INVALID), (dict(s4=None), INVALID),
     (dict(u6=FAKE + 8), ALIGN), (dict(X=FAKE + 2), ALIGN), (dict(K=0), INVALID),
     (dict(K=24584, ld=24584, n_out=0), UNSUPPORTED),

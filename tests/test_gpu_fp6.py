@@ -75,7 +75,7 @@ def fp6_compare(oracle, X, W, outliers, group=0):
     y_i8 = w4.w4a4_outlier_gemm(a, wq)
     torch.cuda.synchronize()
     assert torch.equal(y, y_exp), "the accumulator export's launch wrote a different Y"
-    assert np.array_equal(g4[0].cpu().numpy(), acc4[0]), "acc4"
+    assert np.array_equal(g4.cpu().numpy(), acc4), "acc4 (every group)"
     if n_out:
         assert np.array_equal(g8.cpu().numpy(), acc8), "acc8"
     rel = check_y(y.cpu().numpy(), oracle.to_fp16(ystar))
@@ -101,6 +101,24 @@ CASES = [
 def test_fp6_parity(oracle, M, N, K, n_out):
     X, W, o = wl.draw(M, N, K, n_out, seed=M + 5 * N + K, outlier_factor=40.0)
     fp6_compare(oracle, X, W, o)
+
+
+GROUP_CASES = [
+    # M, N, K, n_out (group 128: K_n a multiple of 128)
+    (256, 128, 384, 128),           # one tile, two groups, two tail tiles
+    (300, 200, 1152, 128),          # ragged M and N, eight groups
+    (37, 520, 640, 0),              # one partial row tile, no outliers, four groups
+    (513, 257, 4352, 256),          # ragged by one, 32 groups, four tail tiles
+    (64, 96, 21760 + 256, 256),     # the longest K: 170 groups
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out", GROUP_CASES)
+def test_fp6_group_parity(oracle, M, N, K, n_out):
+    """The 128-channel group kernel: every group's exact integer sums, the
+    tail sums, Y, the fused call, the u6 producer with group scales."""
+    X, W, o = wl.draw(M, N, K, n_out, seed=M + 3 * N + K, outlier_factor=40.0)
+    fp6_compare(oracle, X, W, o, group=128)
 
 
 def test_fp6_extreme_codes(oracle):
@@ -135,7 +153,7 @@ def test_fp6_extreme_codes(oracle):
         check_y(y.cpu().numpy(), oracle.to_fp16(ystar))
 
 
-@pytest.mark.parametrize("work", [wl.UPPROJ_7B, wl.DOWNPROJ_65B], ids=lambda w: w.name)
+@pytest.mark.parametrize("work", [wl.UPPROJ_7B, wl.DOWNPROJ_65B, wl.QPROJ_7B], ids=lambda w: w.name)
 def test_fp6_full_size_workload(oracle, work):
     X, W, o = wl.draw_workload(work)
     sys.stderr.write(f"[gpu case] FP6 full size {work.name}: "
@@ -175,6 +193,7 @@ def test_u6_producer(oracle, M, K, n_out):
         assert not a.q8.cpu().numpy()[:, n_out:].any()
 
 
-def test_fp6_rejects_group_mode():
-    assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4096, 128, 128) is None
+def test_fp6_kernel_names():
+    assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4096, 128, 128) == "gemm_fp6_group_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(4096, 11008, 4096, 256, 0) == "gemm_fp6_big_kernel<false>"
+    assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4352, 256, 256) is None    # groups of 256
