@@ -467,8 +467,8 @@ def main():
                     help="instead of the layer, time the low-bit KV cache (quantize + gather)")
     ap.add_argument("--path", default="auto", choices=("auto", "fp6", "i8"),
                     help="prefill GEMM path: fp6 (INT4 codes q as FP6 E2M3 q / 2 on the FP6 matrix cores) or i8 "
-                         "(widened nibbles on the i8 matrix cores); auto takes fp6 wherever it applies "
-                         "and no RMSNorm is fused")
+                         "(widened nibbles on the i8 matrix cores); auto takes fp6 where it applies, "
+                         "no RMSNorm is fused and its tiles fill every CU")
     ap.add_argument("--norm", action="store_true",
                     help="producer fused with the preceding RMSNorm (eps 1e-6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -523,10 +523,15 @@ def main():
     norm = None
     if args.norm:
         norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
-    fp6_fits = w4.outlier_gemm_fp6_kernel_name(M, w.N, w.K, w.n_out, w.group) is not None and M > 128
+    # the FP6 kernels take 256 x 256 (per-row scales) or 256 x 128 (128-channel
+    # groups) tiles: the automatic choice wants at least one tile per CU
+    fp6_name = w4.outlier_gemm_fp6_kernel_name(M, w.N, w.K, w.n_out, w.group)
+    fp6_tiles = -(-M // 256) * -(-w.N // (256 if w.group == 0 else 128))
+    fp6_fits = fp6_name is not None and M > 128
+    fp6_auto = fp6_fits and fp6_tiles >= 256
     if args.path == "fp6" and (not fp6_fits or args.norm):
         raise SystemExit("the FP6 path takes per-row scales or 128-channel groups, over 128 rows, no fused RMSNorm")
-    use_fp6 = args.path == "fp6" or (args.path == "auto" and fp6_fits and not args.norm)
+    use_fp6 = args.path == "fp6" or (args.path == "auto" and fp6_auto and not args.norm)
     if use_fp6:
         wf6 = w4.to_fp6(wq)
 

@@ -34,7 +34,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 GEMM_SOURCES = ("gemm_kernels.hip", "gemm_big.hip", "gemm_group.hip", "gemm_decode.hip",
-                "gemm_decode_fused.hip", "gemm_common.h", "w4a4_internal.h")
+                "gemm_decode_fused.hip", "gemm_common.h", "w4a4_internal.h", "gemm_fp6.hip",
+                "gemm_fp6_group.hip", "gemm_fp6_common.h", "gemm_fp6_internal.h")
 COPY_KIB = 512 * 1024
 
 
