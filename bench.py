@@ -143,14 +143,14 @@ class ClockSampler:
 
 def traffic_record(workload_name, M):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter runs
-    (profiles/gemm_traffic.json), if they were taken on the current GEMM
-    sources; else None."""
+    (profiles/gemm_traffic.json), if they were taken on the current sources
+    of that kernel; else None."""
     from mixed_precision_integer_amd import profile_summary as ps
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(ps.traffic_key(workload_name, M))
-    if not rec or rec.get("gemm_sources_sha256_16") != ps.gemm_source_digest():
+    if not rec or rec.get("gemm_sources_sha256_16") != ps.gemm_source_digest(rec.get("kernel", "")):
         return None
     return rec.get("hbm_bytes_per_launch")
 

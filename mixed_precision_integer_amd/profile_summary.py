@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 runs of bench.py for the profiles/ folder.
 
-    python -m mixed_precision_integer_amd.profile_summary DIR WORKLOAD TITLE OUT.md [--m M]
+    python -m mixed_precision_integer_amd.profile_summary DIR WORKLOAD TITLE OUT.md [--m M] [--extra ARGS]
     python -m mixed_precision_integer_amd.profile_summary DIR - TITLE OUT.md --args "BENCH ARGS"
 
 DIR holds the output of five rocprofv3 runs of bench.py (the commands are
@@ -33,9 +33,19 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-GEMM_SOURCES = ("gemm_kernels.hip", "gemm_big.hip", "gemm_group.hip", "gemm_decode.hip",
-                "gemm_decode_fused.hip", "gemm_common.h", "w4a4_internal.h", "gemm_fp6.hip",
-                "gemm_fp6_group.hip", "gemm_fp6_common.h", "gemm_fp6_internal.h")
+# Sources that make up each GEMM kernel (by name prefix): a counter record is
+# valid while these are unchanged. Shared headers count for every kernel.
+SHARED_SOURCES = ("gemm_common.h", "w4a4_internal.h")
+KERNEL_SOURCES = (
+    ("gemm_fp6_big_kernel", ("gemm_fp6.hip", "gemm_fp6_common.h", "gemm_fp6_internal.h")),
+    ("gemm_fp6_group_kernel", ("gemm_fp6_group.hip", "gemm_fp6_common.h", "gemm_fp6_internal.h")),
+    ("gemm_big_kernel", ("gemm_big.hip", "gemm_kernels.hip")),
+    ("gemm_group_kernel", ("gemm_group.hip", "gemm_kernels.hip")),
+    ("gemm_decode", ("gemm_decode.hip", "gemm_kernels.hip")),
+    ("decode_fused_kernel", ("gemm_decode_fused.hip", "gemm_decode.hip", "gemm_kernels.hip")),
+    ("gemm_kernel", ("gemm_kernels.hip",)),
+)
+GEMM_SOURCES = SHARED_SOURCES + tuple(sorted({f for _, fs in KERNEL_SOURCES for f in fs}))
 COPY_KIB = 512 * 1024
 
 
@@ -65,11 +75,21 @@ def _code_only(text: str) -> str:
     return " ".join("".join(out).split())
 
 
-def gemm_source_digest() -> str:
-    """First 16 hex digits of the SHA-256 of the GEMM sources (code only, in a
-    fixed order)."""
+def kernel_sources(kernel: str):
+    """The source files of a GEMM kernel (its name with or without namespace
+    and template arguments), shared headers first."""
+    base = kernel.split("(")[0].split("<")[0].split("::")[-1].strip()
+    for prefix, files in KERNEL_SOURCES:
+        if base.startswith(prefix):
+            return SHARED_SOURCES + files
+    return GEMM_SOURCES
+
+
+def gemm_source_digest(kernel: str = "") -> str:
+    """First 16 hex digits of the SHA-256 of a GEMM kernel's sources (all GEMM
+    sources when no kernel is named; code only, in a fixed order)."""
     h = hashlib.sha256()
-    for name in GEMM_SOURCES:
+    for name in (kernel_sources(kernel) if kernel else GEMM_SOURCES):
         with open(os.path.join(HERE, "csrc", name), encoding="utf-8") as f:
             h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -108,7 +128,7 @@ def _bench_line(log: str):
     return json.loads(lines[-1])
 
 
-def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "") -> str:
+def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "", extra: str = "") -> str:
     stats = _csv(os.path.join(d, "trace"), "kernel_stats.csv")
     fetch = _pmc(os.path.join(d, "fetch"), "FETCH_SIZE")
     write = _pmc(os.path.join(d, "write"), "WRITE_SIZE")
@@ -119,7 +139,7 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "") -> s
     bj = _bench_line(os.path.join(d, "trace.log"))
     c = bj["config"]
     gemm_name = bj["roofline"]["kernel"]
-    run = f"python3 bench.py --workload {workload}{m_arg}"
+    run = f"python3 bench.py --workload {workload}{m_arg}{' ' + extra if extra else ''}"
     L = [f"# {title}\n",
          "Workload: `%s` (M=%d, N=%d, K=%d, n_out=%d, group=%d), seeded synthetic inputs resident in "
          "HBM, buffer sets rotated over more than 512 MB. GEMM kernel for this shape: `%s`.\n"
@@ -179,7 +199,7 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "") -> s
         p = os.path.join(ROOT, "profiles", "gemm_traffic.json")
         rec = json.load(open(p)) if os.path.exists(p) else {}
         rec[traffic_key(c["workload"], c["M"])] = {
-            "gemm_sources_sha256_16": gemm_source_digest(), "kernel": gk[0],
+            "gemm_sources_sha256_16": gemm_source_digest(gk[0]), "kernel": gk[0],
             "hbm_bytes_per_launch": traffic[gk[0]], "fetch_scale_kib": f_scale,
             "write_scale_kib": w_scale, "profile": out}
         with open(p, "w") as f:
@@ -261,13 +281,14 @@ def main():
     ap.add_argument("out")
     ap.add_argument("--m", default=None, help="the --m argument the runs were made with")
     ap.add_argument("--args", default=None, help="bench.py arguments of a kernel-summary run")
+    ap.add_argument("--extra", default="", help="further bench.py arguments of the runs (e.g. --path i8)")
     a = ap.parse_args()
     if a.args is not None:
         print(summarize_kernels(os.path.relpath(a.dir, ROOT) if os.path.isabs(a.dir) else a.dir, a.args,
                                 a.title, a.out))
         return
     print(summarize(os.path.relpath(a.dir, ROOT) if os.path.isabs(a.dir) else a.dir, a.workload, a.title,
-                    a.out, f" --m {a.m}" if a.m else ""))
+                    a.out, f" --m {a.m}" if a.m else "", a.extra))
 
 
 if __name__ == "__main__":
