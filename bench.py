@@ -141,18 +141,23 @@ class ClockSampler:
                 "max_mhz": float(max(self.samples)), "samples": len(self.samples), "source": self.source}
 
 
-def traffic_record(workload_name, M):
+def traffic_record(workload_name, M, kernel):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter runs
-    (profiles/gemm_traffic.json), if they were taken on the current sources
-    of that kernel; else None."""
+    (profiles/gemm_traffic.json), if they were taken of this kernel on its
+    current sources; else None."""
     from mixed_precision_integer_amd import profile_summary as ps
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(ps.traffic_key(workload_name, M))
-    if not rec or rec.get("gemm_sources_sha256_16") != ps.gemm_source_digest(rec.get("kernel", "")):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for key, rec in json.load(open(path)).items():
+        recorded = rec.get("kernel", "").split("(")[0].split("::")[-1]
+        if key != ps.traffic_key(workload_name, M, recorded):
+            continue
+        if recorded != kernel and not recorded.startswith(kernel + "<"):
+            continue
+        if rec.get("gemm_sources_sha256_16") == ps.gemm_source_digest(recorded):
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, X, W, outliers, budget_s, gamma=None, eps=0.0):
@@ -635,7 +640,7 @@ def main():
     else:
         roof["kernel"] = (w4.quant_gemm_kernel_name if one_launch else w4.outlier_gemm_kernel_name)(
             M, w.N, w.K, w.n_out, w.group)
-    roof["traffic"] = traffic_record(w.name, M)
+    roof["traffic"] = traffic_record(w.name, M, roof["kernel"])
 
     # the result is checked: the fused call against producer + GEMM (the same
     # bits whether the fused call takes one launch or two)

@@ -95,8 +95,9 @@ def gemm_source_digest(kernel: str = "") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_key(workload: str, M: int) -> str:
-    return f"{workload}:M={M}"
+def traffic_key(workload: str, M: int, kernel: str) -> str:
+    """Record key: workload, rows and the GEMM kernel's name (no namespace)."""
+    return f"{workload}:M={M}:{kernel.split('(')[0].split('::')[-1]}"
 
 
 def _csv(folder: str, suffix: str):
@@ -198,7 +199,7 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "", extr
     if gk:
         p = os.path.join(ROOT, "profiles", "gemm_traffic.json")
         rec = json.load(open(p)) if os.path.exists(p) else {}
-        rec[traffic_key(c["workload"], c["M"])] = {
+        rec[traffic_key(c["workload"], c["M"], gk[0])] = {
             "gemm_sources_sha256_16": gemm_source_digest(gk[0]), "kernel": gk[0],
             "hbm_bytes_per_launch": traffic[gk[0]], "fetch_scale_kib": f_scale,
             "write_scale_kib": w_scale, "profile": out}
