@@ -141,10 +141,10 @@ class ClockSampler:
                 "max_mhz": float(max(self.samples)), "samples": len(self.samples), "source": self.source}
 
 
-def traffic_record(workload_name, M, kernel):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs
-    (profiles/gemm_traffic.json), if they were taken of this kernel on its
-    current sources; else None."""
+def profile_record(workload_name, M, kernel):
+    """The committed counter record of this kernel on this workload
+    (profiles/gemm_traffic.json), if it was taken on the kernel's current
+    sources; else None."""
     from mixed_precision_integer_amd import profile_summary as ps
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
@@ -156,8 +156,29 @@ def traffic_record(workload_name, M, kernel):
         if recorded != kernel and not recorded.startswith(kernel + "<"):
             continue
         if rec.get("gemm_sources_sha256_16") == ps.gemm_source_digest(recorded):
-            return rec.get("hbm_bytes_per_launch")
+            return rec
     return None
+
+
+def traffic_record(workload_name, M, kernel):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs
+    (profiles/gemm_traffic.json), if they were taken of this kernel on its
+    current sources; else None."""
+    rec = profile_record(workload_name, M, kernel)
+    return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+def sclk_report(clock, rec, kernel):
+    """The GEMM kernel's achieved shader clock: GRBM_GUI_ACTIVE / 8 XCDs / its
+    duration, from the committed counter run of this kernel and workload (the
+    SMU's clock readings taken during the timed region are reported beside
+    it; on this machine they do not follow the shader clock)."""
+    smu = clock.report()
+    out = {"mhz": None, "source": None, "smu_samples": smu}
+    if rec and rec.get("sclk_mhz"):
+        out["mhz"] = rec["sclk_mhz"]
+        out["source"] = f"GRBM_GUI_ACTIVE / 8 XCDs / duration of {kernel}, profiles/{rec.get('profile')}"
+    return out
 
 
 def cpu_baseline(w, X, W, outliers, budget_s, gamma=None, eps=0.0):
@@ -687,7 +708,7 @@ def main():
             "gemm_GBps": gemm_bytes / (gemm_ms * 1e-3) / 1e9,
             "gemm_frac_of_int8_mfma_peak": ops / (gemm_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
         },
-        "sclk": clock.report(),
+        "sclk": sclk_report(clock, profile_record(w.name, M, roof["kernel"]), roof["kernel"]),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X, W, outliers, args.cpu_budget,

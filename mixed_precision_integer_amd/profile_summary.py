@@ -3,14 +3,16 @@
     python -m mixed_precision_integer_amd.profile_summary DIR WORKLOAD TITLE OUT.md [--m M] [--extra ARGS]
     python -m mixed_precision_integer_amd.profile_summary DIR - TITLE OUT.md --args "BENCH ARGS"
 
-DIR holds the output of five rocprofv3 runs of bench.py (the commands are
-written into the summary):
+DIR holds the output of five (or six) rocprofv3 runs of bench.py (the
+commands are written into the summary):
 
     DIR/trace   --kernel-trace --stats over the workload
     DIR/fetch   --pmc FETCH_SIZE over the workload
     DIR/write   --pmc WRITE_SIZE over the workload
     DIR/cfetch  --pmc FETCH_SIZE over a plain 512 MiB device copy
     DIR/cwrite  --pmc WRITE_SIZE over the same copy
+    DIR/clock   --pmc GRBM_GUI_ACTIVE over the workload (optional: the
+                achieved shader clock)
 
 The copy reads and writes exactly 512 MiB, so it gives the scale from the
 counters to bytes. The summary is written to profiles/OUT.md, and the GEMM's
@@ -47,6 +49,7 @@ KERNEL_SOURCES = (
 )
 GEMM_SOURCES = SHARED_SOURCES + tuple(sorted({f for _, fs in KERNEL_SOURCES for f in fs}))
 COPY_KIB = 512 * 1024
+MAX_SCLK_MHZ = 2400.0 * 1.01                 # the chip's peak engine clock, with rounding room
 
 
 def _code_only(text: str) -> str:
@@ -117,6 +120,24 @@ def _pmc(folder: str, counter: str):
             tot[r["Kernel_Name"]] += float(r["Counter_Value"])
             disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
     return {k: (tot[k] / len(disp[k]), len(disp[k])) for k in tot}
+
+
+def _clock(folder: str):
+    """Per kernel: mean GRBM_GUI_ACTIVE, mean duration (µs) and dispatches of
+    a GRBM_GUI_ACTIVE counter run, or {} when there is none."""
+    if not os.path.isdir(folder):
+        return {}
+    tot, dur = collections.defaultdict(float), collections.defaultdict(dict)
+    for r in _csv(folder, "counter_collection.csv"):
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            tot[r["Kernel_Name"]] += float(r["Counter_Value"])
+            dur[r["Kernel_Name"]][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = {}
+    for k, ds in dur.items():
+        if "w4a4" in k and ds:
+            n = len(ds)
+            out[k] = (tot[k] / n, sum(ds.values()) / n, n)
+    return out
 
 
 def _short(name: str) -> str:
@@ -191,6 +212,23 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "", extr
         traffic[_short(kn)] = rb + wb
         L.append(f"| `{_short(kn)}` | {n} | {fk:.0f} | {wk:.0f} | {rb / 1e6:.2f} | {wb / 1e6:.2f} | "
                  f"{(rb + wb) / 1e6:.2f} |")
+    clock = _clock(os.path.join(d, "clock"))
+    if clock:
+        L.append("\n## Achieved shader clock (rocprofv3 --pmc GRBM_GUI_ACTIVE)\n")
+        L.append("```\ntimeout -s KILL 120 rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d "
+                 f"{d}/clock -o p -- {run} --steps 5 --warmup 2 --no-cpu-baseline\n```\n")
+        L.append("GRBM_GUI_ACTIVE counts the cycles the graphics engine is busy, summed over the eight XCDs; "
+                 "divided by 8 and by the dispatch's duration (the counter run's own timestamps) it gives the "
+                 "average shader clock while the kernel ran.\n")
+        L.append("For dispatches of a few tens of µs the counter also takes in cycles around the dispatch, so "
+                 "the quotient can exceed the 2400 MHz the chip runs at; such values are marked and not "
+                 "recorded.\n")
+        L.append("| kernel | dispatches | GRBM_GUI_ACTIVE | average duration µs | clock MHz |")
+        L.append("|---|---|---|---|---|")
+        for kn, (g, dur, n) in clock.items():
+            mhz = g / 8 / dur
+            note = "" if mhz <= MAX_SCLK_MHZ else " (not a clock: above the chip's 2400)"
+            L.append(f"| `{_short(kn)}` | {n} | {g:.0f} | {dur:.2f} | {mhz:.0f}{note} |")
     text = "\n".join(L) + "\n"
     with open(os.path.join(ROOT, "profiles", out), "w") as f:
         f.write(text)
@@ -203,6 +241,11 @@ def summarize(d: str, workload: str, title: str, out: str, m_arg: str = "", extr
             "gemm_sources_sha256_16": gemm_source_digest(gk[0]), "kernel": gk[0],
             "hbm_bytes_per_launch": traffic[gk[0]], "fetch_scale_kib": f_scale,
             "write_scale_kib": w_scale, "profile": out}
+        ck_k = [kk for kk in clock if _short(kk) == gk[0]]
+        if ck_k:
+            g, dur, _ = clock[ck_k[0]]
+            if g / 8 / dur <= MAX_SCLK_MHZ:
+                rec[traffic_key(c["workload"], c["M"], gk[0])]["sclk_mhz"] = g / 8 / dur
         with open(p, "w") as f:
             json.dump(rec, f, indent=1, sort_keys=True)
             f.write("\n")
