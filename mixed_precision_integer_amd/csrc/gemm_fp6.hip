@@ -130,6 +130,12 @@ __device__ __forceinline__ void mma(v16f &acc, const v6i &w, const v6i &x) {
                  : "v"(w), "v"(x), "v"(128));
 }
 
+// acc8 += w^T x on the i8 matrix core (the INT8 tail), written as an
+// instruction so that the sums stay in VGPRs: the AGPRs hold the head's sums.
+__device__ __forceinline__ void mma_i8(v16i &acc, const v4i &w, const v4i &x) {
+    asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(acc) : "v"(w), "v"(x));
+}
+
 // y = acc4 * s4 + acc8 * s8: one product, one fused multiply-add, rounded to
 // fp32 before the fp16 conversion (the same bits in every launch).
 __device__ __forceinline__ float y_value(float acc4, int acc8, float s4, float s8) {
@@ -320,39 +326,48 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
         compiler_fence();
     }
 
-    // ---- epilogue, block by block -----------------------------------------------------
+    // ---- epilogue, a column of four blocks at a time ---------------------------------
+    // The four tail sums of a column are independent MFMA chains, issued side
+    // by side. Lane coordinates are taken afresh here so that nothing derived
+    // from them has to stay live (or spill) across the main loop.
+    uint32_t tid_e = threadIdx.x;
+    asm volatile("" : "+v"(tid_e));
+    const int lane_e = (int)(tid_e & 63), wave_e = (int)(tid_e >> 6);
+    const int wm_e = wave_e >> 1, wn_e = wave_e & 1, li_e = lane_e & 31, lh_e = lane_e >> 5;
     const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const bool vec_store = ((reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2)) & 7) == 0;
+    const bool interior = vec_store && row0 + BM <= a.M && col0 + BN <= a.N;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-        const int nl = wn * WTN + fn * 32 + lh * 4;       // tile-local first column of the lane
-        v4i pb8[MAX_TAIL_TILES][2];
+        const int nl = wn_e * WTN + fn * 32 + lh_e * 4;   // tile-local first column of the lane
+        v16i acc8[FM];
 #pragma unroll
-        for (int j = 0; j < MAX_TAIL_TILES; ++j)
+        for (int fm = 0; fm < FM; ++fm)
+            acc8[fm] = zi;
+#pragma unroll
+        for (int j = 0; j < MAX_TAIL_TILES; ++j) {
+            if (j >= T8)
+                break;                                     // uniform
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                uint4 p = uint4{0, 0, 0, 0};
-                if (j < T8)
-                    p = *reinterpret_cast<const uint4 *>(lds + j * TAIL_TILE + BM * kTileBytes +
-                                                        swz(wn * WTN + fn * 32 + li, 2 * s + lh));
-                pb8[j][s] = v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w};
-            }
+                const uint4 pb = *reinterpret_cast<const uint4 *>(lds + j * TAIL_TILE + BM * kTileBytes +
+                                                                  swz(wn_e * WTN + fn * 32 + li_e, 2 * s + lh_e));
+                const v4i b8 = v4i{(int)pb.x, (int)pb.y, (int)pb.z, (int)pb.w};
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int ml = wm * WTM + fm * 32 + li;
-            const int m = row0 + ml;
-            v16i acc8 = zi;
-#pragma unroll
-            for (int j = 0; j < MAX_TAIL_TILES; ++j) {
-                if (j >= T8)
-                    break;                                 // uniform
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const uint4 p = *reinterpret_cast<const uint4 *>(lds + j * TAIL_TILE + swz(ml, 2 * s + lh));
-                    acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(pb8[j][s], v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w},
-                                                                 acc8, 0, 0, 0);
+                for (int fm = 0; fm < FM; ++fm) {
+                    const uint4 pa = *reinterpret_cast<const uint4 *>(
+                        lds + j * TAIL_TILE + swz(wm_e * WTM + fm * 32 + li_e, 2 * s + lh_e));
+                    mma_i8(acc8[fm], b8, v4i{(int)pa.x, (int)pa.y, (int)pa.z, (int)pa.w});
                 }
             }
+        }
+        // the tail sums come from MFMAs the compiler does not see as such:
+        // their wait states before the VALU reads them
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int ml = wm_e * WTM + fm * 32 + li_e;
+            const int m = row0 + ml;
             if constexpr (EXPORT) {
                 // accumulator export (test path): this workgroup owns the sums
                 if (m < a.M) {
@@ -363,13 +378,14 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
                             const int64_t e = (int64_t)m * a.N + n;
                             a.acc4_out[e] = (int32_t)acc[fm][fn][r];
                             if (a.acc8_out)
-                                a.acc8_out[e] = acc8[r];
+                                a.acc8_out[e] = acc8[fm][r];
                         }
                     }
                 }
             }
             const float rs4 = sS[ml];
             const float rs8 = T8 > 0 ? sS[BM + ml] : 0.0f;    // tail scales are not loaded when T8 == 0
+            _Float16 *row = a.y + (int64_t)m * a.ldy + col0 + nl;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 c4 = *reinterpret_cast<const float4 *>(sS + 2 * BM + nl + q * 8);
@@ -379,17 +395,19 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v[e] = y_value(acc[fm][fn][q * 4 + e], acc8[q * 4 + e], rs4 * cs4[e], rs8 * cs8[e]);
-                const int n = col0 + nl + q * 8;
-                if (m < a.M) {
-                    _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
+                    v[e] = y_value(acc[fm][fn][q * 4 + e], acc8[fm][q * 4 + e], rs4 * cs4[e], rs8 * cs8[e]);
+                const uint2 packed = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
+                if (interior) {                            // uniform: the whole tile is inside Y
+                    *reinterpret_cast<uint2 *>(row + q * 8) = packed;
+                } else if (m < a.M) {
+                    const int n = col0 + nl + q * 8;
                     if (vec_store && n + 3 < a.N) {
-                        *reinterpret_cast<uint2 *>(dst) = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
+                        *reinterpret_cast<uint2 *>(row + q * 8) = packed;
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (n + e < a.N)
-                                dst[e] = (_Float16)v[e];
+                                row[q * 8 + e] = (_Float16)v[e];
                     }
                 }
             }
