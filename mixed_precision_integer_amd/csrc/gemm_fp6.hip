@@ -40,6 +40,7 @@
 //   16-register int32 accumulator; y = fp16(acc4 * (sa4 sw4) + acc8 * (sa8
 //   sw8)).
 #include <algorithm>
+#include <type_traits>
 
 #include "w4a4.h"
 #include "gemm_fp6_common.h"
@@ -123,17 +124,25 @@ static_assert((STAGES - 1) * D <= 63, "vmcnt range");
 // (li, lh) holds token row li and the columns 8 (r / 4) + 4 lh + r % 4.
 // Written as an instruction so that the accumulators stay in AGPRs and the
 // fragments in VGPRs with no copies; the compiler places the waits for the
-// fragments' LDS reads in front of it.
+// fragments' LDS reads in front of it, but not the two wait states an MFMA
+// needs after a VALU write of its operands. Here the operands come straight
+// from LDS reads (no moves in the main loop, whose first MFMA follows the
+// barrier and the DMA issue); the MFMAs elsewhere in these kernels, whose
+// operands the compiler may form with moves, carry an s_nop 1 of their own.
 __device__ __forceinline__ void mma(v16f &acc, const v6i &w, const v6i &x) {
     asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
                  : "+a"(acc)
                  : "v"(w), "v"(x), "v"(128));
 }
 
-// acc8 += w^T x on the i8 matrix core (the INT8 tail), written as an
-// instruction so that the sums stay in VGPRs: the AGPRs hold the head's sums.
+// acc8 += w^T x and acc8 = w^T x on the i8 matrix core (the INT8 tail),
+// written as instructions so that the sums stay in VGPRs: the AGPRs hold the
+// head's sums.
 __device__ __forceinline__ void mma_i8(v16i &acc, const v4i &w, const v4i &x) {
-    asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(acc) : "v"(w), "v"(x));
+    asm volatile("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(acc) : "v"(w), "v"(x));
+}
+__device__ __forceinline__ void mma_i8_0(v16i &acc, const v4i &w, const v4i &x) {
+    asm volatile("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, 0" : "=&v"(acc) : "v"(w), "v"(x));
 }
 
 // y = acc4 * s4 + acc8 * s8: one product, one fused multiply-add, rounded to
@@ -337,29 +346,61 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
     const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const bool vec_store = ((reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2)) & 7) == 0;
     const bool interior = vec_store && row0 + BM <= a.M && col0 + BN <= a.N;
+    // Two copies of the epilogue: one for tiles wholly inside Y (no checks),
+    // one for the edge tiles, each contiguous, so that a tile fetches only the
+    // instructions it runs (the unrolled epilogue is most of the kernel's code).
+    auto epilogue = [&](auto interior_tag) {
+    constexpr bool INTERIOR = decltype(interior_tag)::value;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         const int nl = wn_e * WTN + fn * 32 + lh_e * 4;   // tile-local first column of the lane
         v16i acc8[FM];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-            acc8[fm] = zi;
+            acc8[fm] = zi;                                 // (kept when there is no tail)
+        // all ten fragment reads of a tail tile are issued before its eight
+        // MFMAs (one LDS round trip per tile, not one per MFMA)
 #pragma unroll
         for (int j = 0; j < MAX_TAIL_TILES; ++j) {
             if (j >= T8)
                 break;                                     // uniform
+            v4i b8[2], a8[2][FM];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const uint4 pb = *reinterpret_cast<const uint4 *>(lds + j * TAIL_TILE + BM * kTileBytes +
-                                                                  swz(wn_e * WTN + fn * 32 + li_e, 2 * s + lh_e));
-                const v4i b8 = v4i{(int)pb.x, (int)pb.y, (int)pb.z, (int)pb.w};
+                b8[s] = *reinterpret_cast<const v4i *>(lds + j * TAIL_TILE + BM * kTileBytes +
+                                                       swz(wn_e * WTN + fn * 32 + li_e, 2 * s + lh_e));
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    a8[s][fm] = *reinterpret_cast<const v4i *>(lds + j * TAIL_TILE +
+                                                               swz(wm_e * WTM + fm * 32 + li_e, 2 * s + lh_e));
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm) {
-                    const uint4 pa = *reinterpret_cast<const uint4 *>(
-                        lds + j * TAIL_TILE + swz(wm_e * WTM + fm * 32 + li_e, 2 * s + lh_e));
-                    mma_i8(acc8[fm], b8, v4i{(int)pa.x, (int)pa.y, (int)pa.z, (int)pa.w});
+                    if (j == 0 && s == 0)
+                        mma_i8_0(acc8[fm], b8[s], a8[s][fm]);     // no VALU zero-fill to wait on
+                    else
+                        mma_i8(acc8[fm], b8[s], a8[s][fm]);
                 }
-            }
+        }
+        // the column's scales (the same for its four blocks) and the rows'
+        // scales, read while the tail MFMAs run
+        float cs4[16], cs8[16], rs4[FM], rs8[FM];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 c4 = *reinterpret_cast<const float4 *>(sS + 2 * BM + nl + q * 8);
+            const float4 c8 = *reinterpret_cast<const float4 *>(sS + 3 * BM + nl + q * 8);
+            cs4[4 * q] = c4.x, cs4[4 * q + 1] = c4.y, cs4[4 * q + 2] = c4.z, cs4[4 * q + 3] = c4.w;
+            // tail scales are not loaded when T8 == 0
+            cs8[4 * q] = T8 > 0 ? c8.x : 0.0f, cs8[4 * q + 1] = T8 > 0 ? c8.y : 0.0f;
+            cs8[4 * q + 2] = T8 > 0 ? c8.z : 0.0f, cs8[4 * q + 3] = T8 > 0 ? c8.w : 0.0f;
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int ml = wm_e * WTM + fm * 32 + li_e;
+            rs4[fm] = sS[ml];
+            rs8[fm] = T8 > 0 ? sS[BM + ml] : 0.0f;
         }
         // the tail sums come from MFMAs the compiler does not see as such:
         // their wait states before the VALU reads them
@@ -383,21 +424,18 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
                     }
                 }
             }
-            const float rs4 = sS[ml];
-            const float rs8 = T8 > 0 ? sS[BM + ml] : 0.0f;    // tail scales are not loaded when T8 == 0
             _Float16 *row = a.y + (int64_t)m * a.ldy + col0 + nl;
+            // the block's head sums are read from the AGPRs here, not earlier
+            asm volatile("" : "+a"(acc[fm][fn]));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(sS + 2 * BM + nl + q * 8);
-                const float4 c8v = *reinterpret_cast<const float4 *>(sS + 3 * BM + nl + q * 8);
-                const float4 c8 = T8 > 0 ? c8v : float4{0.0f, 0.0f, 0.0f, 0.0f};
-                const float cs4[4] = {c4.x, c4.y, c4.z, c4.w}, cs8[4] = {c8.x, c8.y, c8.z, c8.w};
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v[e] = y_value(acc[fm][fn][q * 4 + e], acc8[fm][q * 4 + e], rs4 * cs4[e], rs8 * cs8[e]);
+                    v[e] = y_value(acc[fm][fn][q * 4 + e], acc8[fm][q * 4 + e], rs4[fm] * cs4[q * 4 + e],
+                                   rs8[fm] * cs8[q * 4 + e]);
                 const uint2 packed = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
-                if (interior) {                            // uniform: the whole tile is inside Y
+                if constexpr (INTERIOR) {
                     *reinterpret_cast<uint2 *>(row + q * 8) = packed;
                 } else if (m < a.M) {
                     const int n = col0 + nl + q * 8;
@@ -413,6 +451,11 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
             }
         }
     }
+    };
+    if (interior)                                   // uniform
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
 }  // namespace gemm_fp6_impl

@@ -49,12 +49,12 @@ static_assert(MAX_TAIL_TILES * G_TAIL_TILE <= G_SCALES8, "the tail fits the ring
 // copies); block (fm, fn) takes the weight fragment as the first operand, so
 // lane (li, lh) holds token row li and the columns 8 (r / 4) + 4 lh + r % 4.
 __device__ __forceinline__ void mma(v16f &acc, const v6i &w, const v6i &x) {
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
                  : "+v"(acc)
                  : "v"(w), "v"(x), "v"(128));
 }
 __device__ __forceinline__ void mma0(v16f &acc, const v6i &w, const v6i &x) {
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
                  : "=&v"(acc)
                  : "v"(w), "v"(x), "v"(128));
 }
