@@ -45,6 +45,7 @@
 //   turned into two's complement nibbles with one xor per dword.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "quant_internal.h"
 
@@ -169,6 +170,51 @@ __device__ __forceinline__ uint32_t pack6x4(uint32_t x) {
 template <int SRC>
 __device__ __forceinline__ uint32_t quad_read(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, SRC * 0x55, 0xF, 0xF, false);   // quad_perm [SRC x 4]
+}
+
+// Maxima of non-negative floats as unsigned integers (their bit patterns
+// order the same way; no NaN canonicalization): DPP reads of another lane of
+// the same row (dpp_ctrl CTRL).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the wave of values that are already equal within each quad
+// (every lane gets it): two mirrors finish the rows of 16, readlane the wave.
+__device__ __forceinline__ uint32_t wave_max_of_quads(uint32_t v) {
+    v = dpp_max_u32<0x141>(v);                   // row_half_mirror: quads 0 <-> 1 of 8 lanes
+    v = dpp_max_u32<0x140>(v);                   // row_mirror: halves of a row of 16
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+    v = dpp_max_u32<0xB1>(v);
+    v = dpp_max_u32<0x4E>(v);
+    return wave_max_of_quads(v);
+}
+
+// fl32(a / d) for a non-negative fp16 value a and d = 7 or 127, from
+// r = fl32(1 / d): the same correction as exact_quotient, checked exhaustively
+// against the correctly rounded quotient for every finite fp16 a (an infinite
+// a keeps the division's infinite scale).
+__device__ __forceinline__ float div_small_const(float a, float d, float r) {
+#pragma clang fp contract(off)
+    const float q0 = a * r;
+    const float e = __builtin_fmaf(-q0, d, a);
+    const float q = __builtin_fmaf(e, r, q0);
+    return a == __builtin_inff() ? a : q;
+}
+
+// exact_quotient of an fp16 value (the conversion folds into the FMAs)
+__device__ __forceinline__ float exact_quotient_h(_Float16 x, float s, float r) {
+#pragma clang fp contract(off)
+    const float xf = (float)x;
+    const float q0 = __builtin_fmaf(xf, r, 0.0f);
+    const float e = __builtin_fmaf(-q0, s, xf);
+    return __builtin_fmaf(e, r, q0);
 }
 
 // Store the 48 bits of head unit u (channels 8u .. 8u + 7, code i at bit 6i)
@@ -800,6 +846,328 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
     }
 }
 
+// u6 producer with one 32-channel chunk per lane (per-row scales, or group
+// scales of 128 channels; K a multiple of 8).
+//
+// The row kernel's u6 form spends most of its time on VALU work: about a dozen
+// instructions per element for the quotient, the byte packing and the E2M3
+// table lookups. Here each lane owns one whole chunk of the u6 operand (head
+// channels 32c .. 32c + 31), so that gfx950's 32-value FP6 conversion
+// (v_cvt_scalef32_pk32_fp6_f16) forms the chunk's 192-bit image in one
+// instruction: with the integer codes q as fp16 inputs and a conversion scale
+// of 2 it writes the E2M3 code of q / 2 of value i at bits 6i (checked on
+// the device against the code table). Per element what remains is the exact
+// quotient (three mixed-precision FMAs), rint and half a conversion to fp16.
+// * Rows go global -> LDS by DMA in 16-byte pieces, with piece p stored in
+//   slot p ^ ((p >> 4) & 15): a lane gathers the 32 channels of its chunk,
+//   and without the swizzle the 64 lanes of a wave (chunks 64 bytes apart)
+//   would meet in 4 of the 16 bank quads on every 2-byte read.
+// * The LDS byte offsets of a lane's channels are the same for every row and
+//   are formed once per workgroup (channels past the head, or past the tail,
+//   point at 16 zero bytes after the row, so ragged chunks need no masks).
+// * Two row buffers, refilled two rows ahead: once a row is gathered into
+//   registers (second barrier) its buffer takes the row after next, so two
+//   rows are in flight while one is coded.
+// * Every store of a row is issued after the next row's wait, so that the
+//   only memory operations younger than the awaited row's DMA are the next
+//   row's DMA: the wait is vmcnt(rounds), not vmcnt(0), and never waits for
+//   the row in flight behind it.
+// * Group scales (128 channels = 4 chunks = one aligned quad of lanes) need
+//   two DPP steps; the per-row and tail maxima are reduced by DPP inside a
+//   wave and through LDS across waves.
+// * Codes are the definition's: q = rint(fl32(x / s)) by the exact quotient
+//   (Markstein's correction from r = fl32(1 / s), exact for every fp16 x),
+//   and the sign of a zero code is cleared before the conversion (E2M3 has a
+//   negative zero; the operand's zero code is +0).
+//
+// Register budget: 80 VGPRs (six waves per SIMD) for the short-row buckets,
+// which run several workgroups per CU; the 768-lane bucket runs one
+// workgroup per CU (two 48 KB buffers).
+template <int KMAX, int THREADS, bool GROUPED>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS >= 768 ? 3 : 6)))
+void quant_u6_chunk_kernel(QuantArgs a) {
+    typedef _Float16 half32 __attribute__((ext_vector_type(32)));
+    typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+    constexpr int NW = THREADS / 64;
+    constexpr int ROUND = THREADS * 16;
+    constexpr int XB = (KMAX * 2 + ROUND - 1) / ROUND * ROUND;
+    constexpr int BUF = XB + 16;                   // row slots, then 16 zero bytes
+    static_assert(THREADS * 32 >= KMAX, "one chunk per lane");
+    static_assert(BUF < 65536, "offsets within a buffer fit 16 bits");
+    __shared__ __align__(16) unsigned char xrow[2 * BUF];
+    __shared__ uint32_t red_h[NW], red_t[NW];   // fp16 bits of the wave maxima
+
+    const int K = a.K, K_n = a.K_n, n_out = a.n_out;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nfull = K / 8;                       // 16-byte pieces of a row
+    // the swizzle moves pieces within aligned runs of 16 slots: the DMA covers
+    // every slot up to the end of the last run
+    const int rounds = (((nfull + 15) & ~15) + THREADS - 1) / THREADS;
+    const int NCH = (int)(a.pitch4 / 16);          // chunks of the padded head
+    const int W8 = (int)(a.pitch8 / 4);
+    const int64_t T6 = a.pitch4 / 32;
+
+    auto issue_row = [&](int row, int b) {
+        const unsigned char *src = reinterpret_cast<const unsigned char *>(a.src + (int64_t)row * a.ld);
+        const uint32_t d = lds_addr(xrow + b * BUF) + wave_u * 1024;
+        for (int j = 0; j < rounds; ++j) {
+            const int slot = j * THREADS + tid;
+            const int piece = slot ^ ((slot >> 4) & 15);
+            dma16_stream(src, (uint32_t)(piece < nfull ? piece : 0) * 16, d + j * ROUND);
+        }
+    };
+    int row = blockIdx.x;
+    if (gridDim.x % 8 == 0)                        // consecutive rows on one XCD (see the row kernel)
+        row = (int)((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8);
+    if (row < a.rows)
+        issue_row(row, 0);
+    if (row + (int)gridDim.x < a.rows)
+        issue_row(row + gridDim.x, 1);
+    if (tid < 8)
+        reinterpret_cast<uint32_t *>(xrow + (tid >> 2) * BUF + XB)[tid & 3] = 0u;
+
+    // LDS byte offsets (within a buffer) of the lane's 32 head channels and 4
+    // tail channels, two per register. The permutation entries are all
+    // requested before any is used: head entries as 16-byte loads (K is a
+    // multiple of 8, so K / 4 whole int4s), tail entries one by one, indices
+    // clamped into the array and entries into the row.
+    auto slot_of = [&](int ch) -> uint32_t {
+        ch = min(max(ch, 0), K - 1);
+        const int piece = ch >> 3;
+        return (uint32_t)((piece ^ ((piece >> 4) & 15)) * 16 + (ch & 7) * 2);
+    };
+    // (kept unpacked where one workgroup per CU leaves registers to spare)
+    constexpr bool PACKED = THREADS < 768;
+    uint32_t off[16], toff[2], offu[PACKED ? 1 : 32], toffu[PACKED ? 1 : 4];
+    {
+        int e[32], t[4];
+        if (a.perm) {
+            const int4 *perm4 = reinterpret_cast<const int4 *>(a.perm);
+            const int last4 = K / 4 - 1;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int4 q = perm4[min(8 * tid + m, last4)];
+                e[4 * m] = q.x;
+                e[4 * m + 1] = q.y;
+                e[4 * m + 2] = q.z;
+                e[4 * m + 3] = q.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                t[k] = a.perm[min(K_n + 4 * tid + k, K - 1)];
+        } else {
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                e[k] = 32 * tid + k;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                t[k] = K_n + 4 * tid + k;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int j = 32 * tid + 2 * k;
+            off[k] = (j < K_n ? slot_of(e[2 * k]) : (uint32_t)XB) |
+                     ((j + 1 < K_n ? slot_of(e[2 * k + 1]) : (uint32_t)XB) << 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int j = K_n + 4 * tid + 2 * k;
+            toff[k] = ((tid < W8 && j < K) ? slot_of(t[2 * k]) : (uint32_t)XB) |
+                      (((tid < W8 && j + 1 < K) ? slot_of(t[2 * k + 1]) : (uint32_t)XB) << 16);
+        }
+        if constexpr (!PACKED) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                offu[2 * k] = off[k] & 0xFFFF;
+                offu[2 * k + 1] = off[k] >> 16;
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                toffu[2 * k] = toff[k] & 0xFFFF;
+                toffu[2 * k + 1] = toff[k] >> 16;
+            }
+        }
+    }
+    // the lane's places in a row block: image bytes 0..15 and 16..23 of its chunk
+    const uint32_t lo_off = (uint32_t)(tid >> 1) * (uint32_t)kU6Block + 512u * (uint32_t)(tid & 1);
+    const uint32_t hi_off = (uint32_t)(tid >> 1) * (uint32_t)kU6Block + 1024u + 256u * (uint32_t)(tid & 1);
+
+    // the previous row's results, stored after the next wait
+    int prow = -1;
+    u32x6 img = {0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t word = 0;
+    float psc = 0.0f, ps8 = 0.0f;
+    auto store_prev = [&]() {
+        if (prow < 0)
+            return;
+        if (tid < NCH) {
+            // uniform row-block base + the lane's own 32-bit offsets (the
+            // stores then need no 64-bit lane pointers)
+            unsigned char *rowblk = a.u6 + (int64_t)(prow >> 5) * T6 * kU6Block;
+            const int rr = prow & 31;
+            *reinterpret_cast<uint4 *>(rowblk + 16 * rr + lo_off) = uint4{img[0], img[1], img[2], img[3]};
+            *reinterpret_cast<uint2 *>(rowblk + 8 * rr + hi_off) = uint2{img[4], img[5]};
+        }
+        if (GROUPED) {
+            if (tid < NCH && (tid & 3) == 0 && 32 * tid < K_n)
+                a.s4[(int64_t)prow * a.G + (tid >> 2)] = psc;
+        } else if (tid == 0 && a.G > 0) {
+            a.s4[prow] = psc;
+        }
+        if (tid == 0 && a.s8)
+            a.s8[prow] = n_out > 0 ? ps8 : 0.0f;
+        if (tid < W8 && a.q8) {
+            uint32_t o8 = 4u * (uint32_t)tid;   // (kept apart from the base: no 64-bit lane pointer)
+            asm volatile("" : "+v"(o8));
+            *reinterpret_cast<uint32_t *>(a.q8 + (int64_t)prow * a.pitch8 + o8) = word;
+        }
+    };
+
+    // one row from buffer B (a constant, so that the buffer base is the LDS
+    // reads' immediate offset)
+    auto do_row = [&](auto b_tag) {
+        constexpr int B = decltype(b_tag)::value;
+        // (1) this row's DMA has landed (only the next row's DMA, issued
+        //     after it, may still be in flight), in every wave
+        asm volatile("" ::: "memory");
+        switch (rounds) {                          // s_waitcnt takes an immediate: vmcnt(rounds)
+            case 1: __builtin_amdgcn_s_waitcnt(0xF71); break;
+            case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+            case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
+            case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+            default: __builtin_amdgcn_s_waitcnt(kWaitAll); break;
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        store_prev();
+
+        // (2) gather the chunk and the tail word; maxima (the offsets are
+        //     unpacked here, not kept unpacked across the loop)
+        const unsigned char *xb = xrow + B * BUF;
+        half2 v[16], tv[2];
+        if constexpr (PACKED) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                asm volatile("" : "+v"(off[k]));
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                asm volatile("" : "+v"(toff[k]));
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                v[p].x = *reinterpret_cast<const _Float16 *>(xb + (off[p] & 0xFFFF));
+                v[p].y = *reinterpret_cast<const _Float16 *>(xb + (off[p] >> 16));
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                tv[p].x = *reinterpret_cast<const _Float16 *>(xb + (toff[p] & 0xFFFF));
+                tv[p].y = *reinterpret_cast<const _Float16 *>(xb + (toff[p] >> 16));
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                v[p].x = *reinterpret_cast<const _Float16 *>(xb + offu[2 * p]);
+                v[p].y = *reinterpret_cast<const _Float16 *>(xb + offu[2 * p + 1]);
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                tv[p].x = *reinterpret_cast<const _Float16 *>(xb + toffu[2 * p]);
+                tv[p].y = *reinterpret_cast<const _Float16 *>(xb + toffu[2 * p + 1]);
+            }
+        }
+        // |x| as fp16 bits: non-negative values order like unsigned integers
+        typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
+        const ushort2_t mag = {0x7FFF, 0x7FFF};
+        ushort2_t m2 = __builtin_bit_cast(ushort2_t, v[0]) & mag;
+#pragma unroll
+        for (int p = 1; p < 16; ++p)
+            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(ushort2_t, v[p]) & mag);
+        const ushort2_t t2 = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, tv[0]) & mag,
+                                                       __builtin_bit_cast(ushort2_t, tv[1]) & mag);
+        // (fp16 bits of |x| widen to an order-preserving integer: the maxima
+        // are taken on the bits and converted once)
+        uint32_t hm = __builtin_elementwise_max(m2.x, m2.y);
+        hm = dpp_max_u32<0xB1>(hm);               // quad: lanes ^ 1
+        hm = dpp_max_u32<0x4E>(hm);               // quad: lanes ^ 2 (one 128-channel group)
+        if (!GROUPED)
+            hm = wave_max_of_quads(hm);
+        const bool tail_wave = (int)wave_u * 64 < W8;   // uniform: the wave holds tail words
+        uint32_t tm = 0;
+        if (tail_wave)
+            tm = wave_max_dpp(__builtin_elementwise_max(t2.x, t2.y));
+        if (lane == 0) {
+            if (!GROUPED)
+                red_h[wave_u] = hm;
+            red_t[wave_u] = tm;
+        }
+        // (3) every wave has its values: the buffer takes the row after next
+        lds_barrier();
+        if (row + 2 * (int)gridDim.x < a.rows)
+            issue_row(row + 2 * gridDim.x, B);
+
+        uint32_t rb = hm, tb = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            if (!GROUPED)
+                rb = max(rb, red_h[w]);
+            tb = max(tb, red_t[w]);
+        }
+        const float ra = (float)__builtin_bit_cast(_Float16, (uint16_t)rb);
+        const float ta = (float)__builtin_bit_cast(_Float16, (uint16_t)tb);
+        const float sc = div_small_const(ra, 7.0f, 1.0f / 7.0f), rc = recip_or_zero(sc);
+        const float s8 = div_small_const(ta, 127.0f, 1.0f / 127.0f);
+
+        // (4) head codes -> E2M3 image of the chunk (waves wholly past the
+        //     head skip it; other lanes past it hold zeros, never stored)
+        if ((int)wave_u * 64 < NCH) {
+            half32 q;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                const float c0 = __builtin_rintf(exact_quotient_h(v[p].x, sc, rc));
+                const float c1 = __builtin_rintf(exact_quotient_h(v[p].y, sc, rc));
+                const half2 h = __builtin_bit_cast(half2, __builtin_amdgcn_cvt_pkrtz(c0, c1)) + (half2){0, 0};
+                q[2 * p] = h.x;
+                q[2 * p + 1] = h.y;
+            }
+            img = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(q, 2.0f);
+        }
+        // (5) INT8 tail word (waves that hold tail words)
+        if (tail_wave) {
+            const float r8 = recip_or_zero(s8);
+            word = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const _Float16 x = (k & 1) ? tv[k >> 1].y : tv[k >> 1].x;
+                const int qi = (int)__builtin_rintf(exact_quotient_h(x, s8, r8));
+                word |= (uint32_t)(qi & 0xFF) << (8 * k);
+            }
+        }
+        psc = sc;
+        ps8 = s8;
+        prow = row;
+        row += gridDim.x;
+    };
+    while (row < a.rows) {
+        do_row(std::integral_constant<int, 0>{});
+        if (row >= a.rows)
+            break;
+        do_row(std::integral_constant<int, 1>{});
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    store_prev();
+
+    // rows past the last one, up to the end of its 32-row block: code 0
+    const int rows_padded = (a.rows + 31) & ~31;
+    for (int zr = a.rows + (int)blockIdx.x; zr < rows_padded; zr += (int)gridDim.x)
+        if (tid < NCH) {
+            unsigned char *rowblk = a.u6 + (int64_t)(zr >> 5) * T6 * kU6Block;
+            const int rr = zr & 31;
+            *reinterpret_cast<uint4 *>(rowblk + 16 * rr + lo_off) = uint4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<uint2 *>(rowblk + 8 * rr + hi_off) = uint2{0u, 0u};
+        }
+}
+
 // Resident workgroups of one instantiation on the current device, queried on
 // first use (a launch then costs no runtime queries).
 template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL, bool U6>
@@ -823,6 +1191,53 @@ long resident_slots() {
     if (dev >= 0)
         cached[dev].store(slots, std::memory_order_relaxed);
     return slots;
+}
+
+template <int KMAX, int THREADS, bool GROUPED>
+long u6_chunk_slots() {
+    static std::atomic<long> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        dev = -1;
+    if (dev >= 0) {
+        const long c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 256, per_cu = 1;
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_u6_chunk_kernel<KMAX, THREADS, GROUPED>, THREADS, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const long slots = (long)cus * per_cu;
+    if (dev >= 0)
+        cached[dev].store(slots, std::memory_order_relaxed);
+    return slots;
+}
+
+template <int KMAX, int THREADS, bool GROUPED>
+hipError_t launch_u6_chunk_bucket(const QuantArgs &a, hipStream_t stream) {
+    const int grid = (int)std::min<long>(a.rows, u6_chunk_slots<KMAX, THREADS, GROUPED>());
+    hipLaunchKernelGGL((quant_u6_chunk_kernel<KMAX, THREADS, GROUPED>), dim3(grid), dim3(THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+// The chunk kernel takes K a multiple of 8, per-row or 128-channel group
+// scales and a tail of at most one 4-channel word per lane; false: use the
+// row kernel.
+template <bool GROUPED>
+bool launch_u6_chunk(const QuantArgs &a, hipStream_t stream, hipError_t *err) {
+    if (a.K % 8 != 0 || (GROUPED && a.group != 128))
+        return false;
+    const int64_t words = a.pitch8 / 4;
+    if (a.K <= 4096 && words <= 128) *err = launch_u6_chunk_bucket<4096, 128, GROUPED>(a, stream);
+    else if (a.K <= 8192 && words <= 256) *err = launch_u6_chunk_bucket<8192, 256, GROUPED>(a, stream);
+    else if (a.K <= 16384 && words <= 512) *err = launch_u6_chunk_bucket<16384, 512, GROUPED>(a, stream);
+    else if (a.K <= 24576 && words <= 768) *err = launch_u6_chunk_bucket<24576, 768, GROUPED>(a, stream);
+    else return false;
+    return true;
 }
 
 template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool FULL, bool U6>
@@ -876,9 +1291,13 @@ int quant_rows_max_k() { return 24576; }
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream) {
     if (a.rows == 0)
         return hipSuccess;
-    if (a.u6) {                                   // u6 head (no norm): the row kernel
+    if (a.u6) {                                   // u6 head (no norm): chunk kernel, else the row kernel
         if (a.gamma)
             return hipErrorInvalidValue;
+        hipError_t err = hipSuccess;
+        if (a.group > 0 ? quant_impl::launch_u6_chunk<true>(a, stream, &err)
+                        : quant_impl::launch_u6_chunk<false>(a, stream, &err))
+            return err;
         return a.group > 0 ? quant_impl::launch_grouping<true, false, true>(a, stream)
                            : quant_impl::launch_grouping<false, false, true>(a, stream);
     }

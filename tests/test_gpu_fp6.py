@@ -162,31 +162,43 @@ def test_fp6_full_size_workload(oracle, work):
     fp6_compare(oracle, X, W, o, work.group)
 
 
-@pytest.mark.parametrize("M,K,n_out", [
-    (37, 640, 100),        # rows past M in the last block; tail of 100
-    (64, 1003, 11),        # K and K_n not multiples of 8 (ragged row end)
-    (1, 256, 0),           # one row, no outliers
-    (200, 4096, 128),      # the 4096 row bucket, several row blocks
-    (33, 22016, 256),      # the longest rows (24576 bucket)
+@pytest.mark.parametrize("M,K,n_out,group", [
+    (37, 640, 100, 0),         # rows past M in the last block; tail of 100, ragged head chunk
+    (64, 1003, 11, 0),         # K and K_n not multiples of 8 (ragged row end: the row kernel)
+    (1, 256, 0, 0),            # one row, no outliers
+    (200, 4096, 128, 0),       # the 4096 row bucket, several row blocks
+    (3000, 4096, 512, 0),      # more rows than resident workgroups; a tail word on every lane
+    (300, 8192, 64, 0),        # the 8192 bucket
+    (70, 16384, 7, 0),         # the 16384 bucket, ragged head and tail words
+    (33, 22016, 256, 0),       # the longest rows (24576 bucket)
+    (5, 24576, 3072, 0),       # the longest row; one tail word per lane of the 768-lane workgroup
+    (37, 768, 128, 128),       # 128-channel group scales
+    (2048, 4096, 128, 128),    # q_proj-shaped rows with group scales
+    (9, 24576, 128, 128),      # group scales on the longest rows
 ])
-def test_u6_producer(oracle, M, K, n_out):
+def test_u6_producer(oracle, M, K, n_out, group):
     """w4a4_quant_reorder_act_u6 against the oracle: u6 bytes (rows past M up
     to the end of their block written as code 0 over garbage), INT8 tail and
     scales bit-exact."""
+    sys.stderr.write(f"[gpu case] u6 producer M={M} K={K} n_out={n_out} group={group}\n")
+    sys.stderr.flush()
     X, _, o = wl.draw(M, 8, K, n_out, seed=M * 7 + K, outlier_factor=40.0)
     perm_o = oracle.make_perm(K, o)
     perm = torch.from_numpy(perm_o).to(DEV)
     K_n = K - n_out
-    out = w4.alloc_fp6_operand(M, K, n_out, 0, DEV)
+    out = w4.alloc_fp6_operand(M, K, n_out, group, DEV)
     out.u6.fill_(0xFF)
+    out.s4.fill_(float("nan"))
+    if n_out:
+        out.q8.fill_(0x55)
     ld = (K + 7) // 8 * 8                  # row pitch: a multiple of 8 halves
     Xd = torch.zeros((M, ld), dtype=torch.float16, device=DEV)
     Xd[:, :K] = torch.from_numpy(X).to(DEV)
-    a = w4.quant_reorder_act_u6(Xd[:, :K], perm, n_out, 0, out=out)
+    a = w4.quant_reorder_act_u6(Xd[:, :K], perm, n_out, group, out=out)
     torch.cuda.synchronize()
-    q4, s4, q8, s8 = oracle.quantize_rows(X, perm_o, n_out, 0)
+    q4, s4, q8, s8 = oracle.quantize_rows(X, perm_o, n_out, group)
     assert np.array_equal(a.u6.cpu().numpy(), oracle.pack_u6(q4, w4.pitch4_bytes(K_n)))
-    assert np.array_equal(a.s4.cpu().numpy(), s4)
+    assert np.array_equal(a.s4.cpu().numpy().reshape(s4.shape), s4)
     assert np.array_equal(a.s8.cpu().numpy(), s8)
     if n_out:
         assert np.array_equal(a.q8.cpu().numpy()[:, :n_out], q8)
