@@ -868,10 +868,13 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
 // * Two row buffers, refilled two rows ahead: once a row is gathered into
 //   registers (second barrier) its buffer takes the row after next, so two
 //   rows are in flight while one is coded.
-// * Every store of a row is issued after the next row's wait, so that the
-//   only memory operations younger than the awaited row's DMA are the next
-//   row's DMA: the wait is vmcnt(rounds), not vmcnt(0), and never waits for
-//   the row in flight behind it.
+// * Every store of a row is issued after the next row's wait and before the
+//   DMA of the row after it, so the only memory operations younger than an
+//   awaited row's DMA are one row's stores and the DMA behind it: the wait
+//   is vmcnt(rounds) (never for the row in flight behind), and vmcnt(0) for
+//   a workgroup's last row, which has no DMA behind it.
+// * The tail words and the per-row scale stores go to the last lanes, whose
+//   waves hold few or no head chunks.
 // * Group scales (128 channels = 4 chunks = one aligned quad of lanes) need
 //   two DPP steps; the per-row and tail maxima are reduced by DPP inside a
 //   wave and through LDS across waves.
@@ -907,6 +910,9 @@ void quant_u6_chunk_kernel(QuantArgs a) {
     const int NCH = (int)(a.pitch4 / 16);          // chunks of the padded head
     const int W8 = (int)(a.pitch8 / 4);
     const int64_t T6 = a.pitch4 / 32;
+    // tail words go to the last W8 lanes (whose waves hold fewer head
+    // chunks), and so do the per-row scale stores
+    const int tw = tid - (THREADS - W8);
 
     auto issue_row = [&](int row, int b) {
         const unsigned char *src = reinterpret_cast<const unsigned char *>(a.src + (int64_t)row * a.ld);
@@ -955,14 +961,14 @@ void quant_u6_chunk_kernel(QuantArgs a) {
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                t[k] = a.perm[min(K_n + 4 * tid + k, K - 1)];
+                t[k] = a.perm[min(K_n + 4 * max(tw, 0) + k, K - 1)];
         } else {
 #pragma unroll
             for (int k = 0; k < 32; ++k)
                 e[k] = 32 * tid + k;
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                t[k] = K_n + 4 * tid + k;
+                t[k] = K_n + 4 * tw + k;
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -972,9 +978,9 @@ void quant_u6_chunk_kernel(QuantArgs a) {
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int j = K_n + 4 * tid + 2 * k;
-            toff[k] = ((tid < W8 && j < K) ? slot_of(t[2 * k]) : (uint32_t)XB) |
-                      (((tid < W8 && j + 1 < K) ? slot_of(t[2 * k + 1]) : (uint32_t)XB) << 16);
+            const int j = K_n + 4 * tw + 2 * k;
+            toff[k] = ((tw >= 0 && j < K) ? slot_of(t[2 * k]) : (uint32_t)XB) |
+                      (((tw >= 0 && j + 1 < K) ? slot_of(t[2 * k + 1]) : (uint32_t)XB) << 16);
         }
         if constexpr (!PACKED) {
 #pragma unroll
@@ -1012,13 +1018,13 @@ void quant_u6_chunk_kernel(QuantArgs a) {
         if (GROUPED) {
             if (tid < NCH && (tid & 3) == 0 && 32 * tid < K_n)
                 a.s4[(int64_t)prow * a.G + (tid >> 2)] = psc;
-        } else if (tid == 0 && a.G > 0) {
+        } else if (tid == THREADS - 1 && a.G > 0) {
             a.s4[prow] = psc;
         }
-        if (tid == 0 && a.s8)
+        if (tid == THREADS - 1 && a.s8)
             a.s8[prow] = n_out > 0 ? ps8 : 0.0f;
-        if (tid < W8 && a.q8) {
-            uint32_t o8 = 4u * (uint32_t)tid;   // (kept apart from the base: no 64-bit lane pointer)
+        if (tw >= 0 && a.q8) {
+            uint32_t o8 = 4u * (uint32_t)tw;   // (kept apart from the base: no 64-bit lane pointer)
             asm volatile("" : "+v"(o8));
             *reinterpret_cast<uint32_t *>(a.q8 + (int64_t)prow * a.pitch8 + o8) = word;
         }
@@ -1028,15 +1034,22 @@ void quant_u6_chunk_kernel(QuantArgs a) {
     // reads' immediate offset)
     auto do_row = [&](auto b_tag) {
         constexpr int B = decltype(b_tag)::value;
-        // (1) this row's DMA has landed (only the next row's DMA, issued
-        //     after it, may still be in flight), in every wave
+        // (1) this row's DMA has landed in every wave, and this wave's LDS
+        //     writes are done (lgkmcnt(0)). Younger than the DMA are the
+        //     previous row's stores and, unless this is the workgroup's last
+        //     row, the next row's DMA: vmcnt(rounds) then (all but the
+        //     youngest DMA's instructions), vmcnt(0) otherwise.
         asm volatile("" ::: "memory");
-        switch (rounds) {                          // s_waitcnt takes an immediate: vmcnt(rounds)
-            case 1: __builtin_amdgcn_s_waitcnt(0xF71); break;
-            case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
-            case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
-            case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
-            default: __builtin_amdgcn_s_waitcnt(kWaitAll); break;
+        if (row + (int)gridDim.x < a.rows) {
+            switch (rounds) {                      // s_waitcnt takes an immediate: vmcnt(n) lgkmcnt(0)
+                case 1: __builtin_amdgcn_s_waitcnt(0x071); break;
+                case 2: __builtin_amdgcn_s_waitcnt(0x072); break;
+                case 3: __builtin_amdgcn_s_waitcnt(0x073); break;
+                case 4: __builtin_amdgcn_s_waitcnt(0x074); break;
+                default: __builtin_amdgcn_s_waitcnt(kWaitAll); break;
+            }
+        } else {
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
         }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -1091,7 +1104,7 @@ void quant_u6_chunk_kernel(QuantArgs a) {
         hm = dpp_max_u32<0x4E>(hm);               // quad: lanes ^ 2 (one 128-channel group)
         if (!GROUPED)
             hm = wave_max_of_quads(hm);
-        const bool tail_wave = (int)wave_u * 64 < W8;   // uniform: the wave holds tail words
+        const bool tail_wave = (int)wave_u * 64 + 64 > THREADS - W8;   // uniform: the wave holds tail words
         uint32_t tm = 0;
         if (tail_wave)
             tm = wave_max_dpp(__builtin_elementwise_max(t2.x, t2.y));
