@@ -550,13 +550,17 @@ def main():
     if args.norm:
         norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
     # the FP6 kernels take 256 x 256 (per-row scales) or 256 x 128 (128-channel
-    # groups) tiles: the automatic choice wants at least one tile per CU
+    # groups) tiles, or 32 output columns per workgroup (the decode kernel, 33
+    # to 128 rows with 128-channel groups): the automatic choice wants at least
+    # one workgroup per CU
     fp6_name = w4.outlier_gemm_fp6_kernel_name(M, w.N, w.K, w.n_out, w.group)
-    fp6_tiles = -(-M // 256) * -(-w.N // (256 if w.group == 0 else 128))
-    fp6_fits = fp6_name is not None and M > 128
+    fp6_decode = fp6_name is not None and fp6_name.startswith("gemm_fp6_decode_kernel")
+    fp6_tiles = -(-w.N // 32) if fp6_decode else -(-M // 256) * -(-w.N // (256 if w.group == 0 else 128))
+    fp6_fits = fp6_name is not None and (M > 128 or fp6_decode)
     fp6_auto = fp6_fits and fp6_tiles >= 256
     if args.path == "fp6" and (not fp6_fits or args.norm):
-        raise SystemExit("the FP6 path takes per-row scales or 128-channel groups, over 128 rows, no fused RMSNorm")
+        raise SystemExit("the FP6 path takes per-row scales or 128-channel groups (over 32 rows), "
+                         "no fused RMSNorm")
     use_fp6 = args.path == "fp6" or (args.path == "auto" and fp6_auto and not args.norm)
     if use_fp6:
         wf6 = w4.to_fp6(wq)

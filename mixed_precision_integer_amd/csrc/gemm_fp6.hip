@@ -483,10 +483,14 @@ bool gemm_fp6_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
 const char *gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group) {
     if (!gemm_fp6_fits(M, N, K_n, n_out, group))
         return nullptr;
+    if (gemm_fp6_decode_fits(M, K_n, group))
+        return gemm_fp6_decode_kernel_name(M);
     return group == 0 ? "gemm_fp6_big_kernel<false>" : "gemm_fp6_group_kernel<false>";
 }
 
 hipError_t launch_gemm_fp6(const Fp6GemmArgs &a, int32_t group, bool export_acc, hipStream_t stream) {
+    if (gemm_fp6_decode_fits(a.M, a.K_n, group))
+        return launch_gemm_fp6_decode(a, export_acc, stream);
     if (group == 128)
         return launch_gemm_fp6_group(a, export_acc, stream);
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);

@@ -31,5 +31,9 @@ const char *gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K_n, int32_t n_ou
 hipError_t launch_gemm_fp6(const Fp6GemmArgs &a, int32_t group, bool export_acc, hipStream_t stream);
 // The group-scale kernel (group 128; gemm_fp6_group.hip).
 hipError_t launch_gemm_fp6_group(const Fp6GemmArgs &a, bool export_acc, hipStream_t stream);
+// The decode kernel for 33..128 token rows with group 128 (gemm_fp6_decode.hip).
+bool gemm_fp6_decode_fits(int32_t M, int32_t K_n, int32_t group);
+const char *gemm_fp6_decode_kernel_name(int32_t M);
+hipError_t launch_gemm_fp6_decode(const Fp6GemmArgs &a, bool export_acc, hipStream_t stream);
 
 }  // namespace w4a4

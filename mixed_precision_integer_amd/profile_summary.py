@@ -41,6 +41,7 @@ SHARED_SOURCES = ("gemm_common.h", "w4a4_internal.h")
 KERNEL_SOURCES = (
     ("gemm_fp6_big_kernel", ("gemm_fp6.hip", "gemm_fp6_common.h", "gemm_fp6_internal.h")),
     ("gemm_fp6_group_kernel", ("gemm_fp6_group.hip", "gemm_fp6_common.h", "gemm_fp6_internal.h")),
+    ("gemm_fp6_decode_kernel", ("gemm_fp6_decode.hip", "gemm_fp6_common.h", "gemm_fp6_internal.h")),
     ("gemm_big_kernel", ("gemm_big.hip", "gemm_kernels.hip")),
     ("gemm_group_kernel", ("gemm_group.hip", "gemm_kernels.hip")),
     ("gemm_decode", ("gemm_decode.hip", "gemm_kernels.hip")),

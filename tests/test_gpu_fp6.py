@@ -121,6 +121,33 @@ def test_fp6_group_parity(oracle, M, N, K, n_out):
     fp6_compare(oracle, X, W, o, group=128)
 
 
+DECODE_CASES = [
+    # M, N, K, n_out (group 128; 33 to 128 rows: the FP6 decode kernel)
+    (33, 512, 1152, 128),           # two row blocks (the second holds one row), nine groups
+    (70, 100, 2176, 128),           # three row blocks, ragged N (a partial last workgroup)
+    (128, 256, 8320, 128),          # four row blocks, the longest K it takes (64 groups)
+    (100, 64, 640, 0),              # no outliers, five groups: some group ranges are empty
+    (65, 32, 384, 256),             # one group, four tail tiles, one workgroup
+]
+
+
+@pytest.mark.parametrize("M,N,K,n_out", DECODE_CASES)
+def test_fp6_decode_parity(oracle, M, N, K, n_out):
+    """The FP6 decode kernel: every group's exact sums and the tail sums from
+    its main loop, Y, the fused call and the i8 path's Y."""
+    assert w4.outlier_gemm_fp6_kernel_name(M, N, K, n_out, 128).startswith("gemm_fp6_decode_kernel")
+    X, W, o = wl.draw(M, N, K, n_out, seed=M + 7 * N + K, outlier_factor=40.0)
+    fp6_compare(oracle, X, W, o, group=128)
+
+
+@pytest.mark.parametrize("M", [64, 128])
+def test_fp6_decode_full_size(oracle, M):
+    """The Llama-65B decode shape (N = K = 8192, 128 outliers, group 128) at
+    64 and 128 token rows, every output compared."""
+    X, W, o = wl.draw_workload(wl.DECODE_65B, M)
+    fp6_compare(oracle, X, W, o, group=128)
+
+
 def test_fp6_extreme_codes(oracle):
     """All -8 codes (magnitude 8, the largest value used: E2M3 4 times 2) and random
     full-range codes over the longest K: the sums reach 21760 * 64."""
@@ -207,5 +234,8 @@ def test_u6_producer(oracle, M, K, n_out, group):
 
 def test_fp6_kernel_names():
     assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4096, 128, 128) == "gemm_fp6_group_kernel<false>"
+    assert w4.outlier_gemm_fp6_kernel_name(128, 8192, 8192, 128, 128) == "gemm_fp6_decode_kernel<4, false>"
+    assert w4.outlier_gemm_fp6_kernel_name(64, 8192, 8192, 128, 128) == "gemm_fp6_decode_kernel<2, false>"
+    assert w4.outlier_gemm_fp6_kernel_name(256, 8192, 8192, 128, 128) == "gemm_fp6_group_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(4096, 11008, 4096, 256, 0) == "gemm_fp6_big_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4352, 256, 256) is None    # groups of 256
