@@ -37,7 +37,7 @@ namespace gemm_fp6_impl {
 
 constexpr int kDWaves = 8, kDThreads = kDWaves * 64;
 constexpr int kDBN = 32;                            // output columns per workgroup
-constexpr int kDMaxGroups = 16;                     // groups per wave (K_n <= 8192)
+constexpr int kDMaxGroups = 16;                     // groups per wave up to 128 rows (K_n <= 8192)
 
 // One operand fragment of k-step t of a 32-row block: the lane's row li and
 // 32-channel chunk lh (bytes 0..15 at 512 lh + 16 li, 16..23 at
@@ -65,9 +65,15 @@ __device__ __forceinline__ v16f mma_fp6(const v6i &w, const v6i &x, const v16f &
 template <int MB, bool EXPORT>
 __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs a) {
     constexpr int RG = (MB + 1) / 2, KS = kDWaves / RG;
+    constexpr int GMAX = MB > 4 ? 2 * kDMaxGroups : kDMaxGroups;   // groups per wave (K_n <= 8192)
     static_assert(RG * KS == kDWaves, "waves split into block pairs and group ranges");
-    __shared__ float red[MB * KS * 16 * 64];        // [block][range][register][lane]
-    __shared__ float sc[kDWaves][3][32][kDMaxGroups + 1];   // per wave: sa of its two blocks, sw (rows padded)
+    // LDS: the scale tables during the main loop, then (after a barrier) the
+    // partial blocks: red [block][range][register][lane]; sc per wave: sa of
+    // its two blocks and sw, [32 rows][groups], rows padded by one
+    constexpr int RED = MB * KS * 16 * 64, SC = kDWaves * 3 * 32 * (GMAX + 1);
+    __shared__ float lds_f[RED > SC ? RED : SC];
+    float *red = lds_f;
+    float(*sc)[3][32][GMAX + 1] = reinterpret_cast<float(*)[3][32][GMAX + 1]>(lds_f);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, lh = lane >> 5;
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs 
     const int T = (int)(a.pitch4 / 32);             // k-steps of 64 channels
     const int G = T / 2;                            // groups of 128 channels
     const int T8 = (int)(a.pitch8 / kTileBytes);    // tail tiles of 64 channels
-    const int gper = (G + KS - 1) / KS;             // <= kDMaxGroups (checked at launch)
+    const int gper = (G + KS - 1) / KS;             // <= GMAX (checked at launch)
     const int g0 = min(ks * gper, G);
     const int ng = min(g0 + gper, G) - g0;
 
@@ -91,14 +97,15 @@ __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs 
 
     // The scales of the wave's rows and groups go to LDS first, in loads of
     // 16 consecutive groups of 4 rows (a scale per group and row would touch
-    // 32 cache lines per load)
-    float(*ws)[32][kDMaxGroups + 1] = sc[wave];
-    {
-        const int gg = lane & 15;
+    // 32 cache lines per load), for every group of the range
+    float(*ws)[32][GMAX + 1] = sc[wave];
+#pragma unroll
+    for (int gc = 0; gc < GMAX / 16; ++gc) {       // 16 groups at a time
+        const int gg = 16 * gc + (lane & 15);
+        const int g = min(g0 + min(gg, max(ng - 1, 0)), G - 1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 4 * i + (lane >> 4);
-            const int g = min(g0 + min(gg, max(ng - 1, 0)), G - 1);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 if (j < nb)
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs 
     // Group k of the range (clamped to the last one: the requests are issued
     // unconditionally, so the wait counts stay exact across the unrolled
     // steps; a clamped repeat is never used).
-    v6i wf[kDMaxGroups][2], af[kDMaxGroups][2][2];
+    v6i wf[GMAX][2], af[GMAX][2][2];
     auto load_w = [&](int k) {
         const int g = g0 + min(k, ng - 1), t = 2 * g;
         wf[k][0] = fragment(Wb, t, flo, fhi);
@@ -142,10 +149,10 @@ __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs 
             load_w(k);
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int k = 0; k < kDMaxGroups; ++k) {
-            if (k + PA < kDMaxGroups)
+        for (int k = 0; k < GMAX; ++k) {
+            if (k + PA < GMAX)
                 load_a(k + PA);
-            if (k + PW < kDMaxGroups)
+            if (k + PW < GMAX)
                 load_w(k + PW);
             asm volatile("" ::: "memory");         // the requests go out here, not next to their use
 #pragma unroll
@@ -156,13 +163,14 @@ __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs 
                     if constexpr (EXPORT) {
                         const int m = 32 * (b0 + j) + li;
                         if (m < a.M) {
+                            int32_t *dst = a.acc4_out + ((int64_t)(g0 + k) * a.M + m) * a.N + n0 + 4 * lh;
+                            const int nl = a.N - n0 - 4 * lh;   // columns left from dst
 #pragma unroll
-                            for (int e = 0; e < 16; ++e) {
-                                const int n = n0 + 8 * (e / 4) + 4 * lh + e % 4;
-                                if (n < a.N)
-                                    a.acc4_out[((int64_t)(g0 + k) * a.M + m) * a.N + n] = (int32_t)acc[e];
-                            }
+                            for (int e = 0; e < 16; ++e)
+                                if (8 * (e / 4) + e % 4 < nl)
+                                    dst[8 * (e / 4) + e % 4] = (int32_t)acc[e];
                         }
+                        asm volatile("" ::: "memory");
                     }
                     const float swk = ws[2][li][k], sak = ws[j][li][k];
                     const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : swk, lh ? 0.0f : sak, zf, 0, 0, 0);
@@ -212,6 +220,7 @@ __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs 
     }
 
     // ---- partial blocks added in range order (deterministic), then Y
+    __syncthreads();                               // every wave is done with the scale tables
 #pragma unroll
     for (int j = 0; j < 2; ++j)
         if (j < nb)
@@ -250,16 +259,20 @@ __global__ __launch_bounds__(kDThreads) void gemm_fp6_decode_kernel(Fp6GemmArgs 
 using namespace gemm_fp6_impl;
 
 bool gemm_fp6_decode_fits(int32_t M, int32_t K_n, int32_t group) {
-    const int G = K_n / 128;
-    const int KS = M > 64 ? kDWaves / 2 : kDWaves;   // group ranges (4 waves per range pair above 64 rows)
-    return group == 128 && K_n % 128 == 0 && M > 32 && M <= 128 && (G + KS - 1) / KS <= kDMaxGroups;
+    const int G = K_n / 128, mb = (M + 31) / 32;
+    if (mb == 5 || mb == 6 || mb == 7)               // 129..224 rows: the row-block counts with no instantiation
+        return false;
+    const int KS = kDWaves / ((mb + 1) / 2);          // group ranges
+    const int gmax = mb > 4 ? 2 * kDMaxGroups : kDMaxGroups;
+    return group == 128 && K_n % 128 == 0 && M > 32 && M <= 256 && (G + KS - 1) / KS <= gmax;
 }
 
 const char *gemm_fp6_decode_kernel_name(int32_t M) {
     switch ((M + 31) / 32) {
     case 2: return "gemm_fp6_decode_kernel<2, false>";
     case 3: return "gemm_fp6_decode_kernel<3, false>";
-    default: return "gemm_fp6_decode_kernel<4, false>";
+    case 4: return "gemm_fp6_decode_kernel<4, false>";
+    default: return "gemm_fp6_decode_kernel<8, false>";
     }
 }
 
@@ -275,8 +288,10 @@ hipError_t launch_gemm_fp6_decode(const Fp6GemmArgs &a, bool export_acc, hipStre
         W4A4_FP6_DECODE(2)
     } else if (mb == 3) {
         W4A4_FP6_DECODE(3)
-    } else {
+    } else if (mb == 4) {
         W4A4_FP6_DECODE(4)
+    } else {
+        W4A4_FP6_DECODE(8)
     }
 #undef W4A4_FP6_DECODE
     return hipGetLastError();

@@ -128,6 +128,7 @@ DECODE_CASES = [
     (128, 256, 8320, 128),          # four row blocks, the longest K it takes (64 groups)
     (100, 64, 640, 0),              # no outliers, five groups: some group ranges are empty
     (65, 32, 384, 256),             # one group, four tail tiles, one workgroup
+    (250, 96, 2176, 128),           # eight row blocks (the last one partial), 16 groups
 ]
 
 
@@ -140,10 +141,10 @@ def test_fp6_decode_parity(oracle, M, N, K, n_out):
     fp6_compare(oracle, X, W, o, group=128)
 
 
-@pytest.mark.parametrize("M", [64, 128])
+@pytest.mark.parametrize("M", [64, 128, 256])
 def test_fp6_decode_full_size(oracle, M):
     """The Llama-65B decode shape (N = K = 8192, 128 outliers, group 128) at
-    64 and 128 token rows, every output compared."""
+    64, 128 and 256 token rows, every output compared."""
     X, W, o = wl.draw_workload(wl.DECODE_65B, M)
     fp6_compare(oracle, X, W, o, group=128)
 
@@ -236,6 +237,8 @@ def test_fp6_kernel_names():
     assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4096, 128, 128) == "gemm_fp6_group_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(128, 8192, 8192, 128, 128) == "gemm_fp6_decode_kernel<4, false>"
     assert w4.outlier_gemm_fp6_kernel_name(64, 8192, 8192, 128, 128) == "gemm_fp6_decode_kernel<2, false>"
-    assert w4.outlier_gemm_fp6_kernel_name(256, 8192, 8192, 128, 128) == "gemm_fp6_group_kernel<false>"
+    assert w4.outlier_gemm_fp6_kernel_name(256, 8192, 8192, 128, 128) == "gemm_fp6_decode_kernel<8, false>"
+    assert w4.outlier_gemm_fp6_kernel_name(160, 8192, 8192, 128, 128) == "gemm_fp6_group_kernel<false>"
+    assert w4.outlier_gemm_fp6_kernel_name(257, 8192, 8192, 128, 128) == "gemm_fp6_group_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(4096, 11008, 4096, 256, 0) == "gemm_fp6_big_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4352, 256, 256) is None    # groups of 256
