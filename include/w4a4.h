@@ -291,7 +291,7 @@ w4a4_status w4a4_repack_u6(const void *Q4, int32_t rows, int32_t K_n, void *U6, 
  * [w4a4_u6_bytes(M, K_n)] (rows past M up to the end of their 32-row block
  * are written as code 0) instead of packed nibbles. Codes, scales and the
  * INT8 tail are those of w4a4_quant_reorder_act; Au6 equals w4a4_repack_u6
- * of its Aq4 byte for byte. Group 0 only (UNSUPPORTED otherwise); Au6
+ * of its Aq4 byte for byte. Group sizes as w4a4_quant_reorder_act; Au6
  * 16-byte aligned; other arguments as w4a4_quant_reorder_act. */
 w4a4_status w4a4_quant_reorder_act_u6(const void *X, int64_t ldx, const int32_t *perm, int32_t M,
                                       int32_t K, int32_t n_out, int32_t group, void *Au6, void *Aq8,
@@ -305,8 +305,9 @@ const char *w4a4_outlier_gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K, i
 /* The mixed-precision GEMM with u6 INT4 operands (Au6 for the M activation
  * rows, Wu6 for the N weight rows); the INT8 tails and the scales as for
  * w4a4_outlier_gemm, and the same Y definition. Constraints: group 0 (one
- * INT4 scale per row), K_n > 0, at most 256 outlier channels
- * (UNSUPPORTED otherwise), plus those of w4a4_outlier_gemm. No workspace. */
+ * INT4 scale per row) or 128 with K_n a multiple of 128, K_n > 0, at most
+ * 256 outlier channels (UNSUPPORTED otherwise), plus those of
+ * w4a4_outlier_gemm. No workspace. */
 w4a4_status w4a4_outlier_gemm_fp6(const void *Au6, const void *Aq8, const float *sa4,
                                   const float *sa8, const void *Wu6, const void *Wq8,
                                   const float *sw4, const float *sw8, int32_t M, int32_t N,

@@ -54,7 +54,7 @@ struct NormArgs {
 };
 
 // q4: packed nibbles [rows, pitch4]; or, with u6 set (q4 unused), the head
-// as the FP6 GEMM's u6 operand (per-row scales only, no norm).
+// as the FP6 GEMM's u6 operand (no norm).
 w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t rows,
                        int32_t K, int32_t n_out, int32_t group, void *q4, void *q8, float *s4,
                        float *s8, w4a4_stream stream, const NormArgs &norm = NormArgs{nullptr, 0.0f, nullptr},
