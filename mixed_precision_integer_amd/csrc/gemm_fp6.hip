@@ -115,6 +115,9 @@ constexpr int TAIL_TILE = (BM + BN) * kTileBytes;  // 32 KB: A rows, then B rows
 constexpr int SCALES = STAGES * STAGE;             // sa4, sa8, sw4, sw8 of the tile
 constexpr int LDS_BYTES = SCALES + 4 * BM * 4;
 static_assert(MAX_TAIL_TILES * TAIL_TILE <= STAGES * STAGE, "the tail fits in the ring");
+constexpr int Y_ROW = 80;                          // bytes per staged row of a 32 x 32 fp16 block
+constexpr int Y_SLOTS = STAGES * STAGE - (kThreads / 64) * 32 * Y_ROW;   // one slot per wave
+static_assert(MAX_TAIL_TILES * TAIL_TILE <= Y_SLOTS, "the slots stay clear of the tail");
 static_assert(STAGE == 24576 && DPO == 3, "stage layout");
 static_assert((STAGES - 1) * D <= 63, "vmcnt range");
 
@@ -345,7 +348,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
     const int wm_e = wave_e >> 1, wn_e = wave_e & 1, li_e = lane_e & 31, lh_e = lane_e >> 5;
     const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     const bool vec_store = ((reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2)) & 7) == 0;
-    const bool interior = vec_store && row0 + BM <= a.M && col0 + BN <= a.N;
+    const bool interior = ((reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2)) & 15) == 0 &&
+                          row0 + BM <= a.M && col0 + BN <= a.N;
     // Two copies of the epilogue: one for tiles wholly inside Y (no checks),
     // one for the edge tiles, each contiguous, so that a tile fetches only the
     // instructions it runs (the unrolled epilogue is most of the kernel's code).
@@ -436,7 +440,25 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
                                    rs8[fm] * cs8[q * 4 + e]);
                 const uint2 packed = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
                 if constexpr (INTERIOR) {
-                    *reinterpret_cast<uint2 *>(row + q * 8) = packed;
+                    // The block goes through the wave's LDS slot (rows of
+                    // Y_ROW bytes) so that Y is written as 64-byte row pieces,
+                    // 16 bytes per lane, instead of 16-byte pieces of 32 rows.
+                    // A wave's LDS operations run in issue order, so the next
+                    // block's writes follow this block's reads.
+                    unsigned char *slot = lds + Y_SLOTS + wave_e * (32 * Y_ROW);
+                    *reinterpret_cast<uint2 *>(slot + li_e * Y_ROW + 8 * lh_e + 16 * q) = packed;
+                    if (q == 3) {
+                        const int pr = lane_e >> 2, pc = lane_e & 3;
+                        uint4 piece[2];
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+                            piece[i] = *reinterpret_cast<const uint4 *>(slot + (pr + 16 * i) * Y_ROW + 16 * pc);
+                        _Float16 *dst = a.y + (int64_t)(row0 + wm_e * WTM + fm * 32 + pr) * a.ldy + col0 + wn_e * WTN +
+                                        fn * 32 + pc * 8;
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+                            *reinterpret_cast<uint4 *>(dst + (int64_t)(16 * i) * a.ldy) = piece[i];
+                    }
                 } else if (m < a.M) {
                     const int n = col0 + nl + q * 8;
                     if (vec_store && n + 3 < a.N) {

@@ -40,6 +40,8 @@ constexpr int G_D = G_DA + 3;                       // + B (2 or 1) + scales (1 
 constexpr int G_TAIL_TILE = (GBM + GBN) * kTileBytes;   // 24 KB
 constexpr int G_SCALES8 = GSTAGES * GSTAGE;         // sa8[256], sw8[128] of the tile
 constexpr int G_LDS_BYTES = G_SCALES8 + (GBM + GBN) * 4;
+constexpr int G_YP = 2 * GBN + 16;                  // bytes per row of the staged fp16 tile
+static_assert(GBM * G_YP <= G_SCALES8, "the staged tile fits the ring");
 static_assert(G_DA == 3, "whole DMA rounds");
 static_assert(MAX_TAIL_TILES * G_TAIL_TILE <= G_SCALES8, "the tail fits the ring");
 
@@ -259,23 +261,12 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
         compiler_fence();
     }
 
-    // ---- epilogue, block by block -----------------------------------------------------
+    // ---- epilogue: tail sums and final values (packed fp16), then Y through LDS ---------
     const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    const bool vec_store = ((reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2)) & 7) == 0;
+    uint32_t yp[GF][GF][8];
 #pragma unroll
     for (int fn = 0; fn < GF; ++fn) {
         const int nl = wn * GWT + fn * 32 + lh * 4;       // tile-local first column of the lane
-        v4i pb8[MAX_TAIL_TILES][2];
-#pragma unroll
-        for (int j = 0; j < MAX_TAIL_TILES; ++j)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                uint4 p = uint4{0, 0, 0, 0};
-                if (j < T8)
-                    p = *reinterpret_cast<const uint4 *>(lds + j * G_TAIL_TILE + GBM * kTileBytes +
-                                                        swz(wn * GWT + fn * 32 + li, 2 * s + lh));
-                pb8[j][s] = v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w};
-            }
 #pragma unroll
         for (int fm = 0; fm < GF; ++fm) {
             const int ml = wm * GWT + fm * 32 + li;
@@ -287,8 +278,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
                     break;                                 // uniform
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
+                    const uint4 pb = *reinterpret_cast<const uint4 *>(lds + j * G_TAIL_TILE + GBM * kTileBytes +
+                                                                     swz(wn * GWT + fn * 32 + li, 2 * s + lh));
                     const uint4 p = *reinterpret_cast<const uint4 *>(lds + j * G_TAIL_TILE + swz(ml, 2 * s + lh));
-                    acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(pb8[j][s], v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w},
+                    acc8 = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{(int)pb.x, (int)pb.y, (int)pb.z, (int)pb.w},
+                                                                 v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w},
                                                                  acc8, 0, 0, 0);
                 }
             }
@@ -312,19 +306,64 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     v[e] = y_value_g(y[fm][fn][q * 4 + e], acc8[q * 4 + e], rs8 * cs8[e]);
-                const int n = col0 + nl + q * 8;
-                if (m < a.M) {
-                    _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
-                    if (vec_store && n + 3 < a.N) {
-                        *reinterpret_cast<uint2 *>(dst) = uint2{pack_half2(v[0], v[1]), pack_half2(v[2], v[3])};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < a.N)
-                                dst[e] = (_Float16)v[e];
-                    }
-                }
+                yp[fm][fn][2 * q] = pack_half2(v[0], v[1]);
+                yp[fm][fn][2 * q + 1] = pack_half2(v[2], v[3]);
             }
+        }
+    }
+
+    // Every wave is done with the tail tiles: the tile's fp16 values go to
+    // rows of G_YP bytes at the start of the ring, and from there to Y as
+    // 16-byte pieces of whole rows (a store instruction writes four rows of
+    // 256 bytes instead of 32 pieces of 16 bytes).
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+#pragma unroll
+    for (int fn = 0; fn < GF; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < GF; ++fm) {
+            unsigned char *yrow = lds + (wm * GWT + fm * 32 + li) * G_YP + 2 * (wn * GWT + fn * 32 + lh * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2 *>(yrow + 16 * q) = uint2{yp[fm][fn][2 * q], yp[fm][fn][2 * q + 1]};
+        }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    const uintptr_t ya = reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2);
+    const int rr = tid >> 4, ch = tid & 15;               // 16 lanes per row, 32 rows per pass
+    if (row0 + GBM <= a.M && col0 + GBN <= a.N && (ya & 15) == 0) {      // uniform: no checks
+        uint4 v[GBM / 32];
+#pragma unroll
+        for (int p = 0; p < GBM / 32; ++p)
+            v[p] = *reinterpret_cast<const uint4 *>(lds + (p * 32 + rr) * G_YP + 16 * ch);
+        _Float16 *dst = a.y + (int64_t)(row0 + rr) * a.ldy + col0 + ch * 8;
+#pragma unroll
+        for (int p = 0; p < GBM / 32; ++p)
+            *reinterpret_cast<uint4 *>(dst + (int64_t)(p * 32) * a.ldy) = v[p];
+        return;
+    }
+#pragma unroll
+    for (int p = 0; p < GBM / 32; ++p) {
+        const int ml = p * 32 + rr, m = row0 + ml, n = col0 + ch * 8;
+        const uint4 v = *reinterpret_cast<const uint4 *>(lds + ml * G_YP + 16 * ch);
+        if (m >= a.M)
+            continue;
+        _Float16 *dst = a.y + (int64_t)m * a.ldy + n;
+        if (n + 7 < a.N && (ya & 15) == 0) {
+            *reinterpret_cast<uint4 *>(dst) = v;
+        } else if (n + 7 < a.N && (ya & 7) == 0) {
+            reinterpret_cast<uint2 *>(dst)[0] = uint2{v.x, v.y};
+            reinterpret_cast<uint2 *>(dst)[1] = uint2{v.z, v.w};
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < a.N)
+                    reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
         }
     }
 }
