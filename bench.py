@@ -549,13 +549,14 @@ def main():
     norm = None
     if args.norm:
         norm = (torch.from_numpy(wl.draw_norm_weight(w.K, seed=w.seed)).to(dev), 1e-6)
-    # the FP6 kernels take 256 x 256 (per-row scales) or 256 x 128 (128-channel
+    # the FP6 kernels take 256 x 256 (per-row scales) or 128 x 128 (128-channel
     # groups) tiles, or 32 output columns per workgroup (the decode kernel, 33
     # to 128 or 225 to 256 rows with 128-channel groups): the automatic choice
     # wants at least one workgroup per CU
     fp6_name = w4.outlier_gemm_fp6_kernel_name(M, w.N, w.K, w.n_out, w.group)
     fp6_decode = fp6_name is not None and fp6_name.startswith("gemm_fp6_decode_kernel")
-    fp6_tiles = -(-w.N // 32) if fp6_decode else -(-M // 256) * -(-w.N // (256 if w.group == 0 else 128))
+    fp6_tile = 256 if w.group == 0 else 128
+    fp6_tiles = -(-w.N // 32) if fp6_decode else -(-M // fp6_tile) * -(-w.N // fp6_tile)
     fp6_fits = fp6_name is not None and (M > 128 or fp6_decode)
     fp6_auto = fp6_fits and fp6_tiles >= 256
     if args.path == "fp6" and (not fp6_fits or args.norm):

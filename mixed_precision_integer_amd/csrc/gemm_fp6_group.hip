@@ -1,4 +1,4 @@
-// FP6 GEMM for group scales of 128 channels (the 256 x 128 kernel).
+// FP6 GEMM for group scales of 128 channels (the 128 x 128 kernel).
 #include <algorithm>
 
 #include "w4a4.h"
@@ -14,35 +14,39 @@ namespace gemm_fp6_impl {
 // page, Summary paragraph 2 and Key points item 5). A group is two FP6 k-steps.
 // * The fold y += acc_g * (sa sw) costs the VALU one FMA per output element
 //   and group, as much time as the group's FP6 MFMAs: the two have to run
-//   side by side. 256 x 128 output tile per workgroup, eight waves of 64 x 64
-//   (2 x 2 blocks), two waves per SIMD (one wave's fold runs while the other's
-//   MFMAs and LDS reads wait); per wave the group sums (64) and y (64) both in
-//   VGPRs, so the fold reads the sums directly.
+//   side by side. 128 x 128 output tile per workgroup, four waves of 64 x 64
+//   (2 x 2 blocks), and two workgroups per CU (under 80 KB of LDS each), so
+//   each SIMD holds one wave of each: the two workgroups pass their barriers
+//   independently, and one's fold or fragment reads overlap the other's
+//   MFMAs. Per wave the group sums (64) and y (64) both in VGPRs, so the fold
+//   reads the sums directly.
 // * Per group: the eight fragment reads of both k-steps, then for each pair of
 //   blocks the scale products of the previous group (one
 //   v_mfma_f32_32x32x1_2b_f32: exact fp32 outer products of row and column
 //   scales, in the accumulator layout), the fold of that group's sums, and
 //   this group's two k-steps into the same registers (C = 0 on the first).
 // * Ring of three stages of one group each (both k-steps of A and B, the
-//   group's 256 row scales and 128 column scales), two groups ahead; the
+//   group's 128 row scales and 128 column scales), two groups ahead; the
 //   previous group's scales are kept in registers for its fold.
 // * The INT8 tail and the epilogue as in the 256 x 256 kernel:
 //   Y = fp16(y + acc8 * (sa8 sw8)).
-constexpr int kGThreads = 512;
-constexpr int GBM = 256, GBN = 128, GWT = 64, GF = 2;
+constexpr int kGThreads = 256;
+constexpr int GBM = 128, GBN = 128, GWT = 64, GF = 2;
 constexpr int GSTAGES = 3;
-constexpr int G_A = 0;                              // A: k-step s, block i at s * 8 BLK + i BLK
+constexpr int G_A = 0;                              // A: k-step s, block i at s * 4 BLK + i BLK
 constexpr int G_B = 2 * (GBM / 32) * BLK;           // B: k-step s, block i at G_B + s * 4 BLK + i BLK
-constexpr int G_SC = G_B + 2 * (GBN / 32) * BLK;    // sa[256], then sw[128] (and three copies)
-constexpr int GSTAGE = G_SC + 768 * 4;              // 39936 bytes
+constexpr int G_SC = G_B + 2 * (GBN / 32) * BLK;    // sa[128], then sw[128]
+constexpr int GSTAGE = G_SC + (GBM + GBN) * 4;      // 25600 bytes
 constexpr int G_DA = 2 * (GBM / 32) * BLK / 16 / kGThreads;  // 3 DMA units of A per group per lane
-constexpr int G_D = G_DA + 3;                       // + B (2 or 1) + scales (1 or 2): 6 per lane
-constexpr int G_TAIL_TILE = (GBM + GBN) * kTileBytes;   // 24 KB
-constexpr int G_SCALES8 = GSTAGES * GSTAGE;         // sa8[256], sw8[128] of the tile
+constexpr int G_DB = 2 * (GBN / 32) * BLK / 16 / kGThreads;  // 3 of B
+constexpr int G_D = G_DA + G_DB + 1;                // + one scale: 7 per lane
+constexpr int G_TAIL_TILE = (GBM + GBN) * kTileBytes;   // 16 KB
+constexpr int G_SCALES8 = GSTAGES * GSTAGE;         // sa8[128], sw8[128] of the tile
 constexpr int G_LDS_BYTES = G_SCALES8 + (GBM + GBN) * 4;
 constexpr int G_YP = 2 * GBN + 16;                  // bytes per row of the staged fp16 tile
 static_assert(GBM * G_YP <= G_SCALES8, "the staged tile fits the ring");
-static_assert(G_DA == 3, "whole DMA rounds");
+static_assert(G_DA == 3 && G_DB == 3 && GBM + GBN == kGThreads, "whole DMA rounds");
+static_assert(2 * G_LDS_BYTES <= 160 * 1024, "two workgroups per CU");
 static_assert(MAX_TAIL_TILES * G_TAIL_TILE <= G_SCALES8, "the tail fits the ring");
 
 // FP6 MFMA (operands FP6 E2M3 holding q / 2, block scale 2^1 on each):
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;          // 4 x 2 waves of 64 x 64
+    const int wm = wave >> 1, wn = wave & 1;          // 2 x 2 waves of 64 x 64
     const int li = lane & 31, lh = lane >> 5;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
@@ -89,24 +93,18 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
     const int G = T / 2;                           // groups of 128 channels
     const int T8 = (int)(a.pitch8 / kTileBytes);
 
-    // DMA sources. A: unit q = j * 512 + tid, k-step q / 768, block (q % 768) / 96.
-    // B: 768 units; waves 0-3 take units tid and 512 + tid, waves 4-7 unit tid.
-    // Scales: waves 4-7 the 256 row scales (slot tid - 256), every lane a
-    // column scale (slot 256 + tid for waves 0-3, 512 + tid - 256 for 4-7:
-    // four copies; slots 256..383 are read).
-    uint32_t oa[G_DA], ob[2];
+    // DMA sources. A and B alike: unit q = j * 256 + tid (768 per group),
+    // k-step q / 384, block (q % 384) / 96, 16-byte unit q % 96. Scales:
+    // waves 0-1 the 128 row scales, waves 2-3 the 128 column scales.
+    uint32_t oa[G_DA], ob[G_DB];
 #pragma unroll
     for (int j = 0; j < G_DA; ++j) {
-        const int q = j * kGThreads + tid, s = q / 768, i = (q % 768) / 96, u = q % 96;
+        const int q = j * kGThreads + tid, s = q / 384, i = (q % 384) / 96, u = q % 96;
         oa[j] = ((uint32_t)min(row0 / 32 + i, RBA - 1) * (uint32_t)T + (uint32_t)s) * (uint32_t)BLK + 16 * u;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int q = min(j * kGThreads + tid, 767), s = q / 384, i = (q % 384) / 96, u = q % 96;
         ob[j] = ((uint32_t)min(col0 / 32 + i, RBB - 1) * (uint32_t)T + (uint32_t)s) * (uint32_t)BLK + 16 * u;
     }
-    const bool low = wave_u < 4;                   // uniform per wave
-    const int64_t srow = min(row0 + (tid & 255), a.M - 1), scol = min(col0 + (tid & (GBN - 1)), a.N - 1);
+    const bool low = wave_u < 2;                   // uniform per wave
+    const int64_t srow = min(row0 + (tid & (GBM - 1)), a.M - 1), scol = min(col0 + (tid & (GBN - 1)), a.N - 1);
     // ring group gg (past the last: a reload of the last into a stage nothing reads)
     auto issue = [&](int gg) {
         const int g = min(gg, G - 1);
@@ -114,22 +112,21 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
         const uint8_t *A = a.a_u6 + (int64_t)(2 * g) * BLK, *B = a.w_u6 + (int64_t)(2 * g) * BLK;
 #pragma unroll
         for (int j = 0; j < G_DA; ++j)
-            dma16(A, oa[j], st + G_A + j * 8192 + wave_u * 1024);
-        dma16(B, ob[0], st + G_B + wave_u * 1024);
-        if (low) {
-            dma16(B, ob[1], st + G_B + 8192 + wave_u * 1024);
-            dma4(a.sw4 + scol * G + g, st + G_SC + 1024 + wave_u * 256);
-        } else {
-            dma4(a.sa4 + srow * G + g, st + G_SC + (wave_u - 4) * 256);
-            dma4(a.sw4 + scol * G + g, st + G_SC + 2048 + (wave_u - 4) * 256);
-        }
+            dma16(A, oa[j], st + G_A + j * 4096 + wave_u * 1024);
+#pragma unroll
+        for (int j = 0; j < G_DB; ++j)
+            dma16(B, ob[j], st + G_B + j * 4096 + wave_u * 1024);
+        if (low)
+            dma4(a.sa4 + srow * G + g, st + G_SC + wave_u * 256);
+        else
+            dma4(a.sw4 + scol * G + g, st + G_SC + wave_u * 256);   // slots GBM.. (wave 2 starts at 512)
     };
     if (T8 > 0) {                                  // tail scales, ahead of everything
         const uint32_t ss = lds_addr(lds) + G_SCALES8;
         if (low)
             dma4(a.sa8 + srow, ss + wave_u * 256);
-        else if (wave_u < 6)
-            dma4(a.sw8 + scol, ss + GBM * 4 + (wave_u - 4) * 256);
+        else
+            dma4(a.sw8 + scol, ss + wave_u * 256);
     }
 
     float y[GF][GF][16];
@@ -149,7 +146,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int i = 0; i < GF; ++i) {
-            ha[s][i] = G_A + (s * 8 + wm * 2 + i) * BLK + lhi;
+            ha[s][i] = G_A + (s * 4 + wm * 2 + i) * BLK + lhi;
             hb[s][i] = G_B + (s * 4 + wn * 2 + i) * BLK + lhi;
             asm("" : "+v"(ha[s][i]));
             asm("" : "+v"(hb[s][i]));
@@ -197,13 +194,13 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < GF; ++i) {
-                fa[s][i] = load_operand(lds + st + G_A + (s * 8 + wm * 2 + i) * BLK + llo, lds + st + ha[s][i]);
+                fa[s][i] = load_operand(lds + st + G_A + (s * 4 + wm * 2 + i) * BLK + llo, lds + st + ha[s][i]);
                 fb[s][i] = load_operand(lds + st + G_B + (s * 4 + wn * 2 + i) * BLK + llo, lds + st + hb[s][i]);
             }
         const float *sc = reinterpret_cast<const float *>(lds + st + G_SC);
         const float crs = sc[wm * GWT + lh * 32 + li];
-        const float cca = sc[256 + wn * GWT + lh * 32 + li];
-        const float ccb = sc[256 + wn * GWT + (1 - lh) * 32 + li];
+        const float cca = sc[GBM + wn * GWT + lh * 32 + li];
+        const float ccb = sc[GBM + wn * GWT + (1 - lh) * 32 + li];
         // pair c: blocks (0, c) in the first half of S, (1, 1 - c) in the second
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -244,15 +241,13 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
             const uint32_t st = lds_addr(lds) + j * G_TAIL_TILE + wave_u * 1024;
             const uint8_t *A8 = reinterpret_cast<const uint8_t *>(a.a8) + j * kTileBytes;
             const uint8_t *B8 = reinterpret_cast<const uint8_t *>(a.w8) + j * kTileBytes;
+            // 128 rows of 64 bytes per operand: two units of 16 bytes per lane each
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int q = k * kGThreads + tid, r = q >> 2;
-                dma16(A8, (uint32_t)min(row0 + r, a.M - 1) * (uint32_t)a.pitch8 + dma_chunk_offset(q), st + k * 8192);
-            }
-            {
-                const int q = tid, r = q >> 2;
+                dma16(A8, (uint32_t)min(row0 + r, a.M - 1) * (uint32_t)a.pitch8 + dma_chunk_offset(q), st + k * 4096);
                 dma16(B8, (uint32_t)min(col0 + r, a.N - 1) * (uint32_t)a.pitch8 + dma_chunk_offset(q),
-                      st + GBM * kTileBytes);
+                      st + GBM * kTileBytes + k * 4096);
             }
         }
         compiler_fence();
@@ -334,21 +329,22 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     const uintptr_t ya = reinterpret_cast<uintptr_t>(a.y) | (uintptr_t)(a.ldy * 2);
-    const int rr = tid >> 4, ch = tid & 15;               // 16 lanes per row, 32 rows per pass
+    constexpr int RPP = kGThreads / 16;                  // 16 lanes per row: rows per pass
+    const int rr = tid >> 4, ch = tid & 15;
     if (row0 + GBM <= a.M && col0 + GBN <= a.N && (ya & 15) == 0) {      // uniform: no checks
-        uint4 v[GBM / 32];
+        uint4 v[GBM / RPP];
 #pragma unroll
-        for (int p = 0; p < GBM / 32; ++p)
-            v[p] = *reinterpret_cast<const uint4 *>(lds + (p * 32 + rr) * G_YP + 16 * ch);
+        for (int p = 0; p < GBM / RPP; ++p)
+            v[p] = *reinterpret_cast<const uint4 *>(lds + (p * RPP + rr) * G_YP + 16 * ch);
         _Float16 *dst = a.y + (int64_t)(row0 + rr) * a.ldy + col0 + ch * 8;
 #pragma unroll
-        for (int p = 0; p < GBM / 32; ++p)
-            *reinterpret_cast<uint4 *>(dst + (int64_t)(p * 32) * a.ldy) = v[p];
+        for (int p = 0; p < GBM / RPP; ++p)
+            *reinterpret_cast<uint4 *>(dst + (int64_t)(p * RPP) * a.ldy) = v[p];
         return;
     }
 #pragma unroll
-    for (int p = 0; p < GBM / 32; ++p) {
-        const int ml = p * 32 + rr, m = row0 + ml, n = col0 + ch * 8;
+    for (int p = 0; p < GBM / RPP; ++p) {
+        const int ml = p * RPP + rr, m = row0 + ml, n = col0 + ch * 8;
         const uint4 v = *reinterpret_cast<const uint4 *>(lds + ml * G_YP + 16 * ch);
         if (m >= a.M)
             continue;
