@@ -474,6 +474,59 @@ def copy_probe(torch, nbytes, steps, warmup):
                       "GBps": 2 * nbytes / us / 1e3}), flush=True)
 
 
+def read_probe(torch, sizes_mib, steps):
+    """A hand-written streaming read (probe/read_probe.hip, libw4a4_probe.so)
+    of buffers of each size, cold: the launches rotate over buffer sets of more
+    than 1.5 GiB, so that no set is still in the 256 MB last-level cache when it
+    is read again. Swept over workgroup counts, loads of 16 bytes in flight
+    per lane and plain or non-temporal loads; one JSON line per setting (median
+    of `steps` launches, each bracketed by HIP events on its stream), then the
+    best per size."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mixed_precision_integer_amd", "libw4a4_probe.so"))
+    lib.w4a4_read_probe.restype = ctypes.c_int32
+    lib.w4a4_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.w4a4_read_probe_out_words.restype = ctypes.c_int64
+    lib.w4a4_read_probe_out_words.argtypes = [ctypes.c_int32]
+    dev = torch.device("cuda:0")
+    wgs_list, depths = (256, 512, 1024, 2048, 4096), (1, 2, 4, 8, 16)
+    out = torch.empty(int(lib.w4a4_read_probe_out_words(max(wgs_list))), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    best = {}
+    for mib in sizes_mib:
+        nbytes = mib << 20
+        n_sets = max(2, -(-(3 << 29) // nbytes))
+        bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        k = 0
+        for wgs in wgs_list:
+            for depth in depths:
+                for nt in (0, 1):
+                    ts = []
+                    for it in range(steps + 2):
+                        b = bufs[k % n_sets]
+                        k += 1
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        rc = lib.w4a4_read_probe(b.data_ptr(), nbytes, wgs, depth, nt, out.data_ptr(),
+                                                 ctypes.c_void_p(stream.cuda_stream))
+                        e1.record(stream)
+                        if rc != 0:
+                            raise SystemExit(f"w4a4_read_probe returned {rc}")
+                        torch.cuda.synchronize()
+                        if it >= 2:
+                            ts.append(e0.elapsed_time(e1) * 1e3)
+                    us = float(np.median(ts))
+                    rec = {"read_probe_bytes": nbytes, "workgroups": wgs, "loads_in_flight_per_lane": depth,
+                           "nontemporal": bool(nt), "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+                    print(json.dumps(rec), flush=True)
+                    if mib not in best or rec["GBps"] > best[mib]["GBps"]:
+                        best[mib] = rec
+        del bufs
+        torch.cuda.empty_cache()
+    print(json.dumps({"read_probe_best": list(best.values())}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -500,6 +553,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, time a plain device-to-device copy of this many "
                          "MiB (reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--read-probe-mib", type=str, default="",
+                    help="instead of the layer, sweep the hand-written streaming-read probe over these "
+                         "buffer sizes (comma-separated MiB; cold buffers)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -513,6 +569,9 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib << 20, args.steps, args.warmup)
+        return
+    if args.read_probe_mib:
+        read_probe(torch, [int(v) for v in args.read_probe_mib.split(",")], max(3, min(args.steps, 15)))
         return
     if args.select_outliers:
         select_bench(torch, w4, args)

@@ -11,6 +11,10 @@ architectural VGPRs (-amdgpu-mfma-vgpr-form), since its fp32 epilogue reads
 them every scale group; the 256 x 256 GEMMs (i8 and FP6) hold 256 accumulator
 registers per lane, which only fit as AGPRs, and are built without that option.
 Sources are compiled in parallel (at most MAX_JOBS, else the CPU count).
+
+The streaming-read probe (probe/read_probe.hip, a measurement tool that
+bench.py --read-probe calls) is built into a library of its own,
+libw4a4_probe.so, so that nothing of it enters the layer's library.
 """
 from __future__ import annotations
 
@@ -25,6 +29,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libw4a4.so")
+PROBE_LIB = os.path.join(HERE, "libw4a4_probe.so")
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -67,7 +72,10 @@ def build(verbose: bool = False) -> str:
             for f in [pool.submit(_run, c, verbose) for c in cmds]:
                 f.result()
         _run([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
+        probe_tmp = PROBE_LIB + ".tmp"
+        _run([hipcc(), *COMMON, "-shared", os.path.join(HERE, "probe", "read_probe.hip"), "-o", probe_tmp], verbose)
     os.replace(tmp, LIB)
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 

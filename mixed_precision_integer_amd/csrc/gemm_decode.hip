@@ -51,6 +51,9 @@ constexpr int SLOT = 2 * 32 * PAIR;       // 32 weight rows, then 32 token rows
 constexpr int WAVE_LDS = 2 * SLOT;        // two slots per wave
 constexpr int RED_BYTES = WAVES * 16 * 64 * 4;
 static_assert(WAVES * WAVE_LDS >= RED_BYTES, "the reduction reuses the ring");
+constexpr int MAXG = MAXT * WAVES;        // scale groups of a row (K_n <= 16384, groups >= 128 channels)
+constexpr int SC_BYTES = 32 * MAXG * 4;   // the stripe's 32 weight rows (or 32 token rows) of scales
+constexpr int DECODE_LDS = WAVES * WAVE_LDS + 2 * SC_BYTES;
 
 __device__ __forceinline__ v4i as_v4i(uint4 p) { return v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w}; }
 
@@ -77,7 +80,7 @@ __device__ __forceinline__ void export_block(const v16i &acc, int32_t *dst, int 
 
 template <bool EXPORT>
 __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
-    __shared__ __align__(16) unsigned char lds[WAVES * WAVE_LDS];
+    __shared__ __align__(16) unsigned char lds[DECODE_LDS];
 
     const int tid = threadIdx.x;
     // the wave index is uniform, so the tile schedule is scalar code
@@ -91,18 +94,26 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
     const int tb = min(wave * per, T4), te = min(tb + per, T4);
     const int nt = te - tb, np = (nt + 1) / 2;                // tiles and pairs of this wave
 
-    // ---- scales of this wave's tiles and its first INT8 tail tile, requested
-    // before any DMA. The DMA waits are counted by hand; loads complete in
-    // order, so the first wait on a DMA also covers these older loads, and they
-    // travel together with the first pairs.
+    // ---- the INT4 scales of the stripe's weight rows and of the token rows:
+    // each is one contiguous run of rows x G floats, staged into LDS by DMA
+    // of 4 bytes per lane (every lane issues the same count; past the end a
+    // lane repeats the last float into a slot nothing reads), ahead of
+    // everything else. Then the wave's first INT8 tail tile. The DMA waits
+    // are counted by hand; loads complete in order, so the first wait on a
+    // pair also covers these older loads, and they travel with the first pairs.
     const int64_t nrow = min(n0 + li, a.N - 1), mrow = min(li, a.M - 1);
-    float sw[MAXT], sa[MAXT];
-#pragma unroll
-    for (int k = 0; k < MAXT; ++k) {
-        const int g = min(tb + k, T4 - 1) / tiles_per_group;
-        sw[k] = a.sw4[nrow * a.G + g] * (1.0f / 256.0f);
-        sa[k] = a.sa4[mrow * a.G + g];
+    const int wrows = min(32, a.N - n0), xrows = min(32, a.M);
+    float *sws = reinterpret_cast<float *>(lds + WAVES * WAVE_LDS);
+    float *sas = reinterpret_cast<float *>(lds + WAVES * WAVE_LDS + SC_BYTES);
+    {
+        const int nw = wrows * a.G, nx = xrows * a.G;          // <= 32 MAXG floats each
+        const float *wsrc = a.sw4 + (int64_t)n0 * a.G;
+        for (int i = 0; i * THREADS < nw; ++i)
+            dma4s(wsrc, 4u * (uint32_t)min(i * THREADS + tid, nw - 1), lds_addr(sws) + i * THREADS * 4 + wave * 256);
+        for (int i = 0; i * THREADS < nx; ++i)
+            dma4s(a.sa4, 4u * (uint32_t)min(i * THREADS + tid, nx - 1), lds_addr(sas) + i * THREADS * 4 + wave * 256);
     }
+    const int swrow = (int)(nrow - n0) * a.G, sarow = (int)mrow * a.G;
     const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
     const uint8_t *x8row = reinterpret_cast<const uint8_t *>(a.a8) + mrow * a.pitch8 + 16 * lh;
     uint4 tw[2] = {}, tx[2] = {};
@@ -162,7 +173,9 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
         if constexpr (EXPORT)
             export_block(acc, a.acc4_out + (int64_t)((tb + k) / tiles_per_group) * a.M * a.N, 8, a, 0, n0, li, lh);
         // scale products S[n][m] = sw[n] * sa[m] / 256 (the k = 1 lanes give zero)
-        const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw[k], lh ? 0.0f : sa[k], zf, 0, 0, 0);
+        const int g = (tb + k) / tiles_per_group;
+        const float swk = sws[swrow + g] * (1.0f / 256.0f), sak = sas[sarow + g];
+        const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : swk, lh ? 0.0f : sak, zf, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             y[e] = __builtin_fmaf((float)acc[e], S[e], y[e]);
@@ -174,6 +187,15 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
         issue(0);
     if (np > 1)
         issue(1);
+    // every lane's scale DMAs (older than its pairs) have landed
+    compiler_fence();
+    if (np > 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(16));
+    else if (np == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < MAXT / 2; ++j) {
         if (j < np) {

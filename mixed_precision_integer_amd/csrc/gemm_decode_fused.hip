@@ -68,7 +68,8 @@ constexpr int TAIL = MAXM * kTileBytes;    // INT8 codes of the wave's tail tile
 constexpr int SCL = MAXM * MAXT * 4 + MAXM * 4;   // group scales, then tail scales
 constexpr int WAVE_AREA = TOK + TAIL + SCL;
 constexpr int SUMS = WAVES * MAXM * 16;      // partial sums of squares (RMSNorm), 128 bits each
-constexpr int LDS_BYTES = RING + WAVES * WAVE_AREA + SUMS;
+constexpr int WSC = 32 * MAXT * 4;         // weight scales of a wave's tiles, [32 rows][nt]
+constexpr int LDS_BYTES = RING + WAVES * WAVE_AREA + SUMS + WAVES * WSC;
 constexpr int RED_BYTES = WAVES * 16 * 64 * 4;
 static_assert(RING >= RED_BYTES, "the reduction reuses the ring");
 static_assert(LDS_BYTES <= 160 * 1024, "one workgroup per CU");
@@ -145,10 +146,22 @@ __global__ __launch_bounds__(THREADS) void decode_fused_kernel(DecodeFusedArgs a
     const bool tail_wave = T8 > wave;
 
     // ---- loads that do not depend on anything: weight scales and tail ------------
-    float sw[MAXT];
-#pragma unroll
-    for (int k = 0; k < MAXT; ++k)
-        sw[k] = a.sw4[nrow * G + min(tb + k, T4 - 1)] * (1.0f / 256.0f);
+    // The weight scales of the wave's tiles (32 rows x nt floats, nt
+    // consecutive floats per row) go to LDS by DMA of 4 bytes per lane, a
+    // row segment to consecutive lanes, so an instruction touches two to
+    // eight rows instead of the 32 that a per-lane load of one tile's scale
+    // touches. They are older than every later load, so the first wait on a
+    // pair covers them.
+    float *swl = reinterpret_cast<float *>(lds + RING + WAVES * WAVE_AREA + SUMS + wave * WSC);
+    {
+        const int units = 32 * nt, rmax = a.N - 1 - n0;
+        const float *sbase = a.sw4 + (int64_t)n0 * G + tb;
+        for (int i = 0; i * 64 < units; ++i) {
+            const int u = min(i * 64 + lane, units - 1), r = u / nt, k = u - r * nt;
+            dma4s(sbase, 4u * (uint32_t)(min(r, rmax) * G + k), lds_addr(swl) + i * 256);
+        }
+    }
+    const int swr = (int)(nrow - n0) * nt;
     const uint8_t *w8row = reinterpret_cast<const uint8_t *>(a.w8) + nrow * a.pitch8 + 16 * lh;
     uint4 tw[2] = {};
     if (tail_wave) {
@@ -418,14 +431,15 @@ __global__ __launch_bounds__(THREADS) void decode_fused_kernel(DecodeFusedArgs a
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1, x1, acc, 0, 0, 0);
         }
         // scale products S[n][m] = sw[n] * sa[m] / 256 (the k = 1 lanes give zero)
-        const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : sw[k], lh ? 0.0f : sa[k], zf, 0, 0, 0);
+        const float swk = swl[swr + k] * (1.0f / 256.0f);
+        const v16f S = __builtin_amdgcn_mfma_f32_32x32x2f32(lh ? 0.0f : swk, lh ? 0.0f : sa[k], zf, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             y[e] = __builtin_fmaf((float)acc[e], S[e], y[e]);
     };
 
     // ---- INT4 tiles: up to SLOTS pairs in flight; the loop is unrolled (the
-    // scales of tile k sit in registers sw[k], sa[k])
+    // token scales of tile k sit in registers sa[k], the weight scales in LDS)
 #pragma unroll
     for (int j = 0; j < MAXT / 2; ++j) {
         if (j < np) {
