@@ -367,3 +367,32 @@ def test_one_launch_decode_path_bounds():
     assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 256) == "gemm_decode_kernel<false>"
     assert w4.quant_gemm_kernel_name(2048, 4096, 4096, 128, 128) == w4.outlier_gemm_kernel_name(2048, 4096, 4096, 128, 128)
     assert w4.quant_gemm_kernel_name(0, 256, 1152, 128, 128) is None
+
+
+PROBE = os.path.join(ROOT, "mixed_precision_integer_amd", "libw4a4_probe.so")
+
+
+def _probe():
+    if not os.path.exists(PROBE):
+        pytest.skip("libw4a4_probe.so is not built")
+    L = ctypes.CDLL(PROBE)
+    L.w4a4_read_probe.restype = ctypes.c_int32
+    L.w4a4_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.w4a4_read_probe_out_words.restype = ctypes.c_int64
+    L.w4a4_read_probe_out_words.argtypes = [ctypes.c_int32]
+    return L
+
+
+def test_read_probe_library_host_checks():
+    """The streaming-read probe (a measurement tool in a library of its own)
+    exports its two calls and rejects bad arguments before any launch."""
+    L = _probe()
+    assert L.w4a4_read_probe_out_words(256) == 256 * 256
+    assert L.w4a4_read_probe_out_words(0) == -1
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: every call below is rejected
+    assert L.w4a4_read_probe(None, 1024, 256, 4, 0, fake, None) == 1
+    assert L.w4a4_read_probe(fake, 1000, 256, 4, 0, fake, None) == 1      # not a multiple of 16
+    assert L.w4a4_read_probe(fake, 1024, 0, 4, 0, fake, None) == 1        # no workgroups
+    assert L.w4a4_read_probe(fake, 1024, 256, 3, 0, fake, None) == 1      # depth not offered
+    assert L.w4a4_read_probe(ctypes.c_void_p((1 << 20) + 4), 1024, 256, 4, 0, fake, None) == 1
