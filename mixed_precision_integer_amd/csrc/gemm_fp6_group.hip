@@ -25,8 +25,9 @@ namespace gemm_fp6_impl {
 //   v_mfma_f32_32x32x1_2b_f32: exact fp32 outer products of row and column
 //   scales, in the accumulator layout), the fold of that group's sums, and
 //   this group's two k-steps into the same registers (C = 0 on the first).
-// * Ring of three stages of one group each (both k-steps of A and B, the
-//   group's 128 row scales and 128 column scales), two groups ahead; the
+// * Ring of three stages of one group each (both k-steps of A and B), two
+//   groups ahead; the group scales of four groups at a time in a double
+//   buffer beside it, requested with the first group of their block; the
 //   previous group's scales are kept in registers for its fold.
 // * The INT8 tail and the epilogue as in the 256 x 256 kernel:
 //   Y = fp16(y + acc8 * (sa8 sw8)).
@@ -35,19 +36,24 @@ constexpr int GBM = 128, GBN = 128, GWT = 64, GF = 2;
 constexpr int GSTAGES = 3;
 constexpr int G_A = 0;                              // A: k-step s, block i at s * 4 BLK + i BLK
 constexpr int G_B = 2 * (GBM / 32) * BLK;           // B: k-step s, block i at G_B + s * 4 BLK + i BLK
-constexpr int G_SC = G_B + 2 * (GBN / 32) * BLK;    // sa[128], then sw[128]
-constexpr int GSTAGE = G_SC + (GBM + GBN) * 4;      // 25600 bytes
+constexpr int GSTAGE = G_B + 2 * (GBN / 32) * BLK;  // 24576 bytes
 constexpr int G_DA = 2 * (GBM / 32) * BLK / 16 / kGThreads;  // 3 DMA units of A per group per lane
 constexpr int G_DB = 2 * (GBN / 32) * BLK / 16 / kGThreads;  // 3 of B
-constexpr int G_D = G_DA + G_DB + 1;                // + one scale: 7 per lane
+constexpr int G_D = G_DA + G_DB;                    // 6 per lane (+ 4 scale units every G_SB groups)
 constexpr int G_TAIL_TILE = (GBM + GBN) * kTileBytes;   // 16 KB
-constexpr int G_SCALES8 = GSTAGES * GSTAGE;         // sa8[128], sw8[128] of the tile
-constexpr int G_LDS_BYTES = G_SCALES8 + (GBM + GBN) * 4;
+// Group scales go in blocks of G_SB groups: rows [128][G_SB], then columns
+// [128][G_SB], two blocks (double buffer) after the ring. After the loop the
+// first block holds the tail scales sa8[128], sw8[128] of the tile.
+constexpr int G_SB = 4;
+constexpr int G_SBUF = G_SB * (GBM + GBN) * 4;      // 4 KB
+constexpr int G_SCB = GSTAGES * GSTAGE;
+constexpr int G_SCALES8 = G_SCB;
+constexpr int G_LDS_BYTES = G_SCB + 2 * G_SBUF;     // 80 KB: two workgroups per CU
 constexpr int G_YP = 2 * GBN + 16;                  // bytes per row of the staged fp16 tile
-static_assert(GBM * G_YP <= G_SCALES8, "the staged tile fits the ring");
+static_assert(GBM * G_YP <= G_SCB, "the staged tile fits the ring");
 static_assert(G_DA == 3 && G_DB == 3 && GBM + GBN == kGThreads, "whole DMA rounds");
 static_assert(2 * G_LDS_BYTES <= 160 * 1024, "two workgroups per CU");
-static_assert(MAX_TAIL_TILES * G_TAIL_TILE <= G_SCALES8, "the tail fits the ring");
+static_assert(MAX_TAIL_TILES * G_TAIL_TILE <= G_SCB, "the tail fits the ring");
 
 // FP6 MFMA (operands FP6 E2M3 holding q / 2, block scale 2^1 on each):
 // acc += w^T x, and acc = w^T x. Written as instructions so that every
@@ -94,8 +100,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
     const int T8 = (int)(a.pitch8 / kTileBytes);
 
     // DMA sources. A and B alike: unit q = j * 256 + tid (768 per group),
-    // k-step q / 384, block (q % 384) / 96, 16-byte unit q % 96. Scales:
-    // waves 0-1 the 128 row scales, waves 2-3 the 128 column scales.
+    // k-step q / 384, block (q % 384) / 96, 16-byte unit q % 96. Scales: a
+    // block of G_SB groups with the first group of the block, unit u =
+    // i * 256 + tid of each table being row (or column) u / G_SB, group
+    // u % G_SB: a wave's 64 units are the G_SB consecutive floats of 16 rows
+    // (16 cache lines, where one scale per row per group would touch 64).
     uint32_t oa[G_DA], ob[G_DB];
 #pragma unroll
     for (int j = 0; j < G_DA; ++j) {
@@ -116,18 +125,16 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
 #pragma unroll
         for (int j = 0; j < G_DB; ++j)
             dma16(B, ob[j], st + G_B + j * 4096 + wave_u * 1024);
-        if (low)
-            dma4(a.sa4 + srow * G + g, st + G_SC + wave_u * 256);
-        else
-            dma4(a.sw4 + scol * G + g, st + G_SC + wave_u * 256);   // slots GBM.. (wave 2 starts at 512)
+        if (gg % G_SB == 0) {                       // uniform: the scale block of groups gg ..
+            const uint32_t sb = lds_addr(lds) + G_SCB + ((gg / G_SB) & 1) * G_SBUF;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int u = i * kGThreads + tid, r = u / G_SB, gk = min(gg + u % G_SB, G - 1);
+                dma4(a.sa4 + (int64_t)min(row0 + r, a.M - 1) * G + gk, sb + i * 1024 + wave_u * 256);
+                dma4(a.sw4 + (int64_t)min(col0 + r, a.N - 1) * G + gk, sb + GBM * G_SB * 4 + i * 1024 + wave_u * 256);
+            }
+        }
     };
-    if (T8 > 0) {                                  // tail scales, ahead of everything
-        const uint32_t ss = lds_addr(lds) + G_SCALES8;
-        if (low)
-            dma4(a.sa8 + srow, ss + wave_u * 256);
-        else
-            dma4(a.sw8 + scol, ss + wave_u * 256);
-    }
 
     float y[GF][GF][16];
 #pragma unroll
@@ -179,7 +186,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
     float prs = 0.0f, pca = 0.0f, pcb = 0.0f;
     for (int g = 0; g < G; ++g) {
         compiler_fence();
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(G_D));         // group g has landed (g + 1 may not)
+        // group g has landed (g + 1, and the scale block that comes with it, may not)
+        if ((g + 1) % G_SB == 0)
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(G_D + 4));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(G_D));
         __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -197,10 +208,10 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
                 fa[s][i] = load_operand(lds + st + G_A + (s * 4 + wm * 2 + i) * BLK + llo, lds + st + ha[s][i]);
                 fb[s][i] = load_operand(lds + st + G_B + (s * 4 + wn * 2 + i) * BLK + llo, lds + st + hb[s][i]);
             }
-        const float *sc = reinterpret_cast<const float *>(lds + st + G_SC);
-        const float crs = sc[wm * GWT + lh * 32 + li];
-        const float cca = sc[GBM + wn * GWT + lh * 32 + li];
-        const float ccb = sc[GBM + wn * GWT + (1 - lh) * 32 + li];
+        const float *sc = reinterpret_cast<const float *>(lds + G_SCB + ((g / G_SB) & 1) * G_SBUF) + g % G_SB;
+        const float crs = sc[(wm * GWT + lh * 32 + li) * G_SB];
+        const float cca = sc[(GBM + wn * GWT + lh * 32 + li) * G_SB];
+        const float ccb = sc[(GBM + wn * GWT + (1 - lh) * 32 + li) * G_SB];
         // pair c: blocks (0, c) in the first half of S, (1, 1 - c) in the second
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -234,6 +245,13 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     if (T8 > 0) {
+        {                                                          // tail scales into the first scale block
+            const uint32_t ss = lds_addr(lds) + G_SCALES8;
+            if (low)
+                dma4(a.sa8 + srow, ss + wave_u * 256);
+            else
+                dma4(a.sw8 + scol, ss + wave_u * 256);
+        }
 #pragma unroll
         for (int j = 0; j < MAX_TAIL_TILES; ++j) {
             if (j >= T8)
