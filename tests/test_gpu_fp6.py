@@ -242,3 +242,34 @@ def test_fp6_kernel_names():
     assert w4.outlier_gemm_fp6_kernel_name(257, 8192, 8192, 128, 128) == "gemm_fp6_group_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(4096, 11008, 4096, 256, 0) == "gemm_fp6_big_kernel<false>"
     assert w4.outlier_gemm_fp6_kernel_name(2048, 4096, 4352, 256, 256) is None    # groups of 256
+
+
+@pytest.mark.parametrize("M,N,K,n_out,group", [
+    (512, 512, 640, 64, 0),         # 256 x 256 kernel: interior tiles
+    (300, 520, 1152, 128, 0),       # 256 x 256 kernel: edge tiles
+    (384, 384, 1152, 128, 128),     # group kernel, interior tiles
+    (200, 264, 1152, 128, 128),     # group kernel, edge tiles
+    (96, 256, 1152, 128, 128),      # decode kernel
+])
+@pytest.mark.parametrize("pad,col", [(8, 0), (4, 0), (1, 1), (0, 3)], ids=["ld16B", "ld8B", "ld2B", "off2B"])
+def test_fp6_strided_output(M, N, K, n_out, group, pad, col):
+    """Y written into a view with another row stride or a start that is only
+    8- or 2-byte aligned takes the epilogues' narrower store paths; it must
+    equal the contiguous result bit for bit, and nothing outside the view may
+    change."""
+    rng = np.random.default_rng(M + N + pad)
+    X = (rng.standard_normal((M, K)) * 2).astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float16)
+    outliers = np.sort(rng.choice(K, n_out, replace=False)) if n_out else np.zeros(0, np.int64)
+    perm = torch.from_numpy(w4.make_perm(K, outliers)).to(DEV)
+    Xd, Wd = torch.from_numpy(X).to(DEV), torch.from_numpy(W).to(DEV)
+    af = w4.to_fp6(w4.quant_reorder_act(Xd, perm, n_out, group))
+    wf = w4.to_fp6(w4.pack_int4_weights(Wd, perm, n_out, group))
+    ref = w4.outlier_gemm_fp6(af, wf)
+    big = torch.full((M, N + pad + col), float("nan"), dtype=torch.float16, device=DEV)
+    view = big[:, col:col + N]
+    w4.outlier_gemm_fp6(af, wf, out=view)
+    torch.cuda.synchronize()
+    assert torch.equal(view, ref)
+    outside = torch.cat([big[:, :col].flatten(), big[:, col + N:].flatten()])
+    assert bool(torch.isnan(outside).all())
