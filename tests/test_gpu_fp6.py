@@ -203,6 +203,8 @@ def test_fp6_full_size_workload(oracle, work):
     (37, 768, 128, 128),       # 128-channel group scales
     (2048, 4096, 128, 128),    # q_proj-shaped rows with group scales
     (9, 24576, 128, 128),      # group scales on the longest rows
+    (1100, 22016, 256, 0),     # several rows per workgroup of the 24576 bucket
+    (700, 20096, 128, 128),    # the same with group scales
 ])
 def test_u6_producer(oracle, M, K, n_out, group):
     """w4a4_quant_reorder_act_u6 against the oracle: u6 bytes (rows past M up
