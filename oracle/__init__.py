@@ -223,15 +223,20 @@ def e2m3_value(code: int) -> float:
     return -v if s else v
 
 
+# The FP6 operand holds q / U6_DIV, and the matrix instruction's block scale
+# U6_DIV on each operand restores q.
+U6_DIV = 8
+
+
 def e2m3_code(q: int) -> int:
-    """The E2M3 code of the INT4 code q: the code whose value is q / 2 (|q| <=
-    8 here; every half-integer of magnitude <= 4 is exact in E2M3, and the
-    operand scale 2 of the matrix instruction restores q). Zero is +0."""
+    """The E2M3 code of the INT4 code q: the code whose value is q / 8 (|q| <=
+    8 here; the multiples of 1/8 up to 1 in magnitude are exact in E2M3, the
+    ones below 1 as subnormals). Zero is +0."""
     if q == 0:
         return 0
-    hits = [c for c in range(64) if e2m3_value(c) == q / 2]
+    hits = [c for c in range(64) if e2m3_value(c) == q / U6_DIV]
     if len(hits) != 1:
-        raise ValueError(f"{q} / 2 is not exactly representable in E2M3")
+        raise ValueError(f"{q} / {U6_DIV} is not exactly representable in E2M3")
     return hits[0]
 
 
@@ -283,7 +288,7 @@ def pack_u6(q4, pitch4: int) -> np.ndarray:
 
 
 def unpack_u6(u6, rows: int, K_n: int) -> np.ndarray:
-    """Inverse of pack_u6: the INT4 codes [rows, K_n] (twice the values of the E2M3 codes)."""
+    """Inverse of pack_u6: the INT4 codes [rows, K_n] (U6_DIV times the values of the E2M3 codes)."""
     u6 = np.asarray(u6, np.uint8)
     pitch4 = (K_n + 127) // 128 * 64
     T = pitch4 // 32
@@ -298,7 +303,7 @@ def unpack_u6(u6, rows: int, K_n: int) -> np.ndarray:
                     bytes(blk[1024 + 256 * h + 8 * rr:1024 + 256 * h + 8 * rr + 8])
                 bits = int.from_bytes(img, "little")
                 for i in range(32):
-                    out[r, 64 * t + 32 * h + i] = int(2 * e2m3_value((bits >> (6 * i)) & 63))
+                    out[r, 64 * t + 32 * h + i] = int(U6_DIV * e2m3_value((bits >> (6 * i)) & 63))
     return out[:, :K_n]
 
 

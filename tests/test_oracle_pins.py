@@ -381,15 +381,15 @@ def test_e2m3_codes_match_hand_derived(oracle):
     want = json.load(open(E2M3))["codes"]
     for q, code in want.items():
         assert oracle.e2m3_code(int(q)) == code, q
-        assert oracle.e2m3_value(code) == int(q) / 2
+        assert oracle.e2m3_value(code) == int(q) / 8
 
 
 def test_e2m3_value_closed_forms(oracle):
     assert oracle.e2m3_value(0b011111) == 7.5           # the largest finite value: 2^2 * 1.875
-    assert oracle.e2m3_value(0b011000) == 4.0           # 2^2: -8 / 2 in magnitude
+    assert oracle.e2m3_value(0b011000) == 4.0           # 2^2
     assert oracle.e2m3_value(0b000001) == 1 / 8         # the smallest subnormal
     assert oracle.e2m3_value(0b000111) == 7 / 8         # the largest subnormal
-    assert oracle.e2m3_value(0b001000) == 1.0           # the smallest normal
+    assert oracle.e2m3_value(0b001000) == 1.0           # the smallest normal: -8 / 8 in magnitude
     assert oracle.e2m3_value(0b100000) == 0.0           # -0
     assert oracle.e2m3_value(0b110100) == -3.0          # -2^1 * 1.5
     vals = sorted(oracle.e2m3_value(c) for c in range(32))
@@ -431,11 +431,11 @@ def test_pack_u6_round_trip(oracle):
 
 def test_pack_u6_known_bytes(oracle):
     """One chunk by hand: q = [1, -1, 7, -8, 0, ...] in row 0: the E2M3 codes
-    of 0.5, -0.5, 3.5, -4 are 4, 36, 22, 56, at bits 0, 6, 12, 18 ->
-    4 | 36 << 6 | 22 << 12 | 56 << 18 = 0xE16904, the first bytes of block (0, 0)."""
+    of 1/8, -1/8, 7/8, -1 are 1, 33, 7, 40, at bits 0, 6, 12, 18 ->
+    1 | 33 << 6 | 7 << 12 | 40 << 18 = 0xA07841, the first bytes of block (0, 0)."""
     q = np.zeros((1, 32), np.int8)
     q[0, :4] = [1, -1, 7, -8]
     u6 = oracle.pack_u6(q, 64)
     assert u6.size == 2 * 1536
-    assert u6[:4].tolist() == [0x04, 0x69, 0xE1, 0x00]
+    assert u6[:4].tolist() == [0x41, 0x78, 0xA0, 0x00]
     assert not u6[4:].any()
