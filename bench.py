@@ -545,7 +545,7 @@ def main():
     ap.add_argument("--kv", default=None, choices=sorted(KV_WORKLOADS),
                     help="instead of the layer, time the low-bit KV cache (quantize + gather)")
     ap.add_argument("--path", default="auto", choices=("auto", "fp6", "i8"),
-                    help="prefill GEMM path: fp6 (INT4 codes q as FP6 E2M3 q / 2 on the FP6 matrix cores) or i8 "
+                    help="prefill GEMM path: fp6 (INT4 codes q as FP6 E2M3 q / 8 on the FP6 matrix cores) or i8 "
                          "(widened nibbles on the i8 matrix cores); auto takes fp6 where it applies, "
                          "no RMSNorm is fused and its tiles fill every CU")
     ap.add_argument("--norm", action="store_true",

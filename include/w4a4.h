@@ -257,10 +257,11 @@ w4a4_status w4a4_rmsnorm_quant_gemm(const void *X, int64_t ldx, const void *gamm
 /* ---------------------------------------------------------------------------
  * FP6 prefill path. The layer's INT4 x INT4 sums (Atom summary page, Summary
  * paragraph 2 and Key points item 5) formed on CDNA4's FP6 matrix
- * instruction: every INT4 code q is held as the FP6 E2M3 code of q / 2 (sign
+ * instruction: every INT4 code q is held as the FP6 E2M3 code of q / 8 (sign
  * bit 5, exponent bits 4..3 with bias 1, mantissa bits 2..0, as the OCP
- * Microscaling Formats v1.0 define E2M3; exact for |q| <= 8) and multiplied
- * with an operand block scale of 2^1, so products and partial sums are the
+ * Microscaling Formats v1.0 define E2M3; exact for |q| <= 8, and the code is
+ * |q| with the sign in bit 5) and multiplied
+ * with an operand block scale of 2^3, so products and partial sums are the
  * integers below 2^24 of the codes, and the fp32 accumulators hold the exact integer
  * sums: the results are those of w4a4_outlier_gemm, with the same int32
  * accumulators. The INT8 outlier tail is unchanged.

@@ -443,7 +443,7 @@ def select_outliers(Xcal, n_out: int, workspace=None, want_absmax: bool = False)
 
 
 # ---------------------------------------------------------------------------
-# FP6 prefill path: INT4 codes q held as the FP6 E2M3 values q / 2 ("u6" operands)
+# FP6 prefill path: INT4 codes q held as the FP6 E2M3 values q / 8 ("u6" operands)
 # ---------------------------------------------------------------------------
 def u6_bytes(rows: int, K_n: int) -> int:
     return int(lib().w4a4_u6_bytes(rows, K_n))

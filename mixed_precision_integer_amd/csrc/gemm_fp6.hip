@@ -1,5 +1,5 @@
 // Prefill GEMM on the FP6 matrix cores: INT4 x INT4 head with each INT4 code
-// q held as the FP6 E2M3 value q / 2, exact fp32 accumulation; INT8 x INT8 outlier tail
+// q held as the FP6 E2M3 value q / 8, exact fp32 accumulation; INT8 x INT8 outlier tail
 // on the i8 matrix cores; fp32 scale epilogue to fp16.
 //
 // Method: Atom summary page (Summary paragraph 2: INT4 main part plus an
@@ -11,14 +11,16 @@
 // CDNA4 design
 // * CDNA4 has no INT4 matrix instruction, but its FP6 one
 //   (v_mfma_scale_f32_32x32x64_f8f6f4) runs at twice the i8 rate. E2M3 holds
-//   q / 2 exactly for every INT4 code (the multiples of 1/2 up to 4 in
-//   magnitude), and the instruction's block scale 2^1 on each operand gives
-//   back q: every product is the integer qa qw (below 2^7) and every partial
+//   q / 8 exactly for every INT4 code (the multiples of 1/8 up to 1 in
+//   magnitude: subnormals below 1, so the code is |q| with a sign bit), and
+//   the instruction's block scale 2^3 on each operand gives back q: every product is the integer qa qw (below 2^7) and every partial
 //   sum an integer below 2^24 in magnitude (|sum| <= 64 K_n), so the fp32
 //   accumulator holds the exact integer sum whatever order the matrix core
 //   adds in; the accumulator export converts it to int32 unchanged. (E3M2,
-//   which holds q itself, is exact too; with E2M3 codes the matrix core
-//   draws less power on these operands and the kernel runs about 5% faster.)
+//   which holds q itself, and E2M3 of q / 2 are exact too. The matrix core's
+//   power, and with it the clock, depends on the operand bits: E2M3 of q / 2
+//   ran about 5% faster than E3M2 of q, and E2M3 of q / 8, whose codes are
+//   the small integers |q|, about 1.5% faster again.)
 // * The FP6 operand of a lane is a 192-bit image of 32 codes (code i at bits
 //   6i). Unpacking nibbles into it costs more VALU per MFMA than the FP6
 //   rate leaves, so the operands arrive already in that form, in a "u6"
@@ -53,16 +55,14 @@ namespace gemm_fp6_impl {
 // repack: packed two's complement nibbles -> u6 planes
 // ---------------------------------------------------------------------------
 
-// E2M3 codes of |q| / 2 for |q| = 0..8, six bits each (code = e << 3 | m,
-// value 2^(e-1) (1 + m/8), subnormal m/8): 0, 0.5 = 4/8 (subnormal),
-// 1 = 2^0, 1.5, 2 = 2^1, 2.5, 3, 3.5, 4 = 2^2; the sign is bit 5.
-constexpr uint64_t kMagCodes = (0ull << 0) | (4ull << 6) | (8ull << 12) | (12ull << 18) | (16ull << 24) |
-                               (18ull << 30) | (20ull << 36) | (22ull << 42) | (24ull << 48);
-
+// E2M3 code of q / 8 for a two's complement nibble q (code = s << 5 | e << 3
+// | m, value 2^(e-1) (1 + m/8), subnormal m/8): |q| / 8 for |q| = 1..7 is the
+// subnormal m = |q|, and 8 / 8 = 2^0 is e = 1, m = 0, so the code is |q| with
+// the sign in bit 5.
 __device__ __forceinline__ uint32_t e2m3_of_nibble(uint32_t n) {
     const uint32_t neg = (n >> 3) & 1;
     const uint32_t mag = neg ? 16u - n : n;                  // |q| of the two's complement nibble
-    return (neg << 5) | (uint32_t)((kMagCodes >> (6 * mag)) & 63);
+    return (neg << 5) | mag;
 }
 
 // One lane per (row, 64-channel tile): 32 nibble bytes in, the two chunk
@@ -121,8 +121,8 @@ static_assert(MAX_TAIL_TILES * TAIL_TILE <= Y_SLOTS, "the slots stay clear of th
 static_assert(STAGE == 24576 && DPO == 3, "stage layout");
 static_assert((STAGES - 1) * D <= 63, "vmcnt range");
 
-// acc += w^T x for one 32 x 32 block (both operands FP6 E2M3 holding q / 2,
-// block scale exponent 128 = 2^1 on each).
+// acc += w^T x for one 32 x 32 block (both operands FP6 E2M3 holding q / 8,
+// block scale exponent 130 = 2^3 on each).
 // Block (fm, fn) takes the weight fragment as the first operand, so lane
 // (li, lh) holds token row li and the columns 8 (r / 4) + 4 lh + r % 4.
 // Written as an instruction so that the accumulators stay in AGPRs and the
@@ -135,7 +135,7 @@ static_assert((STAGES - 1) * D <= 63, "vmcnt range");
 __device__ __forceinline__ void mma(v16f &acc, const v6i &w, const v6i &x) {
     asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
                  : "+a"(acc)
-                 : "v"(w), "v"(x), "v"(128));
+                 : "v"(w), "v"(x), "v"(130));
 }
 
 // acc8 += w^T x and acc8 = w^T x on the i8 matrix core (the INT8 tail),

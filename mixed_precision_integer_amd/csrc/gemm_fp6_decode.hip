@@ -4,8 +4,8 @@
 // Method: the layer of the QUIK abstract and the Atom summary page (Summary
 // paragraph 2: INT4 groups of 128 channels with their own scales, 8-bit
 // outliers; Key points item 5: symmetric scales factor out of the integer
-// sums), here on gfx950's FP6 matrix instruction: E2M3 codes of q / 2 with a
-// block scale of 2 on each operand give exact integer sums in fp32.
+// sums), here on gfx950's FP6 matrix instruction: E2M3 codes of q / 8 with a
+// block scale of 8 on each operand give exact integer sums in fp32.
 //
 // Design (a decode batch reads each weight once from HBM; the tokens are
 // small and shared by every workgroup, so they are served by L2):
@@ -56,7 +56,7 @@ __device__ __forceinline__ v16f mma_fp6(const v6i &w, const v6i &x, const v16f &
     x8.s012345 = x;
     w8.s67 = v2i{0, 0};
     x8.s67 = v2i{0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, x8, c, 2, 2, 0, 128, 0, 128);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, x8, c, 2, 2, 0, 130, 0, 130);
 }
 
 // Waves: RG pairs of row blocks times KS contiguous ranges of groups

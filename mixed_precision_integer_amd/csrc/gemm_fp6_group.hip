@@ -55,7 +55,7 @@ static_assert(G_DA == 3 && G_DB == 3 && GBM + GBN == kGThreads, "whole DMA round
 static_assert(2 * G_LDS_BYTES <= 160 * 1024, "two workgroups per CU");
 static_assert(MAX_TAIL_TILES * G_TAIL_TILE <= G_SCB, "the tail fits the ring");
 
-// FP6 MFMA (operands FP6 E2M3 holding q / 2, block scale 2^1 on each):
+// FP6 MFMA (operands FP6 E2M3 holding q / 8, block scale 2^3 on each):
 // acc += w^T x, and acc = w^T x. Written as instructions so that every
 // register stays an architectural VGPR (the fold reads the sums with no AGPR
 // copies); block (fm, fn) takes the weight fragment as the first operand, so
@@ -63,12 +63,12 @@ static_assert(MAX_TAIL_TILES * G_TAIL_TILE <= G_SCB, "the tail fits the ring");
 __device__ __forceinline__ void mma(v16f &acc, const v6i &w, const v6i &x) {
     asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
                  : "+v"(acc)
-                 : "v"(w), "v"(x), "v"(128));
+                 : "v"(w), "v"(x), "v"(130));
 }
 __device__ __forceinline__ void mma0(v16f &acc, const v6i &w, const v6i &x) {
     asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
                  : "=&v"(acc)
-                 : "v"(w), "v"(x), "v"(128));
+                 : "v"(w), "v"(x), "v"(130));
 }
 
 __device__ __forceinline__ float y_value_g(float yh, int acc8, float s8) {

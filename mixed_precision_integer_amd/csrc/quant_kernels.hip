@@ -148,15 +148,15 @@ __device__ __forceinline__ void lds_barrier() {
 // 1024 + 256 h + 8 r.
 constexpr int64_t kU6Block = 1536;
 
-// E2M3 codes of q / 2 for four offset codes c = q + 8 (bytes, 0..15): two
+// E2M3 codes of q / 8 for four offset codes c = q + 8 (bytes, 0..15): two
 // 8-entry byte tables (c < 8 and c >= 8) looked up by v_perm with c & 7,
 // then a third v_perm takes each byte from the second table where bit 3 of
-// c is set. Tables: q = -8..-1 -> 56 54 52 50 48 44 40 36; q = 0..7 -> 0 4 8
-// 12 16 18 20 22.
+// c is set. Tables (the code is |q| with the sign in bit 5): q = -8..-1 ->
+// 40 39 38 37 36 35 34 33; q = 0..7 -> 0 1 2 3 4 5 6 7.
 __device__ __forceinline__ uint32_t e2m3_of_offset4(uint32_t c) {
     const uint32_t sel = c & 0x07070707u;
-    const uint32_t neg = __builtin_amdgcn_perm(0x24282C30u, 0x32343638u, sel);
-    const uint32_t pos = __builtin_amdgcn_perm(0x16141210u, 0x0C080400u, sel);
+    const uint32_t neg = __builtin_amdgcn_perm(0x21222324u, 0x25262728u, sel);
+    const uint32_t pos = __builtin_amdgcn_perm(0x07060504u, 0x03020100u, sel);
     return __builtin_amdgcn_perm(pos, neg, ((c >> 1) & 0x04040404u) | 0x03020100u);
 }
 
@@ -556,7 +556,7 @@ void quant_rows_kernel(QuantArgs a) {
 
         // (4) INT4 head: codes + 8 as bytes, even channels in one dword and odd
         //     ones in another, then one nibble interleave and an xor with 8
-        //     (or, for the u6 operand, the FP6 E2M3 codes of q / 2)
+        //     (or, for the u6 operand, the FP6 E2M3 codes of q / 8)
         if constexpr (U6) {
             // The four units of a 32-channel chunk sit in one quad of lanes
             // (units i * THREADS + tid, THREADS and W4 multiples of 4): each
@@ -855,8 +855,9 @@ __global__ __launch_bounds__(256) void quant_group_kernel(QuantArgs a, int NC) {
 // channels 32c .. 32c + 31), so that gfx950's 32-value FP6 conversion
 // (v_cvt_scalef32_pk32_fp6_f16) forms the chunk's 192-bit image in one
 // instruction: with the integer codes q as fp16 inputs and a conversion scale
-// of 2 it writes the E2M3 code of q / 2 of value i at bits 6i (checked on
-// the device against the code table). Per element what remains is the exact
+// of 8 it writes the E2M3 code of q / 8 of value i at bits 6i (every such
+// quotient is exact in E2M3; the GPU tests check every code against the
+// oracle's). Per element what remains is the exact
 // quotient (three mixed-precision FMAs), rint and half a conversion to fp16.
 // * Rows go global -> LDS by DMA in 16-byte pieces, with piece p stored in
 //   slot p ^ ((p >> 4) & 15): a lane gathers the 32 channels of its chunk,
@@ -1142,7 +1143,7 @@ void quant_u6_chunk_kernel(QuantArgs a) {
                 q[2 * p] = h.x;
                 q[2 * p + 1] = h.y;
             }
-            img = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(q, 2.0f);
+            img = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(q, 8.0f);
         }
         // (5) INT8 tail word (waves that hold tail words)
         if (tail_wave) {

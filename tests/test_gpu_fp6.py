@@ -1,4 +1,4 @@
-"""GPU parity of the FP6 prefill path (INT4 codes q held as the FP6 E2M3 values q / 2)
+"""GPU parity of the FP6 prefill path (INT4 codes q held as the FP6 E2M3 values q / 8)
 through the C ABI, against the CPU oracle.
 
 * The u6 conversion (w4a4_repack_u6) is checked byte for byte against the
@@ -150,7 +150,7 @@ def test_fp6_decode_full_size(oracle, M):
 
 
 def test_fp6_extreme_codes(oracle):
-    """All -8 codes (magnitude 8, the largest value used: E2M3 4 times 2) and random
+    """All -8 codes (magnitude 8, the largest value used: E2M3 1 times 8) and random
     full-range codes over the longest K: the sums reach 21760 * 64."""
     rng = np.random.default_rng(321)
     M, N, K_n, n_out = 64, 96, 21760, 256
