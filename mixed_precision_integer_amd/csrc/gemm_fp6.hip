@@ -283,11 +283,15 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_big_kernel(Fp6GemmArgs a) {
         // The sixteen MFMAs of tile t, each followed by one fragment read of
         // tile t + 1 (the first eight) or one DMA unit of tile t + 6 into tile
         // t's stage (the next six), so that every other instruction issues
-        // while an MFMA executes.
+        // while an MFMA executes. The blocks go in serpentine order (fn
+        // forward for even fm, backward for odd), so that consecutive MFMAs
+        // share one operand: fewer operand bits change from one MFMA to the
+        // next, the matrix core draws less power, and at the clock that power
+        // allows the kernel ran about 2% faster than in row order.
         const uint32_t sn = (uint32_t)(((t + 1) % STAGES) * STAGE);
 #pragma unroll
         for (int k = 0; k < FM * FN; ++k) {
-            const int fm = k / FN, fn = k % FN;
+            const int fm = k / FN, fn = fm % 2 == 0 ? k % FN : FN - 1 - k % FN;
             mma(acc[fm][fn], xb[fn], xa[fm]);
             if (k < FM)
                 na[k] = a_frag(sn, k);
