@@ -7,7 +7,7 @@
 // abstract (one-token decode is memory-bound).
 //
 // CDNA4 design (HBM-bound: every weight byte is read once). For M <= 32
-// (gemm_decode_kernel; the row-block kernel further down takes 32 < M <= 128):
+// (gemm_decode_kernel<XI>; the row-block kernel further down takes 32 < M <= 128):
 // * A workgroup owns 32 output columns and all M <= 32 token rows: one
 //   32 x 32 block of v_mfma_i32_32x32x32_i8 with the weight fragment as the
 //   first operand (lane (li, lh) holds token row li and the columns
@@ -15,7 +15,8 @@
 //   results are dropped.
 // * Its eight waves split the INT4 K-tiles (64 bytes of every row, 128
 //   channels) into contiguous ranges. Each wave moves pairs of tiles (128
-//   bytes of each of the 32 weight rows and 32 token rows) into a two-slot
+//   bytes of each of the 32 weight rows and of the token rows, 8 XI of them
+//   for a batch of at most 8 XI rows) into a two-slot
 //   LDS ring of its own by direct global->LDS DMA, eight lanes per row, so
 //   each DMA instruction covers eight whole cache lines; it reads them back
 //   in MFMA layout (16-byte chunks XOR-swizzled by row, conflict-free).
@@ -78,8 +79,14 @@ __device__ __forceinline__ void export_block(const v16i &acc, int32_t *dst, int 
     compiler_fence();
 }
 
-template <bool EXPORT>
+// XI: DMA instructions per pair for the token rows (eight rows each): rows
+// past the batch are never stored, so a batch of at most 8 XI rows moves
+// only its own rows (the MFMA lanes of the rows past them read slot bytes
+// whose results are dropped).
+template <int XI, bool EXPORT>
 __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
+    static_assert(XI >= 1 && XI <= 4, "one to four token DMA instructions per pair");
+    constexpr int PD = 4 + XI;                                // DMA instructions per pair
     __shared__ __align__(16) unsigned char lds[DECODE_LDS];
 
     const int tid = threadIdx.x;
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i)
             dma16(W, dup ? owd[i] : ow[i], st + i * 1024);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < XI; ++i)
             dma16(X, dup ? oxd[i] : ox[i], st + 32 * PAIR + i * 1024);
     };
 
@@ -190,9 +197,9 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
     // every lane's scale DMAs (older than its pairs) have landed
     compiler_fence();
     if (np > 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(16));
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * PD));
     else if (np == 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(PD));
     else
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     __syncthreads();
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(THREADS) void gemm_decode_kernel(GemmArgs a) {
         if (j < np) {
             compiler_fence();
             if (j + 1 < np)
-                __builtin_amdgcn_s_waitcnt(vmcnt_only(8));    // pair j + 1 may stay in flight
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(PD));   // pair j + 1 may stay in flight
             else
                 __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
             compiler_fence();
@@ -543,9 +550,15 @@ bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t 
            ((M <= MAXM && per <= MAXT) || (M <= 4 * MAXM && per <= MAXT_ROWS));
 }
 
-const char *decode_kernel_name(int row_blocks) {
-    switch (row_blocks) {
-    case 1: return "gemm_decode_kernel<false>";
+const char *decode_kernel_name(int rows) {
+    switch ((rows + MAXM - 1) / MAXM) {
+    case 1:
+        switch ((rows + 7) / 8) {
+        case 1: return "gemm_decode_kernel<1, false>";
+        case 2: return "gemm_decode_kernel<2, false>";
+        case 3: return "gemm_decode_kernel<3, false>";
+        default: return "gemm_decode_kernel<4, false>";
+        }
     case 2: return "gemm_decode_rows_kernel<2, false>";
     case 3: return "gemm_decode_rows_kernel<3, false>";
     default: return "gemm_decode_rows_kernel<4, false>";
@@ -556,8 +569,17 @@ template <bool EXPORT>
 static void launch_decode(const GemmArgs &a, hipStream_t stream) {
     const int blocks = (a.N + BN - 1) / BN;
     const int mb = (a.M + MAXM - 1) / MAXM;
-    if (mb <= 1)
-        hipLaunchKernelGGL(gemm_decode_kernel<EXPORT>, dim3(blocks), dim3(THREADS), 0, stream, a);
+    if (mb <= 1) {
+        const int xi = (a.M + 7) / 8;
+        if (xi <= 1)
+            hipLaunchKernelGGL((gemm_decode_kernel<1, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
+        else if (xi == 2)
+            hipLaunchKernelGGL((gemm_decode_kernel<2, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
+        else if (xi == 3)
+            hipLaunchKernelGGL((gemm_decode_kernel<3, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_decode_kernel<4, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
+    }
     else if (mb == 2)
         hipLaunchKernelGGL((gemm_decode_rows_kernel<2, EXPORT>), dim3(blocks), dim3(THREADS), 0, stream, a);
     else if (mb == 3)

@@ -493,7 +493,7 @@ const char *gemm_kernel_name(const GemmPlan &p) {
     case 1: return p.splits > 1 ? "gemm_kernel<128, 128, 2, 2, 4, false, true>" : "gemm_kernel<128, 128, 2, 2, 4, false, false>";
     case 2: return "gemm_big_kernel";
     case 3: return "gemm_group_kernel<false>";
-    case 4: return decode_kernel_name(p.mb);
+    case 4: return decode_kernel_name(p.rows);
     default: return "unknown";
     }
 }
@@ -508,6 +508,7 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t gro
         p.tiles = ceil_div(N, 32);
         p.splits = 1;
         p.mb = ceil_div(M, 32);
+        p.rows = M;
         return p;
     }
     if (gemm_big_fits(M, N, K_n, n_out, w4a4_num_groups(K_n, group))) {

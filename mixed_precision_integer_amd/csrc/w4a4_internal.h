@@ -70,6 +70,7 @@ struct GemmPlan {
     int tiles;                // output tiles
     int splits;               // K splits per output tile
     int mb;                   // decode: 32-row token blocks (1: gemm_decode_kernel)
+    int rows;                 // decode: token rows
     size_t part_offset;       // byte offset of the fp32 partial sums (counters first)
     size_t part_bytes;        // fp32 partial sums
     size_t workspace_bytes;   // 0 when splits == 1
@@ -93,7 +94,7 @@ hipError_t launch_gemm(const GemmArgs &a, bool export_acc, void *workspace, hipS
 
 // Decode kernels for M <= 128 token rows (gemm_decode.hip).
 bool gemm_decode_fits(int32_t M, int32_t N, int32_t K_n, int32_t n_out, int32_t group);
-const char *decode_kernel_name(int row_blocks);
+const char *decode_kernel_name(int rows);
 hipError_t launch_gemm_decode(const GemmArgs &a, bool export_acc, hipStream_t stream);
 
 // Decode layer call with the quantizer fused in (gemm_decode_fused.hip): at

@@ -288,9 +288,9 @@ def test_device_calls_fail_loudly_without_gpu():
 
 
 @pytest.mark.parametrize("shape,name", [
-    ((1, 8192, 8192, 128, 128), "gemm_decode_kernel<false>"),   # decode batch: weights streamed once
-    ((32, 8192, 8192, 128, 128), "gemm_decode_kernel<false>"),
-    ((16, 256, 256, 16, 0), "gemm_decode_kernel<false>"),       # the tiny per-row layer
+    ((1, 8192, 8192, 128, 128), "gemm_decode_kernel<1, false>"),   # decode batch: weights streamed once
+    ((32, 8192, 8192, 128, 128), "gemm_decode_kernel<4, false>"),
+    ((16, 256, 256, 16, 0), "gemm_decode_kernel<2, false>"),       # the tiny per-row layer
     ((2048, 4096, 4096, 128, 128), "gemm_group_kernel<false>"), # 128-channel groups
     ((2048, 11008, 4096, 256, 0), "gemm_big_kernel"),           # per-row scales, >= 256 large tiles
     ((48, 384, 4224, 128, 128), "gemm_decode_rows_kernel<2, false>"),   # two row blocks
@@ -360,11 +360,11 @@ def test_one_launch_decode_path_bounds():
     producer + GEMM launches (a pure function of the shape)."""
     assert w4.quant_gemm_kernel_name(1, 8192, 8192, 128, 128) == "decode_fused_kernel"
     assert w4.quant_gemm_kernel_name(2, 256, 16384 + 64, 64, 128) == "decode_fused_kernel"
-    assert w4.quant_gemm_kernel_name(3, 256, 1152, 128, 128) == "gemm_decode_kernel<false>"
-    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 0) == "gemm_decode_kernel<false>"
-    assert w4.quant_gemm_kernel_name(2, 256, 1280, 256, 128) == "gemm_decode_kernel<false>"
+    assert w4.quant_gemm_kernel_name(3, 256, 1152, 128, 128) == "gemm_decode_kernel<1, false>"
+    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 0) == "gemm_decode_kernel<1, false>"
+    assert w4.quant_gemm_kernel_name(2, 256, 1280, 256, 128) == "gemm_decode_kernel<1, false>"
     assert w4.quant_gemm_kernel_name(2, 256, 16384 + 256, 128, 128) != "decode_fused_kernel"
-    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 256) == "gemm_decode_kernel<false>"
+    assert w4.quant_gemm_kernel_name(2, 256, 1152, 128, 256) == "gemm_decode_kernel<1, false>"
     assert w4.quant_gemm_kernel_name(2048, 4096, 4096, 128, 128) == w4.outlier_gemm_kernel_name(2048, 4096, 4096, 128, 128)
     assert w4.quant_gemm_kernel_name(0, 256, 1152, 128, 128) is None
 

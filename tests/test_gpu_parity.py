@@ -385,13 +385,13 @@ def test_decode_sweep(oracle, M):
 # Every production kernel class is reached by the cases of this file; the
 # export runs the same plan, so its kernel is the production kernel.
 PRODUCTION_KERNELS = {
-    (16, 256, 256, 16, 0): "gemm_decode_kernel<false>",             # the tiny layer
+    (16, 256, 256, 16, 0): "gemm_decode_kernel<2, false>",             # the tiny layer
     (2048, 4096, 4096, 128, 128): "gemm_group_kernel<false>",       # q_proj prefill
     (4096, 11008, 4096, 256, 0): "gemm_big_kernel",                 # up_proj prefill
     (8192, 8192, 22016, 256, 0): "gemm_big_kernel",                 # down_proj prefill
-    (1, 8192, 8192, 128, 128): "gemm_decode_kernel<false>",         # decode sweep
-    (8, 8192, 8192, 128, 128): "gemm_decode_kernel<false>",
-    (32, 8192, 8192, 128, 128): "gemm_decode_kernel<false>",
+    (1, 8192, 8192, 128, 128): "gemm_decode_kernel<1, false>",         # decode sweep
+    (8, 8192, 8192, 128, 128): "gemm_decode_kernel<1, false>",
+    (32, 8192, 8192, 128, 128): "gemm_decode_kernel<4, false>",
     (128, 8192, 8192, 128, 128): "gemm_decode_rows_kernel<4, false>",
     (256, 8192, 8192, 128, 128): "gemm_kernel<128, 128, 2, 2, 4, false, true>",
 }
