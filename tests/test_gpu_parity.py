@@ -190,6 +190,11 @@ DECODE = [
     (32, 2048, 2176, 128, 128),     # a full 32-row block
     (17, 300, 1536, 0, 0),          # no outlier tail, ragged N
     (9, 96, 8320, 128, 128),        # one workgroup short of columns, 64 groups
+    # token rows moved in runs of eight (XI = ceil(M / 8) DMA instructions per
+    # pair); the slot rows past them hold stale bytes whose results are dropped
+    (13, 256, 2176, 128, 128),      # two runs, the second ragged
+    (24, 520, 4224, 128, 0),        # three full runs, per-row scales, ragged N
+    (27, 64, 8320, 128, 128),       # four runs, the last ragged, 64 groups
     # 32 < M <= 128: two to four row blocks per wave, token fragments from L2
     (48, 384, 4224, 128, 128),      # two blocks, the second ragged
     (64, 1000, 4096, 64, 0),        # two full blocks, per-row scales, ragged N
