@@ -546,8 +546,8 @@ def main():
                     help="instead of the layer, time the low-bit KV cache (quantize + gather)")
     ap.add_argument("--path", default="auto", choices=("auto", "fp6", "i8"),
                     help="prefill GEMM path: fp6 (INT4 codes q as FP6 E2M3 q / 8 on the FP6 matrix cores) or i8 "
-                         "(widened nibbles on the i8 matrix cores); auto takes fp6 where it applies, "
-                         "no RMSNorm is fused and its tiles fill every CU")
+                         "(widened nibbles on the i8 matrix cores); auto takes fp6 where it applies "
+                         "and its tiles fill every CU (with --norm too)")
     ap.add_argument("--norm", action="store_true",
                     help="producer fused with the preceding RMSNorm (eps 1e-6)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -618,16 +618,15 @@ def main():
     fp6_tiles = -(-w.N // 32) if fp6_decode else -(-M // fp6_tile) * -(-w.N // fp6_tile)
     fp6_fits = fp6_name is not None and (M > 128 or fp6_decode)
     fp6_auto = fp6_fits and fp6_tiles >= 256
-    if args.path == "fp6" and (not fp6_fits or args.norm):
-        raise SystemExit("the FP6 path takes per-row scales or 128-channel groups (over 32 rows), "
-                         "no fused RMSNorm")
-    use_fp6 = args.path == "fp6" or (args.path == "auto" and fp6_auto and not args.norm)
+    if args.path == "fp6" and not fp6_fits:
+        raise SystemExit("the FP6 path takes per-row scales or 128-channel groups (over 32 rows)")
+    use_fp6 = args.path == "fp6" or (args.path == "auto" and fp6_auto)
     if use_fp6:
         wf6 = w4.to_fp6(wq)
 
         def clone_fp6(op):
             return w4.Fp6Operand(*[None if t is None else t.clone() for t in op[:4]], *op[4:])
-        plans = [w4.Fp6LayerPlan(Xd.clone(), perm, clone_fp6(wf6)) for _ in range(n_sets)]
+        plans = [w4.Fp6LayerPlan(Xd.clone(), perm, clone_fp6(wf6), norm=norm) for _ in range(n_sets)]
     else:
         plans = [w4.LayerPlan(Xd.clone(), perm, clone_op(wq), norm=norm) for _ in range(n_sets)]
     # Small decode batches run the layer as one launch (the quantizer, and the
@@ -728,18 +727,30 @@ def main():
     roof["traffic"] = traffic_record(w.name, M, roof["kernel"])
 
     # the result is checked: the fused call against producer + GEMM (the same
-    # bits whether the fused call takes one launch or two)
+    # bits whether the fused call takes one launch or two); on the FP6 path
+    # with the norm, the producer's operand against the nibble norm producer's
+    # repacked to u6, and then the fused call without the norm checks the GEMM
     yf = torch.empty_like(plans[0].out)
+    chk = plans[0]
+    if use_fp6 and norm is not None:
+        plans[0].produce()
+        ref = w4.to_fp6(w4.rmsnorm_quant_reorder_act(plans[0]._keep[0], norm[0], norm[1], perm, w.n_out, w.group))
+        torch.cuda.synchronize()
+        got = plans[0].a
+        if not (torch.equal(got.u6, ref.u6) and torch.equal(got.s4, ref.s4) and torch.equal(got.s8, ref.s8)
+                and (got.q8 is None or torch.equal(got.q8, ref.q8))):
+            raise SystemExit("FP6 norm producer and nibble norm producer + repack disagree")
+        chk = w4.Fp6LayerPlan(plans[0]._keep[0], perm, plans[0]._keep[2], out=plans[0].out)
     if use_fp6:
-        w4.quant_gemm_fp6(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
+        w4.quant_gemm_fp6(chk._keep[0], perm, chk._keep[2], out=yf)
     elif norm is None:
         w4.quant_gemm(plans[0]._keep[0], perm, plans[0]._keep[2], out=yf)
     else:
         w4.rmsnorm_quant_gemm(plans[0]._keep[0], norm[0], norm[1], perm, plans[0]._keep[2], out=yf)
-    plans[0].produce()
-    plans[0].gemm()
+    chk.produce()
+    chk.gemm()
     torch.cuda.synchronize()
-    if not torch.equal(yf, plans[0].out):
+    if not torch.equal(yf, chk.out):
         raise SystemExit("fused call and producer + GEMM disagree")
 
     out = {

@@ -298,6 +298,18 @@ w4a4_status w4a4_quant_reorder_act_u6(const void *X, int64_t ldx, const int32_t 
                                       int32_t K, int32_t n_out, int32_t group, void *Au6, void *Aq8,
                                       float *sa4, float *sa8, w4a4_stream stream);
 
+/* The FP6 path's producer fused with the preceding RMSNorm (Atom summary
+ * page, Interesting ideas I2: the quantization fused into the operator in
+ * front of the GEMM): w4a4_rmsnorm_quant_reorder_act with the INT4 head
+ * written as the u6 operand Au6 (as w4a4_quant_reorder_act_u6 writes it).
+ * Codes, scales, rstd and the INT8 tail are those of
+ * w4a4_rmsnorm_quant_reorder_act; Au6 equals w4a4_repack_u6 of its Aq4 byte
+ * for byte. Arguments as those two calls. */
+w4a4_status w4a4_rmsnorm_quant_reorder_act_u6(const void *X, int64_t ldx, const void *gamma, float eps,
+                                              const int32_t *perm, int32_t M, int32_t K, int32_t n_out,
+                                              int32_t group, void *Au6, void *Aq8, float *sa4,
+                                              float *sa8, float *rstd, w4a4_stream stream);
+
 /* Name of the kernel w4a4_outlier_gemm_fp6 launches for this shape (as a
  * kernel trace prints it), or NULL for a shape it rejects. */
 const char *w4a4_outlier_gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out,

@@ -39,7 +39,8 @@ EXPORTED = ("w4a4_status_string", "w4a4_num_groups", "w4a4_pitch4_bytes", "w4a4_
             "w4a4_rmsnorm_quant_reorder_act", "w4a4_rmsnorm_quant_gemm",
             "w4a4_select_outliers_workspace_bytes", "w4a4_select_outliers",
             "w4a4_w4a8_gemm", "w4a4_w4a8_gemm_i32", "w4a4_kv_quant", "w4a4_kv_dequant",
-            "w4a4_u6_bytes", "w4a4_repack_u6", "w4a4_quant_reorder_act_u6", "w4a4_outlier_gemm_fp6_kernel_name",
+            "w4a4_u6_bytes", "w4a4_repack_u6", "w4a4_quant_reorder_act_u6",
+            "w4a4_rmsnorm_quant_reorder_act_u6", "w4a4_outlier_gemm_fp6_kernel_name",
             "w4a4_outlier_gemm_fp6", "w4a4_outlier_gemm_fp6_i32", "w4a4_quant_gemm_fp6_workspace_bytes",
             "w4a4_quant_gemm_fp6", "w4a4_quant_gemm_static_max_bytes", "w4a4_quant_gemm_static")
 
@@ -120,6 +121,9 @@ def lib():
     L.w4a4_repack_u6.restype = ctypes.c_int
     L.w4a4_quant_reorder_act_u6.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.w4a4_quant_reorder_act_u6.restype = ctypes.c_int
+    L.w4a4_rmsnorm_quant_reorder_act_u6.argtypes = [vp, i64, vp, f32, vp, i32, i32, i32, i32, vp, vp,
+                                                    vp, vp, vp, vp]
+    L.w4a4_rmsnorm_quant_reorder_act_u6.restype = ctypes.c_int
     L.w4a4_outlier_gemm_fp6_kernel_name.argtypes = [i32, i32, i32, i32, i32]
     L.w4a4_outlier_gemm_fp6_kernel_name.restype = ctypes.c_char_p
     L.w4a4_outlier_gemm_fp6.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i64, vp]
@@ -495,6 +499,25 @@ def quant_reorder_act_u6(X, perm, n_out: int, group: int = 0, out: Fp6Operand = 
     return a
 
 
+def rmsnorm_quant_reorder_act_u6(X, gamma, eps: float, perm, n_out: int, group: int,
+                                 want_rstd: bool = False):
+    """The FP6 path's producer fused with the preceding RMSNorm: the codes,
+    scales and rstd of rmsnorm_quant_reorder_act, the INT4 head written as a
+    u6 operand. Returns the operand, or (operand, rstd fp32 [M])."""
+    torch = _torch()
+    _check(X, torch.float16, "X", 2)
+    _check(perm, torch.int32, "perm", 1)
+    g, e = _norm_args(X, gamma, eps)
+    M, K = X.shape
+    a = alloc_fp6_operand(M, K, n_out, group, X.device)
+    rstd = torch.empty((M,), dtype=torch.float32, device=X.device) if want_rstd else None
+    _ok(lib().w4a4_rmsnorm_quant_reorder_act_u6(X.data_ptr(), X.stride(0) if M else K, g, e, perm.data_ptr(),
+                                                M, K, n_out, group, a.u6.data_ptr(), _nz(a.q8),
+                                                a.s4.data_ptr(), a.s8.data_ptr(), _nz(rstd), _stream()),
+        "w4a4_rmsnorm_quant_reorder_act_u6")
+    return (a, rstd) if want_rstd else a
+
+
 def alloc_fp6_operand(rows: int, K: int, n_out: int, group: int, device) -> Fp6Operand:
     """Empty device buffers of an FP6-path operand of `rows` rows."""
     torch = _torch()
@@ -758,10 +781,11 @@ class LayerPlan:
 class Fp6LayerPlan:
     """Arguments of one FP6-path layer call, marshalled once (the FP6
     counterpart of LayerPlan): ``produce()`` runs w4a4_quant_reorder_act_u6
-    into pre-allocated operands, ``gemm()`` runs w4a4_outlier_gemm_fp6,
-    ``fused()`` is w4a4_quant_gemm_fp6 (the same launches)."""
+    (w4a4_rmsnorm_quant_reorder_act_u6 with norm = (gamma, eps)) into
+    pre-allocated operands, ``gemm()`` runs w4a4_outlier_gemm_fp6,
+    ``fused()`` is w4a4_quant_gemm_fp6 (the same launches; no norm)."""
 
-    def __init__(self, X, perm, w: Fp6Operand, out=None):
+    def __init__(self, X, perm, w: Fp6Operand, out=None, norm=None):
         torch = _torch()
         _check(X, torch.float16, "X", 2)
         _check(perm, torch.int32, "perm", 1)
@@ -774,9 +798,16 @@ class Fp6LayerPlan:
         self._keep = (X, perm, w)
         L = lib()
         st = _stream()
-        self._q = L.w4a4_quant_reorder_act_u6
-        self._qa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), M, K, w.n_out, w.group,
-                    self.a.u6.data_ptr(), _nz(self.a.q8), _nz(self.a.s4), _nz(self.a.s8), st)
+        if norm is None:
+            self._q, self._qn = L.w4a4_quant_reorder_act_u6, "w4a4_quant_reorder_act_u6"
+            self._qa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), M, K, w.n_out, w.group,
+                        self.a.u6.data_ptr(), _nz(self.a.q8), _nz(self.a.s4), _nz(self.a.s8), st)
+        else:
+            g, e = _norm_args(X, *norm)
+            self._keep = (X, perm, w, norm[0])
+            self._q, self._qn = L.w4a4_rmsnorm_quant_reorder_act_u6, "w4a4_rmsnorm_quant_reorder_act_u6"
+            self._qa = (X.data_ptr(), X.stride(0) if M else K, g, e, perm.data_ptr(), M, K, w.n_out, w.group,
+                        self.a.u6.data_ptr(), _nz(self.a.q8), _nz(self.a.s4), _nz(self.a.s8), None, st)
         self._g, self._ga = L.w4a4_outlier_gemm_fp6, (*_fp6_args(self.a, w, self.out), st)
         self._f = L.w4a4_quant_gemm_fp6
         self._fa = (X.data_ptr(), X.stride(0) if M else K, perm.data_ptr(), _nz(w.u6), _nz(w.q8), _nz(w.s4),
@@ -786,7 +817,7 @@ class Fp6LayerPlan:
     def produce(self):
         st = self._q(*self._qa)
         if st:
-            raise W4A4Error(st, "w4a4_quant_reorder_act_u6")
+            raise W4A4Error(st, self._qn)
 
     def gemm(self):
         st = self._g(*self._ga)

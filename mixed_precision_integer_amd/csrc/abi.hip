@@ -70,8 +70,6 @@ w4a4_status quant_rows(const void *src, int64_t ld, const int32_t *perm, int32_t
         return W4A4_OK;                         // empty call: pointers are not used
     if (!src)                                   // perm may be null: the identity order
         return W4A4_ERR_INVALID_ARG;
-    if (u6 && norm.gamma)
-        return W4A4_ERR_UNSUPPORTED;
     if ((K_n > 0 && (!(u6 ? u6 : q4) || !s4)) || (n_out > 0 && (!q8 || !s8)))
         return W4A4_ERR_INVALID_ARG;
     if (!aligned(src, 16) || ld % 8 != 0 || (perm && !aligned(perm, 16)) || (q4 && !aligned(q4, 16)) ||
@@ -651,6 +649,17 @@ w4a4_status w4a4_quant_reorder_act_u6(const void *X, int64_t ldx, const int32_t 
                                       float *sa8, w4a4_stream stream) {
     return quant_rows(X, ldx, perm, M, K, n_out, group, nullptr, Aq8, sa4, sa8, stream,
                       NormArgs{nullptr, 0.0f, nullptr}, Au6);
+}
+
+w4a4_status w4a4_rmsnorm_quant_reorder_act_u6(const void *X, int64_t ldx, const void *gamma, float eps,
+                                              const int32_t *perm, int32_t M, int32_t K, int32_t n_out,
+                                              int32_t group, void *Au6, void *Aq8, float *sa4, float *sa8,
+                                              float *rstd, w4a4_stream stream) {
+    w4a4_status st = norm_check(M, gamma, eps);
+    if (st != W4A4_OK)
+        return st;
+    return quant_rows(X, ldx, perm, M, K, n_out, group, nullptr, Aq8, sa4, sa8, stream,
+                      NormArgs{gamma, eps, rstd}, Au6);
 }
 
 const char *w4a4_outlier_gemm_fp6_kernel_name(int32_t M, int32_t N, int32_t K, int32_t n_out, int32_t group) {

@@ -274,7 +274,6 @@ template <int KMAX, int THREADS, bool GROUPED, bool WIDE_TAIL, bool NORM, bool F
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS <= 512 && !WIDE_TAIL && !NORM ? (FULL ? 6 : 8) : 4)))
 void quant_rows_kernel(QuantArgs a) {
     static_assert(!(FULL && WIDE_TAIL), "a full-row layout has one tail word per lane");
-    static_assert(!(U6 && NORM), "the u6 head is written without the norm");
     using L = RowLds<KMAX, THREADS>;
     constexpr int NW = THREADS / 64;
     constexpr int UMAX = (KMAX / 8 + THREADS - 1) / THREADS;    // head units (8 channels) per lane
@@ -1305,9 +1304,10 @@ int quant_rows_max_k() { return 24576; }
 hipError_t launch_quant_rows(const QuantArgs &a, hipStream_t stream) {
     if (a.rows == 0)
         return hipSuccess;
-    if (a.u6) {                                   // u6 head (no norm): chunk kernel, else the row kernel
+    if (a.u6) {                                   // u6 head: chunk kernel, else (and with the norm) the row kernel
         if (a.gamma)
-            return hipErrorInvalidValue;
+            return a.group > 0 ? quant_impl::launch_grouping<true, true, true>(a, stream)
+                               : quant_impl::launch_grouping<false, true, true>(a, stream);
         hipError_t err = hipSuccess;
         if (a.group > 0 ? quant_impl::launch_u6_chunk<true>(a, stream, &err)
                         : quant_impl::launch_u6_chunk<false>(a, stream, &err))

@@ -194,3 +194,30 @@ def test_norm_empty_batch():
     op = w4.rmsnorm_quant_reorder_act(X, torch.ones(K, dtype=torch.float16, device=DEV), 1e-6,
                                       perm, 16, 0)
     assert op.q4.shape[0] == 0
+
+
+@pytest.mark.parametrize("rows,K,n_out,group,eps", [c for c in NORM_PRODUCER if c[1] > c[2]] + [
+    (1100, 22016, 256, 0, 1e-6),    # the Llama-65B down_proj rows, several per workgroup
+])
+def test_norm_producer_u6_parity(oracle, rows, K, n_out, group, eps):
+    """The FP6 path's norm producer (w4a4_rmsnorm_quant_reorder_act_u6): the
+    u6 head equals the oracle's pack_u6 of its normalized codes byte for byte
+    (rows past the last one up to the end of their block included), and the
+    rstd, the scales and the INT8 tail equal the oracle's."""
+    _say(f"norm producer u6 rows={rows} K={K} n_out={n_out} group={group} eps={eps}")
+    X, _, o = wl.draw(rows, 1, K, n_out, seed=rows + K + n_out + 17, outlier_factor=30.0)
+    gamma = wl.draw_norm_weight(K, seed=K)
+    perm_h = oracle.make_perm(K, o)
+    perm = torch.from_numpy(perm_h).to(DEV)
+    a, rstd = w4.rmsnorm_quant_reorder_act_u6(to_dev(X), torch.from_numpy(gamma).to(DEV), eps, perm, n_out, group,
+                                              want_rstd=True)
+    q4, s4, q8, s8 = oracle.rmsnorm_quantize_rows(X, gamma, eps, perm_h, n_out, group)
+    r = oracle.rms_rstd(X, eps)
+    torch.cuda.synchronize()
+    assert np.array_equal(u32(rstd.cpu().numpy()), u32(r)), "rstd"
+    assert np.array_equal(a.u6.cpu().numpy(), oracle.pack_u6(q4, pitch4(K - n_out))), "u6 head"
+    if n_out:
+        assert np.array_equal(a.q8.cpu().numpy()[:, :n_out], q8), "INT8 codes"
+        assert not a.q8.cpu().numpy()[:, n_out:].any(), "INT8 padding"
+    assert np.array_equal(u32(a.s4.cpu().numpy().reshape(s4.shape)), u32(s4)), "INT4 scales"
+    assert np.array_equal(u32(a.s8.cpu().numpy()), u32(s8 if n_out else np.zeros(rows, np.float32))), "INT8 scales"
