@@ -288,7 +288,9 @@ def summarize_kernels(d: str, bench_args: str, title: str, out: str) -> str:
             f"{roof['peak']:.0f} {roof['unit']} ({100 * roof['frac']:.1f}%, {roof['bound']}-bound, "
             f"{roof['kernel']})")
     if "kernels" in bj:
-        line += "; " + ", ".join(f"{key} {val:.2f}" for key, val in bj["kernels"].items())
+        # numbers only (the line also carries flags and percentile lists)
+        line += "; " + ", ".join(f"{key} {val:.2f}" for key, val in bj["kernels"].items()
+                                 if isinstance(val, (int, float)) and not isinstance(val, bool))
     L.append(line + ".\n")
     L.append("## HBM traffic (rocprofv3 --pmc, one counter per run)\n")
     cmds = [("FETCH_SIZE", "fetch", f"{run} --steps 5 --warmup 2 --no-cpu-baseline"),
