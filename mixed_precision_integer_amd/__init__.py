@@ -690,12 +690,29 @@ class KVCache:
         return out
 
 
+def fp6_path_fills_chip(M: int, N: int, K: int, n_out: int, group: int, cus: int = 256) -> bool:
+    """Whether the FP6 GEMM takes this shape with at least one workgroup per
+    CU (its 256 x 256 or 128 x 128 tiles over more than 128 rows, or the FP6
+    decode kernel's 32-column stripes): the shapes where it beats the i8 path."""
+    name = outlier_gemm_fp6_kernel_name(M, N, K, n_out, group)
+    if name is None:
+        return False
+    if name.startswith("gemm_fp6_decode_kernel"):
+        return -(-N // 32) >= cus
+    tile = 256 if group == 0 else 128
+    return M > 128 and -(-M // tile) * -(-N // tile) >= cus
+
+
 class W4A4Linear:
     """A linear layer y = x W^T with W held as packed INT4 + INT8 outlier
     columns; with norm_weight (fp16 [K]) the layer first applies the RMSNorm
-    in front of it, fused into its producer."""
+    in front of it, fused into its producer. With fp6=True the layer also
+    keeps the weights as a u6 operand (1.5 times the nibble bytes) and runs
+    the FP6 GEMM for the batch sizes where it fills the chip
+    (fp6_path_fills_chip); other batches keep the i8 path."""
 
-    def __init__(self, weight, outlier_idx, group: int = 0, norm_weight=None, eps: float = 1e-6):
+    def __init__(self, weight, outlier_idx, group: int = 0, norm_weight=None, eps: float = 1e-6,
+                 fp6: bool = False):
         torch = _torch()
         K = weight.shape[1]
         self.outlier_idx = np.asarray(outlier_idx, np.int32)
@@ -703,10 +720,17 @@ class W4A4Linear:
         self.n_out = int(self.outlier_idx.size)
         self.group = group
         self.weight = pack_int4_weights(weight, self.perm, self.n_out, group)
+        self.weight_fp6 = to_fp6(self.weight) if fp6 else None
         self.norm_weight, self.eps = norm_weight, eps
         self._ws = None
 
     def __call__(self, X, out=None):
+        M, N = X.shape[0], self.weight.s8.shape[0]
+        if self.weight_fp6 is not None and fp6_path_fills_chip(M, N, self.weight.K, self.n_out, self.group):
+            if self.norm_weight is None:
+                return quant_gemm_fp6(X, self.perm, self.weight_fp6, out=out)
+            a = rmsnorm_quant_reorder_act_u6(X, self.norm_weight, self.eps, self.perm, self.n_out, self.group)
+            return outlier_gemm_fp6(a, self.weight_fp6, out=out)
         need = quant_gemm_workspace_bytes(X.shape[0], self.weight.s8.shape[0], self.weight.K,
                                           self.n_out, self.group)
         if self._ws is None or self._ws.numel() < need:

@@ -275,3 +275,35 @@ def test_fp6_strided_output(M, N, K, n_out, group, pad, col):
     assert torch.equal(view, ref)
     outside = torch.cat([big[:, :col].flatten(), big[:, col + N:].flatten()])
     assert bool(torch.isnan(outside).all())
+
+
+@pytest.mark.parametrize("M,N,K,n_out,group,norm", [
+    (2048, 4096, 4224, 128, 128, False),   # group kernel (512 tiles)
+    (1024, 4096, 2304, 256, 0, False),     # 256 x 256 kernel (64 tiles: below one per CU, i8 path)
+    (4096, 4096, 2304, 256, 0, True),      # 256 x 256 kernel with the norm in front (256 tiles)
+    (96, 8192, 1152, 128, 128, False),     # FP6 decode kernel (256 stripes)
+    (8, 8192, 1152, 128, 128, False),      # decode batch below the FP6 kernels: i8 path
+])
+def test_layer_object_fp6(M, N, K, n_out, group, norm):
+    """W4A4Linear(fp6=True) runs the FP6 GEMM where it fills the chip: its Y
+    equals the explicit FP6 launches bit for bit there, and the i8 layer's Y
+    within the fp32-order tolerance everywhere."""
+    sys.stderr.write(f"[gpu case] layer object fp6 M={M} N={N} K={K} n_out={n_out} group={group} norm={norm}\n")
+    sys.stderr.flush()
+    X, W, o = wl.draw(M, N, K, n_out, seed=M + N + K, outlier_factor=30.0)
+    Xd, Wd = torch.from_numpy(X).to(DEV), torch.from_numpy(W).to(DEV)
+    g = torch.from_numpy(wl.draw_norm_weight(K, seed=K)).to(DEV) if norm else None
+    layer = w4.W4A4Linear(Wd, o, group, norm_weight=g, fp6=True)
+    ref_layer = w4.W4A4Linear(Wd, o, group, norm_weight=g)
+    y, y_i8 = layer(Xd), ref_layer(Xd)
+    fills = w4.fp6_path_fills_chip(M, N, K, n_out, group)
+    if fills:
+        perm = layer.perm
+        a = (w4.rmsnorm_quant_reorder_act_u6(Xd, g, 1e-6, perm, n_out, group) if norm
+             else w4.quant_reorder_act_u6(Xd, perm, n_out, group))
+        y_fp6 = w4.outlier_gemm_fp6(a, layer.weight_fp6)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_fp6), "the layer's FP6 call"
+    torch.cuda.synchronize()
+    assert fills == ((M, N) != (1024, 4096) and M != 8), "shape classes of the cases"
+    check_y(y.cpu().numpy(), y_i8.cpu().numpy())
