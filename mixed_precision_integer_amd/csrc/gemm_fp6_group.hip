@@ -212,19 +212,21 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
         const float crs = sc[(wm * GWT + lh * 32 + li) * G_SB];
         const float cca = sc[(GBM + wn * GWT + lh * 32 + li) * G_SB];
         const float ccb = sc[(GBM + wn * GWT + (1 - lh) * 32 + li) * G_SB];
-        // pair c: blocks (0, c) in the first half of S, (1, 1 - c) in the second
+        // pair c: blocks (0, c) in the first half of S, (1, c) in the second;
+        // the two MFMAs of each k-step share the weight fragment, so fewer
+        // operand bits change between consecutive MFMAs
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             if (g > 0) {
                 const v32f z = {};
-                const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(c ? pcb : pca, prs, z, 0, 0, 0);
+                const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32((c ^ lh) ? pcb : pca, prs, z, 0, 0, 0);
                 fold(0, c, S, 0, g - 1);
-                fold(1, 1 - c, S, 1, g - 1);
+                fold(1, c, S, 1, g - 1);
             }
             mma0(acc[0][c], fb[0][c], fa[0][0]);
-            mma0(acc[1][1 - c], fb[0][1 - c], fa[0][1]);
+            mma0(acc[1][c], fb[0][c], fa[0][1]);
             mma(acc[0][c], fb[1][c], fa[1][0]);
-            mma(acc[1][1 - c], fb[1][1 - c], fa[1][1]);
+            mma(acc[1][c], fb[1][c], fa[1][1]);
         }
         prs = crs, pca = cca, pcb = ccb;
     }
@@ -233,9 +235,9 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp6_group_kernel(Fp6GemmArgs a
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const v32f z = {};
-        const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(c ? pcb : pca, prs, z, 0, 0, 0);
+        const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32((c ^ lh) ? pcb : pca, prs, z, 0, 0, 0);
         fold(0, c, S, 0, G - 1);
-        fold(1, 1 - c, S, 1, G - 1);
+        fold(1, c, S, 1, G - 1);
     }
 
     // ---- the INT8 tail, staged into the ring once every wave is done with it -----------
